@@ -1,0 +1,46 @@
+"""Dense W8A8 projection -- oracle side (test infrastructure).
+
+FreeToken PR #389, "What this adds": the projection weights are quantised at load time
+to e4m3 with one fp32 scale per tensor, the activation gets one dynamic per-tensor
+scale, and the product runs as an FP8 x FP8 GEMM. The memra-engine ``fp8_ffi`` module
+text adds that the activation and weight scales are folded into one scalar applied to
+the accumulator. So
+
+    y[m, n] = (s_a * s_w) * sum_k dec(qa[m, k]) * dec(qw[n, k])
+
+with both operands K-contiguous (a "TN" GEMM), computed here in float64.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .codec import e4m3_decode
+from .quant import quant_tensor_bf16
+
+
+def quantize_weight(w_bits: np.ndarray):
+    """bf16 weight [N, K] -> (e4m3 codes [N, K], fp32 scale s_w): the per-tensor rule."""
+    q, block = quant_tensor_bf16(w_bits)
+    return q, np.float32(block[2])
+
+
+def dense_w8a8(a_codes, a_scale, w_codes, w_scale, with_bound=False):
+    a = e4m3_decode(a_codes) * float(a_scale)
+    w = e4m3_decode(w_codes) * float(w_scale)
+    y = a @ w.T
+    if with_bound:
+        return y, np.abs(a) @ np.abs(w).T
+    return y
+
+
+def dense_w8a8_entries(a_codes, a_scale, w_codes, w_scale, rows, cols):
+    """Selected outputs y[rows[m], cols[m]] and bounds, one at a time."""
+    y = np.empty(len(rows))
+    b = np.empty(len(rows))
+    for m, (i, n) in enumerate(zip(rows, cols)):
+        a = e4m3_decode(a_codes[i]) * float(a_scale)
+        w = e4m3_decode(w_codes[n]) * float(w_scale)
+        y[m] = float(a @ w)
+        b[m] = float(np.abs(a) @ np.abs(w))
+    return y, b

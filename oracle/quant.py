@@ -1,0 +1,73 @@
+"""Dynamic activation quantisation to e4m3 -- oracle side (test infrastructure).
+
+Two granularities:
+
+* per (token, 128-wide K group): the FP8 grouped-expert prefill note, section 1 ("a
+  per-(token, group) activation scale folded into the accumulator path"); this feeds the
+  grouped expert GEMMs;
+* per tensor: FreeToken PR #389, "What this adds" (a dynamic per-tensor activation
+  scale: an amax pass, then the cast), and the memra-engine ``fp8_ffi`` docs (module
+  text: one scalar scale amax/448); this feeds the dense W8A8 projections and is also the
+  load-time weight quantiser ("e4m3 with one fp32 scale each").
+
+Arithmetic, all in fp32 as the scale block of ``fp8_ffi``'s ``Fp8Scratch`` is fp32:
+  amax  = max |x| over the group (exact; NaN elements are skipped)
+  a     = max(amax, AMAX_FLOOR)
+  s     = fp32(a / 448)        the dequantisation scale (correctly rounded division)
+  inv   = fp32(448 / a)        the quantising multiplier ("quant mul" slot of Fp8Scratch)
+  q     = e4m3(fp32(x * inv))
+Readings: the floor constant is not printed on the pages (PR #389 "Testing" names a
+zero-input scale floor without its value); 1e-12 is used. Quantising multiplies by the
+reciprocal, as the scale block's "quant mul" slot implies, rather than dividing.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .codec import bf16_to_f32, e4m3_encode
+
+AMAX_FLOOR = np.float32(1e-12)
+GROUP = 128
+
+
+def _scale_pair(amax: np.ndarray):
+    a = np.maximum(np.asarray(amax, dtype=np.float32), AMAX_FLOOR)
+    s = (a / np.float32(448.0)).astype(np.float32)
+    inv = (np.float32(448.0) / a).astype(np.float32)
+    return a, s, inv
+
+
+def _amax(x: np.ndarray, axis) -> np.ndarray:
+    ax = np.abs(x)
+    ax = np.where(np.isnan(ax), np.float32(0.0), ax)  # NaN is skipped (maxNum)
+    return ax.max(axis=axis).astype(np.float32)
+
+
+def quant_group(x: np.ndarray, group: int = GROUP):
+    """fp32 activations [M, K] -> (e4m3 codes [M, K], fp32 scales [M, K/group])."""
+    x = np.asarray(x, dtype=np.float32)
+    M, K = x.shape
+    assert K % group == 0
+    xg = x.reshape(M, K // group, group)
+    _, s, inv = _scale_pair(_amax(xg, axis=2))
+    prod = (xg * inv[:, :, None]).astype(np.float32)  # fp32 product, correctly rounded
+    q = e4m3_encode(prod).reshape(M, K)
+    return q, s
+
+
+def quant_tensor(x: np.ndarray):
+    """fp32 tensor -> (e4m3 codes, scale block [amax, inv, s, 0] as fp32[4])."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = _amax(x.reshape(-1), axis=0)
+    _, s, inv = _scale_pair(amax)
+    q = e4m3_encode((x * inv).astype(np.float32))
+    return q, np.array([amax, inv, s, 0.0], dtype=np.float32)
+
+
+def quant_group_bf16(x_bits: np.ndarray, group: int = GROUP):
+    return quant_group(bf16_to_f32(x_bits), group)
+
+
+def quant_tensor_bf16(x_bits: np.ndarray):
+    return quant_tensor(bf16_to_f32(x_bits))

@@ -1,0 +1,91 @@
+"""Pins of the oracle's activation quantiser.
+
+* invariant: in every group whose amax is above the floor the largest element maps to
+  the largest code (|code| = 0x7E), because amax * fp32(448/amax) rounds to 448;
+* special case: an all-zero group gives all 0x00 and s = fp32(1e-12)/448; -0.0 gives 0x80;
+* closed-form error bound: |x - dec(q) * s| <= 2^-4 |x| in e4m3's normal range and
+  <= 2^-10 s in the subnormal range (half a code spacing), up to fp32 scale rounding;
+* library cross-check: torch computes x * inv in fp32 and casts with its own e4m3 encoder;
+* per-tensor mode on a single group equals group mode; the scale block layout.
+"""
+
+import numpy as np
+import torch
+
+from oracle.codec import e4m3_decode
+from oracle.quant import AMAX_FLOOR, quant_group, quant_group_bf16, quant_tensor
+from synth import CONFIGS, bf16_bits_from_f32, f32_from_bf16_bits, moe_inputs
+
+
+def _x(seed=0, shape=(37, 512)):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape).astype(np.float32) * np.exp(rng.uniform(-6, 4, (shape[0], 1)))
+    return f32_from_bf16_bits(bf16_bits_from_f32(x.astype(np.float32)))
+
+
+def test_max_element_maps_to_448():
+    x = _x()
+    q, s = quant_group(x)
+    qg = q.reshape(x.shape[0], -1, 128)
+    assert np.all(np.any((qg & 0x7F) == 0x7E, axis=2))
+    assert np.all((qg & 0x7F) != 0x7F)  # no NaN codes from finite input
+
+
+def test_zero_group_and_signed_zero():
+    x = np.zeros((2, 256), np.float32)
+    x[1, :128] = -0.0
+    x[1, 128:] = np.linspace(-1, 1, 128, dtype=np.float32)
+    q, s = quant_group(x)
+    assert np.all(q[0] == 0x00) and np.all(q[1, :128] == 0x80)
+    assert s[0, 0] == np.float32(np.float32(1e-12) / np.float32(448.0))
+    assert s[0, 0] == s[1, 0] and AMAX_FLOOR == np.float32(1e-12)
+
+
+def test_dequant_error_bound():
+    x = _x(1, (64, 1024))
+    q, s = quant_group(x)
+    deq = e4m3_decode(q).reshape(64, 8, 128) * s[:, :, None].astype(np.float64)
+    xx = x.reshape(64, 8, 128).astype(np.float64)
+    err = np.abs(deq - xx)
+    # x * inv is in the subnormal range when |x| < 2^-6 * s (approximately)
+    sub = np.abs(xx) < (2.0 ** -6) * s[:, :, None]
+    bound = np.where(sub, 2.0 ** -10 * s[:, :, None], 2.0 ** -4 * np.abs(xx))
+    assert np.all(err <= bound * (1 + 1e-6) + 1e-30)
+
+
+def test_matches_torch_fp32_mul_and_cast():
+    inp = moe_inputs(CONFIGS["moe_tiny"])
+    q, s = quant_group_bf16(inp["x"])
+    xt = torch.from_numpy(f32_from_bf16_bits(inp["x"]).copy()).reshape(64, -1, 128)
+    amax = xt.abs().amax(dim=2, keepdim=True).clamp_min(1e-12)
+    inv = torch.tensor(448.0, dtype=torch.float32) / amax
+    ref = torch.clamp(xt * inv, -448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(q, ref.reshape(64, -1).numpy())
+    assert np.array_equal(s, (amax / 448.0).reshape(64, -1).numpy())
+
+
+def test_per_tensor_block_and_single_group_equivalence():
+    x = _x(2, (1, 128))
+    qg, sg = quant_group(x)
+    qt, blk = quant_tensor(x)
+    assert np.array_equal(qg, qt) and blk[2] == sg[0, 0]
+    assert blk[0] == np.abs(x).max() and blk[1] == np.float32(448.0) / blk[0] and blk[3] == 0
+
+
+def test_per_tensor_outlier_channels_set_the_scale():
+    inp_x = _x(3, (16, 256))
+    inp_x[:, 5] *= 20
+    q, blk = quant_tensor(inp_x)
+    assert blk[0] == np.abs(inp_x).max()
+    assert (q.reshape(-1) & 0x7F).max() == 0x7E
+
+
+def test_nan_policy():
+    x = _x(4, (2, 128))
+    x[0, 3] = np.nan
+    q, s = quant_group(x)
+    assert q[0, 3] == 0x7F
+    x2 = x.copy()
+    x2[0, 3] = 0.0
+    q2, s2 = quant_group(x2)
+    assert s[0, 0] == s2[0, 0]  # NaN does not take part in amax
