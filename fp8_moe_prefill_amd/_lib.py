@@ -1,0 +1,230 @@
+"""ctypes binding of ``libfp8moe.so`` (argument marshalling only).
+
+Every function here takes torch tensors that live on a HIP device, checks their dtypes,
+shapes and contiguity, allocates outputs with torch when the caller passes none, and calls
+the C ABI on torch's current stream. All computation happens in the library's HIP kernels;
+there is no CPU path. If the library is missing this module raises at import.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp8moe.so")
+
+GROUP = 128
+DTYPE_F32, DTYPE_BF16 = 0, 1
+EPI_STORE, EPI_SWIGLU_QUANT = 0, 1
+OP_QUANT_ACT, OP_ROUTE_PERMUTE = 0, 1
+
+_c_void_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+SIGNATURES = {
+    "fp8moe_abi_version": (_i32, []),
+    "fp8moe_status_str": (ctypes.c_char_p, [_i32]),
+    "fp8moe_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
+    "fp8_quant_act": (_i32, [_c_void_p, _i64, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _sz,
+                             _c_void_p]),
+    "moe_route_permute": (_i32, [_c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
+                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
+                                 _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "fp8_grouped_expert_gemm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
+                                       _c_void_p, _c_void_p, _i64, _i32, _i64, _i64, _i32, _i32,
+                                       _c_void_p, _c_void_p, _c_void_p]),
+    "fp8_dense_gemm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i32,
+                              _c_void_p, _c_void_p]),
+    "moe_unpermute_combine": (_i32, [_c_void_p, _i32, _c_void_p, _c_void_p, _i64, _i32, _i64,
+                                     _i32, _c_void_p, _c_void_p]),
+}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m fp8_moe_prefill_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = load_library()
+
+
+class Fp8MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} "
+                         f"({_lib.fp8moe_status_str(status).decode()})")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise Fp8MoeError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _dt(dtype) -> int:
+    return {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[dtype]
+
+
+def workspace_bytes(op: int, a: int, b: int, c: int) -> int:
+    n = _lib.fp8moe_workspace_bytes(op, a, b, c)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid workspace query")
+    return n
+
+
+def _workspace(nbytes: int, device, ws=None):
+    if nbytes == 0:
+        return None
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def abi_version() -> int:
+    return _lib.fp8moe_abi_version()
+
+
+# ------------------------------------------------------------------------------------
+# The five entry points
+# ------------------------------------------------------------------------------------
+
+
+def fp8_quant_act(x: torch.Tensor, group: int = GROUP, q=None, scales=None, ws=None,
+                  stream=None):
+    """bf16 [M, K] -> (e4m3 codes uint8 [M, K], fp32 scales [M, K/128] or block[4])."""
+    _dev(x, "x", torch.bfloat16)
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        shape = (M, K // GROUP) if group == GROUP else (4,)
+        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    nbytes = workspace_bytes(OP_QUANT_ACT, M, K, group)
+    wsb = _workspace(nbytes, x.device, ws)
+    _check("fp8_quant_act", _lib.fp8_quant_act(_ptr(x), M, K, group, _ptr(q), _ptr(scales),
+                                               _ptr(wsb), nbytes, _stream(stream)))
+    return q, scales
+
+
+def moe_route_permute(logits: torch.Tensor, k: int, xq=None, xs=None, out=None, ws=None,
+                      stream=None) -> dict:
+    """fp32 logits [T, E] -> dict(ids, weights, offsets, sorted, pos[, xq_perm, xs_perm])."""
+    _dev(logits, "logits", torch.float32)
+    T, E = logits.shape
+    dev = logits.device
+    o = out if out is not None else {}
+    ids = o.get("ids", torch.empty((T, k), dtype=torch.int32, device=dev))
+    w = o.get("weights", torch.empty((T, k), dtype=torch.float32, device=dev))
+    offsets = o.get("offsets", torch.empty(E + 1, dtype=torch.int32, device=dev))
+    sorted_ = o.get("sorted", torch.empty(T * k, dtype=torch.int32, device=dev))
+    pos = o.get("pos", torch.empty(T * k, dtype=torch.int32, device=dev))
+    H = 0
+    xq_perm = xs_perm = None
+    if xq is not None:
+        _dev(xq, "xq", torch.uint8)
+        _dev(xs, "xs", torch.float32)
+        H = xq.shape[1]
+        xq_perm = o.get("xq_perm", torch.empty((T * k, H), dtype=torch.uint8, device=dev))
+        xs_perm = o.get("xs_perm", torch.empty((T * k, H // GROUP), dtype=torch.float32,
+                                               device=dev))
+    nbytes = workspace_bytes(OP_ROUTE_PERMUTE, T, E, k)
+    wsb = _workspace(nbytes, dev, ws)
+    _check("moe_route_permute", _lib.moe_route_permute(
+        _ptr(logits), T, E, k, _ptr(ids), _ptr(w), _ptr(offsets), _ptr(sorted_), _ptr(pos),
+        _ptr(xq), _ptr(xs), H, _ptr(xq_perm), _ptr(xs_perm), _ptr(wsb), nbytes, _stream(stream)))
+    r = dict(ids=ids, weights=w, offsets=offsets, sorted=sorted_, pos=pos)
+    if xq is not None:
+        r.update(xq_perm=xq_perm, xs_perm=xs_perm)
+    return r
+
+
+def fp8_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=EPI_STORE,
+                            out_dtype=torch.float32, sorted_=None, k_route: int = 1, out=None,
+                            out_scales=None, stream=None):
+    """Grouped expert GEMM. STORE -> out [R, N]; SWIGLU_QUANT -> (codes [R, N/2],
+    scales [R, N/256])."""
+    _dev(a, "a", torch.uint8)
+    _dev(a_scales, "a_scales", torch.float32)
+    _dev(w, "w", torch.uint8)
+    _dev(w_scales, "w_scales", torch.float32)
+    _dev(offsets, "offsets", torch.int32)
+    E, N, Kh = w.shape
+    K = Kh * 2
+    dev = a.device
+    if sorted_ is not None:
+        _dev(sorted_, "sorted", torch.int32)
+    if epilogue == EPI_SWIGLU_QUANT:
+        I = N // 2
+        if out is None:
+            out = torch.empty((R, I), dtype=torch.uint8, device=dev)
+        if out_scales is None:
+            out_scales = torch.empty((R, I // GROUP), dtype=torch.float32, device=dev)
+        dt = DTYPE_F32
+    else:
+        if out is None:
+            out = torch.empty((R, N), dtype=out_dtype, device=dev)
+        dt = _dt(out.dtype)
+    _check("fp8_grouped_expert_gemm", _lib.fp8_grouped_expert_gemm(
+        _ptr(a), _ptr(a_scales), _ptr(sorted_), k_route, _ptr(w), _ptr(w_scales), _ptr(offsets),
+        R, E, N, K, epilogue, dt, _ptr(out), _ptr(out_scales), _stream(stream)))
+    return (out, out_scales) if epilogue == EPI_SWIGLU_QUANT else out
+
+
+def fp8_dense_gemm(a, a_scale_blk, w, w_scale, out_dtype=torch.bfloat16, out=None, stream=None):
+    """e4m3 [M, K] x e4m3 [N, K]^T with scales s_a = a_scale_blk[2], s_w = w_scale[0]."""
+    _dev(a, "a", torch.uint8)
+    _dev(w, "w", torch.uint8)
+    _dev(a_scale_blk, "a_scale_blk", torch.float32)
+    _dev(w_scale, "w_scale", torch.float32)
+    M, K = a.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check("fp8_dense_gemm", _lib.fp8_dense_gemm(_ptr(a), _ptr(a_scale_blk), _ptr(w),
+                                                 _ptr(w_scale), M, N, K, _dt(out.dtype),
+                                                 _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_unpermute_combine(y, pos, weights, out_dtype=torch.bfloat16, out=None, stream=None):
+    """out[t] = sum_j weights[t, j] * y[pos[t*k + j]]."""
+    _dev(y, "y")
+    _dev(pos, "pos", torch.int32)
+    _dev(weights, "weights", torch.float32)
+    T, k = weights.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=y.device)
+    _check("moe_unpermute_combine", _lib.moe_unpermute_combine(
+        _ptr(y), _dt(y.dtype), _ptr(pos), _ptr(weights), T, k, H, _dt(out.dtype), _ptr(out),
+        _stream(stream)))
+    return out

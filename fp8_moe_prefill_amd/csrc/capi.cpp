@@ -1,0 +1,162 @@
+// C ABI of the FP8 MoE prefill library: host-side argument validation, then the launch.
+//
+// Every check runs before anything is enqueued, so a failing call has no side effects and
+// its status is known synchronously; none of them reads device memory (no host sync).
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "fp8moe.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+constexpr int64_t kMaxGroupedK = 8192;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t launch_status(hipError_t e) { return e == hipSuccess ? FP8MOE_OK : FP8MOE_ERR_LAUNCH; }
+
+size_t quant_ws(int64_t M, int64_t K, int32_t group) {
+  if (group == 0 && M * K > fp8moe::kQuantFusedMax)
+    return (size_t)fp8moe::kQuantPartials * sizeof(float);
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fp8moe_abi_version(void) { return kAbiVersion; }
+
+const char* fp8moe_status_str(int32_t status) {
+  switch (status) {
+    case FP8MOE_OK: return "ok";
+    case FP8MOE_ERR_NULL: return "a required pointer is NULL";
+    case FP8MOE_ERR_SHAPE: return "a size is out of range or not a required multiple";
+    case FP8MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FP8MOE_ERR_WORKSPACE: return "workspace is smaller than fp8moe_workspace_bytes()";
+    case FP8MOE_ERR_UNSUPPORTED: return "an enum argument has an unknown value";
+    case FP8MOE_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+size_t fp8moe_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c) {
+  if (op == FP8MOE_OP_QUANT_ACT) {
+    if (a < 1 || b < 1 || (c != 0 && c != FP8MOE_GROUP)) return (size_t)-1;
+    return quant_ws(a, b, (int32_t)c);
+  }
+  if (op == FP8MOE_OP_ROUTE_PERMUTE) {
+    if (a < 1 || b < 1 || b > kMaxE || c < 1 || c > b || c > kMaxK) return (size_t)-1;
+    return fp8moe::route_workspace_bytes(a, (int32_t)b);
+  }
+  return (size_t)-1;
+}
+
+int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int32_t group, uint8_t* q,
+                      float* scales, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !q || !scales) return FP8MOE_ERR_NULL;
+  if (group != 0 && group != FP8MOE_GROUP) return FP8MOE_ERR_UNSUPPORTED;
+  if (M < 1 || K < 1 || M > (int64_t(1) << 40) / K) return FP8MOE_ERR_SHAPE;
+  if (group == FP8MOE_GROUP && K % FP8MOE_GROUP != 0) return FP8MOE_ERR_SHAPE;
+  if (group == 0 && (M * K) % 8 != 0) return FP8MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scales)) return FP8MOE_ERR_ALIGN;
+  size_t need = quant_ws(M, K, group);
+  if (need > 0 && (!ws || ws_bytes < need)) return FP8MOE_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return FP8MOE_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (group == FP8MOE_GROUP) return launch_status(fp8moe::launch_quant_group(xb, M, K, q, scales, st));
+  return launch_status(
+      fp8moe::launch_quant_tensor(xb, M * K, q, scales, static_cast<float*>(ws), st));
+}
+
+int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids,
+                          float* weights, int32_t* offsets, int32_t* sorted, int32_t* pos,
+                          const uint8_t* xq, const float* xs, int64_t H, uint8_t* xq_perm,
+                          float* xs_perm, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !ids || !weights || !offsets || !sorted || !pos || !ws) return FP8MOE_ERR_NULL;
+  const bool any_gather = xq || xs || xq_perm || xs_perm;
+  const bool all_gather = xq && xs && xq_perm && xs_perm;
+  if (any_gather && !all_gather) return FP8MOE_ERR_NULL;
+  if (T < 1 || E < 1 || E > kMaxE || k < 1 || k > E || k > kMaxK) return FP8MOE_ERR_SHAPE;
+  if (T * (int64_t)k >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
+  if (all_gather && (H < FP8MOE_GROUP || H % FP8MOE_GROUP != 0)) return FP8MOE_ERR_SHAPE;
+  const void* ptrs[] = {logits, ids, weights, offsets, sorted, pos, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
+  if (all_gather && (!aligned16(xq) || !aligned16(xs) || !aligned16(xq_perm) || !aligned16(xs_perm)))
+    return FP8MOE_ERR_ALIGN;
+  if (ws_bytes < fp8moe::route_workspace_bytes(T, E)) return FP8MOE_ERR_WORKSPACE;
+  return launch_status(fp8moe::launch_route_permute(
+      logits, T, E, k, ids, weights, offsets, sorted, pos, all_gather ? xq : nullptr, xs, H,
+      xq_perm, xs_perm, ws, static_cast<hipStream_t>(stream)));
+}
+
+int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,
+                                int32_t k_route, const uint8_t* w, const float* w_scales,
+                                const int32_t* offsets, int64_t R, int32_t E, int64_t N,
+                                int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
+                                float* out_scales, void* stream) {
+  if (epilogue != FP8MOE_EPI_STORE && epilogue != FP8MOE_EPI_SWIGLU_QUANT)
+    return FP8MOE_ERR_UNSUPPORTED;
+  if (epilogue == FP8MOE_EPI_STORE && out_dtype != FP8MOE_DTYPE_F32 &&
+      out_dtype != FP8MOE_DTYPE_BF16)
+    return FP8MOE_ERR_UNSUPPORTED;
+  if (!a || !a_scales || !w || !w_scales || !offsets || !out) return FP8MOE_ERR_NULL;
+  if (epilogue == FP8MOE_EPI_SWIGLU_QUANT && !out_scales) return FP8MOE_ERR_NULL;
+  if (R < 0 || R >= (int64_t(1) << 31) || E < 1 || E > kMaxE) return FP8MOE_ERR_SHAPE;
+  if (K < FP8MOE_GROUP || K % FP8MOE_GROUP != 0 || K > kMaxGroupedK) return FP8MOE_ERR_SHAPE;
+  if (N < 16 || N >= (int64_t(1) << 24)) return FP8MOE_ERR_SHAPE;
+  if (epilogue == FP8MOE_EPI_STORE && N % 16 != 0) return FP8MOE_ERR_SHAPE;
+  if (epilogue == FP8MOE_EPI_SWIGLU_QUANT && N % 256 != 0) return FP8MOE_ERR_SHAPE;
+  if (sorted && k_route < 1) return FP8MOE_ERR_SHAPE;
+  const void* ptrs[] = {a, a_scales, w, w_scales, offsets, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
+  if ((sorted && !aligned16(sorted)) || (out_scales && !aligned16(out_scales)))
+    return FP8MOE_ERR_ALIGN;
+  if (R == 0) return FP8MOE_OK;
+  return launch_status(fp8moe::launch_grouped_gemm(a, a_scales, sorted, k_route, w, w_scales,
+                                                   offsets, R, E, N, K, epilogue, out_dtype,
+                                                   out, out_scales,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+int32_t fp8_dense_gemm(const uint8_t* a, const float* a_scale_blk, const uint8_t* w,
+                       const float* w_scale, int64_t M, int64_t N, int64_t K, int32_t out_dtype,
+                       void* out, void* stream) {
+  if (out_dtype != FP8MOE_DTYPE_F32 && out_dtype != FP8MOE_DTYPE_BF16)
+    return FP8MOE_ERR_UNSUPPORTED;
+  if (!a || !a_scale_blk || !w || !w_scale || !out) return FP8MOE_ERR_NULL;
+  if (M < 1 || M >= (int64_t(1) << 31) || N < 16 || N % 16 != 0 || N >= (int64_t(1) << 31))
+    return FP8MOE_ERR_SHAPE;
+  if (K < 128 || K % 128 != 0 || K >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
+  const void* ptrs[] = {a, a_scale_blk, w, w_scale, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
+  return launch_status(fp8moe::launch_dense_gemm(a, a_scale_blk, w, w_scale, M, N, K, out_dtype,
+                                                 out, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_unpermute_combine(const void* y, int32_t y_dtype, const int32_t* pos,
+                              const float* weights, int64_t T, int32_t k, int64_t H,
+                              int32_t out_dtype, void* out, void* stream) {
+  if ((y_dtype != FP8MOE_DTYPE_F32 && y_dtype != FP8MOE_DTYPE_BF16) ||
+      (out_dtype != FP8MOE_DTYPE_F32 && out_dtype != FP8MOE_DTYPE_BF16))
+    return FP8MOE_ERR_UNSUPPORTED;
+  if (!y || !pos || !weights || !out) return FP8MOE_ERR_NULL;
+  if (T < 1 || k < 1 || k > kMaxK || H < 8 || H % 8 != 0) return FP8MOE_ERR_SHAPE;
+  if (T * (int64_t)k >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
+  const void* ptrs[] = {y, pos, weights, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
+  return launch_status(fp8moe::launch_combine(y, y_dtype, pos, weights, T, k, H, out_dtype, out,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

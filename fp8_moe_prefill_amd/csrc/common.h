@@ -1,0 +1,87 @@
+// Device helpers shared by the HIP kernels of the FP8 MoE prefill library (gfx950).
+//
+// e4m3 here is OCP e4m3fn: the format the activation scale amax/448 implies (memra-engine
+// fp8_ffi module docs: "f32 -> e4m3 with ONE per-batch scalar scale (amax/448)").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8moe {
+
+constexpr int kGroup = 128;       // K-group of every group-wise scale
+constexpr float kE4m3Max = 448.f;
+constexpr float kAmaxFloor = 1e-12f;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// bf16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+// Scale pair of one quantisation group from its amax: s = a/448 and inv = 448/a with
+// a = max(amax, 1e-12). Both are IEEE divisions (the library is built without fast-math,
+// so '/' is correctly rounded).
+__device__ __forceinline__ void scale_pair(float amax, float& s, float& inv) {
+  float a = fmaxf(amax, kAmaxFloor);
+  s = a / kE4m3Max;
+  inv = kE4m3Max / a;
+}
+
+// Four fp32 values -> four e4m3 bytes (byte i = value i), round to nearest even,
+// saturating to +-448, sign of zero kept, NaN -> 0x7F. The hardware conversion rounds to
+// nearest even but does not saturate, so values are clamped first.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  float ca = __builtin_amdgcn_fmed3f(a, -kE4m3Max, kE4m3Max);
+  float cb = __builtin_amdgcn_fmed3f(b, -kE4m3Max, kE4m3Max);
+  float cc = __builtin_amdgcn_fmed3f(c, -kE4m3Max, kE4m3Max);
+  float cd = __builtin_amdgcn_fmed3f(d, -kE4m3Max, kE4m3Max);
+  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
+  r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, (int)r, true);
+  // NaN policy: 0x7F. (med3 of a NaN input is not guaranteed to stay NaN.)
+  if (a != a) r = (r & 0xFFFFFF00u) | 0x7Fu;
+  if (b != b) r = (r & 0xFFFF00FFu) | 0x7F00u;
+  if (c != c) r = (r & 0xFF00FFFFu) | 0x7F0000u;
+  if (d != d) r = (r & 0x00FFFFFFu) | 0x7F000000u;
+  return r;
+}
+
+// Max over the 16 lanes that share (lane / 16).
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2). Renumber
+// them so that each XCD works through one contiguous range of logical tiles: tiles that
+// share operands then run on the same L2.
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t bid, uint32_t nblocks) {
+  constexpr uint32_t kXcd = 8;
+  uint32_t per = nblocks / kXcd, rem = nblocks % kXcd;
+  uint32_t x = bid % kXcd, i = bid / kXcd;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
+}  // namespace fp8moe

@@ -1,0 +1,158 @@
+// Dynamic activation quantisation bf16 -> e4m3 (fp8_quant_act).
+//
+// Group mode: one scale per (row, 128 columns) -- the per-(token, group) activation scale
+// of "FP8 grouped-expert prefill with on-chip int4-to-e4m3 dequant", section 1.
+// Per-tensor mode: one scale for the whole tensor -- FreeToken PR #389, "What this adds"
+// (an amax pass, then the cast; one fused launch for small tensors, a reduction plus a
+// cast launch above 64k elements, chosen by shape only).
+// Scale rule amax/448: memra-engine fp8_ffi module docs.
+//
+// Both modes are HBM-bound streaming kernels: each thread reads 16 bytes (8 bf16) and
+// writes 8 bytes; a 128-group is the 16 consecutive lanes of a quarter wave, so its amax
+// is a 4-step cross-lane reduction with no LDS and no host synchronisation.
+#include "common.h"
+#include "launch.h"
+
+namespace fp8moe {
+namespace {
+
+struct F8 {
+  float v[8];
+};
+
+__device__ __forceinline__ F8 unpack8(uint4 u) {
+  F8 f;
+  f.v[0] = bf16_lo(u.x); f.v[1] = bf16_hi(u.x);
+  f.v[2] = bf16_lo(u.y); f.v[3] = bf16_hi(u.y);
+  f.v[4] = bf16_lo(u.z); f.v[5] = bf16_hi(u.z);
+  f.v[6] = bf16_lo(u.w); f.v[7] = bf16_hi(u.w);
+  return f;
+}
+
+__device__ __forceinline__ float amax8(const F8& f) {
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f.v[j]));  // fmaxf skips NaN
+  return m;
+}
+
+__device__ __forceinline__ uint2 encode8(const F8& f, float inv) {
+  uint2 r;
+  r.x = e4m3x4(f.v[0] * inv, f.v[1] * inv, f.v[2] * inv, f.v[3] * inv);
+  r.y = e4m3x4(f.v[4] * inv, f.v[5] * inv, f.v[6] * inv, f.v[7] * inv);
+  return r;
+}
+
+// One thread per 8 consecutive elements; 16 threads per 128-group.
+__global__ __launch_bounds__(256) void quant_group_kernel(const uint4* __restrict__ x,
+                                                          int64_t nthreads,
+                                                          uint2* __restrict__ q,
+                                                          float* __restrict__ scales) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  bool valid = i < nthreads;  // nthreads is a multiple of 16: groups are all-or-nothing
+  uint4 u = valid ? x[i] : make_uint4(0, 0, 0, 0);
+  F8 f = unpack8(u);
+  float m = max16(amax8(f));
+  float s, inv;
+  scale_pair(m, s, inv);
+  if (valid) {
+    q[i] = encode8(f, inv);
+    if ((threadIdx.x & 15) == 0) scales[i >> 4] = s;
+  }
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = 0.f;
+  for (int j = 0; j < nw; ++j) r = fmaxf(r, red[j]);
+  __syncthreads();
+  return r;
+}
+
+// Small tensors: one workgroup does the amax pass and the cast.
+__global__ __launch_bounds__(1024) void quant_tensor_fused_kernel(const uint4* __restrict__ x,
+                                                                 int64_t nchunks,
+                                                                 uint2* __restrict__ q,
+                                                                 float* __restrict__ block) {
+  __shared__ float red[16];
+  float m = 0.f;
+  for (int64_t i = threadIdx.x; i < nchunks; i += blockDim.x) m = fmaxf(m, amax8(unpack8(x[i])));
+  float amax = block_max(m, red);
+  float s, inv;
+  scale_pair(amax, s, inv);
+  if (threadIdx.x == 0) {
+    block[0] = amax; block[1] = inv; block[2] = s; block[3] = 0.f;
+  }
+  for (int64_t i = threadIdx.x; i < nchunks; i += blockDim.x) q[i] = encode8(unpack8(x[i]), inv);
+}
+
+// Large tensors, pass 1: per-workgroup partial amax (no atomics: the result does not
+// depend on scheduling order).
+__global__ __launch_bounds__(256) void quant_tensor_amax_kernel(const uint4* __restrict__ x,
+                                                               int64_t nchunks,
+                                                               float* __restrict__ partials) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks;
+       i += (int64_t)gridDim.x * 256)
+    m = fmaxf(m, amax8(unpack8(x[i])));
+  float r = block_max(m, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = r;
+}
+
+// Large tensors, pass 2: every workgroup reduces the partials, then casts its share.
+__global__ __launch_bounds__(256) void quant_tensor_cast_kernel(const uint4* __restrict__ x,
+                                                               int64_t nchunks,
+                                                               const float* __restrict__ partials,
+                                                               int npart, uint2* __restrict__ q,
+                                                               float* __restrict__ block) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int j = threadIdx.x; j < npart; j += 256) m = fmaxf(m, partials[j]);
+  float amax = block_max(m, red);
+  float s, inv;
+  scale_pair(amax, s, inv);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    block[0] = amax; block[1] = inv; block[2] = s; block[3] = 0.f;
+  }
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks;
+       i += (int64_t)gridDim.x * 256)
+    q[i] = encode8(unpack8(x[i]), inv);
+}
+
+}  // namespace
+
+hipError_t launch_quant_group(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
+                              float* scales, hipStream_t st) {
+  int64_t nthreads = M * K / 8;
+  int64_t blocks = (nthreads + 255) / 256;
+  quant_group_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, st>>>(
+      reinterpret_cast<const uint4*>(x), nthreads, reinterpret_cast<uint2*>(q), scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* block,
+                               float* partials, hipStream_t st) {
+  int64_t nchunks = n / 8;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint2* qv = reinterpret_cast<uint2*>(q);
+  if (n <= kQuantFusedMax) {
+    quant_tensor_fused_kernel<<<1, 1024, 0, st>>>(xv, nchunks, qv, block);
+    return hipGetLastError();
+  }
+  int64_t want = (nchunks + 256 * 8 - 1) / (256 * 8);  // ~8 chunks per thread
+  int npart = (int)(want < kQuantPartials ? want : kQuantPartials);
+  quant_tensor_amax_kernel<<<npart, 256, 0, st>>>(xv, nchunks, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t cast_blocks = (nchunks + 255) / 256;
+  if (cast_blocks > 8192) cast_blocks = 8192;
+  quant_tensor_cast_kernel<<<(uint32_t)cast_blocks, 256, 0, st>>>(xv, nchunks, partials, npart,
+                                                                  qv, block);
+  return hipGetLastError();
+}
+
+}  // namespace fp8moe

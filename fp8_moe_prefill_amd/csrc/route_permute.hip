@@ -1,0 +1,237 @@
+// Top-k routing and the grouping of routed (token, expert) pairs by expert
+// (moe_route_permute).
+//
+// "FP8 grouped-expert prefill with on-chip int4-to-e4m3 dequant", section 1, replaces one
+// dispatch per routed token with one grouped expert GEMM per layer. That GEMM needs the
+// routed pairs grouped by expert and each expert's row range, computed on the device so
+// the host never waits for the routing.
+//
+// Design: a stable counting sort with no order-dependent atomics, so every output is a
+// pure function of the logits.
+//   1. topk_hist:  one wave per token selects the top k by (logit desc, expert asc) with
+//                  a 64-lane argmax per pick; a workgroup owns a chunk of 16 tokens and
+//                  counts its pairs per expert in LDS (integer adds commute).
+//   2. chunk_scan: one workgroup per expert scans that expert's per-chunk counts.
+//   3. scatter:    one workgroup per chunk recomputes the expert offsets (a scan over E),
+//                  ranks each pair among the chunk's earlier pairs of the same expert and
+//                  writes sorted[] and pos[].
+//   4. gather:     optional copy of the e4m3 rows and scales into grouped order.
+#include "common.h"
+#include "launch.h"
+
+namespace fp8moe {
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+
+// Inclusive scan of one int per thread over a 256-thread workgroup.
+__device__ __forceinline__ int block_inclusive_scan256(int v, int* tmp /*[4]*/) {
+  int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) tmp[w] = v;
+  __syncthreads();
+  int add = 0;
+  for (int j = 0; j < w; ++j) add += tmp[j];
+  __syncthreads();
+  return v + add;
+}
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict__ logits,
+                                                        int64_t T, int E, int k,
+                                                        int32_t* __restrict__ ids,
+                                                        float* __restrict__ wts,
+                                                        int32_t* __restrict__ cnt) {
+  __shared__ int hist[kMaxE];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+
+  const int nj = (E + 63) / 64;
+  for (int tt = wv; tt < kRouteChunk; tt += 4) {
+    int64_t t = (int64_t)blockIdx.x * kRouteChunk + tt;
+    if (t >= T) break;  // wave-uniform
+    float v[kMaxE / 64];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxE / 64; ++j) {
+      int e = lane + 64 * j;
+      float lv = (j < nj && e < E) ? logits[t * E + e] : -INFINITY;
+      v[j] = lv != lv ? -INFINITY : lv;  // NaN ranks as -inf: every pick stays a valid expert
+    }
+    // lane s keeps the s-th pick
+    float my_v = -INFINITY, top_v = 0.f;
+    int my_i = 0;
+    for (int s = 0; s < k; ++s) {
+      float bv = -INFINITY;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < kMaxE / 64; ++j) {
+        int e = lane + 64 * j;
+        if (j < nj && e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) {
+          bv = v[j];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        float ov = __shfl_xor(bv, o);
+        int oi = __shfl_xor(bi, o);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      // (bv, bi) is now the same on every lane
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (lane == s) {
+        my_v = bv;
+        my_i = bi;
+      }
+      if (s == 0) top_v = bv;
+    }
+    // renormalised softmax over the k picks
+    float ex = lane < k ? expf(my_v - top_v) : 0.f;
+    float sum = ex;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    if (lane < k) {
+      ids[t * k + lane] = my_i;
+      wts[t * k + lane] = ex / sum;
+      atomicAdd(&hist[my_i], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) cnt[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// One workgroup per expert: exclusive scan of its count over the chunks (in place) and
+// the expert's total.
+__global__ __launch_bounds__(256) void chunk_scan_kernel(int32_t* __restrict__ cnt, int64_t C,
+                                                         int E, int32_t* __restrict__ tot) {
+  __shared__ int tmp[4];
+  __shared__ int tile_sum;
+  const int e = blockIdx.x;
+  int carry = 0;
+  for (int64_t base = 0; base < C; base += 256) {
+    int64_t c = base + threadIdx.x;
+    int v = c < C ? cnt[c * E + e] : 0;
+    int inc = block_inclusive_scan256(v, tmp);
+    if (c < C) cnt[c * E + e] = carry + inc - v;
+    if (threadIdx.x == 255) tile_sum = inc;
+    __syncthreads();
+    carry += tile_sum;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) tot[e] = carry;
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ ids,
+                                                      int64_t T, int E, int k,
+                                                      const int32_t* __restrict__ cbase,
+                                                      const int32_t* __restrict__ tot,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ sorted,
+                                                      int32_t* __restrict__ pos) {
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_e[kRouteChunk * kMaxK];
+  __shared__ int tmp[4];
+  // expert offsets: exclusive scan of the totals, 4 experts per thread
+  int loc[4];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int e = threadIdx.x * 4 + j;
+    loc[j] = e < E ? tot[e] : 0;
+    sum += loc[j];
+  }
+  int inc = block_inclusive_scan256(sum, tmp);
+  int run = inc - sum;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int e = threadIdx.x * 4 + j;
+    if (e < E) s_off[e] = run;
+    run += loc[j];
+  }
+  if (threadIdx.x == 255) s_off[E] = inc;  // = T*k
+  const int64_t c = blockIdx.x;
+  const int64_t p0 = c * kRouteChunk * k;
+  int64_t pend = (c + 1) * kRouteChunk;
+  if (pend > T) pend = T;
+  const int np = (int)(pend * k - p0);
+  for (int i = threadIdx.x; i < np; i += 256) s_e[i] = ids[p0 + i];
+  __syncthreads();
+  if (c == 0)
+    for (int e = threadIdx.x; e <= E; e += 256) offsets[e] = s_off[e];
+  for (int i = threadIdx.x; i < np; i += 256) {
+    int e = s_e[i];
+    int rank = 0;
+    for (int j = 0; j < i; ++j) rank += (s_e[j] == e);
+    int row = s_off[e] + cbase[c * E + e] + rank;
+    sorted[row] = (int32_t)(p0 + i);
+    pos[p0 + i] = row;
+  }
+}
+
+// Grouped row i <- token sorted[i] / k: e4m3 row (H bytes) and its H/128 scales.
+__global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ sorted, int k,
+                                                     int64_t R, int64_t H,
+                                                     const uint4* __restrict__ xq,
+                                                     const float* __restrict__ xs,
+                                                     uint4* __restrict__ xq_perm,
+                                                     float* __restrict__ xs_perm) {
+  const int64_t per_row = H / 16;
+  const int64_t G = H / kGroup;
+  int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t row = j / per_row;
+  if (row < R) {
+    int64_t tok = sorted[row] / k;
+    int64_t col = j - row * per_row;
+    xq_perm[j] = xq[tok * per_row + col];
+    if (col < G) xs_perm[row * G + col] = xs[tok * G + col];
+  }
+}
+
+}  // namespace
+
+size_t route_workspace_bytes(int64_t T, int32_t E) {
+  int64_t C = (T + kRouteChunk - 1) / kRouteChunk;
+  size_t n = (size_t)(C * E + E) * sizeof(int32_t);
+  return (n + 255) & ~(size_t)255;
+}
+
+hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
+                                int32_t* ids, float* w, int32_t* offsets, int32_t* sorted,
+                                int32_t* pos, const uint8_t* xq, const float* xs, int64_t H,
+                                uint8_t* xq_perm, float* xs_perm, void* ws, hipStream_t st) {
+  int64_t C = (T + kRouteChunk - 1) / kRouteChunk;
+  int32_t* cnt = static_cast<int32_t*>(ws);
+  int32_t* tot = cnt + C * E;
+  topk_hist_kernel<<<dim3((uint32_t)C), 256, 0, st>>>(logits, T, E, k, ids, w, cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  chunk_scan_kernel<<<dim3((uint32_t)E), 256, 0, st>>>(cnt, C, E, tot);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  scatter_kernel<<<dim3((uint32_t)C), 256, 0, st>>>(ids, T, E, k, cnt, tot, offsets, sorted,
+                                                    pos);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (xq != nullptr) {
+    int64_t R = T * k;
+    int64_t n = R * (H / 16);
+    gather_kernel<<<dim3((uint32_t)((n + 255) / 256)), 256, 0, st>>>(
+        sorted, k, R, H, reinterpret_cast<const uint4*>(xq), xs,
+        reinterpret_cast<uint4*>(xq_perm), xs_perm);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace fp8moe

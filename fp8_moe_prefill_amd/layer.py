@@ -1,0 +1,81 @@
+"""Composition of the C-ABI calls into the MoE prefill layer and a W8A8 projection.
+
+"FP8 grouped-expert prefill with on-chip int4-to-e4m3 dequant", section 1: the MoE layer
+runs the activation quantiser, the routing/grouping, ONE grouped gate|up GEMM (SwiGLU and
+the e4m3 requantisation fused in its epilogue), ONE grouped down GEMM, and the weighted
+combine -- five launches families per layer, no per-token dispatch, no host sync.
+FreeToken PR #389, "What this adds": a W8A8 projection is a per-tensor activation
+quantisation followed by an FP8 x FP8 GEMM with the folded scalar scale.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+
+@dataclass
+class ExpertBank:
+    """Resident expert weights of one MoE layer (device tensors).
+
+    w_gu: packed int4 [E, 2I, H/2] (gate rows 0..I-1, up rows I..2I-1), s_gu fp32
+    [E, 2I, H/128]; w_dn: packed int4 [E, H, I/2], s_dn fp32 [E, H, I/128].
+    """
+
+    w_gu: torch.Tensor
+    s_gu: torch.Tensor
+    w_dn: torch.Tensor
+    s_dn: torch.Tensor
+
+    @property
+    def E(self) -> int:
+        return self.w_gu.shape[0]
+
+    @property
+    def I(self) -> int:
+        return self.w_gu.shape[1] // 2
+
+    @property
+    def H(self) -> int:
+        return self.w_dn.shape[1]
+
+    @staticmethod
+    def from_host(d: dict, device) -> "ExpertBank":
+        return ExpertBank(*(torch.from_numpy(d[n]).to(device) for n in ("w_gu", "s_gu", "w_dn",
+                                                                        "s_dn")))
+
+
+def moe_layer(x: torch.Tensor, logits: torch.Tensor, bank: ExpertBank, k: int,
+              keep: bool = False, stream=None):
+    """bf16 activations [T, H] and fp32 router logits [T, E] -> bf16 [T, H].
+
+    With ``keep`` the intermediate tensors are returned too (for parity checks)."""
+    T = x.shape[0]
+    R = T * k
+    xq, xs = _lib.fp8_quant_act(x, _lib.GROUP, stream=stream)
+    rt = _lib.moe_route_permute(logits, k, stream=stream)
+    hq, hs = _lib.fp8_grouped_expert_gemm(xq, xs, bank.w_gu, bank.s_gu, rt["offsets"], R,
+                                          _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"],
+                                          k_route=k, stream=stream)
+    y = _lib.fp8_grouped_expert_gemm(hq, hs, bank.w_dn, bank.s_dn, rt["offsets"], R,
+                                     _lib.EPI_STORE, out_dtype=torch.bfloat16, stream=stream)
+    out = _lib.moe_unpermute_combine(y, rt["pos"], rt["weights"], torch.bfloat16, stream=stream)
+    if keep:
+        return out, dict(xq=xq, xs=xs, hq=hq, hs=hs, y=y, **rt)
+    return out
+
+
+def quantize_weight(w: torch.Tensor, stream=None):
+    """Load-time per-tensor e4m3 weight (PR #389): bf16 [N, K] -> (codes, s_w [1] fp32)."""
+    q, blk = _lib.fp8_quant_act(w, 0, stream=stream)
+    return q, blk[2:3].clone()
+
+
+def w8a8_linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                out_dtype=torch.bfloat16, stream=None):
+    """bf16 [M, K] activations -> dynamic per-tensor e4m3 -> W8A8 GEMM -> [M, N]."""
+    xq, blk = _lib.fp8_quant_act(x, 0, stream=stream)
+    return _lib.fp8_dense_gemm(xq, blk, wq, w_scale, out_dtype, stream=stream)

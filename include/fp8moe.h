@@ -1,0 +1,219 @@
+/*
+ * fp8moe.h -- C ABI of the FP8 (OCP e4m3fn) MoE prefill library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library computes the hot path of an FP8 grouped-expert MoE prefill layer and the
+ * W8A8 dense projections next to it:
+ *
+ *   fp8_quant_act            bf16 activations -> e4m3 codes + fp32 scales
+ *   moe_route_permute        router logits -> top-k experts, weights, expert offsets,
+ *                            the grouped (permuted) row order
+ *   fp8_grouped_expert_gemm  one launch over all experts: e4m3 rows x packed-int4 bank
+ *                            (dequantised to e4m3 on-chip), scales folded into the fp32
+ *                            accumulator; optional fused SwiGLU + e4m3 requantisation
+ *   fp8_dense_gemm           W8A8 GEMM with per-tensor activation and weight scales
+ *   moe_unpermute_combine    weighted sum of each token's k expert rows
+ *
+ * Sources (by page title and section):
+ *   [P1] "FP8 grouped-expert prefill with on-chip int4-to-e4m3 dequant"
+ *        (octopusresearch.org), section 1 Contribution.
+ *   [P2] FreeToken PR #389 "load-time per-tensor FP8 dense projections (W8A8 via
+ *        _scaled_mm)", sections "What this adds" and "Limits".
+ *   [P4] memra-engine fp8_ffi module docs (docs.rs), module text and struct Fp8Scratch.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major, densely packed, owned by the
+ *     caller. The library never allocates, frees or synchronises; scratch memory is a
+ *     caller-provided workspace whose size fp8moe_workspace_bytes() reports.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues work
+ *     on that stream and returns; there is no device-to-host synchronisation inside any
+ *     call ([P2] "No host sync anywhere"; [P4] "no host sync anywhere"), so every call
+ *     can be captured into a HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued; a non-zero status
+ *     means nothing was launched. Value problems (NaN inputs, all-zero groups) are not
+ *     errors: they follow the documented numeric policy, since checking them would need
+ *     a host sync.
+ *   - bf16 tensors are passed as `const void*` holding IEEE bf16 bit patterns.
+ *   - e4m3 means OCP e4m3fn bytes: max 448, NaN = 0x7F/0xFF, no infinities.
+ *     Quantisation rounds to nearest even, saturates to +-448 and keeps the sign of zero.
+ *   - Alignment: every pointer must be 16-byte aligned.
+ *   - Calls on different streams touching disjoint memory may run concurrently; the
+ *     library keeps no global mutable state.
+ */
+#ifndef FP8MOE_H
+#define FP8MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------------ */
+#define FP8MOE_OK 0
+#define FP8MOE_ERR_NULL (-1)         /* a required pointer is NULL                   */
+#define FP8MOE_ERR_SHAPE (-2)        /* a size is out of range or not a multiple     */
+#define FP8MOE_ERR_ALIGN (-3)        /* a pointer is not 16-byte aligned              */
+#define FP8MOE_ERR_WORKSPACE (-4)    /* workspace smaller than fp8moe_workspace_bytes */
+#define FP8MOE_ERR_UNSUPPORTED (-5)  /* an enum argument has an unknown value         */
+#define FP8MOE_ERR_LAUNCH (-6)       /* the HIP runtime rejected a kernel launch      */
+
+/* ---- enums ------------------------------------------------------------------- */
+#define FP8MOE_GROUP 128             /* the K-group of every group-wise scale        */
+
+#define FP8MOE_DTYPE_F32 0
+#define FP8MOE_DTYPE_BF16 1
+
+#define FP8MOE_EPI_STORE 0           /* write the folded fp32 accumulator            */
+#define FP8MOE_EPI_SWIGLU_QUANT 1    /* h = silu(gate) * up, then e4m3 per (row,128)  */
+
+/* ops for fp8moe_workspace_bytes */
+#define FP8MOE_OP_QUANT_ACT 0
+#define FP8MOE_OP_ROUTE_PERMUTE 1
+
+/* Version of this ABI (bumped on any signature change). */
+int32_t fp8moe_abi_version(void);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* fp8moe_status_str(int32_t status);
+
+/*
+ * fp8moe_workspace_bytes -- device scratch an entry point needs.
+ *   op = FP8MOE_OP_QUANT_ACT:      a = M, b = K, c = group (128 or 0)
+ *   op = FP8MOE_OP_ROUTE_PERMUTE:  a = T, b = E, c = k
+ * Returns 0 for an op that needs none, (size_t)-1 for invalid arguments.
+ */
+size_t fp8moe_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c);
+
+/*
+ * fp8_quant_act -- dynamic activation quantisation to e4m3.
+ *
+ * [P1] section 1: a per-(token, group) activation scale; [P2] "What this adds": a
+ * dynamic per-tensor activation scale (an amax pass, then the cast); [P4] module text:
+ * the scale is amax/448; struct Fp8Scratch: a 4-float block {amax, quant mul, scale}.
+ *
+ *   x       bf16 [M, K]
+ *   group   FP8MOE_GROUP (128): one scale per (row, 128 consecutive columns);
+ *           0: one scale for the whole tensor
+ *   q       out, e4m3 [M, K]
+ *   scales  out; group=128: fp32 [M, K/128], scale of (row m, group g) at m*K/128 + g;
+ *           group=0: fp32[4] = {amax, 448/a, a/448, 0} with a = max(amax, 1e-12)
+ *   ws      workspace of fp8moe_workspace_bytes(FP8MOE_OP_QUANT_ACT, M, K, group)
+ *           bytes (may be NULL if that is 0)
+ * Arithmetic (fp32): a = max(max|x| over the group, 1e-12); s = a/448 and
+ * inv = 448/a, both correctly rounded; q = e4m3(x * inv). NaN inputs encode to 0x7F
+ * and are skipped by the amax.
+ * Constraints: M >= 1, K >= 1; group=128 needs K % 128 == 0; group=0 needs
+ * M*K % 8 == 0.
+ */
+int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int32_t group, uint8_t* q,
+                      float* scales, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_permute -- top-k routing and grouping of the routed (token, expert) pairs.
+ *
+ * [P1] section 1: per-token expert dispatch is replaced by one grouped GEMM per layer,
+ * which needs the routed pairs grouped by expert with per-expert row offsets computed
+ * on the device (no host round trip).
+ *
+ *   logits   fp32 [T, E]
+ *   ids      out, int32 [T, k]: experts of token t by descending logit; equal logits
+ *            go to the lower expert index first
+ *   weights  out, fp32 [T, k]: softmax over the k selected logits (the top-k
+ *            renormalised softmax)
+ *   offsets  out, int32 [E+1]: expert e owns grouped rows offsets[e] .. offsets[e+1]-1;
+ *            offsets[0] = 0, offsets[E] = T*k
+ *   sorted   out, int32 [T*k]: grouped row i holds pair p = sorted[i] = t*k + j; within
+ *            an expert pairs keep increasing p (a stable order)
+ *   pos      out, int32 [T*k]: pos[p] = the grouped row of pair p
+ *   xq, xs, H      optional (all NULL/0 or all set): e4m3 [T, H] rows and fp32
+ *                  [T, H/128] scales to gather into grouped order
+ *   xq_perm, xs_perm  out when gathering: e4m3 [T*k, H], fp32 [T*k, H/128]
+ *   ws       workspace of fp8moe_workspace_bytes(FP8MOE_OP_ROUTE_PERMUTE, T, E, k)
+ * Constraints: T >= 1, 1 <= E <= 1024, 1 <= k <= min(E, 32), T*k < 2^31;
+ * H % 128 == 0 when gathering. Every output is a pure function of the inputs (no
+ * order-dependent atomics), so repeated calls give identical bytes.
+ */
+int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
+                          int32_t* ids, float* weights, int32_t* offsets, int32_t* sorted,
+                          int32_t* pos, const uint8_t* xq, const float* xs, int64_t H,
+                          uint8_t* xq_perm, float* xs_perm, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * fp8_grouped_expert_gemm -- one launch over every expert.
+ *
+ * [P1] section 1: a single grouped expert GEMM per layer; int4 weights turned into
+ * e4m3 on-chip without unpacking the resident packed-int4 bank; the per-(token, group)
+ * activation scale folded into the accumulator.
+ *
+ * For grouped row i in expert e's range [offsets[e], offsets[e+1]) and column n:
+ *   y[i, n] = sum_g a_scales[r, g] * w_scales[e, n, g]
+ *                   * sum_{k in group g} e4m3(a[r, k]) * int4(w[e, n, k])
+ * with r = i, or r = sorted[i] / k_route when `sorted` is given (the A rows are then
+ * gathered on the fly from token order and no permuted copy is needed).
+ *
+ *   a          e4m3 [Ra, K]  (Ra = R without `sorted`, Ra = R / k_route with it)
+ *   a_scales   fp32 [Ra, K/128]
+ *   sorted     NULL, or int32 [R] pair ids from moe_route_permute
+ *   k_route    experts per token (used only with `sorted`)
+ *   w          packed int4 [E, N, K/2]: byte b of row (e, n) holds k = 2b in its low
+ *              nibble and k = 2b+1 in its high nibble, two's complement -8..7
+ *   w_scales   fp32 [E, N, K/128]
+ *   offsets    int32 [E+1] on the device (from moe_route_permute), offsets[E] = R
+ *   R          total grouped rows (the host-side bound; not read back from offsets)
+ *   epilogue   FP8MOE_EPI_STORE: out is [R, N] in out_dtype (fp32 or bf16, RNE);
+ *              FP8MOE_EPI_SWIGLU_QUANT: N = 2I with gate columns 0..I-1 and up columns
+ *              I..2I-1; h = silu(gate) * up in fp32 is quantised like fp8_quant_act
+ *              (group 128) into out = e4m3 [R, I] and out_scales = fp32 [R, I/128]
+ * Constraints: R >= 0 (R = 0 is a no-op), 1 <= E <= 1024, K % 128 == 0, K >= 128;
+ * STORE: N % 16 == 0; SWIGLU_QUANT: N % 256 == 0.
+ */
+int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales,
+                                const int32_t* sorted, int32_t k_route, const uint8_t* w,
+                                const float* w_scales, const int32_t* offsets, int64_t R,
+                                int32_t E, int64_t N, int64_t K, int32_t epilogue,
+                                int32_t out_dtype, void* out, float* out_scales,
+                                void* stream);
+
+/*
+ * fp8_dense_gemm -- W8A8 projection y = (s_a * s_w) * (qa . qw^T).
+ *
+ * [P2] "What this adds": e4m3 weights with one fp32 scale per tensor, a dynamic
+ * per-tensor activation scale, an FP8 x FP8 GEMM; [P4] module text: the two scales are
+ * folded into one device scalar, with no host sync.
+ *
+ *   a            e4m3 [M, K] (from fp8_quant_act with group = 0)
+ *   a_scale_blk  fp32[4] scale block from fp8_quant_act; element 2 (s_a) is used
+ *   w            e4m3 [N, K]
+ *   w_scale      fp32[1] on the device, s_w
+ *   out          [M, N] fp32 or bf16 (RNE) per out_dtype
+ * Constraints: M >= 1, N % 16 == 0, K % 128 == 0.
+ */
+int32_t fp8_dense_gemm(const uint8_t* a, const float* a_scale_blk, const uint8_t* w,
+                       const float* w_scale, int64_t M, int64_t N, int64_t K,
+                       int32_t out_dtype, void* out, void* stream);
+
+/*
+ * moe_unpermute_combine -- out[t, :] = sum_{j=0..k-1} weights[t, j] * y[pos[t*k+j], :]
+ *
+ * [P1] section 1: the grouped GEMM's rows are returned to token order and weighted by
+ * the router. The sum runs in fp32 in increasing j; no atomics, so the result is
+ * deterministic.
+ *
+ *   y        [T*k, H] in y_dtype (fp32 or bf16), grouped order
+ *   pos      int32 [T*k] from moe_route_permute
+ *   weights  fp32 [T, k]
+ *   out      [T, H] in out_dtype (fp32 or bf16, RNE)
+ * Constraints: T >= 1, 1 <= k <= 32, H % 8 == 0.
+ */
+int32_t moe_unpermute_combine(const void* y, int32_t y_dtype, const int32_t* pos,
+                              const float* weights, int64_t T, int32_t k, int64_t H,
+                              int32_t out_dtype, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8MOE_H */

@@ -7,7 +7,7 @@ grouped by expert, with per-expert row offsets, so one launch can cover every ex
 Readings where the pages are silent:
 * selection is by fp32 logit, descending; equal logits go to the lower expert index
   first (softmax is monotone, so this is the same set as selecting by probability, and
-  it avoids ties that softmax rounding would create);
+  it avoids ties that softmax rounding would create); a NaN logit ranks as -inf;
 * the weights are the softmax renormalised over the selected k experts, which equals
   the full softmax renormalised over the top k;
 * pairs are numbered p = t*k + j; within an expert, pairs keep increasing p order (a
@@ -22,6 +22,7 @@ import numpy as np
 def topk_route(logits: np.ndarray, k: int):
     """fp32 logits [T, E] -> (ids int32 [T, k], weights float64 [T, k])."""
     lg = np.asarray(logits, dtype=np.float32)
+    lg = np.where(np.isnan(lg), np.float32(-np.inf), lg)
     T, E = lg.shape
     assert 1 <= k <= E
     ids = np.empty((T, k), dtype=np.int32)

@@ -1,0 +1,157 @@
+"""The C-ABI library on the CPU: it loads, exports every function ``include/fp8moe.h``
+declares, and rejects bad arguments on the host before touching the GPU.
+
+No call here reaches a kernel launch: each one fails a host-side check first (the
+pointers passed are never dereferenced).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8moe.h")
+LIB = os.path.join(ROOT, "fp8_moe_prefill_amd", "libfp8moe.so")
+
+OK, NULL, SHAPE, ALIGN, WS, UNSUP = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int32_t|size_t|const char\*)\s+(\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built (python -m fp8_moe_prefill_amd.build)")
+    from fp8_moe_prefill_amd._lib import load_library
+    return load_library(LIB)
+
+
+def test_header_declares_the_five_entry_points():
+    fns = declared_functions()
+    for name in ["fp8_quant_act", "moe_route_permute", "fp8_grouped_expert_gemm",
+                 "fp8_dense_gemm", "moe_unpermute_combine"]:
+        assert name in fns
+    assert "fp8moe_workspace_bytes" in fns and "fp8moe_status_str" in fns
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert lib.fp8moe_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for s in range(-6, 1):
+        assert lib.fp8moe_status_str(s)
+    assert lib.fp8moe_status_str(-99) == b"unknown status"
+
+
+def test_workspace_queries(lib):
+    assert lib.fp8moe_workspace_bytes(0, 64, 256, 128) == 0
+    assert lib.fp8moe_workspace_bytes(0, 2048, 4096, 0) == 4096
+    assert lib.fp8moe_workspace_bytes(0, 8, 8, 0) == 0  # fused single-workgroup path
+    n = lib.fp8moe_workspace_bytes(1, 4096, 64, 8)
+    assert n >= (4096 // 16) * 64 * 4 and n % 256 == 0
+    bad = ctypes.c_size_t(-1).value
+    assert lib.fp8moe_workspace_bytes(1, 16, 2000, 8) == bad  # E > 1024
+    assert lib.fp8moe_workspace_bytes(1, 16, 8, 9) == bad  # k > E
+    assert lib.fp8moe_workspace_bytes(0, 16, 100, 64) == bad
+    assert lib.fp8moe_workspace_bytes(7, 1, 1, 1) == bad
+
+
+P = 0x1000  # aligned dummy device address, never dereferenced
+U = 0x1004  # misaligned
+
+
+def test_quant_act_validation(lib):
+    f = lib.fp8_quant_act
+    assert f(None, 4, 128, 128, P, P, None, 0, None) == NULL
+    assert f(P, 4, 128, 64, P, P, None, 0, None) == UNSUP
+    assert f(P, 0, 128, 128, P, P, None, 0, None) == SHAPE
+    assert f(P, 4, 100, 128, P, P, None, 0, None) == SHAPE
+    assert f(P, 3, 3, 0, P, P, None, 0, None) == SHAPE  # M*K % 8
+    assert f(U, 4, 128, 128, P, P, None, 0, None) == ALIGN
+    assert f(P, 2048, 4096, 0, P, P, None, 0, None) == WS
+    assert f(P, 2048, 4096, 0, P, P, P, 100, None) == WS
+
+
+def _route(lib, logits=P, T=16, E=8, k=2, ws=P, ws_bytes=1 << 20, xq=None, xs=None, H=0,
+           xqp=None, xsp=None, ids=P):
+    return lib.moe_route_permute(logits, T, E, k, ids, P, P, P, P, xq, xs, H, xqp, xsp, ws,
+                                 ws_bytes, None)
+
+
+def test_route_validation(lib):
+    assert _route(lib, logits=None) == NULL
+    assert _route(lib, ws=None) == NULL
+    assert _route(lib, xq=P) == NULL  # gather arguments must come together
+    assert _route(lib, T=0) == SHAPE
+    assert _route(lib, E=0) == SHAPE
+    assert _route(lib, E=1025, k=2) == SHAPE
+    assert _route(lib, k=0) == SHAPE
+    assert _route(lib, E=4, k=5) == SHAPE
+    assert _route(lib, E=64, k=33) == SHAPE
+    assert _route(lib, T=1 << 28, k=8) == SHAPE  # T*k >= 2^31
+    assert _route(lib, xq=P, xs=P, xqp=P, xsp=P, H=100) == SHAPE
+    assert _route(lib, ids=U) == ALIGN
+    assert _route(lib, ws_bytes=16) == WS
+
+
+def _gg(lib, a=P, R=256, E=8, N=512, K=256, epi=0, dt=0, out_scales=P, sorted_=None, kr=1,
+        out=P):
+    return lib.fp8_grouped_expert_gemm(a, P, sorted_, kr, P, P, P, R, E, N, K, epi, dt, out,
+                                       out_scales, None)
+
+
+def test_grouped_gemm_validation(lib):
+    assert _gg(lib, epi=2) == UNSUP
+    assert _gg(lib, dt=3) == UNSUP
+    assert _gg(lib, a=None) == NULL
+    assert _gg(lib, epi=1, out_scales=None) == NULL
+    assert _gg(lib, R=-1) == SHAPE
+    assert _gg(lib, E=0) == SHAPE
+    assert _gg(lib, E=1025) == SHAPE
+    assert _gg(lib, K=100) == SHAPE
+    assert _gg(lib, K=0) == SHAPE
+    assert _gg(lib, K=16384) == SHAPE
+    assert _gg(lib, N=24) == SHAPE
+    assert _gg(lib, epi=1, N=384) == SHAPE  # SwiGLU needs N % 256 == 0
+    assert _gg(lib, sorted_=P, kr=0) == SHAPE
+    assert _gg(lib, out=U) == ALIGN
+    assert _gg(lib, R=0) == OK  # empty input is a no-op; nothing is launched
+
+
+def test_dense_gemm_validation(lib):
+    f = lib.fp8_dense_gemm
+    assert f(P, P, P, P, 16, 64, 128, 5, P, None) == UNSUP
+    assert f(None, P, P, P, 16, 64, 128, 0, P, None) == NULL
+    assert f(P, P, P, P, 0, 64, 128, 0, P, None) == SHAPE
+    assert f(P, P, P, P, 16, 24, 128, 0, P, None) == SHAPE
+    assert f(P, P, P, P, 16, 64, 96, 0, P, None) == SHAPE
+    assert f(P, P, U, P, 16, 64, 128, 0, P, None) == ALIGN
+
+
+def test_combine_validation(lib):
+    f = lib.moe_unpermute_combine
+    assert f(P, 2, P, P, 4, 2, 64, 1, P, None) == UNSUP
+    assert f(None, 1, P, P, 4, 2, 64, 1, P, None) == NULL
+    assert f(P, 1, P, P, 0, 2, 64, 1, P, None) == SHAPE
+    assert f(P, 1, P, P, 4, 33, 64, 1, P, None) == SHAPE
+    assert f(P, 1, P, P, 4, 2, 60, 1, P, None) == SHAPE
+    assert f(P, 1, U, P, 4, 2, 64, 1, P, None) == ALIGN
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    import fp8_moe_prefill_amd as f
+    with pytest.raises(ValueError):
+        f.fp8_quant_act(torch.zeros((4, 128), dtype=torch.bfloat16))

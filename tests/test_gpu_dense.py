@@ -1,0 +1,72 @@
+"""fp8_dense_gemm (and the per-tensor quantiser feeding it) on the GPU vs the oracle.
+
+Shapes: M = 1, 16, 300 (FreeToken PR #389, "Testing": the op against the dequantised
+weight at M=1/16/300) and the full 2048 x 4096 x {6144, 4096} projections, sampled.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.dense import dense_w8a8, dense_w8a8_entries, quantize_weight
+from oracle.numeric import bf16_bits, round_bf16
+from oracle.quant import quant_tensor_bf16
+from oracle.tol import check_close, gemm_bound
+from synth import CONFIGS, bf16_bits_from_f32, dense_inputs
+from tests.gpu_util import assert_bytes_equal, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(x_bits, w_bits, out_dtype=torch.float32):
+    import fp8_moe_prefill_amd as f
+    wq, sw = f.quantize_weight(dev(w_bits))
+    xq, blk = f.fp8_quant_act(dev(x_bits), 0)
+    y = f.fp8_dense_gemm(xq, blk, wq, sw, out_dtype)
+    torch.cuda.synchronize()
+    return host(y), host(xq), host(blk), host(wq), host(sw)
+
+
+@pytest.mark.parametrize("M", [1, 16, 300])
+def test_small_m(M):
+    inp = dense_inputs(CONFIGS["dense_w8a8"], M=M)
+    w = inp["w_qkv"][:528]  # N = 528: a ragged last tile
+    y, xq, blk, wq, sw = _gpu(inp["x"], w)
+    rq, rblk = quant_tensor_bf16(inp["x"])
+    rwq, rsw = quantize_weight(w)
+    assert_bytes_equal(xq, rq, "activation codes")
+    assert_bytes_equal(wq, rwq, "weight codes")
+    assert sw[0] == rsw
+    ref, b = dense_w8a8(rq, rblk[2], rwq, rsw, with_bound=True)
+    check_close(y.astype(np.float64), ref, gemm_bound(b), f"dense M={M}")
+
+
+def test_identity_weight():
+    K = 512
+    w = bf16_bits_from_f32(np.eye(K, dtype=np.float32))
+    x = bf16_bits_from_f32(np.random.default_rng(0).standard_normal((33, K)).astype(np.float32))
+    y, xq, blk, wq, sw = _gpu(x, w)
+    from oracle.codec import e4m3_decode
+    ref = e4m3_decode(xq) * float(blk[2])
+    assert np.allclose(y, ref, rtol=2e-7, atol=0)
+
+
+def test_bf16_output_is_rounded_fp32_output():
+    inp = dense_inputs(CONFIGS["dense_w8a8"], M=300)
+    y32 = _gpu(inp["x"], inp["w_o"][:256], torch.float32)[0]
+    y16 = _gpu(inp["x"], inp["w_o"][:256], torch.bfloat16)[0]
+    assert_bytes_equal(y16, bf16_bits(round_bf16(y32.astype(np.float64))), "bf16 = RNE(fp32)")
+
+
+@pytest.mark.parametrize("which", ["w_qkv", "w_o"])
+def test_full_size_sampled(which):
+    inp = dense_inputs(CONFIGS["dense_w8a8"])
+    x = inp["x"] if which == "w_qkv" else inp["x_o"]
+    y, xq, blk, wq, sw = _gpu(x, inp[which])
+    rq, rblk = quant_tensor_bf16(x)
+    assert_bytes_equal(xq, rq, "activation codes")
+    rng = np.random.default_rng(5)
+    rows = rng.integers(0, y.shape[0], 3000)
+    cols = rng.integers(0, y.shape[1], 3000)
+    ref, b = dense_w8a8_entries(rq, rblk[2], wq, sw[0], rows, cols)
+    check_close(y[rows, cols].astype(np.float64), ref, gemm_bound(b), f"dense {which}")

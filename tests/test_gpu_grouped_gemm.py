@@ -1,0 +1,199 @@
+"""fp8_grouped_expert_gemm on the GPU vs the oracle.
+
+Floating outputs: |gpu - oracle| <= 1e-3 * sum_k |a_k w_k| + 1e-6 per element (fp32
+output); the bf16 output equals the fp32 output rounded to nearest even, bit for bit.
+SwiGLU + requantisation: checked against the oracle's SwiGLU applied to the GPU's own fp32
+gate/up accumulators (same kernel, same accumulation order), where a code may differ only
+by one step and only next to a rounding midpoint.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.codec import e4m3_decode, e4m3_encode
+from oracle.moe import grouped_gemm, grouped_gemm_rows, swiglu
+from oracle.numeric import bf16_bits
+from oracle.numeric import round_bf16
+from oracle.quant import quant_group, quant_group_bf16
+from oracle.route import group_pairs, permute_rows, topk_route
+from oracle.tol import check_close, gemm_bound
+from synth import CONFIGS, moe_inputs
+from tests.gpu_util import assert_bytes_equal, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import fp8_moe_prefill_amd as f
+    return f
+
+
+def _problem(counts, K, N, seed=0, scale_spread=True):
+    rng = np.random.default_rng(seed)
+    R = int(sum(counts))
+    E = len(counts)
+    x = rng.standard_normal((R, K)).astype(np.float32)
+    if scale_spread:
+        x *= rng.uniform(0.01, 30, (R, 1)).astype(np.float32)
+    aq, as_ = quant_group(x)
+    wp = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    ws = rng.uniform(0.005, 0.02, size=(E, N, K // 128)).astype(np.float32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return aq, as_, wp, ws, off
+
+
+def _gemm(aq, as_, wp, ws, off, out_dtype=torch.float32, sorted_=None, k_route=1, R=None):
+    f = _lib()
+    R = aq.shape[0] if R is None else R
+    y = f.fp8_grouped_expert_gemm(dev(aq), dev(as_), dev(wp), dev(ws), dev(off), R,
+                                  f.EPI_STORE, out_dtype,
+                                  sorted_=None if sorted_ is None else dev(sorted_),
+                                  k_route=k_route)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("counts,K,N", [
+    ([0, 37, 130, 1, 200], 256, 512),      # empty, ragged, single-row experts
+    ([128, 128], 128, 256),                 # exact tiles, one K group
+    ([300], 384, 48),                       # one expert, N not a multiple of 64
+    ([5, 0, 0, 261, 17, 64, 0, 9], 1024, 272),
+])
+def test_store_f32_within_bound(counts, K, N):
+    aq, as_, wp, ws, off = _problem(counts, K, N, seed=K + N)
+    y = host(_gemm(aq, as_, wp, ws, off)).astype(np.float64)
+    ref, b = grouped_gemm(aq, as_, wp, ws, off, with_bound=True)
+    check_close(y, ref, gemm_bound(b), "grouped gemm fp32")
+
+
+def test_bf16_output_is_rounded_fp32_output():
+    aq, as_, wp, ws, off = _problem([40, 0, 300, 77], 512, 256, seed=3)
+    y32 = host(_gemm(aq, as_, wp, ws, off, torch.float32)).astype(np.float64)
+    y16 = host(_gemm(aq, as_, wp, ws, off, torch.bfloat16))
+    assert_bytes_equal(y16, bf16_bits(round_bf16(y32)), "bf16 = RNE(fp32)")
+
+
+def test_integer_operands_exact():
+    """Integer activations (exact in e4m3) with unit scales: every partial sum is an
+    integer below 2^24, so the fp32 result must be exact."""
+    rng = np.random.default_rng(4)
+    R, K, N = 200, 512, 128
+    aq = e4m3_encode(rng.integers(-16, 17, size=(R, K)).astype(np.float64))
+    as_ = np.ones((R, K // 128), np.float32)
+    wp = rng.integers(0, 256, size=(3, N, K // 2), dtype=np.uint8)
+    ws = np.ones((3, N, K // 128), np.float32)
+    off = np.array([0, 60, 61, R], np.int32)
+    y = host(_gemm(aq, as_, wp, ws, off)).astype(np.float64)
+    ref = grouped_gemm(aq, as_, wp, ws, off)
+    assert np.array_equal(y, ref)
+
+
+def test_on_the_fly_gather_equals_permuted_copy():
+    """Rows gathered from token order through `sorted` give the same bits as a GEMM on
+    the explicitly permuted activations."""
+    c = CONFIGS["moe_tiny"]
+    inp = moe_inputs(c)
+    xq, xs = quant_group_bf16(inp["x"])
+    ids, _ = topk_route(inp["logits"], c.k)
+    off, sorted_, _ = group_pairs(ids, c.E)
+    R = c.T * c.k
+    y_gather = host(_gemm(xq, xs, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k,
+                          R=R))
+    aq = permute_rows(xq, sorted_, c.k)
+    as_ = permute_rows(xs, sorted_, c.k)
+    y_perm = host(_gemm(aq, as_, inp["w_gu"], inp["s_gu"], off))
+    assert_bytes_equal(y_gather.view(np.uint32), y_perm.view(np.uint32), "gather vs permuted")
+    ref, b = grouped_gemm(aq, as_, inp["w_gu"], inp["s_gu"], off, with_bound=True)
+    check_close(y_perm.astype(np.float64), ref, gemm_bound(b), "tiny gate|up")
+
+
+def _swiglu_check(hq, hs, y_gu32):
+    """Codes/scales of the SwiGLU epilogue vs the oracle's SwiGLU on the GPU's own fp32
+    gate|up accumulators."""
+    h = swiglu(y_gu32.astype(np.float64)).astype(np.float32)
+    rq, rs = quant_group(h)
+    # scales: exact unless the amax element's h differs in its last bits (fp32 silu)
+    ds = np.abs(hs.astype(np.float64) - rs) / rs
+    assert ds.max() <= 4e-6, ds.max()
+    same = hq == rq
+    frac = same.mean()
+    assert frac >= 0.999, frac
+    if not same.all():
+        i = np.nonzero(~same)
+        # adjacent codes only (same sign; code indices one apart)
+        def idx(c):  # position on the signed code line; +0 and -0 coincide
+            c = c.astype(np.int64)
+            return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+        assert np.all(np.abs(idx(hq[i]) - idx(rq[i])) <= 1)
+        # and the oracle's pre-quantisation value sits next to the midpoint of the two
+        G = hs.shape[1]
+        hg = h.reshape(h.shape[0], G, 128)
+        amax = np.maximum(np.abs(hg).max(axis=2), np.float32(1e-12)).astype(np.float32)
+        inv = (np.float32(448.0) / amax).astype(np.float32)
+        u = (hg * inv[:, :, None]).astype(np.float32).reshape(h.shape)[i].astype(np.float64)
+        mid = 0.5 * (e4m3_decode(hq[i]) + e4m3_decode(rq[i]))
+        assert np.all(np.abs(np.abs(u) - np.abs(mid)) <= 1e-5 * np.abs(u) + 1e-9)
+
+
+@pytest.mark.parametrize("cfg", ["moe_tiny", "moe_prefill"])
+def test_swiglu_quant_epilogue(cfg):
+    c = CONFIGS[cfg]
+    inp = moe_inputs(c)
+    f = _lib()
+    xq, xs = quant_group_bf16(inp["x"])
+    ids, _ = topk_route(inp["logits"], c.k)
+    off, sorted_, _ = group_pairs(ids, c.E)
+    R = c.T * c.k
+    args = (dev(xq), dev(xs), dev(inp["w_gu"]), dev(inp["s_gu"]), dev(off), R)
+    hq, hs = f.fp8_grouped_expert_gemm(*args, f.EPI_SWIGLU_QUANT, sorted_=dev(sorted_),
+                                       k_route=c.k)
+    y32 = f.fp8_grouped_expert_gemm(*args, f.EPI_STORE, torch.float32, sorted_=dev(sorted_),
+                                    k_route=c.k)
+    torch.cuda.synchronize()
+    _swiglu_check(host(hq), host(hs), host(y32))
+
+
+def test_gate_up_full_size_sampled():
+    """Gate|up GEMM of the 4096-token, 64-expert layer (fp32 out) on 4000 sampled outputs,
+    each computed by the oracle one at a time."""
+    c = CONFIGS["moe_prefill"]
+    inp = moe_inputs(c)
+    xq, xs = quant_group_bf16(inp["x"])
+    ids, _ = topk_route(inp["logits"], c.k)
+    off, sorted_, _ = group_pairs(ids, c.E)
+    R = c.T * c.k
+    y = host(_gemm(xq, xs, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k, R=R))
+    rng = np.random.default_rng(11)
+    rows = rng.integers(0, R, 4000)
+    cols = rng.integers(0, 2 * c.I, 4000)
+    rows[:64] = off[1:65] - 1  # last row of every expert
+    aq = permute_rows(xq, sorted_, c.k)
+    as_ = permute_rows(xs, sorted_, c.k)
+    ref, b = grouped_gemm_rows(aq, as_, inp["w_gu"], inp["s_gu"], off, rows, cols)
+    check_close(y[rows, cols].astype(np.float64), ref, gemm_bound(b), "gate|up sampled")
+
+
+def test_down_full_size_sampled():
+    """Down GEMM (K = 768) of the same layer on the GPU's own intermediate codes."""
+    c = CONFIGS["moe_prefill"]
+    inp = moe_inputs(c)
+    f = _lib()
+    rng = np.random.default_rng(12)
+    R = c.T * c.k
+    counts = np.bincount(rng.integers(0, c.E, R), minlength=c.E)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    h = (rng.standard_normal((R, c.I)) * rng.uniform(0.1, 10, (R, 1))).astype(np.float32)
+    hq, hs = quant_group(h)
+    y = host(_gemm(hq, hs, inp["w_dn"], inp["s_dn"], off, torch.float32))
+    rows = rng.integers(0, R, 4000)
+    cols = rng.integers(0, c.H, 4000)
+    ref, b = grouped_gemm_rows(hq, hs, inp["w_dn"], inp["s_dn"], off, rows, cols)
+    check_close(y[rows, cols].astype(np.float64), ref, gemm_bound(b), "down sampled")
+
+
+def test_repeat_runs_identical():
+    aq, as_, wp, ws, off = _problem([100, 3, 250], 256, 256, seed=9)
+    a = host(_gemm(aq, as_, wp, ws, off))
+    b = host(_gemm(aq, as_, wp, ws, off))
+    assert_bytes_equal(a.view(np.uint32), b.view(np.uint32), "repeat")

@@ -1,0 +1,99 @@
+"""The whole MoE layer (quantise, route, gate|up + SwiGLU + requantise, down, combine)
+through the C ABI vs the oracle.
+
+Stage by stage on identical inputs: quantiser bytes and routing indices bit-exact; the
+down GEMM and the combine checked on the GPU's own intermediate codes, so the strict
+bounds apply; the final output additionally compared to the oracle's end-to-end result
+through the element bound of the combine (each row's own rounding included).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.moe import combine, grouped_gemm, grouped_gemm_rows, moe_layer
+from oracle.numeric import cosine
+from oracle.quant import quant_group_bf16
+from oracle.route import group_pairs, topk_route
+from oracle.tol import check_close, gemm_bound, half_ulp_bf16
+from synth import CONFIGS, moe_inputs
+from tests.gpu_util import assert_bytes_equal, bf16_values, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_layer(cfg, T=None):
+    import fp8_moe_prefill_amd as f
+    c = CONFIGS[cfg]
+    inp = moe_inputs(c, T=T)
+    bank = f.ExpertBank.from_host(inp, "cuda:0")
+    out, st = f.moe_layer(dev(inp["x"]), dev(inp["logits"]), bank, c.k, keep=True)
+    torch.cuda.synchronize()
+    return c, inp, out, st
+
+
+def test_tiny_layer_all_outputs():
+    c, inp, out, st = _gpu_layer("moe_tiny")
+    ref = moe_layer(inp["x"], inp["logits"], inp["w_gu"], inp["s_gu"], inp["w_dn"],
+                    inp["s_dn"], c.k)
+    assert_bytes_equal(host(st["xq"]), ref["xq"], "xq")
+    assert_bytes_equal(host(st["ids"]), ref["ids"], "ids")
+    assert_bytes_equal(host(st["offsets"]), ref["offsets"], "offsets")
+    assert_bytes_equal(host(st["sorted"]), ref["sorted"], "sorted")
+    assert_bytes_equal(host(st["pos"]), ref["pos"], "pos")
+    # down GEMM on the GPU's own intermediate codes
+    hq, hs = host(st["hq"]), host(st["hs"])
+    y_ref, b = grouped_gemm(hq, hs, inp["w_dn"], inp["s_dn"], ref["offsets"], with_bound=True)
+    y = bf16_values(st["y"])
+    check_close(y, y_ref, gemm_bound(b) + half_ulp_bf16(y_ref), "down (bf16 out)")
+    # combine on the GPU's own rows and weights
+    o_ref = combine(y, host(st["pos"]), host(st["weights"]).astype(np.float64))
+    mag = combine(np.abs(y), host(st["pos"]), host(st["weights"]).astype(np.float64))
+    check_close(bf16_values(out), o_ref, 1e-6 * mag + half_ulp_bf16(o_ref), "combine")
+    # end to end: the oracle's layer output vs the GPU's
+    assert cosine(bf16_values(out), ref["out"]) > 0.999
+
+
+@pytest.mark.parametrize("cfg", ["moe_prefill", "moe_skewed"])
+def test_full_layer_sampled(cfg):
+    c, inp, out, st = _gpu_layer(cfg)
+    xq, xs = quant_group_bf16(inp["x"])
+    assert_bytes_equal(host(st["xq"]), xq, "xq")
+    assert_bytes_equal(host(st["xs"]).view(np.uint32), xs.view(np.uint32), "xs")
+    ids, w = topk_route(inp["logits"], c.k)
+    off, sorted_, pos = group_pairs(ids, c.E)
+    assert_bytes_equal(host(st["ids"]), ids, "ids")
+    assert_bytes_equal(host(st["offsets"]), off, "offsets")
+    assert_bytes_equal(host(st["sorted"]), sorted_, "sorted")
+    assert_bytes_equal(host(st["pos"]), pos, "pos")
+    if cfg == "moe_skewed":
+        assert (np.diff(off) == 0).sum() >= 1
+    # down GEMM, sampled, on the GPU's intermediate codes
+    hq, hs = host(st["hq"]), host(st["hs"])
+    y = st["y"]
+    R = c.T * c.k
+    rng = np.random.default_rng(21)
+    rows = rng.integers(0, R, 2000)
+    cols = rng.integers(0, c.H, 2000)
+    yr, b = grouped_gemm_rows(hq, hs, inp["w_dn"], inp["s_dn"], off, rows, cols)
+    ys = y[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].float().cpu().numpy()
+    check_close(ys.astype(np.float64), yr, gemm_bound(b) + half_ulp_bf16(yr), "down sampled")
+    # combine on sampled tokens
+    toks = rng.integers(0, c.T, 64)
+    yv = bf16_values(y)
+    o = bf16_values(out)
+    wv = host(st["weights"]).astype(np.float64)
+    p = host(st["pos"]).reshape(c.T, c.k)
+    for t in toks:
+        ref = sum(wv[t, j] * yv[p[t, j]] for j in range(c.k))
+        mag = sum(abs(wv[t, j]) * np.abs(yv[p[t, j]]) for j in range(c.k))
+        check_close(o[t], ref, 1e-6 * mag + half_ulp_bf16(ref), "combine sampled")
+
+
+def test_layer_repeat_runs_identical():
+    _, _, out1, st1 = _gpu_layer("moe_prefill", T=512)
+    _, _, out2, st2 = _gpu_layer("moe_prefill", T=512)
+    for n in ("xq", "hq", "hs", "y", "sorted", "pos"):
+        a, b = host(st1[n]), host(st2[n])
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), n
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))

@@ -1,0 +1,97 @@
+"""moe_route_permute on the GPU vs the oracle: ids, offsets, sorted, pos and the gathered
+rows bit-exact; weights within 1e-5 relative."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.route import group_pairs, permute_rows, topk_route
+from synth import CONFIGS, moe_inputs
+from tests.gpu_util import assert_bytes_equal, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_route(logits, k, xq=None, xs=None):
+    import fp8_moe_prefill_amd as f
+    r = f.moe_route_permute(dev(logits), k, xq=None if xq is None else dev(xq),
+                            xs=None if xs is None else dev(xs))
+    torch.cuda.synchronize()
+    return {n: host(t) for n, t in r.items()}
+
+
+def _check(logits, k, gpu):
+    E = logits.shape[1]
+    ids, w = topk_route(logits, k)
+    off, sorted_, pos = group_pairs(ids, E)
+    assert_bytes_equal(gpu["ids"], ids, "ids")
+    assert_bytes_equal(gpu["offsets"], off, "offsets")
+    assert_bytes_equal(gpu["sorted"], sorted_, "sorted")
+    assert_bytes_equal(gpu["pos"], pos, "pos")
+    err = np.abs(gpu["weights"].astype(np.float64) - w)
+    assert np.all(err <= 1e-5 * w + 1e-7), err.max()
+    return ids, off, sorted_, pos
+
+
+@pytest.mark.parametrize("cfg", ["moe_tiny", "moe_prefill", "moe_skewed"])
+def test_config_routing(cfg):
+    c = CONFIGS[cfg]
+    from synth.inputs import router_logits
+    logits = router_logits(c.seed, f"{c.name}.logits", c.T, c.E, c.zipf_s)
+    gpu = _gpu_route(logits, c.k)
+    _, off, _, _ = _check(logits, c.k, gpu)
+    if cfg == "moe_skewed":
+        assert (np.diff(off) == 0).sum() >= 1  # some experts receive no rows
+
+
+def test_ties_and_degenerate_shapes():
+    rng = np.random.default_rng(0)
+    lg = np.round(rng.standard_normal((37, 16))).astype(np.float32)  # many exact ties
+    lg[3] = 0.0  # all equal
+    lg[4, :] = -0.0
+    lg[4, 7] = 0.0
+    _check(lg, 4, _gpu_route(lg, 4))
+    _check(lg, 16, _gpu_route(lg, 16))  # k = E
+    one = rng.standard_normal((5, 1)).astype(np.float32)
+    _check(one, 1, _gpu_route(one, 1))  # E = 1
+    t1 = rng.standard_normal((1, 64)).astype(np.float32)
+    _check(t1, 8, _gpu_route(t1, 8))  # T = 1
+
+
+@pytest.mark.parametrize("E,k", [(1024, 8), (200, 32), (65, 3)])
+def test_wide_expert_counts(E, k):
+    rng = np.random.default_rng(E)
+    lg = rng.standard_normal((50, E)).astype(np.float32)
+    _check(lg, k, _gpu_route(lg, k))
+
+
+def test_one_hot_expert_and_empty_experts():
+    lg = np.full((300, 32), -5.0, np.float32)
+    lg[:, 3] = 5.0  # every token's first choice
+    lg[:, 9] = 4.0
+    gpu = _gpu_route(lg, 2)
+    _, off, _, _ = _check(lg, 2, gpu)
+    counts = np.diff(off)
+    assert counts[3] == 300 and counts[9] == 300 and counts.sum() == 600
+
+
+def test_gather_rows_and_scales():
+    c = CONFIGS["moe_tiny"]
+    rng = np.random.default_rng(1)
+    xq = rng.integers(0, 256, size=(c.T, c.H), dtype=np.uint8)
+    xs = rng.uniform(0.001, 1, size=(c.T, c.H // 128)).astype(np.float32)
+    logits = moe_inputs(c)["logits"]
+    gpu = _gpu_route(logits, c.k, xq, xs)
+    _, _, sorted_, _ = _check(logits, c.k, gpu)
+    assert_bytes_equal(gpu["xq_perm"], permute_rows(xq, sorted_, c.k), "gathered rows")
+    assert_bytes_equal(gpu["xs_perm"].view(np.uint32), permute_rows(xs, sorted_, c.k).view(np.uint32),
+                       "gathered scales")
+
+
+def test_repeat_runs_identical():
+    c = CONFIGS["moe_prefill"]
+    logits = moe_inputs(c)["logits"]
+    a = _gpu_route(logits, c.k)
+    b = _gpu_route(logits, c.k)
+    for n in a:
+        assert np.array_equal(a[n].view(np.uint8), b[n].view(np.uint8)), n
