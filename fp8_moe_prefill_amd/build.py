@@ -27,7 +27,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-fno-gpu-rdc",
           # packed fp32 VALU ops off (see the library's numerics notes)
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math"]
+          "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
+          # MFMA in its VGPR form (C/D in VGPRs), so the VALU fold reads the MFMA result
+          # without accumulator-register copies
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc() -> str:

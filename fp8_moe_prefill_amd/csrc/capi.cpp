@@ -14,7 +14,7 @@ namespace {
 constexpr int32_t kAbiVersion = 1;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
-constexpr int64_t kMaxGroupedK = 8192;
+constexpr int64_t kMaxGroupedK = 4096;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -115,6 +115,7 @@ int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales, const i
   if (epilogue == FP8MOE_EPI_STORE && N % 16 != 0) return FP8MOE_ERR_SHAPE;
   if (epilogue == FP8MOE_EPI_SWIGLU_QUANT && N % 256 != 0) return FP8MOE_ERR_SHAPE;
   if (sorted && k_route < 1) return FP8MOE_ERR_SHAPE;
+  if (R * K >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;  // 32-bit A row offsets
   const void* ptrs[] = {a, a_scales, w, w_scales, offsets, out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FP8MOE_ERR_ALIGN;

@@ -158,8 +158,9 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
  *   a_scales   fp32 [Ra, K/128]
  *   sorted     NULL, or int32 [R] pair ids from moe_route_permute
  *   k_route    experts per token (used only with `sorted`)
- *   w          packed int4 [E, N, K/2]: byte b of row (e, n) holds k = 2b in its low
- *              nibble and k = 2b+1 in its high nibble, two's complement -8..7
+ *   w          packed int4 [E, N, K/2], two's complement -8..7. Each little-endian
+ *              32-bit word j of row (e, n) holds k = 8j..8j+7: its byte b (0..3) has
+ *              k = 8j+b in the low nibble and k = 8j+4+b in the high nibble
  *   w_scales   fp32 [E, N, K/128]
  *   offsets    int32 [E+1] on the device (from moe_route_permute), offsets[E] = R
  *   R          total grouped rows (the host-side bound; not read back from offsets)
@@ -167,8 +168,8 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
  *              FP8MOE_EPI_SWIGLU_QUANT: N = 2I with gate columns 0..I-1 and up columns
  *              I..2I-1; h = silu(gate) * up in fp32 is quantised like fp8_quant_act
  *              (group 128) into out = e4m3 [R, I] and out_scales = fp32 [R, I/128]
- * Constraints: R >= 0 (R = 0 is a no-op), 1 <= E <= 1024, K % 128 == 0, K >= 128;
- * STORE: N % 16 == 0; SWIGLU_QUANT: N % 256 == 0.
+ * Constraints: R >= 0 (R = 0 is a no-op), 1 <= E <= 1024, K % 128 == 0,
+ * 128 <= K <= 4096, R*K < 2^32; STORE: N % 16 == 0; SWIGLU_QUANT: N % 256 == 0.
  */
 int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales,
                                 const int32_t* sorted, int32_t k_route, const uint8_t* w,

@@ -121,7 +121,8 @@ def test_grouped_gemm_validation(lib):
     assert _gg(lib, E=1025) == SHAPE
     assert _gg(lib, K=100) == SHAPE
     assert _gg(lib, K=0) == SHAPE
-    assert _gg(lib, K=16384) == SHAPE
+    assert _gg(lib, K=8192) == SHAPE
+    assert _gg(lib, R=1 << 22, K=2048) == SHAPE  # R*K >= 2^32
     assert _gg(lib, N=24) == SHAPE
     assert _gg(lib, epi=1, N=384) == SHAPE  # SwiGLU needs N % 256 == 0
     assert _gg(lib, sorted_=P, kr=0) == SHAPE
