@@ -1,0 +1,191 @@
+"""Benchmark of the FP8 MoE prefill hot path on one MI355X.
+
+A step is one MoE prefill layer -- activation quantisation, top-k routing and grouping,
+the grouped gate|up GEMM with fused SwiGLU + requantisation, the grouped down GEMM, and
+the weighted combine -- over the 4096-token workload (hidden 2048, 64 experts, top-8,
+intermediate 768, packed-int4 experts with group-128 scales). Inputs are synthetic and
+already resident in HBM; three copies of the weight bank and of the inputs are rotated so
+the 151 MB bank cannot stay in the 256 MB Infinity Cache between steps.
+
+Prints one JSON line: MoE prefill tokens/s for the whole layer, plus the roofline of the
+dominant kernel (the grouped gate|up GEMM, FP8 MFMA bound) measured with HIP events on the
+launch stream inside the timed region, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] [--dense]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "grouped FP8 expert GEMM TFLOP/s (% FP8 MFMA peak); MoE prefill tokens/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_gate_up_moe_prefill_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "fp8_moe_prefill_amd", "csrc", "grouped_gemm.hip")
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dense", action="store_true",
+                    help="also time the W8A8 dense projections (2048 x 4096 x {6144, 4096})")
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    return ap.parse_args()
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_per_launch():
+    """HBM bytes per gate|up launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs, or None when the kernel source changed after they were taken."""
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != source_hash(GEMM_SOURCE):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(n_tokens: int):
+    """The NumPy oracle on the first n_tokens tokens of the same layer (same weights)."""
+    import numpy as np  # noqa: F401
+
+    from oracle.moe import moe_layer
+    from synth import CONFIGS, moe_inputs
+
+    c = CONFIGS["moe_prefill"]
+    inp = moe_inputs(c, T=n_tokens)
+    t0 = time.perf_counter()
+    moe_layer(inp["x"], inp["logits"], inp["w_gu"], inp["s_gu"], inp["w_dn"], inp["s_dn"], c.k)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"the NumPy fp64 oracle MoE layer on the first {n_tokens} of the 4096 "
+                      f"tokens (all 64 experts), {dt:.1f} s"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the multi-GPU expert-parallel path is not built", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_moe_prefill_amd as f
+    from synth import CONFIGS, dense_inputs, moe_inputs
+
+    dev = torch.device("cuda:0")
+    c = CONFIGS["moe_prefill"]
+    ROT = 3
+    xs, lgs, banks = [], [], []
+    for r in range(ROT):
+        inp = moe_inputs(c, seed=r)
+        xs.append(torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16))
+        lgs.append(torch.from_numpy(inp["logits"]).to(dev))
+        banks.append(f.ExpertBank.from_host(inp, dev))
+    runner = f.MoELayerRunner(c.T, c.H, c.E, c.k, c.I, dev)
+    R = c.T * c.k
+
+    for i in range(args.warmup):
+        runner.run(xs[i % ROT], lgs[i % ROT], banks[i % ROT])
+    torch.cuda.synchronize()
+
+    stages = f.MoELayerRunner.STAGES
+    ev = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for s in stages} for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        runner.run(xs[i % ROT], lgs[i % ROT], banks[i % ROT], events=ev[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    per = {s: float(np.mean([e[s][0].elapsed_time(e[s][1]) for e in ev])) for s in stages}
+
+    flop_gu = 4.0 * R * c.H * c.I
+    flop_dn = 2.0 * R * c.I * c.H
+    gu_tflops = flop_gu / (per["gate_up"] * 1e-3) / 1e12
+    gemm_tflops = (flop_gu + flop_dn) / ((per["gate_up"] + per["down"]) * 1e-3) / 1e12
+    traffic = traffic_per_launch()
+
+    out = {
+        "metric": METRIC,
+        "value": c.T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": "moe_prefill: one MoE prefill layer, T=4096 tokens, hidden 2048, "
+                               "64 experts, top-8, intermediate 768 (SwiGLU), packed int4 "
+                               "experts with group-128 fp32 scales, e4m3 activations with "
+                               "per-(token,128) scales",
+                   "tokens": c.T, "hidden": c.H, "experts": c.E, "top_k": c.k,
+                   "intermediate": c.I, "weight_banks_rotated": ROT},
+        "grouped_gemm": {"tflops": gemm_tflops, "frac_fp8_peak": gemm_tflops / PEAK_FP8_TFLOPS,
+                         "gate_up_us": per["gate_up"] * 1e3, "down_us": per["down"] * 1e3},
+        "stages_us": {s: per[s] * 1e3 for s in stages},
+        "roofline": {"kernel": "grouped_gemm gate|up (+SwiGLU+requant)", "bound": "mfma",
+                     "achieved": gu_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gu_tflops / PEAK_FP8_TFLOPS, "traffic": traffic,
+                     "algorithmic_flop_per_launch": flop_gu},
+    }
+
+    if args.dense:
+        d = dense_inputs(CONFIGS["dense_w8a8"])
+        x = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+        res = {}
+        for wn in ("w_qkv", "w_o"):
+            w = torch.from_numpy(d[wn].view(np.int16)).to(dev).view(torch.bfloat16)
+            wq, sw = f.quantize_weight(w)
+            xq, blk = f.fp8_quant_act(x, 0)
+            y = f.fp8_dense_gemm(xq, blk, wq, sw)
+            for _ in range(3):
+                f.fp8_dense_gemm(xq, blk, wq, sw, out=y)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(20):
+                f.fp8_dense_gemm(xq, blk, wq, sw, out=y)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / 20 * 1e3
+            fl = 2.0 * x.shape[0] * w.shape[0] * x.shape[1]
+            res[wn] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12}
+        out["dense_w8a8"] = res
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

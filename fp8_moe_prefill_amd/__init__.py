@@ -11,4 +11,4 @@ from ._lib import (  # noqa: F401
     abi_version, fp8_dense_gemm, fp8_grouped_expert_gemm, fp8_quant_act, moe_route_permute,
     moe_unpermute_combine, workspace_bytes,
 )
-from .layer import ExpertBank, moe_layer, quantize_weight, w8a8_linear  # noqa: F401
+from .layer import ExpertBank, MoELayerRunner, moe_layer, quantize_weight, w8a8_linear  # noqa: F401

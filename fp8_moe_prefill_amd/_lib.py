@@ -142,20 +142,23 @@ def moe_route_permute(logits: torch.Tensor, k: int, xq=None, xs=None, out=None, 
     T, E = logits.shape
     dev = logits.device
     o = out if out is not None else {}
-    ids = o.get("ids", torch.empty((T, k), dtype=torch.int32, device=dev))
-    w = o.get("weights", torch.empty((T, k), dtype=torch.float32, device=dev))
-    offsets = o.get("offsets", torch.empty(E + 1, dtype=torch.int32, device=dev))
-    sorted_ = o.get("sorted", torch.empty(T * k, dtype=torch.int32, device=dev))
-    pos = o.get("pos", torch.empty(T * k, dtype=torch.int32, device=dev))
+
+    def buf(name, shape, dtype):
+        return o[name] if name in o else torch.empty(shape, dtype=dtype, device=dev)
+
+    ids = buf("ids", (T, k), torch.int32)
+    w = buf("weights", (T, k), torch.float32)
+    offsets = buf("offsets", (E + 1,), torch.int32)
+    sorted_ = buf("sorted", (T * k,), torch.int32)
+    pos = buf("pos", (T * k,), torch.int32)
     H = 0
     xq_perm = xs_perm = None
     if xq is not None:
         _dev(xq, "xq", torch.uint8)
         _dev(xs, "xs", torch.float32)
         H = xq.shape[1]
-        xq_perm = o.get("xq_perm", torch.empty((T * k, H), dtype=torch.uint8, device=dev))
-        xs_perm = o.get("xs_perm", torch.empty((T * k, H // GROUP), dtype=torch.float32,
-                                               device=dev))
+        xq_perm = buf("xq_perm", (T * k, H), torch.uint8)
+        xs_perm = buf("xs_perm", (T * k, H // GROUP), torch.float32)
     nbytes = workspace_bytes(OP_ROUTE_PERMUTE, T, E, k)
     wsb = _workspace(nbytes, dev, ws)
     _check("moe_route_permute", _lib.moe_route_permute(

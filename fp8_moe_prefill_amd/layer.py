@@ -79,3 +79,62 @@ def w8a8_linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
     """bf16 [M, K] activations -> dynamic per-tensor e4m3 -> W8A8 GEMM -> [M, N]."""
     xq, blk = _lib.fp8_quant_act(x, 0, stream=stream)
     return _lib.fp8_dense_gemm(xq, blk, wq, w_scale, out_dtype, stream=stream)
+
+
+class MoELayerRunner:
+    """One MoE layer with every intermediate buffer allocated once (for serving loops and
+    timing): call ``run(x, logits, bank)`` repeatedly; outputs are overwritten in place.
+
+    The optional ``events`` dict of (start, end) torch.cuda.Event pairs, keyed by stage
+    name, is recorded around the corresponding launches on the current stream."""
+
+    STAGES = ("quant", "route", "gate_up", "down", "combine")
+
+    def __init__(self, T: int, H: int, E: int, k: int, I: int, device):
+        R = T * k
+        self.T, self.H, self.E, self.k, self.I, self.R = T, H, E, k, I, R
+        dev = torch.device(device)
+        u8, f32, i32 = torch.uint8, torch.float32, torch.int32
+        self.xq = torch.empty((T, H), dtype=u8, device=dev)
+        self.xs = torch.empty((T, H // _lib.GROUP), dtype=f32, device=dev)
+        self.route = dict(ids=torch.empty((T, k), dtype=i32, device=dev),
+                          weights=torch.empty((T, k), dtype=f32, device=dev),
+                          offsets=torch.empty(E + 1, dtype=i32, device=dev),
+                          sorted=torch.empty(R, dtype=i32, device=dev),
+                          pos=torch.empty(R, dtype=i32, device=dev))
+        nws = _lib.workspace_bytes(_lib.OP_ROUTE_PERMUTE, T, E, k)
+        self.ws = torch.empty(max(nws, 256), dtype=u8, device=dev)
+        self.hq = torch.empty((R, I), dtype=u8, device=dev)
+        self.hs = torch.empty((R, I // _lib.GROUP), dtype=f32, device=dev)
+        self.y = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def run(self, x, logits, bank: ExpertBank, events=None, stream=None):
+        ev = events or {}
+
+        def mark(name, i):
+            if name in ev:
+                ev[name][i].record()
+
+        rt = self.route
+        mark("quant", 0)
+        _lib.fp8_quant_act(x, _lib.GROUP, q=self.xq, scales=self.xs, stream=stream)
+        mark("quant", 1)
+        mark("route", 0)
+        _lib.moe_route_permute(logits, self.k, out=rt, ws=self.ws, stream=stream)
+        mark("route", 1)
+        mark("gate_up", 0)
+        _lib.fp8_grouped_expert_gemm(self.xq, self.xs, bank.w_gu, bank.s_gu, rt["offsets"],
+                                     self.R, _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"],
+                                     k_route=self.k, out=self.hq, out_scales=self.hs,
+                                     stream=stream)
+        mark("gate_up", 1)
+        mark("down", 0)
+        _lib.fp8_grouped_expert_gemm(self.hq, self.hs, bank.w_dn, bank.s_dn, rt["offsets"],
+                                     self.R, _lib.EPI_STORE, out=self.y, stream=stream)
+        mark("down", 1)
+        mark("combine", 0)
+        _lib.moe_unpermute_combine(self.y, rt["pos"], rt["weights"], out=self.out,
+                                   stream=stream)
+        mark("combine", 1)
+        return self.out
