@@ -116,6 +116,7 @@ int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales, const i
   if (epilogue == FP8MOE_EPI_SWIGLU_QUANT && N % 256 != 0) return FP8MOE_ERR_SHAPE;
   if (sorted && k_route < 1) return FP8MOE_ERR_SHAPE;
   if (R * K >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;  // 32-bit A row offsets
+  if (N * (K / 2) >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;  // 32-bit offsets in one expert
   const void* ptrs[] = {a, a_scales, w, w_scales, offsets, out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FP8MOE_ERR_ALIGN;

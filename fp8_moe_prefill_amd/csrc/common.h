@@ -55,6 +55,22 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return r;
 }
 
+// Two finite fp32 values -> two e4m3 bytes (low half of the result), round to nearest even,
+// saturating. For values that are finite by construction (no NaN handling).
+__device__ __forceinline__ uint32_t e4m3x2_finite(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -kE4m3Max, kE4m3Max),
+                                                    __builtin_amdgcn_fmed3f(b, -kE4m3Max, kE4m3Max),
+                                                    0, false) & 0xFFFFu;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> two bf16 (round to nearest even) packed low|high, one instruction.
+__device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Max over the 16 lanes that share (lane / 16).
 __device__ __forceinline__ float max16(float v) {
   v = fmaxf(v, __shfl_xor(v, 1));

@@ -18,7 +18,11 @@ namespace {
 
 constexpr int TM = 128, TN = 128;
 
-__device__ __forceinline__ int t_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// chunk c of row r at position c ^ (r & 7) ^ ((r >> 3) & 1): conflict-free ds_read_b128 of
+// one chunk across 16 consecutive rows
+__device__ __forceinline__ int t_off(int r, int c) {
+  return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4);
+}
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256, 2) void dense_gemm_kernel(

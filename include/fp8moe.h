@@ -169,7 +169,7 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
  *              I..2I-1; h = silu(gate) * up in fp32 is quantised like fp8_quant_act
  *              (group 128) into out = e4m3 [R, I] and out_scales = fp32 [R, I/128]
  * Constraints: R >= 0 (R = 0 is a no-op), 1 <= E <= 1024, K % 128 == 0,
- * 128 <= K <= 4096, R*K < 2^32; STORE: N % 16 == 0; SWIGLU_QUANT: N % 256 == 0.
+ * 128 <= K <= 4096, R*K < 2^32, N*K/2 < 2^32; STORE: N % 16 == 0; SWIGLU_QUANT: N % 256 == 0.
  */
 int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales,
                                 const int32_t* sorted, int32_t k_route, const uint8_t* w,
