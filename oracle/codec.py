@@ -12,12 +12,9 @@ Readings where the pages are silent (all plain IEEE-style choices):
 * the sign is kept on zero: -0.0 and negatives that round to zero give 0x80;
 * NaN encodes to 0x7F.
 
-int4: two's-complement values -8..7, two per byte, eight per little-endian 32-bit word.
-Word j of a bank row covers k = 8j .. 8j+7; its byte b (0..3) holds k = 8j + b in the low
-nibble and k = 8j + 4 + b in the high nibble. (The prefill note, section 1, keeps the bank
-packed and converts it on-chip; it is silent on the nibble order. This order is the one
-in which the low nibbles of a word are four consecutive k and the high nibbles the next
-four, so a 4-lane byte split of a word yields K-ordered bytes.)
+int4: two's-complement values -8..7, two per byte, the LOW nibble holding the even
+index along K (the prefill note, section 1, keeps the bank packed; it is silent on the
+nibble order, and low-first is the plain reading).
 """
 
 from __future__ import annotations
@@ -76,25 +73,21 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
 
 
 def unpack_int4(packed: np.ndarray) -> np.ndarray:
-    """Packed bytes [..., K/2] -> int4 values [..., K] (int8, -8..7), K-interleaved words."""
+    """Packed bytes [..., K/2] -> int4 values [..., K] (int8, -8..7), low nibble first."""
     p = np.asarray(packed, dtype=np.uint8)
-    assert p.shape[-1] % 4 == 0
-    words = p.reshape(*p.shape[:-1], p.shape[-1] // 4, 4)
-    lo = (words & 0xF).astype(np.int16)  # k = 8j + b
-    hi = (words >> 4).astype(np.int16)   # k = 8j + 4 + b
-    q = np.concatenate([lo, hi], axis=-1).reshape(*p.shape[:-1], p.shape[-1] * 2)
+    lo = (p & 0xF).astype(np.int16)
+    hi = (p >> 4).astype(np.int16)
+    q = np.stack([lo, hi], axis=-1).reshape(*p.shape[:-1], p.shape[-1] * 2)
     q = np.where(q >= 8, q - 16, q)  # two's-complement sign extension
     return q.astype(np.int8)
 
 
 def pack_int4(q: np.ndarray) -> np.ndarray:
-    """int4 values [..., K] (K % 8 == 0) -> packed bytes [..., K/2], the inverse of
-    ``unpack_int4``."""
+    """int4 values [..., K] (even K) -> packed bytes [..., K/2], low nibble = even k."""
     q = np.asarray(q, dtype=np.int16)
-    assert q.shape[-1] % 8 == 0
-    n = (q & 0xF).astype(np.uint8).reshape(*q.shape[:-1], q.shape[-1] // 8, 8)
-    words = n[..., :4] | (n[..., 4:] << 4)
-    return words.reshape(*q.shape[:-1], q.shape[-1] // 2).astype(np.uint8)
+    assert q.shape[-1] % 2 == 0
+    n = (q & 0xF).astype(np.uint8)
+    return (n[..., 0::2] | (n[..., 1::2] << 4)).astype(np.uint8)
 
 
 def int4_e4m3_table() -> np.ndarray:

@@ -100,23 +100,21 @@ def test_encode_special_values():
 
 
 def test_int4_unpack_sign_extension_and_order():
-    # one word: byte b holds k = b (low nibble) and k = 4 + b (high nibble)
-    # byte 0 = 0x8F: k0 = 0xF = -1, k4 = 0x8 = -8; byte 1 = 0x70: k1 = 0, k5 = 7; ...
-    got = unpack_int4(np.array([0x8F, 0x70, 0x12, 0x34], np.uint8))
-    assert list(got) == [-1, 0, 2, 4, -8, 7, 1, 3]
-    # bit-level: every value of every position of a word, one at a time
+    # byte 0x8F: low nibble 0xF = -1 (even k), high nibble 0x8 = -8 (odd k)
+    assert list(unpack_int4(np.array([0x8F, 0x70, 0x12], np.uint8))) == [-1, -8, 0, 7, 2, 1]
+    # bit-level: every value at every position of a 4-byte row, one at a time
     for pos in range(8):
         for v in range(-8, 8):
             q = np.zeros(8, np.int8)
             q[pos] = v
             b = np.zeros(4, np.uint8)
-            b[pos % 4] = (v & 0xF) << (4 * (pos // 4))
+            b[pos // 2] = (v & 0xF) << (4 * (pos % 2))
             assert list(unpack_int4(b)) == list(q)
 
 
 def test_int4_pack_unpack_round_trip():
     rng = np.random.default_rng(0)
-    q = rng.integers(-8, 8, size=(5, 7, 256)).astype(np.int8)  # K % 8 == 0
+    q = rng.integers(-8, 8, size=(5, 7, 256)).astype(np.int8)
     assert np.array_equal(unpack_int4(pack_int4(q)), q)
     b = rng.integers(0, 256, size=(3, 64), dtype=np.uint8)
     assert np.array_equal(pack_int4(unpack_int4(b)), b)

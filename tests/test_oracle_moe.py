@@ -33,9 +33,8 @@ def _brute(a_codes, a_scales, w_packed, w_scales, offsets):
                 for g in range(K // 128):
                     part = 0.0
                     for kk in range(g * 128, g * 128 + 128):
-                        j, r = divmod(kk, 8)  # word j, position r in the word
-                        byte = int(w_packed[e, n, 4 * j + r % 4])
-                        nib = (byte >> 4) if r >= 4 else (byte & 15)
+                        byte = int(w_packed[e, n, kk // 2])
+                        nib = (byte >> 4) if kk % 2 else (byte & 15)
                         qv = nib - 16 if nib >= 8 else nib
                         part += DEC[a_codes[i, kk]] * qv
                     acc += float(a_scales[i, g]) * float(w_scales[e, n, g]) * part
@@ -70,11 +69,11 @@ def test_single_expert_is_dense_gemm():
     aq, as_, wp, ws, _ = _tiny(1, R=9, K=384, N=5, E=1)
     y = grouped_gemm(aq, as_, wp, ws, np.array([0, 9], np.int32))
     a = DEC[aq] * np.repeat(as_.astype(np.float64), 128, axis=1)
+    lo = (wp & 15).astype(np.int64)
+    hi = (wp >> 4).astype(np.int64)
     q = np.empty((5, 384), np.int64)
-    for kk in range(384):
-        j, r = divmod(kk, 8)
-        byte = wp[0, :, 4 * j + r % 4].astype(np.int64)
-        q[:, kk] = (byte >> 4) if r >= 4 else (byte & 15)
+    q[:, 0::2] = lo[0]
+    q[:, 1::2] = hi[0]
     q = np.where(q >= 8, q - 16, q)
     w = q * np.repeat(ws[0].astype(np.float64), 128, axis=1)
     assert np.allclose(y, np.matmul(a, w.T), rtol=1e-12, atol=1e-15)
