@@ -9,6 +9,6 @@ has not been built (``python -m fp8_moe_prefill_amd.build``).
 from ._lib import (  # noqa: F401
     DTYPE_BF16, DTYPE_F32, EPI_STORE, EPI_SWIGLU_QUANT, GROUP, Fp8MoeError, LIB_PATH,
     abi_version, fp8_dense_gemm, fp8_grouped_expert_gemm, fp8_quant_act, moe_route_permute,
-    moe_unpermute_combine, workspace_bytes,
+    moe_unpermute_combine, pack_expert_bank, workspace_bytes,
 )
 from .layer import ExpertBank, MoELayerRunner, moe_layer, quantize_weight, w8a8_linear  # noqa: F401

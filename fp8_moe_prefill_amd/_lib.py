@@ -35,6 +35,8 @@ SIGNATURES = {
     "moe_route_permute": (_i32, [_c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
                                  _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "fp8moe_pack_expert_bank": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p,
+                                       _c_void_p, _c_void_p]),
     "fp8_grouped_expert_gemm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
                                        _c_void_p, _c_void_p, _i64, _i32, _i64, _i64, _i32, _i32,
                                        _c_void_p, _c_void_p, _c_void_p]),
@@ -114,7 +116,7 @@ def abi_version() -> int:
 
 
 # ------------------------------------------------------------------------------------
-# The five entry points
+# The entry points
 # ------------------------------------------------------------------------------------
 
 
@@ -137,7 +139,10 @@ def fp8_quant_act(x: torch.Tensor, group: int = GROUP, q=None, scales=None, ws=N
 
 def moe_route_permute(logits: torch.Tensor, k: int, xq=None, xs=None, out=None, ws=None,
                       stream=None) -> dict:
-    """fp32 logits [T, E] -> dict(ids, weights, offsets, sorted, pos[, xq_perm, xs_perm])."""
+    """fp32 logits [T, E] -> dict(ids, weights, offsets, sorted, pos[, xq_perm][, xs_perm]).
+
+    ``xq`` (e4m3 [T, H]) is gathered into xq_perm [T*k, H]; ``xs`` (fp32 [T, H/128]) into
+    xs_perm [H/128, T*k], group-major. Either may be given alone."""
     _dev(logits, "logits", torch.float32)
     T, E = logits.shape
     dev = logits.device
@@ -155,10 +160,12 @@ def moe_route_permute(logits: torch.Tensor, k: int, xq=None, xs=None, out=None, 
     xq_perm = xs_perm = None
     if xq is not None:
         _dev(xq, "xq", torch.uint8)
-        _dev(xs, "xs", torch.float32)
         H = xq.shape[1]
         xq_perm = buf("xq_perm", (T * k, H), torch.uint8)
-        xs_perm = buf("xs_perm", (T * k, H // GROUP), torch.float32)
+    if xs is not None:
+        _dev(xs, "xs", torch.float32)
+        H = xs.shape[1] * GROUP
+        xs_perm = buf("xs_perm", (H // GROUP, T * k), torch.float32)
     nbytes = workspace_bytes(OP_ROUTE_PERMUTE, T, E, k)
     wsb = _workspace(nbytes, dev, ws)
     _check("moe_route_permute", _lib.moe_route_permute(
@@ -166,15 +173,35 @@ def moe_route_permute(logits: torch.Tensor, k: int, xq=None, xs=None, out=None, 
         _ptr(xq), _ptr(xs), H, _ptr(xq_perm), _ptr(xs_perm), _ptr(wsb), nbytes, _stream(stream)))
     r = dict(ids=ids, weights=w, offsets=offsets, sorted=sorted_, pos=pos)
     if xq is not None:
-        r.update(xq_perm=xq_perm, xs_perm=xs_perm)
+        r.update(xq_perm=xq_perm)
+    if xs is not None:
+        r.update(xs_perm=xs_perm)
     return r
+
+
+def pack_expert_bank(w: torch.Tensor, w_scales: torch.Tensor, out=None, stream=None):
+    """Canonical bank (packed int4 [E, N, K/2], low nibble = even k; fp32 scales
+    [E, N, K/128]) -> the grouped GEMM's layout: (bank bytes, kept as a [E, N, K/2] uint8
+    tensor, and scales [E, K/128, N])."""
+    _dev(w, "w", torch.uint8)
+    _dev(w_scales, "w_scales", torch.float32)
+    E, N, Kh = w.shape
+    K = Kh * 2
+    if out is None:
+        out = (torch.empty_like(w),
+               torch.empty((E, K // GROUP, N), dtype=torch.float32, device=w.device))
+    wp, sp = out
+    _check("fp8moe_pack_expert_bank", _lib.fp8moe_pack_expert_bank(
+        _ptr(w), _ptr(w_scales), E, N, K, _ptr(wp), _ptr(sp), _stream(stream)))
+    return wp, sp
 
 
 def fp8_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=EPI_STORE,
                             out_dtype=torch.float32, sorted_=None, k_route: int = 1, out=None,
                             out_scales=None, stream=None):
-    """Grouped expert GEMM. STORE -> out [R, N]; SWIGLU_QUANT -> (codes [R, N/2],
-    scales [R, N/256])."""
+    """Grouped expert GEMM on a bank from ``pack_expert_bank`` (w [E, N, K/2] bytes,
+    w_scales [E, K/128, N]); a_scales are group-major [K/128, R]. STORE -> out [R, N];
+    SWIGLU_QUANT -> (codes [R, N/2], scales [N/256, R], group-major)."""
     _dev(a, "a", torch.uint8)
     _dev(a_scales, "a_scales", torch.float32)
     _dev(w, "w", torch.uint8)
@@ -182,6 +209,12 @@ def fp8_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=
     _dev(offsets, "offsets", torch.int32)
     E, N, Kh = w.shape
     K = Kh * 2
+    if tuple(a_scales.shape) != (K // GROUP, R):
+        raise ValueError(f"a_scales must be [K/128, R] = {(K // GROUP, R)}, "
+                         f"got {tuple(a_scales.shape)}")
+    if tuple(w_scales.shape) != (E, K // GROUP, N):
+        raise ValueError(f"w_scales must be [E, K/128, N] = {(E, K // GROUP, N)}, "
+                         f"got {tuple(w_scales.shape)}")
     dev = a.device
     if sorted_ is not None:
         _dev(sorted_, "sorted", torch.int32)
@@ -190,7 +223,7 @@ def fp8_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=
         if out is None:
             out = torch.empty((R, I), dtype=torch.uint8, device=dev)
         if out_scales is None:
-            out_scales = torch.empty((R, I // GROUP), dtype=torch.float32, device=dev)
+            out_scales = torch.empty((I // GROUP, R), dtype=torch.float32, device=dev)
         dt = DTYPE_F32
     else:
         if out is None:

@@ -18,8 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp8moe.so")
 
-KERNELS = ["quant_act.hip", "route_permute.hip", "grouped_gemm.hip", "dense_gemm.hip",
-           "combine.hip"]
+KERNELS = ["quant_act.hip", "route_permute.hip", "bank_pack.hip", "grouped_gemm.hip",
+           "dense_gemm.hip", "combine.hip"]
 HOST = ["capi.cpp"]
 
 ARCH = "gfx950"

@@ -11,10 +11,10 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
-constexpr int64_t kMaxGroupedK = 4096;
+constexpr int64_t kMaxGroupedK = 16384;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -80,21 +80,38 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, 
                           const uint8_t* xq, const float* xs, int64_t H, uint8_t* xq_perm,
                           float* xs_perm, void* ws, size_t ws_bytes, void* stream) {
   if (!logits || !ids || !weights || !offsets || !sorted || !pos || !ws) return FP8MOE_ERR_NULL;
-  const bool any_gather = xq || xs || xq_perm || xs_perm;
-  const bool all_gather = xq && xs && xq_perm && xs_perm;
-  if (any_gather && !all_gather) return FP8MOE_ERR_NULL;
+  // the row gather (xq -> xq_perm) and the scale gather (xs -> xs_perm) are independent
+  // options, each all-or-nothing
+  if ((xq != nullptr) != (xq_perm != nullptr)) return FP8MOE_ERR_NULL;
+  if ((xs != nullptr) != (xs_perm != nullptr)) return FP8MOE_ERR_NULL;
+  const bool rows = xq != nullptr, scales = xs != nullptr;
   if (T < 1 || E < 1 || E > kMaxE || k < 1 || k > E || k > kMaxK) return FP8MOE_ERR_SHAPE;
   if (T * (int64_t)k >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
-  if (all_gather && (H < FP8MOE_GROUP || H % FP8MOE_GROUP != 0)) return FP8MOE_ERR_SHAPE;
+  if ((rows || scales) && (H < FP8MOE_GROUP || H % FP8MOE_GROUP != 0)) return FP8MOE_ERR_SHAPE;
   const void* ptrs[] = {logits, ids, weights, offsets, sorted, pos, ws};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
-  if (all_gather && (!aligned16(xq) || !aligned16(xs) || !aligned16(xq_perm) || !aligned16(xs_perm)))
-    return FP8MOE_ERR_ALIGN;
+  if (rows && (!aligned16(xq) || !aligned16(xq_perm))) return FP8MOE_ERR_ALIGN;
+  if (scales && (!aligned16(xs) || !aligned16(xs_perm))) return FP8MOE_ERR_ALIGN;
   if (ws_bytes < fp8moe::route_workspace_bytes(T, E)) return FP8MOE_ERR_WORKSPACE;
   return launch_status(fp8moe::launch_route_permute(
-      logits, T, E, k, ids, weights, offsets, sorted, pos, all_gather ? xq : nullptr, xs, H,
-      xq_perm, xs_perm, ws, static_cast<hipStream_t>(stream)));
+      logits, T, E, k, ids, weights, offsets, sorted, pos, xq, xs, H, xq_perm, xs_perm, ws,
+      static_cast<hipStream_t>(stream)));
+}
+
+int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t E, int64_t N,
+                                int64_t K, uint8_t* w_packed, float* w_scales_packed,
+                                void* stream) {
+  if (!w || !w_scales || !w_packed || !w_scales_packed) return FP8MOE_ERR_NULL;
+  if (E < 1 || E > kMaxE) return FP8MOE_ERR_SHAPE;
+  if (N < 16 || N % 16 != 0 || N >= (int64_t(1) << 24)) return FP8MOE_ERR_SHAPE;
+  if (K < FP8MOE_GROUP || K % FP8MOE_GROUP != 0 || K > kMaxGroupedK) return FP8MOE_ERR_SHAPE;
+  if (N * (K / 2) >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;
+  const void* ptrs[] = {w, w_scales, w_packed, w_scales_packed};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
+  return launch_status(fp8moe::launch_pack_bank(w, w_scales, E, N, K, w_packed, w_scales_packed,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,

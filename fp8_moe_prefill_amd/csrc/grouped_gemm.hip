@@ -5,40 +5,47 @@
 // memory and are turned into e4m3 on-chip; the per-(token, group) activation scale and the
 // per-group weight scale are folded into the fp32 accumulator:
 //
-//   y[i, n] = sum_g  s_a[i, g] * s_w[e, n, g] * sum_{k in g} e4m3(a[i, k]) * q[e, n, k]
+//   y[i, n] = sum_g  s_a[g, i] * s_w[e, g, n] * sum_{k in g} e4m3(a[i, k]) * q[e, n, k]
 //
 // gfx950 design:
 // * The MFMA is v_mfma_f32_16x16x128_f8f6f4: its K of 128 is exactly one scale group, so
 //   each group is one MFMA per 16x16 output tile, followed by the fold
-//   acc += P * (s_a * s_w) (two VALU ops per output per group). VALU, not the matrix
-//   core, is the scarce unit: at full MFMA rate the fold alone fills the VALU, so every
-//   other VALU op in the loop is kept to a minimum.
+//   acc += P * (s_a * s_w) (two VALU ops per output per group). On gfx950 an FP8 MFMA of
+//   this shape occupies most of the VALU issue slots of its own 32 cycles, so VALU, not the
+//   matrix core, is the scarce unit: every VALU op in the loop other than the fold is kept
+//   to a minimum.
 // * Nibble -> e4m3 in two ops per four weights: e4m3 codes 0x00..0x0F are exactly
 //   u * 2^-9 (the subnormals and the first normal binade share the spacing 2^-9), so the
 //   offset nibble u = n ^ 8 = q + 8 (q the int4 value) IS the e4m3 code of (q + 8) * 2^-9.
 //   The +8 is removed inside the MFMA: its accumulator input is seeded with
 //   -8 * 2^-9 * sum_k a_k for that row and group, and that row sum is itself one MFMA of
 //   the A tile against a constant all-ones operand (one extra MFMA per 16 rows per group,
-//   +6%). The 2^9 is folded into the weight scale (exact). The bank's K-interleaved
-//   nibble order makes the low nibbles of a 32-bit word four consecutive k, so a byte
-//   split (and, shift+and) gives K-ordered e4m3 bytes with no permutes.
-// * Workgroup tile 128 rows x 512 accumulator columns, 8 waves side by side along N
+//   +3%). The 2^9 is folded into the weight scale (exact). The prepacked bank stores the
+//   nibbles of a 32-bit word so that its low nibbles are four consecutive k and its high
+//   nibbles the next four: a byte split gives K-ordered e4m3 bytes with no permutes.
+// * Tile 128 rows x 512 accumulator columns per workgroup, 8 waves side by side along N
 //   (each wave: all 128 rows x 64 columns = 8 x 4 MFMA tiles, 128 fp32 accumulators per
-//   lane; two waves per SIMD). Per K group the tile stages 16 KB of A and 32 KB of packed
-//   B for 16.8 MFLOP (330 FLOP per staged byte): the L2-to-CU stream, not HBM, is what
-//   this kernel has to keep fed. A (e4m3 rows, gathered from token order through
-//   `sorted` when given), each wave's packed B slice and both scale vectors go straight
-//   from global memory into LDS (global_load_lds, no VGPR staging) in three stages, two
-//   groups in flight, one barrier per group. Each wave stages exactly the 16 A rows whose
-//   sums it computes, so the seeds of group g+1 are formed as soon as the wave's own loads
-//   land, before the group's single barrier.
-// * One launch covers all experts: the grid is the host-known bound ceil(R/128) + E
-//   m-tiles times the n-tiles; each workgroup finds its (expert, m-tile) from the device
-//   offsets (a workgroup-wide scan over E) and exits if surplus.
-// * Epilogues: STORE writes fp32 or bf16; SWIGLU_QUANT pairs gate columns n and up
-//   columns I+n in the same wave, forms h = silu(gate) * up in fp32, takes the per-row
-//   amax over the workgroup's 128 h columns (= one 128-group of the down GEMM's K) and
-//   writes e4m3 codes plus fp32 scales, so h never goes to HBM in fp32 or bf16.
+//   lane; two waves per SIMD). Per K group a tile stages 16 KB of A and 32 KB of packed B
+//   for 16.8 MFLOP. A (e4m3 rows, gathered from token order through `sorted` when given),
+//   each wave's packed B slice (one contiguous 1 KB block per 16 columns in the prepacked
+//   bank) and both scale vectors (contiguous per group in their group-major layouts) go
+//   straight from global memory into LDS (LDS DMA, no VGPR staging) through a ring of
+//   three stages: two groups in flight, one barrier per group.
+// * Persistent: the grid is one workgroup per CU and each workgroup walks its list of
+//   (expert, 128-row, 512-column) tiles as one continuous stream of K groups, so the loads
+//   of a tile's first groups overlap the previous tile's last groups and its epilogue, and
+//   no workgroup pays a cold start per tile. Tiles are dealt in contiguous ranges per XCD
+//   (each XCD has its own L2), so the m-tiles of one expert, which share B, and the
+//   n-tiles of one m-tile, which share A, run on the same L2. Row tiles past the end of an
+//   expert's last, partial m-tile are skipped.
+// * The expert of each tile comes from the device offsets (a workgroup-wide scan of the
+//   per-expert m-tile counts, then a binary search), so one launch covers all experts with
+//   no host round trip.
+// * Epilogues: STORE writes fp32 or bf16; SWIGLU_QUANT pairs gate columns n and up columns
+//   I+n in the same wave, forms h = silu(gate) * up in fp32, takes the per-row amax over the
+//   workgroup's 128 h columns (= one 128-group of the down GEMM's K) and writes e4m3 codes
+//   plus fp32 scales, so h never goes to HBM in fp32 or bf16.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -47,20 +54,19 @@
 namespace fp8moe {
 namespace {
 
-constexpr int BM = 128;        // rows per workgroup tile
+constexpr int BM = 128;        // rows per tile
 constexpr int NW = 8;          // waves per workgroup
 constexpr int NT_THREADS = NW * 64;
 constexpr int WCOLS = 64;      // accumulator columns per wave
 constexpr int WCOLS_WG = NW * WCOLS;           // 512 accumulator columns per workgroup
 constexpr int BW_BYTES = WCOLS * kGroup / 2;   // packed B slice of one wave, one group
+constexpr int kBlockBytes = 16 * kGroup / 2;   // prepacked bank block: 16 columns, one group
 constexpr float kWeightScaleMul = 512.f;       // 2^9: B codes are (q + 8) * 2^-9
 constexpr uint32_t kOnes = 0x38383838u;        // four e4m3 1.0
+constexpr int kMaxExperts = 1024;
 
 // One pipeline stage in LDS: the A tile, the waves' packed B slices, the A scales of the
 // 128 rows, the weight scales of the 512 columns, and the row-sum seeds of its group.
-// The three stages are distinct __shared__ objects and every access names its stage at
-// compile time, so the compiler can tell that the direct-to-LDS loads filling one stage
-// never alias the reads of another and does not make those reads wait for the loads.
 struct __attribute__((aligned(16))) Stage {
   uint8_t a[BM * kGroup];
   uint8_t b[NW * BW_BYTES];
@@ -85,29 +91,54 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* tmp /*[NW]*/) {
   return v + add;
 }
 
+// Read-only data read with a wave-uniform address through the scalar unit (SMEM): the
+// value lands in an SGPR and is waited for with lgkmcnt, never with vmcnt, so it does not
+// interact with the counted waits of the LDS DMA pipeline.
+__device__ __forceinline__ int sload(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 // global -> LDS without VGPR staging: lane i of the wave copies `size` bytes from
 // base + voff (base wave-uniform, voff per lane) to LDS byte address lds + size * i (lds
 // wave-uniform, passed in M0). Issued as inline assembly so that the compiler does not
 // track these loads: it would otherwise make LDS reads of the stage being computed wait
 // for every load in flight (vmcnt(0)), which serialises the pipeline. The kernel waits
-// for them itself, by count, and a workgroup barrier then publishes them. The s_nop is
-// the wait state the hardware needs between the write of M0 and the LDS DMA.
+// for them itself, by count, and a workgroup barrier then publishes them. Because the
+// compiler does not see the load, it cannot insert the wait states the ISA requires
+// around a vector memory instruction's operands, so the asm provides them: 5 before it,
+// for a VALU write of an SGPR (v_readlane / v_readfirstlane, e.g. a restored spill) that
+// the load reads as its base address (this also covers the one after a write of M0), and
+// 1 after it, before an instruction may overwrite an SGPR the load reads.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, const void* lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1\n\ts_nop 0"
                :: "v"(voff), "s"(base), "{m0}"(lds_addr(lds)) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, const void* lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1\n\ts_nop 0"
                :: "v"(voff), "s"(base), "{m0}"(lds_addr(lds)) : "memory");
+}
+constexpr int kDmaPerGroup = 8;  // loads each wave issues per K group (see dma_group)
+
+// Waits and barriers of the pipeline. They are compiler memory barriers ("memory"
+// clobber), so no LDS access moves across them. The barrier drains this wave's LDS
+// traffic first (the only data other waves read after it); the direct-to-LDS loads are
+// waited for by count: vmcnt(8) leaves exactly the newest group's loads in flight.
+__device__ __forceinline__ void wait_all_but_one_group() {
+  static_assert(kDmaPerGroup == 8, "vmcnt immediate below");
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+}
+__device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // bitop3 truth table of (a ^ b) & c, with a, b, c in the 0xF0 / 0xCC / 0xAA positions
 constexpr int kXorAnd = (0xF0 ^ 0xCC) & 0xAA;
 
-// 16 packed bytes (32 int4, K-interleaved words) -> MFMA B operand of (q + 8) * 2^-9.
+// 16 prepacked bytes (32 int4) -> MFMA B operand of (q + 8) * 2^-9.
 __device__ __forceinline__ v8i convert_b(uint4 p) {
   v8i b;
   const uint32_t w[4] = {p.x, p.y, p.z, p.w};
@@ -125,7 +156,6 @@ __device__ __forceinline__ v8i convert_b(uint4 p) {
 // on 16 distinct 16-byte bank groups whether the LDS serves 8 or 16 lanes per cycle.
 __device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int a_off(int r, int c) { return r * 128 + ((c ^ a_swz(r)) << 4); }
-
 __device__ __forceinline__ v8i lds_a_operand(const uint8_t* tile, int r, int q) {
   uint4 lo = *reinterpret_cast<const uint4*>(&tile[a_off(r, 2 * q)]);
   uint4 hi = *reinterpret_cast<const uint4*>(&tile[a_off(r, 2 * q + 1)]);
@@ -165,123 +195,154 @@ __device__ __forceinline__ float row4_max16(const float m[4], int c16) {
   return keep;
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt
-// [11:8])
-constexpr int kWaitAll = 0;
-constexpr int kWaitVm8 = 8 | (7 << 4) | (0xF << 8);      // vmcnt <= 8, nothing else
-constexpr int kWaitLgkm0 = 0xF | (7 << 4) | (3 << 14);   // lgkmcnt == 0, nothing else
-
-// Workgroup barrier without the release fence of __syncthreads(): that fence waits for
-// every outstanding global load, including the direct-to-LDS loads of the groups still in
-// flight. LDS writes of this wave are drained first (they are the only writes other waves
-// read after the barrier); the direct-to-LDS loads are waited for explicitly by count.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_barrier();
-}
+// Tile (expert, first grouped row, valid rows, n-tile) of a logical tile.
+struct TileDesc {
+  int e, row_begin, rows, nt;
+};
 
 template <int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As,
-    const int32_t* __restrict__ sorted, int k_route, const uint8_t* __restrict__ W,
-    const float* __restrict__ Ws, const int32_t* __restrict__ offsets, int E, int N, int K,
-    int NT, void* __restrict__ out, float* __restrict__ out_scales) {
-  __shared__ Stage st0, st1, st2;
+    const int32_t* __restrict__ sorted, int k_route, int a_rows, const uint8_t* __restrict__ W,
+    const float* __restrict__ Ws, const int32_t* __restrict__ offsets, int R, int E, int N,
+    int K, int NT, void* __restrict__ out, float* __restrict__ out_scales) {
+  __shared__ Stage ring[3];
+  __shared__ int s_mstart[kMaxExperts + 1];  // m-tiles before expert e
   __shared__ int s_tmp[NW];
-  __shared__ int s_tile[3];
-  __shared__ int s_total;
+  __shared__ int s_src[NW][16];  // pair ids of the 16 rows each wave stages for the next tile
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in an SGPR
   const int q = lane >> 4, c16 = lane & 15;
   const int G = K / kGroup;
+  const int I = N / 2;
+  const int NB = N / 16;
   const int kshift = (k_route & (k_route - 1)) == 0 ? __builtin_ctz(k_route) : -1;
-  const uint32_t L = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int mt = (int)(L / (uint32_t)NT), nt = (int)(L % (uint32_t)NT);
 
-  // ---- which expert and which 128-row slice of it this workgroup owns
+  // ---- m-tiles per expert, prefix-summed (2 experts per thread, E <= 1024)
   {
     int loc[2], sum = 0;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      int e = tid * 2 + j;
-      int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-      loc[j] = (c + BM - 1) / BM;
+      const int e = tid * 2 + j;
+      const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+      loc[j] = c > 0 ? (c + BM - 1) / BM : 0;
       sum += loc[j];
     }
-    int inc = block_inclusive_scan(sum, s_tmp);
-    int run = inc - sum;
+    int run = block_inclusive_scan(sum, s_tmp) - sum;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      if (mt >= run && mt < run + loc[j]) {
-        int e = tid * 2 + j;
-        int rb = offsets[e] + (mt - run) * BM;
-        s_tile[0] = e;
-        s_tile[1] = rb;
-        s_tile[2] = min(BM, offsets[e + 1] - rb);
-      }
+      const int e = tid * 2 + j;
       run += loc[j];
+      if (e < E) s_mstart[e + 1] = run;
     }
-    if (tid == NT_THREADS - 1) s_total = inc;
+    if (tid == 0) s_mstart[0] = 0;
     __syncthreads();
   }
-  if (mt >= s_total) return;  // surplus workgroup (uniform)
-  const int e = __builtin_amdgcn_readfirstlane(s_tile[0]);
-  const int row_begin = __builtin_amdgcn_readfirstlane(s_tile[1]);
-  const int rows = __builtin_amdgcn_readfirstlane(s_tile[2]);
 
-  // ---- sources: wave-uniform bases (advanced per group in scalar registers) plus
-  // per-lane 32-bit byte offsets. Wave wv stages rows 16wv .. 16wv+15 of every A tile (the
-  // rows whose sums it also computes, so it needs nobody else's loads for that): chunk
-  // p = (2wv+j)*64 + lane of the swizzled tile for j = 0, 1.
-  auto src_row = [&](int r) {
-    const int grow = row_begin + min(r, rows - 1);
-    if (!sorted) return grow;
-    const int p = sorted[grow];
-    if (kshift >= 0) return p >> kshift;  // uniform branch: no division for 2^n experts/token
-    return p / k_route;
+  // ---- this workgroup's tiles. Logical tile L = m-tile * NT + n-tile; XCD x (workgroups
+  // x, x + nx, ...) owns the contiguous range [b_x, e_x) and its workgroups take every
+  // nwg_x-th tile of it.
+  const int64_t ntiles = (int64_t)__builtin_amdgcn_readfirstlane(s_mstart[E]) * NT;
+  const int nx = min(8, (int)gridDim.x);
+  const int x = (int)blockIdx.x % nx, u = (int)blockIdx.x / nx;
+  const int nwg_x = ((int)gridDim.x - x + nx - 1) / nx;
+  const int64_t b_x = ntiles * x / nx, e_x = ntiles * (x + 1) / nx;
+  const int64_t first = b_x + u;
+  const int my_tiles = first < e_x ? (int)((e_x - 1 - first) / nwg_x + 1) : 0;
+  if (my_tiles == 0) return;  // uniform
+  const int total_steps = my_tiles * G;
+
+  auto tile_of = [&](int j) {
+    const int64_t L = first + (int64_t)j * nwg_x;
+    const int mt = (int)(L / NT);
+    TileDesc d;
+    d.nt = (int)(L - (int64_t)mt * NT);
+    int lo = 0, hi = E;  // s_mstart[lo] <= mt < s_mstart[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(s_mstart[mid]) <= mt) lo = mid;
+      else hi = mid;
+    }
+    d.e = lo;
+    d.row_begin = sload(offsets + lo) + (mt - __builtin_amdgcn_readfirstlane(s_mstart[lo])) * BM;
+    d.rows = min(BM, sload(offsets + lo + 1) - d.row_begin);
+    return d;
   };
-  uint32_t a_off32[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int p = (wv * 2 + j) * 64 + lane;
-    const int r = p >> 3, c = (p & 7) ^ a_swz(r);
-    a_off32[j] = (uint32_t)src_row(r) * (uint32_t)K + (uint32_t)(c * 16);
-  }
-  // A scale of row 16wv + lane (lanes 0..15; rows past the tile read a valid row and are
-  // never stored)
-  const uint32_t as_off32 = (uint32_t)src_row(wv * 16 + (lane & 15)) * (uint32_t)G * 4u;
-  // accumulator column j (0..511) of the workgroup -> bank column. SwiGLU: the workgroup
-  // covers two 128-wide h groups (j >> 8); in each, wave (j >> 6) & 3 holds gate columns
-  // for (j >> 5) & 1 == 0 and the matching up columns (I + ...) for (j >> 5) & 1 == 1.
-  const int I = N / 2;
-  auto bank_col = [&](int j) {
+
+  // accumulator column j (0..511) of n-tile nt -> bank column. SwiGLU: the tile covers two
+  // 128-wide h groups (j >> 8); in each, wave (j >> 6) & 3 holds gate columns for
+  // (j >> 5) & 1 == 0 and the matching up columns (I + ...) for (j >> 5) & 1 == 1.
+  auto bank_col = [&](int nt, int j) {
     if (EPI == FP8MOE_EPI_SWIGLU_QUANT)
       return min(((j >> 5) & 1 ? I : 0) + nt * 256 + (j >> 8) * 128 + ((j >> 6) & 3) * 32 +
                      (j & 31),
                  N - 1);
     return min(nt * WCOLS_WG + j, N - 1);
   };
-  const uint8_t* const Wexp = W + (int64_t)e * N * (K / 2);
-  const float* const Wsexp = Ws + (int64_t)e * N * G;
-  const uint32_t ws_off32 = (uint32_t)bank_col(wv * WCOLS + lane) * (uint32_t)G * 4u;
-  uint32_t b_off32[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-    b_off32[s] = (uint32_t)bank_col(wv * WCOLS + 16 * s + c16) * (uint32_t)(K / 2) +
-                 (uint32_t)(q * 16);
 
-  // 8 loads per wave per group (the counted waits below rely on that number)
-  auto load_group = [&](int g, Stage& st) {
-    const uint8_t* ag = A + g * kGroup;
+  // ---- DMA stream state: the tile whose groups are being loaded, and the next one (its
+  // descriptor, and the pair ids of its rows brought into LDS by the wave's own loads one
+  // group ahead, older than that group's loads, so the group's counted wait covers them)
+  TileDesc pend = tile_of(0);
+  auto fetch_rows = [&](const TileDesc& d) {
+    if (sorted && lane < 16)
+      dma4(sorted, (uint32_t)max(min(d.row_begin + min(wv * 16 + lane, d.rows - 1), R - 1), 0) * 4u,
+           &s_src[wv][0]);
+  };
+  fetch_rows(pend);
+  wait_all_loads();
+
+  uint32_t a_off32[2] = {0, 0}, as_off32 = 0, ws_off32 = 0;
+  uint32_t b_blk[4] = {0, 0, 0, 0};  // byte offset of this wave's 4 column blocks in its expert
+  const uint8_t* w_exp = W;
+  const float* ws_exp = Ws;
+  const uint32_t lane16 = (uint32_t)lane * 16u;
+
+  auto dma_group = [&](int d, Stage& st) {
+    const int jd = d / G, gd = d - jd * G;
+    if (gd == 0) {
+      // a new tile enters the stream: set up its sources from the prefetched descriptor
+      const TileDesc t = pend;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rl = 8 * j + (lane >> 3);  // row (of this wave's 16) staged by this lane
+        int src;
+        if (sorted) {
+          const int p = s_src[wv][rl];
+          src = kshift >= 0 ? (p >> kshift) : (p / k_route);  // uniform branch
+        } else {
+          src = t.row_begin + min(wv * 16 + rl, t.rows - 1);
+        }
+        src = max(min(src, a_rows - 1), 0);
+        const int c = (lane & 7) ^ a_swz(rl);
+        a_off32[j] = (uint32_t)src * (uint32_t)K + (uint32_t)(c * 16);
+      }
+      as_off32 =
+          (uint32_t)max(min(t.row_begin + min(wv * 16 + (lane & 15), t.rows - 1), R - 1), 0) * 4u;
+      ws_off32 = (uint32_t)bank_col(t.nt, wv * WCOLS + lane) * 4u;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        b_blk[s] = (uint32_t)(bank_col(t.nt, wv * WCOLS + 16 * s) / 16) * (uint32_t)G * kBlockBytes;
+      w_exp = W + (int64_t)t.e * NB * G * kBlockBytes;
+      ws_exp = Ws + (int64_t)t.e * G * N;
+      // the LDS reads of s_src above complete before any later load may refill it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    // the next tile enters the stream at the next group: fetch its descriptor and rows now,
+    // before this group's loads
+    if (gd == G - 1 && jd + 1 < my_tiles) {
+      pend = tile_of(jd + 1);
+      fetch_rows(pend);
+    }
+    const uint8_t* ag = A + gd * kGroup;
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(ag, a_off32[j], st.a + (wv * 2 + j) * 1024);
-    const uint8_t* bg = Wexp + g * (kGroup / 2);
     uint8_t* sb = st.b + wv * BW_BYTES;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dma16(bg, b_off32[s], sb + s * 1024);
-    dma4(Wsexp + g, ws_off32, st.ws + wv * WCOLS);
-    if (lane < 16) dma4(As + g, as_off32, st.as + wv * 16);
+    for (int s = 0; s < 4; ++s) dma16(w_exp + b_blk[s] + gd * kBlockBytes, lane16, sb + s * 1024);
+    dma4(ws_exp + (int64_t)gd * N, ws_off32, st.ws + wv * WCOLS);
+    if (lane < 16) dma4(As + (int64_t)gd * R, as_off32, st.as + wv * 16);
   };
 
   // sum of this wave's 16-row tile of the A tile of stage st -> st.ra as -sum/64, the
@@ -300,25 +361,14 @@ __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
 
   float acc[8][4][4];
 
-  // ---- prologue: groups 0 and 1 in flight, the seeds of group 0 formed
-  load_group(0, st0);
-  if (G > 1) load_group(1, st1);
-  if (G > 1)  // own group-0 loads landed (group 1's may still be in flight)
-    __builtin_amdgcn_s_waitcnt(kWaitVm8);
-  else
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-  row_sums(st0);
-  lds_barrier();
-
-  // ---- one K group. Three stages: group g is computed while g+1 and g+2 stream into LDS.
+  // ---- one K group of the current tile from stage `cur`; tmax = row tiles in use.
   // The group is 32 steps; step i = 4t + s issues the MFMA of tile (t, s) and folds the
   // MFMA of step i-2 (already complete), so the matrix core and the VALU work side by
-  // side; a sched_barrier after every step pins that interleaving. The first group
-  // initialises the accumulators (no separate zeroing).
-  auto group = [&](int g, auto first_tag, Stage& cur, Stage& nx1, Stage& nx2) {
+  // side; a sched_barrier after every step pins that interleaving. The first group of a
+  // tile initialises the accumulators (no separate zeroing).
+  auto group = [&](auto first_tag, const Stage& cur) {
     constexpr bool FIRST = decltype(first_tag)::value;
-    const bool has2 = g + 2 < G;
-    if (has2) load_group(g + 2, nx2);
+    constexpr int tmax = BM / 16;
     const uint8_t* ta = cur.a;
     const uint8_t* tb = cur.b + wv * BW_BYTES;
     const float* ra = cur.ra;
@@ -367,144 +417,193 @@ __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const int t = i >> 2, s = i & 3;
-      if (s == 0 && t < 7) {  // A operand and seed of the next row tile
-        aop[(t + 1) & 1] = lds_a_operand(ta, (t + 1) * 16 + c16, q);
-        const float4 c4 = *reinterpret_cast<const float4*>(&ra[(t + 1) * 16 + 4 * q]);
-        seed[(t + 1) & 1] = (v4f){c4.x, c4.y, c4.z, c4.w};
+      if (t < tmax) {  // uniform
+        if (s == 0 && t + 1 < tmax) {  // A operand and seed of the next row tile
+          aop[(t + 1) & 1] = lds_a_operand(ta, (t + 1) * 16 + c16, q);
+          const float4 c4 = *reinterpret_cast<const float4*>(&ra[(t + 1) * 16 + 4 * q]);
+          seed[(t + 1) & 1] = (v4f){c4.x, c4.y, c4.z, c4.w};
+        }
+        if (s == 2 && t + 1 < tmax)  // A scales of the next row tile (tile t-1's folds are done)
+          sa[(t + 1) & 1] = *reinterpret_cast<const float4*>(&sag[(t + 1) * 16 + 4 * q]);
+        pb[i % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop[t & 1], bop[s],
+                                                                     seed[t & 1], 0, 0, 0, 0, 0, 0);
       }
-      if (s == 2 && t < 7)  // A scales of the next row tile (tile t-1's folds are done)
-        sa[(t + 1) & 1] = *reinterpret_cast<const float4*>(&sag[(t + 1) * 16 + 4 * q]);
-      pb[i % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop[t & 1], bop[s],
-                                                                   seed[t & 1], 0, 0, 0, 0, 0, 0);
-      if (i >= 2) fold(i - 2);
+      if (i >= 2 && ((i - 2) >> 2) < tmax) fold(i - 2);
       __builtin_amdgcn_sched_barrier(0);
     }
-    fold(30);
-    fold(31);
-    // own loads of group g+1 landed (group g+2's may still be in flight)
-    if (has2)
-      __builtin_amdgcn_s_waitcnt(kWaitVm8);
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
-    if (g + 1 < G) row_sums(nx1);
-    lds_barrier();
+    if (tmax == 8) {
+      fold(30);
+      fold(31);
+    }
   };
 
-  // group g uses stage g % 3 (named statically, see Stage)
-  group(0, std::true_type{}, st0, st1, st2);
-  for (int g = 1; g < G; g += 3) {
-    group(g, std::false_type{}, st1, st2, st0);
-    if (g + 1 < G) group(g + 1, std::false_type{}, st2, st0, st1);
-    if (g + 2 < G) group(g + 2, std::false_type{}, st0, st1, st2);
-  }
+  // ---- epilogue of a finished tile. Output element (t, s, r) of this lane: row
+  // t*16 + 4q + r, workgroup column wv*64 + s*16 + c16. `scr` is the stage the tile's last
+  // group was computed from: free until the loads of a later group are issued into it.
+  auto epilogue = [&](const TileDesc& t, Stage& scr) {
+    const int rows = t.rows, row_begin = t.row_begin, nt = t.nt;
+    if (EPI == FP8MOE_EPI_STORE && OUT_BF16) {
+      // stage the bf16 tile in LDS 32 rows at a time (32 KB), then write whole 1 KB row
+      // segments
+      uint16_t* s_out = reinterpret_cast<uint16_t*>(scr.b);
+      const int ncols = min(WCOLS_WG, N - nt * WCOLS_WG);  // multiple of 16
+      uint16_t* o16 = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+      for (int part = 0; part < 4; ++part) {
+        if (32 * part >= rows) break;  // uniform
+#pragma unroll
+        for (int t8 = 2 * part; t8 < 2 * part + 2; ++t8)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int s = 0; s < 4; s += 2) {
+              const uint32_t pk = bf16x2(acc[t8][s][r], acc[t8][s + 1][r]);
+              uint16_t* o = &s_out[((t8 - 2 * part) * 16 + 4 * q + r) * WCOLS_WG + wv * WCOLS +
+                                   s * 16 + c16];
+              o[0] = (uint16_t)(pk & 0xFFFFu);
+              o[16] = (uint16_t)(pk >> 16);
+            }
+        lds_barrier();
+        for (int i = tid; i < 32 * (WCOLS_WG / 8); i += NT_THREADS) {
+          const int rl = i >> 6, ch = i & 63, row = 32 * part + rl;
+          if (row < rows && ch * 8 < ncols)
+            *reinterpret_cast<uint4*>(&o16[(int64_t)(row_begin + row) * N + nt * WCOLS_WG + ch * 8]) =
+                *reinterpret_cast<const uint4*>(&s_out[rl * WCOLS_WG + ch * 8]);
+        }
+        lds_barrier();
+      }
+    } else if (EPI == FP8MOE_EPI_STORE) {
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = t8 * 16 + 4 * q + r;
+          if (row < rows) {
+            const int64_t orow = (int64_t)(row_begin + row) * N;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const int cc = nt * WCOLS_WG + wv * WCOLS + s * 16 + c16;
+              if (cc < N) reinterpret_cast<float*>(out)[orow + cc] = acc[t8][s][r];
+            }
+          }
+        }
+    } else {
+      // SwiGLU + e4m3 per (row, 128 h columns). Wave wv works on h group hg = wv >> 2 of the
+      // tile; its h column of (t, s', r) is (wv & 3)*32 + s'*16 + c16 within the group. h
+      // overwrites the gate accumulators.
+      const int hg = wv >> 2;
+      float* s_amax = reinterpret_cast<float*>(scr.a);      // [8 waves][BM]
+      float* s_inv = s_amax + NW * BM;                       // [2 h groups][BM]
+      uint8_t* s_codes = scr.b;                              // [2][BM][128]
+      const int tmax = (rows + 15) >> 4;
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) {
+        if (t8 >= tmax) break;  // uniform
+        float m[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          m[r] = 0.f;
+#pragma unroll
+          for (int sp = 0; sp < 2; ++sp) {
+            const float gt = acc[t8][sp][r], up = acc[t8][sp + 2][r];
+            const float hv = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
+            acc[t8][sp][r] = hv;
+            m[r] = fmaxf(m[r], fabsf(hv));
+          }
+        }
+        // max of rows r = 0..3 over the 16 lanes of this row group (transposing butterfly)
+        const float mr = row4_max16(m, c16);
+        if (c16 < 4) s_amax[wv * BM + t8 * 16 + 4 * q + 2 * (c16 & 1) + ((c16 >> 1) & 1)] = mr;
+      }
+      lds_barrier();
+      if (tid < 2 * BM) {
+        const int g2 = tid >> 7, row = tid & (BM - 1);
+        const float* am = s_amax + g2 * 4 * BM + row;
+        const float m = fmaxf(fmaxf(am[0], am[BM]), fmaxf(am[2 * BM], am[3 * BM]));
+        float sc, inv;
+        scale_pair(m, sc, inv);
+        s_inv[tid] = inv;
+        const int hcol = nt * 256 + g2 * 128;
+        if (row < rows && hcol < I) out_scales[(int64_t)(hcol / kGroup) * R + row_begin + row] = sc;
+      }
+      lds_barrier();
+      const float* inv_g = s_inv + hg * BM;
+      uint8_t* codes_g = s_codes + hg * BM * 128;
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) {
+        if (t8 >= tmax) break;  // uniform
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = t8 * 16 + 4 * q + r;
+          const float inv = inv_g[row];
+          const uint32_t c2 = e4m3x2_finite(acc[t8][0][r] * inv, acc[t8][1][r] * inv);
+          codes_g[row * 128 + (wv & 3) * 32 + c16] = (uint8_t)(c2 & 0xFF);
+          codes_g[row * 128 + (wv & 3) * 32 + 16 + c16] = (uint8_t)((c2 >> 8) & 0xFF);
+        }
+      }
+      lds_barrier();
+      uint8_t* o8 = reinterpret_cast<uint8_t*>(out);
+      for (int i = tid; i < 2 * BM * 8; i += NT_THREADS) {
+        const int g2 = i >> 10, row = (i >> 3) & (BM - 1), ch = i & 7;
+        const int hcol = nt * 256 + g2 * 128;
+        if (row < rows && hcol < I)
+          *reinterpret_cast<uint4*>(&o8[(int64_t)(row_begin + row) * I + hcol + ch * 16]) =
+              *reinterpret_cast<const uint4*>(&s_codes[(g2 * BM + row) * 128 + ch * 16]);
+      }
+      lds_barrier();
+    }
+  };
 
-  // ---- epilogues. Output element (t, s, r) of this lane: row t*16 + 4q + r, workgroup
-  // column wv*64 + s*16 + c16.
-  if (EPI == FP8MOE_EPI_STORE && OUT_BF16) {
-    // stage the bf16 tile in LDS 32 rows at a time (32 KB), then write whole 1 KB row
-    // segments
-    uint16_t* s_out = reinterpret_cast<uint16_t*>(st0.b);
-    const int ncols = min(WCOLS_WG, N - nt * WCOLS_WG);  // multiple of 16
-    uint16_t* o16 = reinterpret_cast<uint16_t*>(out);
-#pragma unroll
-    for (int part = 0; part < 4; ++part) {
-#pragma unroll
-      for (int t = 2 * part; t < 2 * part + 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int s = 0; s < 4; s += 2) {
-            const uint32_t pk = bf16x2(acc[t][s][r], acc[t][s + 1][r]);
-            uint16_t* o = &s_out[((t - 2 * part) * 16 + 4 * q + r) * WCOLS_WG + wv * WCOLS +
-                                 s * 16 + c16];
-            o[0] = (uint16_t)(pk & 0xFFFFu);
-            o[16] = (uint16_t)(pk >> 16);
-          }
-      __syncthreads();
-      for (int i = tid; i < 32 * (WCOLS_WG / 8); i += NT_THREADS) {
-        const int rl = i >> 6, ch = i & 63, row = 32 * part + rl;
-        if (row < rows && ch * 8 < ncols)
-          *reinterpret_cast<uint4*>(&o16[(int64_t)(row_begin + row) * N + nt * WCOLS_WG + ch * 8]) =
-              *reinterpret_cast<const uint4*>(&s_out[rl * WCOLS_WG + ch * 8]);
-      }
-      __syncthreads();
-    }
-  } else if (EPI == FP8MOE_EPI_STORE) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = t * 16 + 4 * q + r;
-        if (row < rows) {
-          const int64_t orow = (int64_t)(row_begin + row) * N;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const int cc = nt * WCOLS_WG + wv * WCOLS + s * 16 + c16;
-            if (cc < N) reinterpret_cast<float*>(out)[orow + cc] = acc[t][s][r];
-          }
-        }
-      }
+  // ---- prologue: groups 0 and 1 in flight, the seeds of group 0 formed
+  dma_group(0, ring[0]);
+  if (total_steps > 1) {
+    // with one group per tile, group 1 starts a new tile whose rows group 0's call fetched
+    if (G == 1) wait_all_but_one_group();
+    dma_group(1, ring[1]);
+    wait_all_but_one_group();
   } else {
-    // SwiGLU + e4m3 per (row, 128 h columns). Wave wv works on h group hg = wv >> 2 of the
-    // workgroup; its h column of (t, s', r) is (wv & 3)*32 + s'*16 + c16 within the group.
-    const int hg = wv >> 2;
-    float* s_amax = reinterpret_cast<float*>(st0.a);       // [8 waves][BM]
-    float* s_inv = s_amax + NW * BM;                        // [2 h groups][BM]
-    uint8_t* s_codes = st0.b;                               // [2][BM][128]
-    float h[8][2][4];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      float m[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        m[r] = 0.f;
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-          float gt = acc[t][sp][r], up = acc[t][sp + 2][r];
-          float hv = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
-          h[t][sp][r] = hv;
-          m[r] = fmaxf(m[r], fabsf(hv));
-        }
-      }
-      // max of rows r = 0..3 over the 16 lanes of this row group (transposing butterfly)
-      const float mr = row4_max16(m, c16);
-      if (c16 < 4) s_amax[wv * BM + t * 16 + 4 * q + 2 * (c16 & 1) + ((c16 >> 1) & 1)] = mr;
-    }
-    __syncthreads();
-    if (tid < 2 * BM) {
-      const int g2 = tid >> 7, row = tid & (BM - 1);
-      const float* am = s_amax + g2 * 4 * BM + row;
-      float m = fmaxf(fmaxf(am[0], am[BM]), fmaxf(am[2 * BM], am[3 * BM]));
-      float sc, inv;
-      scale_pair(m, sc, inv);
-      s_inv[tid] = inv;
-      const int hcol = nt * 256 + g2 * 128;
-      if (row < rows && hcol < I)
-        out_scales[(int64_t)(row_begin + row) * (I / kGroup) + hcol / kGroup] = sc;
-    }
-    __syncthreads();
-    const float* inv_g = s_inv + hg * BM;
-    uint8_t* codes_g = s_codes + hg * BM * 128;
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = t * 16 + 4 * q + r;
-        const float inv = inv_g[row];
-        uint32_t c2 = e4m3x2_finite(h[t][0][r] * inv, h[t][1][r] * inv);
-        codes_g[row * 128 + (wv & 3) * 32 + c16] = (uint8_t)(c2 & 0xFF);
-        codes_g[row * 128 + (wv & 3) * 32 + 16 + c16] = (uint8_t)((c2 >> 8) & 0xFF);
-      }
-    __syncthreads();
-    uint8_t* o8 = reinterpret_cast<uint8_t*>(out);
-    for (int i = tid; i < 2 * BM * 8; i += NT_THREADS) {
-      const int g2 = i >> 10, row = (i >> 3) & (BM - 1), ch = i & 7;
-      const int hcol = nt * 256 + g2 * 128;
-      if (row < rows && hcol < I)
-        *reinterpret_cast<uint4*>(&o8[(int64_t)(row_begin + row) * I + hcol + ch * 16]) =
-            *reinterpret_cast<const uint4*>(&s_codes[(g2 * BM + row) * 128 + ch * 16]);
-    }
+    wait_all_loads();
   }
+  row_sums(ring[0]);
+  lds_barrier();
+
+  // ---- the stream of K groups: group s is computed from stage s % 3 while s+1 and s+2
+  // stream into the other two stages. Tiles are consecutive runs of G groups; the first
+  // group of a tile initialises the accumulators, the epilogue follows its last group.
+  int s = 0;
+  auto step = [&](auto first_tag) {
+    const int stage = s % 3;
+    const bool more2 = s + 2 < total_steps;
+    if (more2) dma_group(s + 2, ring[stage == 0 ? 2 : stage - 1]);
+    group(first_tag, ring[stage]);
+    // own loads of group s+1 landed (group s+2's may still be in flight)
+    if (more2)
+      wait_all_but_one_group();
+    else
+      wait_all_loads();
+    if (s + 1 < total_steps) row_sums(ring[stage == 2 ? 0 : stage + 1]);
+    lds_barrier();
+    ++s;
+  };
+  for (int j = 0; j < my_tiles; ++j) {
+    step(std::true_type{});
+    for (int g = 1; g < G; ++g) step(std::false_type{});
+    epilogue(tile_of(j), ring[(s + 2) % 3]);
+  }
+}
+
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -515,24 +614,25 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const in
                                int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
                                float* out_scales, hipStream_t st) {
   if (R == 0) return hipSuccess;
-  const int64_t mtiles = (R + BM - 1) / BM + E;
+  const int64_t mtiles = (R + BM - 1) / BM + E;  // bound on the m-tiles over all experts
   // SwiGLU: a tile covers 256 h columns (gate and up); otherwise 512 output columns
   const int NT = epilogue == FP8MOE_EPI_SWIGLU_QUANT ? (int)((N / 2 + 255) / 256)
                                                      : (int)((N + WCOLS_WG - 1) / WCOLS_WG);
-  const int64_t blocks = mtiles * NT;
-  dim3 grid((uint32_t)blocks), block(NT_THREADS);
+  const int64_t grid = std::min<int64_t>(cu_count(), mtiles * NT);
+  const int a_rows = (int)(sorted ? R / k_route : R);
+  dim3 g((uint32_t)grid), block(NT_THREADS);
   if (epilogue == FP8MOE_EPI_SWIGLU_QUANT)
-    grouped_gemm_kernel<FP8MOE_EPI_SWIGLU_QUANT, false><<<grid, block, 0, st>>>(
-        a, a_scales, sorted, k_route, w, w_scales, offsets, E, (int)N, (int)K, NT, out,
-        out_scales);
+    grouped_gemm_kernel<FP8MOE_EPI_SWIGLU_QUANT, false><<<g, block, 0, st>>>(
+        a, a_scales, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N, (int)K,
+        NT, out, out_scales);
   else if (out_dtype == FP8MOE_DTYPE_BF16)
-    grouped_gemm_kernel<FP8MOE_EPI_STORE, true><<<grid, block, 0, st>>>(
-        a, a_scales, sorted, k_route, w, w_scales, offsets, E, (int)N, (int)K, NT, out,
-        nullptr);
+    grouped_gemm_kernel<FP8MOE_EPI_STORE, true><<<g, block, 0, st>>>(
+        a, a_scales, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N, (int)K,
+        NT, out, nullptr);
   else
-    grouped_gemm_kernel<FP8MOE_EPI_STORE, false><<<grid, block, 0, st>>>(
-        a, a_scales, sorted, k_route, w, w_scales, offsets, E, (int)N, (int)K, NT, out,
-        nullptr);
+    grouped_gemm_kernel<FP8MOE_EPI_STORE, false><<<g, block, 0, st>>>(
+        a, a_scales, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N, (int)K,
+        NT, out, nullptr);
   return hipGetLastError();
 }
 

@@ -28,6 +28,9 @@ hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32
                                 int32_t* pos, const uint8_t* xq, const float* xs, int64_t H,
                                 uint8_t* xq_perm, float* xs_perm, void* ws, hipStream_t st);
 
+hipError_t launch_pack_bank(const uint8_t* w, const float* w_scales, int64_t E, int64_t N,
+                            int64_t K, uint8_t* w_packed, float* ws_packed, hipStream_t st);
+
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,
                                int32_t k_route, const uint8_t* w, const float* w_scales,
                                const int32_t* offsets, int64_t R, int32_t E, int64_t N,

@@ -15,7 +15,8 @@
 //   3. scatter:    one workgroup per chunk recomputes the expert offsets (a scan over E),
 //                  ranks each pair among the chunk's earlier pairs of the same expert and
 //                  writes sorted[] and pos[].
-//   4. gather:     optional copy of the e4m3 rows and scales into grouped order.
+//   4. gather:     optional copies of the e4m3 rows and (group-major) scales into grouped
+//                  order.
 #include "common.h"
 #include "launch.h"
 
@@ -181,22 +182,30 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   }
 }
 
-// Grouped row i <- token sorted[i] / k: e4m3 row (H bytes) and its H/128 scales.
-__global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ sorted, int k,
-                                                     int64_t R, int64_t H,
-                                                     const uint4* __restrict__ xq,
-                                                     const float* __restrict__ xs,
-                                                     uint4* __restrict__ xq_perm,
-                                                     float* __restrict__ xs_perm) {
+// Grouped row i <- token sorted[i] / k: its e4m3 row (H bytes), 16 bytes per thread.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const int32_t* __restrict__ sorted,
+                                                          int k, int64_t R, int64_t H,
+                                                          const uint4* __restrict__ xq,
+                                                          uint4* __restrict__ xq_perm) {
   const int64_t per_row = H / 16;
-  const int64_t G = H / kGroup;
-  int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  int64_t row = j / per_row;
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = j / per_row;
   if (row < R) {
-    int64_t tok = sorted[row] / k;
-    int64_t col = j - row * per_row;
-    xq_perm[j] = xq[tok * per_row + col];
-    if (col < G) xs_perm[row * G + col] = xs[tok * G + col];
+    const int64_t tok = sorted[row] / k;
+    xq_perm[j] = xq[tok * per_row + (j - row * per_row)];
+  }
+}
+
+// Scales of grouped row i, group-major: xs_perm[g * R + i] = xs[(sorted[i] / k) * G + g].
+// One thread per (g, i), consecutive threads on consecutive grouped rows.
+__global__ __launch_bounds__(256) void gather_scales_kernel(const int32_t* __restrict__ sorted,
+                                                            int k, int64_t R, int64_t G,
+                                                            const float* __restrict__ xs,
+                                                            float* __restrict__ xs_perm) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j < R * G) {
+    const int64_t g = j / R, row = j - g * R;
+    xs_perm[j] = xs[(int64_t)(sorted[row] / k) * G + g];
   }
 }
 
@@ -223,12 +232,17 @@ hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32
   scatter_kernel<<<dim3((uint32_t)C), 256, 0, st>>>(ids, T, E, k, cnt, tot, offsets, sorted,
                                                     pos);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t R = T * k;
   if (xq != nullptr) {
-    int64_t R = T * k;
-    int64_t n = R * (H / 16);
-    gather_kernel<<<dim3((uint32_t)((n + 255) / 256)), 256, 0, st>>>(
-        sorted, k, R, H, reinterpret_cast<const uint4*>(xq), xs,
-        reinterpret_cast<uint4*>(xq_perm), xs_perm);
+    const int64_t n = R * (H / 16);
+    gather_rows_kernel<<<dim3((uint32_t)((n + 255) / 256)), 256, 0, st>>>(
+        sorted, k, R, H, reinterpret_cast<const uint4*>(xq), reinterpret_cast<uint4*>(xq_perm));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (xs != nullptr) {
+    const int64_t n = R * (H / kGroup);
+    gather_scales_kernel<<<dim3((uint32_t)((n + 255) / 256)), 256, 0, st>>>(
+        sorted, k, R, H / kGroup, xs, xs_perm);
     e = hipGetLastError();
   }
   return e;

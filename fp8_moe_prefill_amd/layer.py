@@ -19,10 +19,11 @@ from . import _lib
 
 @dataclass
 class ExpertBank:
-    """Resident expert weights of one MoE layer (device tensors).
+    """Resident expert weights of one MoE layer (device tensors), in the layout the grouped
+    GEMM streams (see ``pack_expert_bank``).
 
-    w_gu: packed int4 [E, 2I, H/2] (gate rows 0..I-1, up rows I..2I-1), s_gu fp32
-    [E, 2I, H/128]; w_dn: packed int4 [E, H, I/2], s_dn fp32 [E, H, I/128].
+    w_gu: bank bytes [E, 2I, H/2] (gate rows 0..I-1, up rows I..2I-1), s_gu fp32
+    [E, H/128, 2I]; w_dn: bank bytes [E, H, I/2], s_dn fp32 [E, I/128, H].
     """
 
     w_gu: torch.Tensor
@@ -43,9 +44,18 @@ class ExpertBank:
         return self.w_dn.shape[1]
 
     @staticmethod
+    def from_canonical(w_gu, s_gu, w_dn, s_dn, stream=None) -> "ExpertBank":
+        """Canonical device tensors (packed int4 [E, N, K/2], low nibble = even k; scales
+        [E, N, K/128]) -> the packed layout (one-time, at load)."""
+        gu = _lib.pack_expert_bank(w_gu, s_gu, stream=stream)
+        dn = _lib.pack_expert_bank(w_dn, s_dn, stream=stream)
+        return ExpertBank(gu[0], gu[1], dn[0], dn[1])
+
+    @staticmethod
     def from_host(d: dict, device) -> "ExpertBank":
-        return ExpertBank(*(torch.from_numpy(d[n]).to(device) for n in ("w_gu", "s_gu", "w_dn",
-                                                                        "s_dn")))
+        """Canonical host arrays w_gu, s_gu, w_dn, s_dn -> a packed bank on ``device``."""
+        t = [torch.from_numpy(d[n]).to(device) for n in ("w_gu", "s_gu", "w_dn", "s_dn")]
+        return ExpertBank.from_canonical(*t)
 
 
 def moe_layer(x: torch.Tensor, logits: torch.Tensor, bank: ExpertBank, k: int,
@@ -56,10 +66,10 @@ def moe_layer(x: torch.Tensor, logits: torch.Tensor, bank: ExpertBank, k: int,
     T = x.shape[0]
     R = T * k
     xq, xs = _lib.fp8_quant_act(x, _lib.GROUP, stream=stream)
-    rt = _lib.moe_route_permute(logits, k, stream=stream)
-    hq, hs = _lib.fp8_grouped_expert_gemm(xq, xs, bank.w_gu, bank.s_gu, rt["offsets"], R,
-                                          _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"],
-                                          k_route=k, stream=stream)
+    rt = _lib.moe_route_permute(logits, k, xs=xs, stream=stream)
+    hq, hs = _lib.fp8_grouped_expert_gemm(xq, rt["xs_perm"], bank.w_gu, bank.s_gu,
+                                          rt["offsets"], R, _lib.EPI_SWIGLU_QUANT,
+                                          sorted_=rt["sorted"], k_route=k, stream=stream)
     y = _lib.fp8_grouped_expert_gemm(hq, hs, bank.w_dn, bank.s_dn, rt["offsets"], R,
                                      _lib.EPI_STORE, out_dtype=torch.bfloat16, stream=stream)
     out = _lib.moe_unpermute_combine(y, rt["pos"], rt["weights"], torch.bfloat16, stream=stream)
@@ -101,11 +111,12 @@ class MoELayerRunner:
                           weights=torch.empty((T, k), dtype=f32, device=dev),
                           offsets=torch.empty(E + 1, dtype=i32, device=dev),
                           sorted=torch.empty(R, dtype=i32, device=dev),
-                          pos=torch.empty(R, dtype=i32, device=dev))
+                          pos=torch.empty(R, dtype=i32, device=dev),
+                          xs_perm=torch.empty((H // _lib.GROUP, R), dtype=f32, device=dev))
         nws = _lib.workspace_bytes(_lib.OP_ROUTE_PERMUTE, T, E, k)
         self.ws = torch.empty(max(nws, 256), dtype=u8, device=dev)
         self.hq = torch.empty((R, I), dtype=u8, device=dev)
-        self.hs = torch.empty((R, I // _lib.GROUP), dtype=f32, device=dev)
+        self.hs = torch.empty((I // _lib.GROUP, R), dtype=f32, device=dev)
         self.y = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
@@ -121,10 +132,10 @@ class MoELayerRunner:
         _lib.fp8_quant_act(x, _lib.GROUP, q=self.xq, scales=self.xs, stream=stream)
         mark("quant", 1)
         mark("route", 0)
-        _lib.moe_route_permute(logits, self.k, out=rt, ws=self.ws, stream=stream)
+        _lib.moe_route_permute(logits, self.k, xs=self.xs, out=rt, ws=self.ws, stream=stream)
         mark("route", 1)
         mark("gate_up", 0)
-        _lib.fp8_grouped_expert_gemm(self.xq, self.xs, bank.w_gu, bank.s_gu, rt["offsets"],
+        _lib.fp8_grouped_expert_gemm(self.xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"],
                                      self.R, _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"],
                                      k_route=self.k, out=self.hq, out_scales=self.hs,
                                      stream=stream)

@@ -127,9 +127,12 @@ int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int32_t group, uint8_
  *   sorted   out, int32 [T*k]: grouped row i holds pair p = sorted[i] = t*k + j; within
  *            an expert pairs keep increasing p (a stable order)
  *   pos      out, int32 [T*k]: pos[p] = the grouped row of pair p
- *   xq, xs, H      optional (all NULL/0 or all set): e4m3 [T, H] rows and fp32
- *                  [T, H/128] scales to gather into grouped order
- *   xq_perm, xs_perm  out when gathering: e4m3 [T*k, H], fp32 [T*k, H/128]
+ *   xq, xq_perm    optional pair (both NULL or both set): e4m3 rows [T, H] gathered into
+ *                  grouped order, xq_perm = e4m3 [T*k, H]
+ *   xs, xs_perm    optional pair (both NULL or both set): fp32 scales [T, H/128] gathered
+ *                  into grouped order, GROUP-MAJOR: xs_perm[g * T*k + i] is the scale of
+ *                  group g of grouped row i (the layout fp8_grouped_expert_gemm reads)
+ *   H              row width of xq / xs (needed when either pair is set)
  *   ws       workspace of fp8moe_workspace_bytes(FP8MOE_OP_ROUTE_PERMUTE, T, E, k)
  * Constraints: T >= 1, 1 <= E <= 1024, 1 <= k <= min(E, 32), T*k < 2^31;
  * H % 128 == 0 when gathering. Every output is a pure function of the inputs (no
@@ -142,6 +145,33 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
                           void* stream);
 
 /*
+ * fp8moe_pack_expert_bank -- one-time repacking of a packed-int4 expert bank (and its
+ * scales) into the layout fp8_grouped_expert_gemm streams. A byte permutation and a
+ * transpose: nothing is dequantised or widened, the bank stays at 4 bits per weight.
+ *
+ * [P1] section 1: the int4 bank stays packed and resident and is converted to e4m3
+ * on-chip; its nibble order and block layout are this library's choice (the pages fix
+ * neither), made so that one wave-wide load brings one contiguous 1 KB block.
+ *
+ *   w                canonical bank, packed int4 [E, N, K/2], two's complement -8..7:
+ *                    byte i of row (e, n) holds k = 2i in its low nibble and k = 2i+1 in
+ *                    its high nibble
+ *   w_scales         fp32 [E, N, K/128]
+ *   w_packed         out, E*N*K/2 bytes. Block (e, c, g) of 1024 bytes, at byte
+ *                    ((e * N/16 + c) * K/128 + g) * 1024, holds columns 16c .. 16c+15 and
+ *                    k in [128g, 128g+128): its 16 bytes at 16 * (16h + i) are column
+ *                    16c + i, k = 128g + 32h + 0..31, as four little-endian 32-bit words;
+ *                    byte b of word j holds k0 + b in the low nibble and k0 + 4 + b in the
+ *                    high nibble, k0 = 128g + 32h + 8j
+ *   w_scales_packed  out, fp32 [E, K/128, N] (the scales of one K group contiguous)
+ * The outputs must not overlap the inputs. Constraints: 1 <= E <= 1024, N % 16 == 0,
+ * 128 <= K <= 16384, K % 128 == 0, N*K/2 < 2^32.
+ */
+int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t E, int64_t N,
+                                int64_t K, uint8_t* w_packed, float* w_scales_packed,
+                                void* stream);
+
+/*
  * fp8_grouped_expert_gemm -- one launch over every expert.
  *
  * [P1] section 1: a single grouped expert GEMM per layer; int4 weights turned into
@@ -149,27 +179,29 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
  * activation scale folded into the accumulator.
  *
  * For grouped row i in expert e's range [offsets[e], offsets[e+1]) and column n:
- *   y[i, n] = sum_g a_scales[r, g] * w_scales[e, n, g]
+ *   y[i, n] = sum_g a_scales[g, i] * w_scales[e, n, g]
  *                   * sum_{k in group g} e4m3(a[r, k]) * int4(w[e, n, k])
  * with r = i, or r = sorted[i] / k_route when `sorted` is given (the A rows are then
- * gathered on the fly from token order and no permuted copy is needed).
+ * gathered on the fly from token order and no permuted copy of them is needed; their
+ * scales come already grouped, see moe_route_permute's xs_perm).
  *
  *   a          e4m3 [Ra, K]  (Ra = R without `sorted`, Ra = R / k_route with it)
- *   a_scales   fp32 [Ra, K/128]
+ *   a_scales   fp32 [K/128, R], group-major: the scale of group g of grouped row i is
+ *              a_scales[g * R + i]
  *   sorted     NULL, or int32 [R] pair ids from moe_route_permute
  *   k_route    experts per token (used only with `sorted`)
- *   w          packed int4 [E, N, K/2], two's complement -8..7. Each little-endian
- *              32-bit word j of row (e, n) holds k = 8j..8j+7: its byte b (0..3) has
- *              k = 8j+b in the low nibble and k = 8j+4+b in the high nibble
- *   w_scales   fp32 [E, N, K/128]
+ *   w          the bank as laid out by fp8moe_pack_expert_bank
+ *   w_scales   its scales, fp32 [E, K/128, N] (fp8moe_pack_expert_bank's w_scales_packed)
  *   offsets    int32 [E+1] on the device (from moe_route_permute), offsets[E] = R
  *   R          total grouped rows (the host-side bound; not read back from offsets)
  *   epilogue   FP8MOE_EPI_STORE: out is [R, N] in out_dtype (fp32 or bf16, RNE);
  *              FP8MOE_EPI_SWIGLU_QUANT: N = 2I with gate columns 0..I-1 and up columns
  *              I..2I-1; h = silu(gate) * up in fp32 is quantised like fp8_quant_act
- *              (group 128) into out = e4m3 [R, I] and out_scales = fp32 [R, I/128]
+ *              (group 128) into out = e4m3 [R, I] and out_scales = fp32 [I/128, R],
+ *              group-major like a_scales (ready to be the next GEMM's a_scales)
  * Constraints: R >= 0 (R = 0 is a no-op), 1 <= E <= 1024, K % 128 == 0,
- * 128 <= K <= 4096, R*K < 2^32, N*K/2 < 2^32; STORE: N % 16 == 0; SWIGLU_QUANT: N % 256 == 0.
+ * 128 <= K <= 16384, R*K < 2^32, N*K/2 < 2^32; STORE: N % 16 == 0; SWIGLU_QUANT:
+ * N % 256 == 0.
  */
 int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales,
                                 const int32_t* sorted, int32_t k_route, const uint8_t* w,

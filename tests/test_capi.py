@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
     raw = ctypes.CDLL(LIB)
     for name in declared_functions():
         assert hasattr(raw, name), name
-    assert lib.fp8moe_abi_version() == 1
+    assert lib.fp8moe_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -92,7 +92,9 @@ def _route(lib, logits=P, T=16, E=8, k=2, ws=P, ws_bytes=1 << 20, xq=None, xs=No
 def test_route_validation(lib):
     assert _route(lib, logits=None) == NULL
     assert _route(lib, ws=None) == NULL
-    assert _route(lib, xq=P) == NULL  # gather arguments must come together
+    assert _route(lib, xq=P) == NULL  # each gather pair must come together
+    assert _route(lib, xs=P) == NULL
+    assert _route(lib, xqp=P) == NULL
     assert _route(lib, T=0) == SHAPE
     assert _route(lib, E=0) == SHAPE
     assert _route(lib, E=1025, k=2) == SHAPE
@@ -101,6 +103,8 @@ def test_route_validation(lib):
     assert _route(lib, E=64, k=33) == SHAPE
     assert _route(lib, T=1 << 28, k=8) == SHAPE  # T*k >= 2^31
     assert _route(lib, xq=P, xs=P, xqp=P, xsp=P, H=100) == SHAPE
+    assert _route(lib, xs=P, xsp=P, H=100) == SHAPE  # scales-only gather
+    assert _route(lib, xs=P, xsp=U, H=256) == ALIGN
     assert _route(lib, ids=U) == ALIGN
     assert _route(lib, ws_bytes=16) == WS
 
@@ -121,13 +125,30 @@ def test_grouped_gemm_validation(lib):
     assert _gg(lib, E=1025) == SHAPE
     assert _gg(lib, K=100) == SHAPE
     assert _gg(lib, K=0) == SHAPE
-    assert _gg(lib, K=8192) == SHAPE
+    assert _gg(lib, K=32768) == SHAPE
     assert _gg(lib, R=1 << 22, K=2048) == SHAPE  # R*K >= 2^32
     assert _gg(lib, N=24) == SHAPE
     assert _gg(lib, epi=1, N=384) == SHAPE  # SwiGLU needs N % 256 == 0
     assert _gg(lib, sorted_=P, kr=0) == SHAPE
     assert _gg(lib, out=U) == ALIGN
     assert _gg(lib, R=0) == OK  # empty input is a no-op; nothing is launched
+    assert _gg(lib, R=64, N=1 << 20, K=16384) == SHAPE  # N*K/2 >= 2^32
+
+
+def _pack(lib, w=P, s=P, E=4, N=64, K=256, wp=P, sp=P):
+    return lib.fp8moe_pack_expert_bank(w, s, E, N, K, wp, sp, None)
+
+
+def test_pack_bank_validation(lib):
+    assert _pack(lib, w=None) == NULL
+    assert _pack(lib, sp=None) == NULL
+    assert _pack(lib, E=0) == SHAPE
+    assert _pack(lib, E=1025) == SHAPE
+    assert _pack(lib, N=24) == SHAPE
+    assert _pack(lib, K=200) == SHAPE
+    assert _pack(lib, K=32768) == SHAPE
+    assert _pack(lib, N=1 << 20, K=16384) == SHAPE
+    assert _pack(lib, wp=U) == ALIGN
 
 
 def test_dense_gemm_validation(lib):

@@ -1,5 +1,9 @@
 """fp8_grouped_expert_gemm on the GPU vs the oracle.
 
+The bank is the oracle's canonical one, put into the kernel's layout on the device by
+fp8moe_pack_expert_bank; activation scales go in group-major ([K/128, R], grouped row
+order), the SwiGLU epilogue's scales come back group-major.
+
 Floating outputs: |gpu - oracle| <= 1e-3 * sum_k |a_k w_k| + 1e-6 per element (fp32
 output); the bf16 output equals the fp32 output rounded to nearest even, bit for bit.
 SwiGLU + requantisation: checked against the oracle's SwiGLU applied to the GPU's own fp32
@@ -43,10 +47,23 @@ def _problem(counts, K, N, seed=0, scale_spread=True):
     return aq, as_, wp, ws, off
 
 
-def _gemm(aq, as_, wp, ws, off, out_dtype=torch.float32, sorted_=None, k_route=1, R=None):
+def _bank(wp, ws):
+    f = _lib()
+    return f.pack_expert_bank(dev(wp), dev(ws))
+
+
+def _gm(scales_rows):
+    """[R, K/128] scales in grouped row order -> the group-major device layout."""
+    return dev(np.ascontiguousarray(scales_rows.T))
+
+
+def _gemm(aq, as_grouped, wp, ws, off, out_dtype=torch.float32, sorted_=None, k_route=1,
+          R=None):
+    """STORE-mode grouped GEMM. as_grouped: [R, K/128] scales of the grouped rows."""
     f = _lib()
     R = aq.shape[0] if R is None else R
-    y = f.fp8_grouped_expert_gemm(dev(aq), dev(as_), dev(wp), dev(ws), dev(off), R,
+    w, s = _bank(wp, ws)
+    y = f.fp8_grouped_expert_gemm(dev(aq), _gm(as_grouped), w, s, dev(off), R,
                                   f.EPI_STORE, out_dtype,
                                   sorted_=None if sorted_ is None else dev(sorted_),
                                   k_route=k_route)
@@ -98,10 +115,10 @@ def test_on_the_fly_gather_equals_permuted_copy():
     ids, _ = topk_route(inp["logits"], c.k)
     off, sorted_, _ = group_pairs(ids, c.E)
     R = c.T * c.k
-    y_gather = host(_gemm(xq, xs, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k,
-                          R=R))
     aq = permute_rows(xq, sorted_, c.k)
     as_ = permute_rows(xs, sorted_, c.k)
+    y_gather = host(_gemm(xq, as_, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k,
+                          R=R))
     y_perm = host(_gemm(aq, as_, inp["w_gu"], inp["s_gu"], off))
     assert_bytes_equal(y_gather.view(np.uint32), y_perm.view(np.uint32), "gather vs permuted")
     ref, b = grouped_gemm(aq, as_, inp["w_gu"], inp["s_gu"], off, with_bound=True)
@@ -145,13 +162,15 @@ def test_swiglu_quant_epilogue(cfg):
     ids, _ = topk_route(inp["logits"], c.k)
     off, sorted_, _ = group_pairs(ids, c.E)
     R = c.T * c.k
-    args = (dev(xq), dev(xs), dev(inp["w_gu"]), dev(inp["s_gu"]), dev(off), R)
+    w, s = _bank(inp["w_gu"], inp["s_gu"])
+    args = (dev(xq), _gm(permute_rows(xs, sorted_, c.k)), w, s, dev(off), R)
     hq, hs = f.fp8_grouped_expert_gemm(*args, f.EPI_SWIGLU_QUANT, sorted_=dev(sorted_),
                                        k_route=c.k)
     y32 = f.fp8_grouped_expert_gemm(*args, f.EPI_STORE, torch.float32, sorted_=dev(sorted_),
                                     k_route=c.k)
     torch.cuda.synchronize()
-    _swiglu_check(host(hq), host(hs), host(y32))
+    assert tuple(hs.shape) == (c.I // 128, R)
+    _swiglu_check(host(hq), np.ascontiguousarray(host(hs).T), host(y32))
 
 
 def test_gate_up_full_size_sampled():
@@ -163,13 +182,13 @@ def test_gate_up_full_size_sampled():
     ids, _ = topk_route(inp["logits"], c.k)
     off, sorted_, _ = group_pairs(ids, c.E)
     R = c.T * c.k
-    y = host(_gemm(xq, xs, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k, R=R))
+    aq = permute_rows(xq, sorted_, c.k)
+    as_ = permute_rows(xs, sorted_, c.k)
+    y = host(_gemm(xq, as_, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k, R=R))
     rng = np.random.default_rng(11)
     rows = rng.integers(0, R, 4000)
     cols = rng.integers(0, 2 * c.I, 4000)
     rows[:64] = off[1:65] - 1  # last row of every expert
-    aq = permute_rows(xq, sorted_, c.k)
-    as_ = permute_rows(xs, sorted_, c.k)
     ref, b = grouped_gemm_rows(aq, as_, inp["w_gu"], inp["s_gu"], off, rows, cols)
     check_close(y[rows, cols].astype(np.float64), ref, gemm_bound(b), "gate|up sampled")
 
@@ -197,3 +216,36 @@ def test_repeat_runs_identical():
     a = host(_gemm(aq, as_, wp, ws, off))
     b = host(_gemm(aq, as_, wp, ws, off))
     assert_bytes_equal(a.view(np.uint32), b.view(np.uint32), "repeat")
+
+
+def test_pack_expert_bank_layout():
+    """The packed bank holds exactly the canonical int4 values at the documented
+    positions, and the scales are transposed (decoded here from the header's description
+    of the layout, independently of the kernels)."""
+    f = _lib()
+    rng = np.random.default_rng(5)
+    E, N, K = 3, 48, 384
+    wp = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    ws = rng.uniform(0.005, 0.02, size=(E, N, K // 128)).astype(np.float32)
+    pw, ps = f.pack_expert_bank(dev(wp), dev(ws))
+    torch.cuda.synchronize()
+    pw, ps = host(pw).reshape(-1), host(ps)
+    from oracle.codec import unpack_int4
+    q = unpack_int4(wp)  # [E, N, K] canonical values
+    G = K // 128
+    got = np.empty_like(q)
+    for e in range(E):
+        for c in range(N // 16):
+            for g in range(G):
+                blk = pw[((e * (N // 16) + c) * G + g) * 1024:][:1024]
+                for h in range(4):
+                    for i in range(16):
+                        b16 = blk[16 * (16 * h + i):][:16]
+                        for j in range(4):
+                            for b in range(4):
+                                byte = int(b16[4 * j + b])
+                                k0 = 128 * g + 32 * h + 8 * j
+                                for kk, nib in ((k0 + b, byte & 15), (k0 + 4 + b, byte >> 4)):
+                                    got[e, 16 * c + i, kk] = nib - 16 if nib >= 8 else nib
+    assert np.array_equal(got, q)
+    assert np.array_equal(ps, np.transpose(ws, (0, 2, 1)))

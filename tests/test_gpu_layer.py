@@ -42,7 +42,7 @@ def test_tiny_layer_all_outputs():
     assert_bytes_equal(host(st["sorted"]), ref["sorted"], "sorted")
     assert_bytes_equal(host(st["pos"]), ref["pos"], "pos")
     # down GEMM on the GPU's own intermediate codes
-    hq, hs = host(st["hq"]), host(st["hs"])
+    hq, hs = host(st["hq"]), np.ascontiguousarray(host(st["hs"]).T)
     y_ref, b = grouped_gemm(hq, hs, inp["w_dn"], inp["s_dn"], ref["offsets"], with_bound=True)
     y = bf16_values(st["y"])
     check_close(y, y_ref, gemm_bound(b) + half_ulp_bf16(y_ref), "down (bf16 out)")
@@ -69,7 +69,7 @@ def test_full_layer_sampled(cfg):
     if cfg == "moe_skewed":
         assert (np.diff(off) == 0).sum() >= 1
     # down GEMM, sampled, on the GPU's intermediate codes
-    hq, hs = host(st["hq"]), host(st["hs"])
+    hq, hs = host(st["hq"]), np.ascontiguousarray(host(st["hs"]).T)
     y = st["y"]
     R = c.T * c.k
     rng = np.random.default_rng(21)

@@ -84,7 +84,8 @@ def test_gather_rows_and_scales():
     gpu = _gpu_route(logits, c.k, xq, xs)
     _, _, sorted_, _ = _check(logits, c.k, gpu)
     assert_bytes_equal(gpu["xq_perm"], permute_rows(xq, sorted_, c.k), "gathered rows")
-    assert_bytes_equal(gpu["xs_perm"].view(np.uint32), permute_rows(xs, sorted_, c.k).view(np.uint32),
+    assert_bytes_equal(gpu["xs_perm"].view(np.uint32),
+                       np.ascontiguousarray(permute_rows(xs, sorted_, c.k).T).view(np.uint32),
                        "gathered scales")
 
 
