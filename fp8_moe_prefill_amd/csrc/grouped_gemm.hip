@@ -23,18 +23,19 @@
 //   +3%). The 2^9 is folded into the weight scale (exact). The prepacked bank stores the
 //   nibbles of a 32-bit word so that its low nibbles are four consecutive k and its high
 //   nibbles the next four: a byte split gives K-ordered e4m3 bytes with no permutes.
-// * Tile 128 rows x 512 accumulator columns per workgroup, 8 waves side by side along N
+// * Tile 128 rows x 256 accumulator columns per workgroup, 4 waves side by side along N
 //   (each wave: all 128 rows x 64 columns = 8 x 4 MFMA tiles, 128 fp32 accumulators per
-//   lane; two waves per SIMD). Per K group a tile stages 16 KB of A and 32 KB of packed B
-//   for 16.8 MFLOP. A (e4m3 rows, gathered from token order through `sorted` when given),
+//   lane), two workgroups per CU (two waves per SIMD, one from each). Per K group a tile
+//   stages 16 KB of A and 16 KB of packed B for 8.4 MFLOP. A (e4m3 rows, gathered from token order through `sorted` when given),
 //   each wave's packed B slice (one contiguous 1 KB block per 16 columns in the prepacked
 //   bank) and both scale vectors (contiguous per group in their group-major layouts) go
-//   straight from global memory into LDS (LDS DMA, no VGPR staging) through a ring of
-//   three stages: two groups in flight, one barrier per group.
-// * Persistent: the grid is one workgroup per CU and each workgroup walks its list of
-//   (expert, 128-row, 512-column) tiles as one continuous stream of K groups, so the loads
-//   of a tile's first groups overlap the previous tile's last groups and its epilogue, and
-//   no workgroup pays a cold start per tile. Tiles are dealt in contiguous ranges per XCD
+//   straight from global memory into LDS (LDS DMA, no VGPR staging) through two stages:
+//   the next group streams in while the current one is computed, one barrier per group.
+// * Persistent: the grid is two workgroups per CU and each walks its list of
+//   (expert, 128-row, 256-column) tiles as one continuous stream of K groups, so the first
+//   loads of a tile overlap the previous tile's tail, and no workgroup pays a cold start
+//   per tile. The two workgroups of a CU are independent: one's barrier waits, memory
+//   waits and epilogue are covered by the other's MFMA work. Tiles are dealt in contiguous ranges per XCD
 //   (each XCD has its own L2), so the m-tiles of one expert, which share B, and the
 //   n-tiles of one m-tile, which share A, run on the same L2. Row tiles past the end of an
 //   expert's last, partial m-tile are skipped.
@@ -43,8 +44,8 @@
 //   no host round trip.
 // * Epilogues: STORE writes fp32 or bf16; SWIGLU_QUANT pairs gate columns n and up columns
 //   I+n in the same wave, forms h = silu(gate) * up in fp32, takes the per-row amax over the
-//   workgroup's 128 h columns (= one 128-group of the down GEMM's K) and writes e4m3 codes
-//   plus fp32 scales, so h never goes to HBM in fp32 or bf16.
+//   tile's 128 h columns (= one 128-group of the down GEMM's K) and writes e4m3 codes plus
+//   fp32 scales, so h never goes to HBM in fp32 or bf16.
 #include <algorithm>
 #include <type_traits>
 
@@ -55,10 +56,11 @@ namespace fp8moe {
 namespace {
 
 constexpr int BM = 128;        // rows per tile
-constexpr int NW = 8;          // waves per workgroup
+constexpr int NW = 4;          // waves per workgroup (two workgroups per CU)
 constexpr int NT_THREADS = NW * 64;
+constexpr int RPW = BM / NW;   // A rows each wave stages (and sums)
 constexpr int WCOLS = 64;      // accumulator columns per wave
-constexpr int WCOLS_WG = NW * WCOLS;           // 512 accumulator columns per workgroup
+constexpr int WCOLS_WG = NW * WCOLS;           // 256 accumulator columns per workgroup
 constexpr int BW_BYTES = WCOLS * kGroup / 2;   // packed B slice of one wave, one group
 constexpr int kBlockBytes = 16 * kGroup / 2;   // prepacked bank block: 16 columns, one group
 constexpr float kWeightScaleMul = 512.f;       // 2^9: B codes are (q + 8) * 2^-9
@@ -120,16 +122,11 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, const void
   asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1\n\ts_nop 0"
                :: "v"(voff), "s"(base), "{m0}"(lds_addr(lds)) : "memory");
 }
-constexpr int kDmaPerGroup = 8;  // loads each wave issues per K group (see dma_group)
 
 // Waits and barriers of the pipeline. They are compiler memory barriers ("memory"
 // clobber), so no LDS access moves across them. The barrier drains this wave's LDS
 // traffic first (the only data other waves read after it); the direct-to-LDS loads are
-// waited for by count: vmcnt(8) leaves exactly the newest group's loads in flight.
-__device__ __forceinline__ void wait_all_but_one_group() {
-  static_assert(kDmaPerGroup == 8, "vmcnt immediate below");
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-}
+// waited for with vmcnt.
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -201,15 +198,15 @@ struct TileDesc {
 };
 
 template <int EPI, bool OUT_BF16>
-__global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
+__global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As,
     const int32_t* __restrict__ sorted, int k_route, int a_rows, const uint8_t* __restrict__ W,
     const float* __restrict__ Ws, const int32_t* __restrict__ offsets, int R, int E, int N,
     int K, int NT, void* __restrict__ out, float* __restrict__ out_scales) {
-  __shared__ Stage ring[3];
+  __shared__ Stage ring[2];
   __shared__ int s_mstart[kMaxExperts + 1];  // m-tiles before expert e
   __shared__ int s_tmp[NW];
-  __shared__ int s_src[NW][16];  // pair ids of the 16 rows each wave stages for the next tile
+  __shared__ int s_src[NW][RPW];  // pair ids of the rows each wave stages for the next tile
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in an SGPR
@@ -219,20 +216,21 @@ __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
   const int NB = N / 16;
   const int kshift = (k_route & (k_route - 1)) == 0 ? __builtin_ctz(k_route) : -1;
 
-  // ---- m-tiles per expert, prefix-summed (2 experts per thread, E <= 1024)
+  // ---- m-tiles per expert, prefix-summed (4 experts per thread, E <= 1024)
   {
-    int loc[2], sum = 0;
+    constexpr int EPT = kMaxExperts / NT_THREADS;
+    int loc[EPT], sum = 0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = tid * 2 + j;
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid * EPT + j;
       const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
       loc[j] = c > 0 ? (c + BM - 1) / BM : 0;
       sum += loc[j];
     }
     int run = block_inclusive_scan(sum, s_tmp) - sum;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = tid * 2 + j;
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid * EPT + j;
       run += loc[j];
       if (e < E) s_mstart[e + 1] = run;
     }
@@ -270,14 +268,12 @@ __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
     return d;
   };
 
-  // accumulator column j (0..511) of n-tile nt -> bank column. SwiGLU: the tile covers two
-  // 128-wide h groups (j >> 8); in each, wave (j >> 6) & 3 holds gate columns for
-  // (j >> 5) & 1 == 0 and the matching up columns (I + ...) for (j >> 5) & 1 == 1.
+  // accumulator column j (0..255) of n-tile nt -> bank column. SwiGLU: the tile covers one
+  // 128-wide h group; wave j >> 6 holds gate columns for (j >> 5) & 1 == 0 and the
+  // matching up columns (I + ...) for (j >> 5) & 1 == 1.
   auto bank_col = [&](int nt, int j) {
     if (EPI == FP8MOE_EPI_SWIGLU_QUANT)
-      return min(((j >> 5) & 1 ? I : 0) + nt * 256 + (j >> 8) * 128 + ((j >> 6) & 3) * 32 +
-                     (j & 31),
-                 N - 1);
+      return min(((j >> 5) & 1 ? I : 0) + nt * 128 + (j >> 6) * 32 + (j & 31), N - 1);
     return min(nt * WCOLS_WG + j, N - 1);
   };
 
@@ -286,14 +282,14 @@ __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
   // group ahead, older than that group's loads, so the group's counted wait covers them)
   TileDesc pend = tile_of(0);
   auto fetch_rows = [&](const TileDesc& d) {
-    if (sorted && lane < 16)
-      dma4(sorted, (uint32_t)max(min(d.row_begin + min(wv * 16 + lane, d.rows - 1), R - 1), 0) * 4u,
+    if (sorted && lane < RPW)
+      dma4(sorted, (uint32_t)max(min(d.row_begin + min(wv * RPW + lane, d.rows - 1), R - 1), 0) * 4u,
            &s_src[wv][0]);
   };
   fetch_rows(pend);
   wait_all_loads();
 
-  uint32_t a_off32[2] = {0, 0}, as_off32 = 0, ws_off32 = 0;
+  uint32_t a_off32[RPW / 8] = {}, as_off32 = 0, ws_off32 = 0;
   uint32_t b_blk[4] = {0, 0, 0, 0};  // byte offset of this wave's 4 column blocks in its expert
   const uint8_t* w_exp = W;
   const float* ws_exp = Ws;
@@ -305,21 +301,21 @@ __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
       // a new tile enters the stream: set up its sources from the prefetched descriptor
       const TileDesc t = pend;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int rl = 8 * j + (lane >> 3);  // row (of this wave's 16) staged by this lane
+      for (int j = 0; j < RPW / 8; ++j) {
+        const int rl = 8 * j + (lane >> 3);  // row (of this wave's RPW) staged by this lane
         int src;
         if (sorted) {
           const int p = s_src[wv][rl];
           src = kshift >= 0 ? (p >> kshift) : (p / k_route);  // uniform branch
         } else {
-          src = t.row_begin + min(wv * 16 + rl, t.rows - 1);
+          src = t.row_begin + min(wv * RPW + rl, t.rows - 1);
         }
         src = max(min(src, a_rows - 1), 0);
         const int c = (lane & 7) ^ a_swz(rl);
         a_off32[j] = (uint32_t)src * (uint32_t)K + (uint32_t)(c * 16);
       }
       as_off32 =
-          (uint32_t)max(min(t.row_begin + min(wv * 16 + (lane & 15), t.rows - 1), R - 1), 0) * 4u;
+          (uint32_t)max(min(t.row_begin + min(wv * RPW + (lane & (RPW - 1)), t.rows - 1), R - 1), 0) * 4u;
       ws_off32 = (uint32_t)bank_col(t.nt, wv * WCOLS + lane) * 4u;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -337,12 +333,12 @@ __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
     }
     const uint8_t* ag = A + gd * kGroup;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(ag, a_off32[j], st.a + (wv * 2 + j) * 1024);
+    for (int j = 0; j < RPW / 8; ++j) dma16(ag, a_off32[j], st.a + (wv * (RPW / 8) + j) * 1024);
     uint8_t* sb = st.b + wv * BW_BYTES;
 #pragma unroll
     for (int s = 0; s < 4; ++s) dma16(w_exp + b_blk[s] + gd * kBlockBytes, lane16, sb + s * 1024);
     dma4(ws_exp + (int64_t)gd * N, ws_off32, st.ws + wv * WCOLS);
-    if (lane < 16) dma4(As + (int64_t)gd * R, as_off32, st.as + wv * 16);
+    if (lane < RPW) dma4(As + (int64_t)gd * R, as_off32, st.as + wv * RPW);
   };
 
   // sum of this wave's 16-row tile of the A tile of stage st -> st.ra as -sum/64, the
@@ -351,12 +347,16 @@ __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
                     (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   auto row_sums = [&](Stage& st) {
-    v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lds_a_operand(st.a, wv * 16 + c16, q),
-                                                              ones, zero, 0, 0, 0, 0, 0, 0);
-    if (c16 == 0)
-      *reinterpret_cast<float4*>(&st.ra[wv * 16 + 4 * q]) =
-          make_float4(pr[0] * -0.015625f, pr[1] * -0.015625f, pr[2] * -0.015625f,
-                      pr[3] * -0.015625f);
+#pragma unroll
+    for (int h = 0; h < RPW / 16; ++h) {
+      const int r0 = wv * RPW + h * 16;
+      v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lds_a_operand(st.a, r0 + c16, q),
+                                                                ones, zero, 0, 0, 0, 0, 0, 0);
+      if (c16 == 0)
+        *reinterpret_cast<float4*>(&st.ra[r0 + 4 * q]) =
+            make_float4(pr[0] * -0.015625f, pr[1] * -0.015625f, pr[2] * -0.015625f,
+                        pr[3] * -0.015625f);
+    }
   };
 
   float acc[8][4][4];
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
   auto epilogue = [&](const TileDesc& t, Stage& scr) {
     const int rows = t.rows, row_begin = t.row_begin, nt = t.nt;
     if (EPI == FP8MOE_EPI_STORE && OUT_BF16) {
-      // stage the bf16 tile in LDS 32 rows at a time (32 KB), then write whole 1 KB row
+      // stage the bf16 tile in LDS 32 rows at a time (16 KB), then write whole 512 B row
       // segments
       uint16_t* s_out = reinterpret_cast<uint16_t*>(scr.b);
       const int ncols = min(WCOLS_WG, N - nt * WCOLS_WG);  // multiple of 16
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
             }
         lds_barrier();
         for (int i = tid; i < 32 * (WCOLS_WG / 8); i += NT_THREADS) {
-          const int rl = i >> 6, ch = i & 63, row = 32 * part + rl;
+          const int rl = i / (WCOLS_WG / 8), ch = i % (WCOLS_WG / 8), row = 32 * part + rl;
           if (row < rows && ch * 8 < ncols)
             *reinterpret_cast<uint4*>(&o16[(int64_t)(row_begin + row) * N + nt * WCOLS_WG + ch * 8]) =
                 *reinterpret_cast<const uint4*>(&s_out[rl * WCOLS_WG + ch * 8]);
@@ -488,13 +488,12 @@ __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
           }
         }
     } else {
-      // SwiGLU + e4m3 per (row, 128 h columns). Wave wv works on h group hg = wv >> 2 of the
-      // tile; its h column of (t, s', r) is (wv & 3)*32 + s'*16 + c16 within the group. h
-      // overwrites the gate accumulators.
-      const int hg = wv >> 2;
-      float* s_amax = reinterpret_cast<float*>(scr.a);      // [8 waves][BM]
-      float* s_inv = s_amax + NW * BM;                       // [2 h groups][BM]
-      uint8_t* s_codes = scr.b;                              // [2][BM][128]
+      // SwiGLU + e4m3 per (row, 128 h columns): the tile is one 128-wide h group; wave wv
+      // holds its h columns wv*32 + s'*16 + c16 (s' = 0, 1) for (t, s', r). h overwrites
+      // the gate accumulators.
+      float* s_amax = reinterpret_cast<float*>(scr.a);      // [NW waves][BM]
+      float* s_inv = s_amax + NW * BM;                       // [BM]
+      uint8_t* s_codes = scr.b;                              // [BM][128]
       const int tmax = (rows + 15) >> 4;
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
@@ -516,79 +515,68 @@ __global__ __launch_bounds__(NT_THREADS, 1) void grouped_gemm_kernel(
         if (c16 < 4) s_amax[wv * BM + t8 * 16 + 4 * q + 2 * (c16 & 1) + ((c16 >> 1) & 1)] = mr;
       }
       lds_barrier();
-      if (tid < 2 * BM) {
-        const int g2 = tid >> 7, row = tid & (BM - 1);
-        const float* am = s_amax + g2 * 4 * BM + row;
-        const float m = fmaxf(fmaxf(am[0], am[BM]), fmaxf(am[2 * BM], am[3 * BM]));
+      const int hcol = nt * 128;
+      if (tid < BM) {
+        const int row = tid;
+        float m = s_amax[row];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) m = fmaxf(m, s_amax[w * BM + row]);
         float sc, inv;
         scale_pair(m, sc, inv);
-        s_inv[tid] = inv;
-        const int hcol = nt * 256 + g2 * 128;
+        s_inv[row] = inv;
         if (row < rows && hcol < I) out_scales[(int64_t)(hcol / kGroup) * R + row_begin + row] = sc;
       }
       lds_barrier();
-      const float* inv_g = s_inv + hg * BM;
-      uint8_t* codes_g = s_codes + hg * BM * 128;
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
         if (t8 >= tmax) break;  // uniform
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = t8 * 16 + 4 * q + r;
-          const float inv = inv_g[row];
+          const float inv = s_inv[row];
           const uint32_t c2 = e4m3x2_finite(acc[t8][0][r] * inv, acc[t8][1][r] * inv);
-          codes_g[row * 128 + (wv & 3) * 32 + c16] = (uint8_t)(c2 & 0xFF);
-          codes_g[row * 128 + (wv & 3) * 32 + 16 + c16] = (uint8_t)((c2 >> 8) & 0xFF);
+          s_codes[row * 128 + wv * 32 + c16] = (uint8_t)(c2 & 0xFF);
+          s_codes[row * 128 + wv * 32 + 16 + c16] = (uint8_t)((c2 >> 8) & 0xFF);
         }
       }
       lds_barrier();
       uint8_t* o8 = reinterpret_cast<uint8_t*>(out);
-      for (int i = tid; i < 2 * BM * 8; i += NT_THREADS) {
-        const int g2 = i >> 10, row = (i >> 3) & (BM - 1), ch = i & 7;
-        const int hcol = nt * 256 + g2 * 128;
+      for (int i = tid; i < BM * 8; i += NT_THREADS) {
+        const int row = i >> 3, ch = i & 7;
         if (row < rows && hcol < I)
           *reinterpret_cast<uint4*>(&o8[(int64_t)(row_begin + row) * I + hcol + ch * 16]) =
-              *reinterpret_cast<const uint4*>(&s_codes[(g2 * BM + row) * 128 + ch * 16]);
+              *reinterpret_cast<const uint4*>(&s_codes[row * 128 + ch * 16]);
       }
       lds_barrier();
     }
   };
 
-  // ---- prologue: groups 0 and 1 in flight, the seeds of group 0 formed
+  // ---- prologue: group 0 loaded, its seeds formed
   dma_group(0, ring[0]);
-  if (total_steps > 1) {
-    // with one group per tile, group 1 starts a new tile whose rows group 0's call fetched
-    if (G == 1) wait_all_but_one_group();
-    dma_group(1, ring[1]);
-    wait_all_but_one_group();
-  } else {
-    wait_all_loads();
-  }
+  wait_all_loads();
   row_sums(ring[0]);
   lds_barrier();
 
-  // ---- the stream of K groups: group s is computed from stage s % 3 while s+1 and s+2
-  // stream into the other two stages. Tiles are consecutive runs of G groups; the first
-  // group of a tile initialises the accumulators, the epilogue follows its last group.
+  // ---- the stream of K groups: group s is computed from stage s % 2 while group s+1
+  // streams into the other stage (issued as soon as the barrier frees it). Two workgroups
+  // share each CU, so one workgroup's waits, barriers and epilogue overlap the other's
+  // compute. Tiles are consecutive runs of G groups; the first group of a tile initialises
+  // the accumulators, the epilogue follows its last group.
   int s = 0;
   auto step = [&](auto first_tag) {
-    const int stage = s % 3;
-    const bool more2 = s + 2 < total_steps;
-    if (more2) dma_group(s + 2, ring[stage == 0 ? 2 : stage - 1]);
+    const int stage = s & 1;
+    const bool more = s + 1 < total_steps;
+    if (more) dma_group(s + 1, ring[stage ^ 1]);
     group(first_tag, ring[stage]);
-    // own loads of group s+1 landed (group s+2's may still be in flight)
-    if (more2)
-      wait_all_but_one_group();
-    else
-      wait_all_loads();
-    if (s + 1 < total_steps) row_sums(ring[stage == 2 ? 0 : stage + 1]);
+    wait_all_loads();  // own loads of group s+1 landed
+    if (more) row_sums(ring[stage ^ 1]);
     lds_barrier();
     ++s;
   };
   for (int j = 0; j < my_tiles; ++j) {
     step(std::true_type{});
     for (int g = 1; g < G; ++g) step(std::false_type{});
-    epilogue(tile_of(j), ring[(s + 2) % 3]);
+    epilogue(tile_of(j), ring[(s + 1) & 1]);
   }
 }
 
@@ -615,10 +603,10 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const in
                                float* out_scales, hipStream_t st) {
   if (R == 0) return hipSuccess;
   const int64_t mtiles = (R + BM - 1) / BM + E;  // bound on the m-tiles over all experts
-  // SwiGLU: a tile covers 256 h columns (gate and up); otherwise 512 output columns
-  const int NT = epilogue == FP8MOE_EPI_SWIGLU_QUANT ? (int)((N / 2 + 255) / 256)
+  // SwiGLU: a tile covers 128 h columns (gate and up); otherwise 256 output columns
+  const int NT = epilogue == FP8MOE_EPI_SWIGLU_QUANT ? (int)((N / 2 + 127) / 128)
                                                      : (int)((N + WCOLS_WG - 1) / WCOLS_WG);
-  const int64_t grid = std::min<int64_t>(cu_count(), mtiles * NT);
+  const int64_t grid = std::min<int64_t>(2 * (int64_t)cu_count(), mtiles * NT);
   const int a_rows = (int)(sorted ? R / k_route : R);
   dim3 g((uint32_t)grid), block(NT_THREADS);
   if (epilogue == FP8MOE_EPI_SWIGLU_QUANT)
