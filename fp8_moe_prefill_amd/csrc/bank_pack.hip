@@ -5,15 +5,18 @@
 // int4 bank stays packed and resident; this call only reorders its bytes (and transposes
 // its scales) once, when the weights are loaded, so that every K group of every 16 columns
 // is one contiguous 1 KB block that one wave-wide load brings in, and the scales of one K
-// group are contiguous across columns. Nothing is dequantised or widened.
+// group are contiguous across columns. Nothing is dequantised or widened. The columns of a
+// 64-column group are interleaved over its four blocks so that the GEMM's MFMA lanes end
+// up with four consecutive output columns each.
 //
 // Canonical input: w [E][N][K/2], byte i of row (e, n) holds k = 2i (low nibble) and 2i+1
 // (high nibble); w_scales [E][N][K/128].
-// Output: block (e, c, g) of 1024 bytes at ((e * N/16 + c) * K/128 + g) * 1024 for columns
-// 16c .. 16c+15 and k in [128g, 128g + 128). Its 16 bytes at 16 * (16h + i) hold column
-// 16c + i, k = 128g + 32h + 0..31, as four little-endian words; byte b of word j holds
-// k0 + b in the low nibble and k0 + 4 + b in the high nibble (k0 = 128g + 32h + 8j).
-// Scales: [E][K/128][N].
+// Output: block (e, c, g) of 1024 bytes at ((e * N/16 + c) * K/128 + g) * 1024 holds the
+// 16 columns n(c, i) = 64 * (c / 4) + 4 * i + c % 4 (i = 0..15: every 4th column of a
+// 64-column group, so the four blocks of a group interleave) and k in [128g, 128g + 128).
+// Its 16 bytes at 16 * (16h + i) hold column n(c, i), k = 128g + 32h + 0..31, as four
+// little-endian words; byte b of word j holds k0 + b in the low nibble and k0 + 4 + b in
+// the high nibble (k0 = 128g + 32h + 8j). Scales: [E][K/128][N].
 #include "common.h"
 #include "launch.h"
 
@@ -33,7 +36,7 @@ __global__ __launch_bounds__(256) void pack_bank_kernel(const uint32_t* __restri
   const int64_t ecb = blk / G;
   const int cb = (int)(ecb % NB);
   const int64_t e = ecb / NB;
-  const int n = cb * 16 + (lane & 15);
+  const int n = 64 * (cb >> 2) + 4 * (lane & 15) + (cb & 3);
   const int k0 = g * kGroup + (lane >> 4) * 32 + j * 8;
   // canonical k0 .. k0+7 are the 4 bytes at k0/2: k0 + m sits at bits 4m of this word
   const uint32_t c = w[((e * N + n) * (int64_t)(K / 2) + k0 / 2) >> 2];

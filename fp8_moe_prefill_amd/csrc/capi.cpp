@@ -104,7 +104,7 @@ int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t
                                 void* stream) {
   if (!w || !w_scales || !w_packed || !w_scales_packed) return FP8MOE_ERR_NULL;
   if (E < 1 || E > kMaxE) return FP8MOE_ERR_SHAPE;
-  if (N < 16 || N % 16 != 0 || N >= (int64_t(1) << 24)) return FP8MOE_ERR_SHAPE;
+  if (N < 64 || N % 64 != 0 || N >= (int64_t(1) << 24)) return FP8MOE_ERR_SHAPE;
   if (K < FP8MOE_GROUP || K % FP8MOE_GROUP != 0 || K > kMaxGroupedK) return FP8MOE_ERR_SHAPE;
   if (N * (K / 2) >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;
   const void* ptrs[] = {w, w_scales, w_packed, w_scales_packed};
@@ -129,7 +129,7 @@ int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales, const i
   if (R < 0 || R >= (int64_t(1) << 31) || E < 1 || E > kMaxE) return FP8MOE_ERR_SHAPE;
   if (K < FP8MOE_GROUP || K % FP8MOE_GROUP != 0 || K > kMaxGroupedK) return FP8MOE_ERR_SHAPE;
   if (N < 16 || N >= (int64_t(1) << 24)) return FP8MOE_ERR_SHAPE;
-  if (epilogue == FP8MOE_EPI_STORE && N % 16 != 0) return FP8MOE_ERR_SHAPE;
+  if (epilogue == FP8MOE_EPI_STORE && N % 64 != 0) return FP8MOE_ERR_SHAPE;
   if (epilogue == FP8MOE_EPI_SWIGLU_QUANT && N % 256 != 0) return FP8MOE_ERR_SHAPE;
   if (sorted && k_route < 1) return FP8MOE_ERR_SHAPE;
   if (R * K >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;  // 32-bit A row offsets

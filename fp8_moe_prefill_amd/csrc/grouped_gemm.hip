@@ -213,7 +213,7 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   const int q = lane >> 4, c16 = lane & 15;
   const int G = K / kGroup;
   const int I = N / 2;
-  const int NB = N / 16;
+  const int NB = N / 16;  // 16-column blocks of the bank
   const int kshift = (k_route & (k_route - 1)) == 0 ? __builtin_ctz(k_route) : -1;
 
   // ---- m-tiles per expert, prefix-summed (4 experts per thread, E <= 1024)
@@ -268,13 +268,31 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
     return d;
   };
 
-  // accumulator column j (0..255) of n-tile nt -> bank column. SwiGLU: the tile covers one
-  // 128-wide h group; wave j >> 6 holds gate columns for (j >> 5) & 1 == 0 and the
-  // matching up columns (I + ...) for (j >> 5) & 1 == 1.
-  auto bank_col = [&](int nt, int j) {
+  // Columns. In the prepacked bank, block b of 16 columns holds bank columns
+  // 64*(b/4) + 4*i + b%4 (i = 0..15), so MFMA tile s of a wave reading block 4k + s gives
+  // lane c16 bank column 64k + 4*c16 + s: each lane ends up with 4 consecutive columns.
+  // STORE: wave wv of n-tile nt covers the 64 columns 64k.., k = 4nt + wv.
+  // SWIGLU: the tile covers h columns 128nt..128nt+127; wave wv covers the 64-column h
+  // group k = 2nt + (wv >> 1), pairs 2*(wv & 1) + {0, 1} of every 4: tiles 0, 1 read gate
+  // blocks 4k + 2*(wv & 1) + {0, 1}, tiles 2, 3 the matching up blocks (I/64 groups on),
+  // so lane c16 holds gate and up of h columns 64k + 4*c16 + 2*(wv & 1) + {0, 1}.
+  const int NG = N / 64;  // 64-column groups of the bank
+  auto tile_block = [&](int nt, int s) {  // bank block of MFMA tile s of this wave
+    int b;
     if (EPI == FP8MOE_EPI_SWIGLU_QUANT)
-      return min(((j >> 5) & 1 ? I : 0) + nt * 128 + (j >> 6) * 32 + (j & 31), N - 1);
-    return min(nt * WCOLS_WG + j, N - 1);
+      b = 4 * (2 * nt + (wv >> 1) + (s >= 2 ? I / 64 : 0)) + 2 * (wv & 1) + (s & 1);
+    else
+      b = 4 * (4 * nt + wv) + s;
+    return min(b, 4 * NG - 1);
+  };
+  auto ws_col = [&](int nt, int l) {  // weight-scale column staged by lane l of this wave
+    int c;
+    if (EPI == FP8MOE_EPI_SWIGLU_QUANT)
+      c = (l >= 32 ? I : 0) + 64 * (2 * nt + (wv >> 1)) + 4 * ((l & 31) >> 1) + 2 * (wv & 1) +
+          (l & 1);
+    else
+      c = 64 * (4 * nt + wv) + l;
+    return min(c, N - 1);
   };
 
   // ---- DMA stream state: the tile whose groups are being loaded, and the next one (its
@@ -316,10 +334,10 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
       }
       as_off32 =
           (uint32_t)max(min(t.row_begin + min(wv * RPW + (lane & (RPW - 1)), t.rows - 1), R - 1), 0) * 4u;
-      ws_off32 = (uint32_t)bank_col(t.nt, wv * WCOLS + lane) * 4u;
+      ws_off32 = (uint32_t)ws_col(t.nt, lane) * 4u;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        b_blk[s] = (uint32_t)(bank_col(t.nt, wv * WCOLS + 16 * s) / 16) * (uint32_t)G * kBlockBytes;
+        b_blk[s] = (uint32_t)tile_block(t.nt, s) * (uint32_t)G * kBlockBytes;
       w_exp = W + (int64_t)t.e * NB * G * kBlockBytes;
       ws_exp = Ws + (int64_t)t.e * G * N;
       // the LDS reads of s_src above complete before any later load may refill it
@@ -379,7 +397,10 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bop[s] = convert_b(*reinterpret_cast<const uint4*>(&tb[s * 1024 + lane * 16]));
-      sw[s] = swg[s * 16 + c16] * kWeightScaleMul;
+      // staged scale of this lane's column in tile s (see ws_col)
+      const int wi = EPI == FP8MOE_EPI_SWIGLU_QUANT ? (s >= 2 ? 32 : 0) + 2 * c16 + (s & 1)
+                                                    : 4 * c16 + s;
+      sw[s] = swg[wi] * kWeightScaleMul;
     }
 
     v8i aop[2];
@@ -442,59 +463,38 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   // group was computed from: free until the loads of a later group are issued into it.
   auto epilogue = [&](const TileDesc& t, Stage& scr) {
     const int rows = t.rows, row_begin = t.row_begin, nt = t.nt;
-    if (EPI == FP8MOE_EPI_STORE && OUT_BF16) {
-      // stage the bf16 tile in LDS 32 rows at a time (16 KB), then write whole 512 B row
-      // segments
-      uint16_t* s_out = reinterpret_cast<uint16_t*>(scr.b);
-      const int ncols = min(WCOLS_WG, N - nt * WCOLS_WG);  // multiple of 16
-      uint16_t* o16 = reinterpret_cast<uint16_t*>(out);
+    const int tmax = (rows + 15) >> 4;
+    if (EPI == FP8MOE_EPI_STORE) {
+      // each lane holds 4 consecutive output columns (tiles s = 0..3) of rows t*16 + 4q + r:
+      // 16 lanes cover 64 consecutive columns of a row, so every store instruction writes
+      // whole 128 B (bf16) or 256 B (fp32) row segments, straight from registers
+      const int col0 = nt * WCOLS_WG + wv * WCOLS + 4 * c16;
 #pragma unroll
-      for (int part = 0; part < 4; ++part) {
-        if (32 * part >= rows) break;  // uniform
-#pragma unroll
-        for (int t8 = 2 * part; t8 < 2 * part + 2; ++t8)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int s = 0; s < 4; s += 2) {
-              const uint32_t pk = bf16x2(acc[t8][s][r], acc[t8][s + 1][r]);
-              uint16_t* o = &s_out[((t8 - 2 * part) * 16 + 4 * q + r) * WCOLS_WG + wv * WCOLS +
-                                   s * 16 + c16];
-              o[0] = (uint16_t)(pk & 0xFFFFu);
-              o[16] = (uint16_t)(pk >> 16);
-            }
-        lds_barrier();
-        for (int i = tid; i < 32 * (WCOLS_WG / 8); i += NT_THREADS) {
-          const int rl = i / (WCOLS_WG / 8), ch = i % (WCOLS_WG / 8), row = 32 * part + rl;
-          if (row < rows && ch * 8 < ncols)
-            *reinterpret_cast<uint4*>(&o16[(int64_t)(row_begin + row) * N + nt * WCOLS_WG + ch * 8]) =
-                *reinterpret_cast<const uint4*>(&s_out[rl * WCOLS_WG + ch * 8]);
-        }
-        lds_barrier();
-      }
-    } else if (EPI == FP8MOE_EPI_STORE) {
-#pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8)
+      for (int t8 = 0; t8 < 8; ++t8) {
+        if (t8 >= tmax) break;  // uniform
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = t8 * 16 + 4 * q + r;
-          if (row < rows) {
-            const int64_t orow = (int64_t)(row_begin + row) * N;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const int cc = nt * WCOLS_WG + wv * WCOLS + s * 16 + c16;
-              if (cc < N) reinterpret_cast<float*>(out)[orow + cc] = acc[t8][s][r];
-            }
+          if (row < rows && col0 < N) {
+            const int64_t o = (int64_t)(row_begin + row) * N + col0;
+            if (OUT_BF16)
+              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + o) =
+                  make_uint2(bf16x2(acc[t8][0][r], acc[t8][1][r]),
+                             bf16x2(acc[t8][2][r], acc[t8][3][r]));
+            else
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o) =
+                  make_float4(acc[t8][0][r], acc[t8][1][r], acc[t8][2][r], acc[t8][3][r]);
           }
         }
+      }
     } else {
-      // SwiGLU + e4m3 per (row, 128 h columns): the tile is one 128-wide h group; wave wv
-      // holds its h columns wv*32 + s'*16 + c16 (s' = 0, 1) for (t, s', r). h overwrites
-      // the gate accumulators.
+      // SwiGLU + e4m3 per (row, 128 h columns): the tile is one 128-wide h group; lane c16 of
+      // wave wv holds h columns 64*(wv >> 1) + 4*c16 + 2*(wv & 1) + s' (s' = 0, 1) of rows
+      // t*16 + 4q + r (gate in tile s', up in tile s' + 2). h overwrites the gate
+      // accumulators.
       float* s_amax = reinterpret_cast<float*>(scr.a);      // [NW waves][BM]
       float* s_inv = s_amax + NW * BM;                       // [BM]
       uint8_t* s_codes = scr.b;                              // [BM][128]
-      const int tmax = (rows + 15) >> 4;
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
         if (t8 >= tmax) break;  // uniform
@@ -527,16 +527,17 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
         if (row < rows && hcol < I) out_scales[(int64_t)(hcol / kGroup) * R + row_begin + row] = sc;
       }
       lds_barrier();
+      const int hc = 64 * (wv >> 1) + 4 * c16 + 2 * (wv & 1);  // this lane's h column pair
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
         if (t8 >= tmax) break;  // uniform
+        const float4 inv4 = *reinterpret_cast<const float4*>(&s_inv[t8 * 16 + 4 * q]);
+        const float inv[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = t8 * 16 + 4 * q + r;
-          const float inv = s_inv[row];
-          const uint32_t c2 = e4m3x2_finite(acc[t8][0][r] * inv, acc[t8][1][r] * inv);
-          s_codes[row * 128 + wv * 32 + c16] = (uint8_t)(c2 & 0xFF);
-          s_codes[row * 128 + wv * 32 + 16 + c16] = (uint8_t)((c2 >> 8) & 0xFF);
+          const uint32_t c2 = e4m3x2_finite(acc[t8][0][r] * inv[r], acc[t8][1][r] * inv[r]);
+          *reinterpret_cast<uint16_t*>(&s_codes[row * 128 + hc]) = (uint16_t)c2;
         }
       }
       lds_barrier();

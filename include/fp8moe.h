@@ -158,13 +158,14 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
  *                    its high nibble
  *   w_scales         fp32 [E, N, K/128]
  *   w_packed         out, E*N*K/2 bytes. Block (e, c, g) of 1024 bytes, at byte
- *                    ((e * N/16 + c) * K/128 + g) * 1024, holds columns 16c .. 16c+15 and
- *                    k in [128g, 128g+128): its 16 bytes at 16 * (16h + i) are column
- *                    16c + i, k = 128g + 32h + 0..31, as four little-endian 32-bit words;
- *                    byte b of word j holds k0 + b in the low nibble and k0 + 4 + b in the
- *                    high nibble, k0 = 128g + 32h + 8j
+ *                    ((e * N/16 + c) * K/128 + g) * 1024, holds the 16 columns
+ *                    n(c, i) = 64*(c/4) + 4*i + c%4 (i = 0..15) and k in [128g, 128g+128):
+ *                    its 16 bytes at 16 * (16h + i) are column n(c, i),
+ *                    k = 128g + 32h + 0..31, as four little-endian 32-bit words; byte b of
+ *                    word j holds k0 + b in the low nibble and k0 + 4 + b in the high
+ *                    nibble, k0 = 128g + 32h + 8j
  *   w_scales_packed  out, fp32 [E, K/128, N] (the scales of one K group contiguous)
- * The outputs must not overlap the inputs. Constraints: 1 <= E <= 1024, N % 16 == 0,
+ * The outputs must not overlap the inputs. Constraints: 1 <= E <= 1024, N % 64 == 0,
  * 128 <= K <= 16384, K % 128 == 0, N*K/2 < 2^32.
  */
 int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t E, int64_t N,
@@ -200,7 +201,7 @@ int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t
  *              (group 128) into out = e4m3 [R, I] and out_scales = fp32 [I/128, R],
  *              group-major like a_scales (ready to be the next GEMM's a_scales)
  * Constraints: R >= 0 (R = 0 is a no-op), 1 <= E <= 1024, K % 128 == 0,
- * 128 <= K <= 16384, R*K < 2^32, N*K/2 < 2^32; STORE: N % 16 == 0; SWIGLU_QUANT:
+ * 128 <= K <= 16384, R*K < 2^32, N*K/2 < 2^32; STORE: N % 64 == 0; SWIGLU_QUANT:
  * N % 256 == 0.
  */
 int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales,

@@ -128,6 +128,7 @@ def test_grouped_gemm_validation(lib):
     assert _gg(lib, K=32768) == SHAPE
     assert _gg(lib, R=1 << 22, K=2048) == SHAPE  # R*K >= 2^32
     assert _gg(lib, N=24) == SHAPE
+    assert _gg(lib, N=80) == SHAPE  # STORE needs N % 64 == 0
     assert _gg(lib, epi=1, N=384) == SHAPE  # SwiGLU needs N % 256 == 0
     assert _gg(lib, sorted_=P, kr=0) == SHAPE
     assert _gg(lib, out=U) == ALIGN
@@ -145,6 +146,7 @@ def test_pack_bank_validation(lib):
     assert _pack(lib, E=0) == SHAPE
     assert _pack(lib, E=1025) == SHAPE
     assert _pack(lib, N=24) == SHAPE
+    assert _pack(lib, N=80) == SHAPE
     assert _pack(lib, K=200) == SHAPE
     assert _pack(lib, K=32768) == SHAPE
     assert _pack(lib, N=1 << 20, K=16384) == SHAPE

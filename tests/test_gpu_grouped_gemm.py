@@ -74,8 +74,8 @@ def _gemm(aq, as_grouped, wp, ws, off, out_dtype=torch.float32, sorted_=None, k_
 @pytest.mark.parametrize("counts,K,N", [
     ([0, 37, 130, 1, 200], 256, 512),      # empty, ragged, single-row experts
     ([128, 128], 128, 256),                 # exact tiles, one K group
-    ([300], 384, 48),                       # one expert, N not a multiple of 64
-    ([5, 0, 0, 261, 17, 64, 0, 9], 1024, 272),
+    ([300], 384, 64),                       # one expert, one 64-column group
+    ([5, 0, 0, 261, 17, 64, 0, 9], 1024, 320),  # N not a multiple of the 256-wide tile
 ])
 def test_store_f32_within_bound(counts, K, N):
     aq, as_, wp, ws, off = _problem(counts, K, N, seed=K + N)
@@ -224,7 +224,7 @@ def test_pack_expert_bank_layout():
     of the layout, independently of the kernels)."""
     f = _lib()
     rng = np.random.default_rng(5)
-    E, N, K = 3, 48, 384
+    E, N, K = 3, 128, 384
     wp = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
     ws = rng.uniform(0.005, 0.02, size=(E, N, K // 128)).astype(np.float32)
     pw, ps = f.pack_expert_bank(dev(wp), dev(ws))
@@ -246,6 +246,7 @@ def test_pack_expert_bank_layout():
                                 byte = int(b16[4 * j + b])
                                 k0 = 128 * g + 32 * h + 8 * j
                                 for kk, nib in ((k0 + b, byte & 15), (k0 + 4 + b, byte >> 4)):
-                                    got[e, 16 * c + i, kk] = nib - 16 if nib >= 8 else nib
+                                    n = 64 * (c // 4) + 4 * i + c % 4
+                                    got[e, n, kk] = nib - 16 if nib >= 8 else nib
     assert np.array_equal(got, q)
     assert np.array_equal(ps, np.transpose(ws, (0, 2, 1)))
