@@ -8,9 +8,10 @@
 //
 // Design: a stable counting sort with no order-dependent atomics, so every output is a
 // pure function of the logits.
-//   1. topk_hist:  one wave per token selects the top k by (logit desc, expert asc) with
-//                  a 64-lane argmax per pick; a workgroup owns a chunk of 16 tokens and
-//                  counts its pairs per expert in LDS (integer adds commute).
+//   1. topk_hist:  one wave per token selects the top k by (logit desc, expert asc), one
+//                  wave argmax (DPP within rows, v_readlane across them) per pick; a
+//                  workgroup owns a chunk of 16 tokens and counts its pairs per expert in
+//                  LDS (integer adds commute).
 //   2. chunk_scan: one workgroup per expert scans that expert's per-chunk counts.
 //   3. scatter:    one workgroup per chunk recomputes the expert offsets (a scan over E),
 //                  ranks each pair among the chunk's earlier pairs of the same expert and
@@ -46,52 +47,87 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// value of lane - o within the same 16-lane row; lanes below o keep `old`
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL,
+                                                    0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, 0xF, 0xF, false);
+}
+
+// Best (value desc, index asc) over the wave, returned in SGPRs. Within each 16-lane row
+// four DPP row_shr steps carry the row's best into its last lane; the four row winners
+// are then compared through v_readlane on the scalar unit. No LDS round trips.
+__device__ __forceinline__ void wave_argmax(float v, int i, float& bv, int& bi) {
+  float ov = dpp_f<0x111>(v, v); int oi = dpp_i<0x111>(i, i);  // row_shr:1
+  if (better(ov, oi, v, i)) { v = ov; i = oi; }
+  ov = dpp_f<0x112>(v, v); oi = dpp_i<0x112>(i, i);            // row_shr:2
+  if (better(ov, oi, v, i)) { v = ov; i = oi; }
+  ov = dpp_f<0x114>(v, v); oi = dpp_i<0x114>(i, i);            // row_shr:4
+  if (better(ov, oi, v, i)) { v = ov; i = oi; }
+  ov = dpp_f<0x118>(v, v); oi = dpp_i<0x118>(i, i);            // row_shr:8
+  if (better(ov, oi, v, i)) { v = ov; i = oi; }
+  bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+  bi = __builtin_amdgcn_readlane(i, 15);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r + 15));
+    const int ri = __builtin_amdgcn_readlane(i, 16 * r + 15);
+    if (better(rv, ri, bv, bi)) { bv = rv; bi = ri; }
+  }
+}
+
+// Top-k of each token and the per-chunk expert histogram. A workgroup owns a chunk of
+// kRouteChunk tokens; each wave takes kRouteChunk/4 of them, loads all their logits first
+// (lane e holds experts e, e+64, ...), then picks the k best one at a time: a per-lane
+// best over the lane's untaken experts, the wave argmax, and the winner marked taken.
+template <int NJ>  // experts per lane: E <= 64 * NJ
 __global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict__ logits,
                                                         int64_t T, int E, int k,
                                                         int32_t* __restrict__ ids,
                                                         float* __restrict__ wts,
                                                         int32_t* __restrict__ cnt) {
+  constexpr int TPW = kRouteChunk / 4;  // tokens per wave
   __shared__ int hist[kMaxE];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
   __syncthreads();
 
-  const int nj = (E + 63) / 64;
-  for (int tt = wv; tt < kRouteChunk; tt += 4) {
-    int64_t t = (int64_t)blockIdx.x * kRouteChunk + tt;
-    if (t >= T) break;  // wave-uniform
-    float v[kMaxE / 64];
-    uint32_t taken = 0;
+  float v[TPW][NJ];
 #pragma unroll
-    for (int j = 0; j < kMaxE / 64; ++j) {
-      int e = lane + 64 * j;
-      float lv = (j < nj && e < E) ? logits[t * E + e] : -INFINITY;
-      v[j] = lv != lv ? -INFINITY : lv;  // NaN ranks as -inf: every pick stays a valid expert
+  for (int u = 0; u < TPW; ++u) {
+    const int64_t t = (int64_t)blockIdx.x * kRouteChunk + wv * TPW + u;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      const float lv = (t < T && e < E) ? logits[t * E + e] : -INFINITY;
+      v[u][j] = lv != lv ? -INFINITY : lv;  // NaN ranks as -inf: every pick stays a valid expert
     }
-    // lane s keeps the s-th pick
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int64_t t = (int64_t)blockIdx.x * kRouteChunk + wv * TPW + u;
+    if (t >= T) break;  // wave-uniform
+    uint32_t taken = 0;
     float my_v = -INFINITY, top_v = 0.f;
     int my_i = 0;
     for (int s = 0; s < k; ++s) {
-      float bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
+      float lv = -INFINITY;
+      int li = 0x7FFFFFFF;
 #pragma unroll
-      for (int j = 0; j < kMaxE / 64; ++j) {
-        int e = lane + 64 * j;
-        if (j < nj && e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) {
-          bv = v[j];
-          bi = e;
+      for (int j = 0; j < NJ; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E && !((taken >> j) & 1u) && better(v[u][j], e, lv, li)) {
+          lv = v[u][j];
+          li = e;
         }
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        float ov = __shfl_xor(bv, o);
-        int oi = __shfl_xor(bi, o);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      // (bv, bi) is now the same on every lane
+      float bv;
+      int bi;
+      wave_argmax(lv, li, bv, bi);
       if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
       if (lane == s) {
         my_v = bv;
@@ -100,7 +136,7 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict_
       if (s == 0) top_v = bv;
     }
     // renormalised softmax over the k picks
-    float ex = lane < k ? expf(my_v - top_v) : 0.f;
+    const float ex = lane < k ? expf(my_v - top_v) : 0.f;
     float sum = ex;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
@@ -224,7 +260,13 @@ hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32
   int64_t C = (T + kRouteChunk - 1) / kRouteChunk;
   int32_t* cnt = static_cast<int32_t*>(ws);
   int32_t* tot = cnt + C * E;
-  topk_hist_kernel<<<dim3((uint32_t)C), 256, 0, st>>>(logits, T, E, k, ids, w, cnt);
+  const dim3 grid((uint32_t)C);
+  if (E <= 64)
+    topk_hist_kernel<1><<<grid, 256, 0, st>>>(logits, T, E, k, ids, w, cnt);
+  else if (E <= 256)
+    topk_hist_kernel<4><<<grid, 256, 0, st>>>(logits, T, E, k, ids, w, cnt);
+  else
+    topk_hist_kernel<16><<<grid, 256, 0, st>>>(logits, T, E, k, ids, w, cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   chunk_scan_kernel<<<dim3((uint32_t)E), 256, 0, st>>>(cnt, C, E, tot);
