@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libfp8moe.so")
 GROUP = 128
 DTYPE_F32, DTYPE_BF16 = 0, 1
 EPI_STORE, EPI_SWIGLU_QUANT = 0, 1
-OP_QUANT_ACT, OP_ROUTE_PERMUTE = 0, 1
+OP_QUANT_ACT, OP_ROUTE_PERMUTE, OP_ATTENTION = 0, 1, 2
 
 _c_void_p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -44,6 +44,11 @@ SIGNATURES = {
                               _c_void_p, _c_void_p]),
     "moe_unpermute_combine": (_i32, [_c_void_p, _i32, _c_void_p, _c_void_p, _i64, _i32, _i64,
                                      _i32, _c_void_p, _c_void_p]),
+    "fp8moe_rmsnorm": (_i32, [_c_void_p, _c_void_p, _i64, _i64, ctypes.c_double, _c_void_p,
+                              _c_void_p, _c_void_p]),
+    "fp8moe_bf16_gemm": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p]),
+    "fp8moe_causal_attention": (_i32, [_c_void_p, _i64, _i32, _i32, _i32, _c_void_p, _c_void_p,
+                                       _sz, _c_void_p]),
 }
 
 
@@ -264,3 +269,67 @@ def moe_unpermute_combine(y, pos, weights, out_dtype=torch.bfloat16, out=None, s
         _ptr(y), _dt(y.dtype), _ptr(pos), _ptr(weights), T, k, H, _dt(out.dtype), _ptr(out),
         _stream(stream)))
     return out
+
+
+# ------------------------------------------------------------------------------------
+# Depth-stack support: residual + RMSNorm, bf16 GEMM, causal GQA attention
+# ------------------------------------------------------------------------------------
+
+RMSNORM_EPS = 1e-6
+
+
+def rmsnorm(x: torch.Tensor, delta=None, eps: float = RMSNORM_EPS, x_out=None, y=None,
+            stream=None):
+    """y = bf16(RMSNorm(x)) or, with ``delta``, x_out = bf16(x + delta) and
+    y = bf16(RMSNorm(x_out)). ``x_out`` may be ``x`` (in-place). Returns y, or
+    (x_out, y) when ``delta`` is given."""
+    _dev(x, "x", torch.bfloat16)
+    T, H = x.shape
+    if delta is not None:
+        _dev(delta, "delta", torch.bfloat16)
+        if delta.shape != x.shape:
+            raise ValueError("delta must have the shape of x")
+        if x_out is None:
+            x_out = torch.empty_like(x)
+        _dev(x_out, "x_out", torch.bfloat16)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", torch.bfloat16)
+    _check("fp8moe_rmsnorm", _lib.fp8moe_rmsnorm(_ptr(x), _ptr(delta), T, H, float(eps),
+                                                 _ptr(x_out), _ptr(y), _stream(stream)))
+    return (x_out, y) if delta is not None else y
+
+
+def bf16_gemm(a: torch.Tensor, w: torch.Tensor, out=None, stream=None):
+    """fp32 [M, N] = a [M, K] . w [N, K]^T, bf16 operands."""
+    _dev(a, "a", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    M, K = a.shape
+    N, K2 = w.shape
+    if K2 != K:
+        raise ValueError("a and w must share K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    _dev(out, "out", torch.float32)
+    _check("fp8moe_bf16_gemm", _lib.fp8moe_bf16_gemm(_ptr(a), _ptr(w), M, N, K, _ptr(out),
+                                                     _stream(stream)))
+    return out
+
+
+def causal_attention(qkv: torch.Tensor, n_q: int, n_kv: int, head_dim: int = 128, out=None,
+                     ws=None, stream=None):
+    """bf16 [T, (n_q + 2 n_kv) * d] fused q|k|v -> bf16 [T, n_q * d]."""
+    _dev(qkv, "qkv", torch.bfloat16)
+    T, W = qkv.shape
+    if W != (n_q + 2 * n_kv) * head_dim:
+        raise ValueError("qkv width must be (n_q + 2 n_kv) * head_dim")
+    if out is None:
+        out = torch.empty((T, n_q * head_dim), dtype=torch.bfloat16, device=qkv.device)
+    _dev(out, "out", torch.bfloat16)
+    nbytes = workspace_bytes(OP_ATTENTION, T, n_kv, head_dim)
+    wsb = _workspace(nbytes, qkv.device, ws)
+    _check("fp8moe_causal_attention",
+           _lib.fp8moe_causal_attention(_ptr(qkv), T, n_q, n_kv, head_dim, _ptr(out), _ptr(wsb),
+                                        nbytes, _stream(stream)))
+    return out
+

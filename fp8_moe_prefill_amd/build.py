@@ -19,7 +19,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp8moe.so")
 
 KERNELS = ["quant_act.hip", "route_permute.hip", "bank_pack.hip", "grouped_gemm.hip",
-           "dense_gemm.hip", "combine.hip"]
+           "dense_gemm.hip", "combine.hip", "rmsnorm.hip", "bf16_gemm.hip",
+           "attention.hip"]
 HOST = ["capi.cpp"]
 
 ARCH = "gfx950"

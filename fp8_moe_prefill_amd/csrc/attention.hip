@@ -1,0 +1,246 @@
+// Causal grouped-query attention of the depth stack (fp8moe_causal_attention).
+//
+// The FP8 grouped-expert prefill note ("FP8 grouped-expert prefill with on-chip int4-to-e4m3
+// dequant", sections 1 and 3) quantises the q/k/v/o projections around an attention core
+// that stays in bf16. Its plain reading: softmax(q k^T / sqrt(d)) v per query head over the
+// causal prefix, query head h reading kv head h / (n_q / n_kv), no rotary embedding, bf16
+// inputs and output, fp32 softmax and accumulation.
+//
+// gfx950 design (one pass over the keys with a running max, so the T x T score matrix never
+// leaves registers):
+// * a workgroup owns one kv head, 32 queries and four query heads of that kv head's group,
+//   one per wave; the K tile and the transposed V tile of 64 keys are staged once in LDS
+//   (double-buffered, next tile's global loads in flight during the MFMAs) and shared by
+//   the four waves;
+// * each wave computes S^T = K Q^T (v_mfma_f32_16x16x32_bf16, keys as rows), so a lane's
+//   scores all belong to one query: the running max, the rescale of the output and the
+//   row sum need no lane exchange except the 4-lane max per tile;
+// * O^T = V^T P^T: P leaves the S^T accumulators as the B operand directly (same lane),
+//   split into two bf16 terms hi + lo so that the product keeps the fp32 softmax's
+//   accuracy (a single bf16 rounding of the weights would cost 2^-9 relative); V^T comes
+//   from LDS; the output accumulators are again per query;
+// * V is transposed once per layer into a [n_kv][d][T_pad] workspace by a small kernel
+//   (zero-filled past T), so V^T tiles load as contiguous rows.
+// Workgroups of the latest query blocks (most keys) are launched first.
+#include "common.h"
+#include "launch.h"
+
+namespace fp8moe {
+namespace {
+
+constexpr int D = 128;        // head dim
+constexpr int QB = 32;        // queries per workgroup (two 16-query MFMA tiles per wave)
+constexpr int KT = 64;        // keys per tile
+constexpr int KS = D * 2 + 16;   // K tile row stride in LDS (bytes): 256 + 16 pad
+constexpr int VS = KT * 2 + 16;  // V^T tile row stride in LDS (bytes): 128 + 16 pad
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// [T, ld] column block of V (kv head j) -> vt[j][d][t], zero for t in [T, Tp)
+__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ qkv,
+                                                          int T, int ld, int v_col0, int Tp,
+                                                          uint16_t* __restrict__ vt) {
+  __shared__ uint16_t tile[64][65];
+  const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64;  // c: column within the V block
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int t = t0 + r;
+    tile[r][tx] = t < T ? qkv[(int64_t)t * ld + v_col0 + c0 + tx] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) vt[(int64_t)(c0 + r) * Tp + t0 + tx] = tile[tx][r];
+}
+
+__global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __restrict__ qkv,
+                                                           const uint16_t* __restrict__ vt,
+                                                           uint16_t* __restrict__ out, int T,
+                                                           int ld, int n_q, int n_kv, int Tp,
+                                                           int n_hg, float c_log2) {
+  __shared__ __attribute__((aligned(16))) uint8_t sK[2][KT * KS];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[2][D * VS];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int rep = n_q / n_kv;
+  const int nqb = (T + QB - 1) / QB;
+  const int per_qb = n_kv * n_hg;
+  const int qb = nqb - 1 - (int)(blockIdx.x / per_qb);  // latest query blocks first
+  const int rest = (int)(blockIdx.x % per_qb);
+  const int j = rest / n_hg, hg = rest % n_hg;
+  const int hr = hg * 4 + wv;               // head within the kv group
+  const bool live = hr < rep;               // a wave past the group's heads only helps load
+  const int h = j * rep + min(hr, rep - 1);
+  const int q0 = qb * QB;
+  const int nkt = min(q0 + QB - 1, T - 1) / KT + 1;
+
+  // Q fragments: lane (g, c16) holds query q0 + 16 qt + c16, dims 32 kk + 8 g .. +7
+  bf16x8_t qf[2][4];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int t = min(q0 + 16 * qt + c16, T - 1);
+    const uint16_t* src = qkv + (int64_t)t * ld + h * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[qt][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(src + 32 * kk));
+  }
+
+  // staging of one key tile: K rows (64 x 256 B) and V^T rows (128 x 128 B), 4 chunks of
+  // 16 B each per thread
+  const uint16_t* kbase = qkv + (n_q + j) * D;
+  const uint16_t* vbase = vt + (int64_t)j * D * Tp;
+  uint4 rk[4], rv[4];
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * KT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int key = min(k0 + (c >> 4), T - 1);
+      rk[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)key * ld + (c & 15) * 8);
+      rv[i] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(c >> 3) * Tp + k0 + (c & 7) * 8);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<uint4*>(&sK[buf][(c >> 4) * KS + (c & 15) * 16]) = rk[i];
+      *reinterpret_cast<uint4*>(&sV[buf][(c >> 3) * VS + (c & 7) * 16]) = rv[i];
+    }
+  };
+
+  v4f o[2][8];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[qt][dt] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nkt;
+    if (more) load_tile(kt + 1);
+
+    // S^T[key 16 s + 4 g + r][query 16 qt + c16], s = 16-key subtile
+    v4f st[2][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) st[qt][s] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8_t a = as_bf16x8(
+            *reinterpret_cast<const uint4*>(&sK[cur][(16 * s + c16) * KS + kk * 64 + g * 16]));
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+          st[qt][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qt][kk], st[qt][s], 0, 0, 0);
+      }
+    }
+
+    // online softmax in the log2 domain; only the last tile can hold keys past a query
+    const bool diag = kt == nkt - 1;
+    bf16x8_t pb[2][2], pl[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int qi = q0 + 16 * qt + c16;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = st[qt][s][r] * c_log2;
+          if (diag && kt * KT + 16 * s + 4 * g + r > qi) v = -INFINITY;
+          st[qt][s][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[qt], mx);
+      const float alpha = exp2f(m_run[qt] - m_new);
+      m_run[qt] = m_new;
+      float ls = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // p enters P.V as hi + lo, two bf16 terms (about 16 significant bits): the
+          // product keeps fp32-level accuracy on the bf16 matrix cores
+          const float p = exp2f(st[qt][s][r] - m_new);
+          const __bf16 hi = (__bf16)p;
+          ls += p;
+          pb[qt][s >> 1][4 * (s & 1) + r] = hi;
+          pl[qt][s >> 1][4 * (s & 1) + r] = (__bf16)(p - (float)hi);
+        }
+      l_part[qt] = l_part[qt] * alpha + ls;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[qt][dt] *= alpha;
+    }
+
+    // O^T[d 16 dt + 4 g + r][query 16 qt + c16] += V^T P^T over two 32-key steps; the key
+    // slots of lane group g are 32 c + 4 g + 0..3 and 32 c + 16 + 4 g + 0..3 for both
+    // operands
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint8_t* vrow = &sV[cur][(16 * dt + c16) * VS];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (32 * c + 4 * g) * 2);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (32 * c + 16 + 4 * g) * 2);
+        const bf16x8_t a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qt][c], o[qt][dt], 0, 0, 0);
+          o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[qt][c], o[qt][dt], 0, 0, 0);
+        }
+      }
+    }
+
+    if (more) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (!live) return;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float l = l_part[qt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int qi = q0 + 16 * qt + c16;
+    if (qi >= T) continue;
+    const float inv = 1.f / l;
+    uint16_t* dst = out + (int64_t)qi * (n_q * D) + h * D + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const v4f v = o[qt][dt] * inv;
+      *reinterpret_cast<uint2*>(dst + 16 * dt) = make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
+    }
+  }
+}
+
+}  // namespace
+
+size_t attention_workspace_bytes(int64_t T, int32_t n_kv) {
+  const int64_t Tp = (T + KT - 1) / KT * KT;
+  return (size_t)n_kv * D * Tp * sizeof(uint16_t);
+}
+
+hipError_t launch_attention(const uint16_t* qkv, int64_t T, int32_t n_q, int32_t n_kv,
+                            uint16_t* out, uint16_t* vt, hipStream_t st) {
+  const int ld = (n_q + 2 * n_kv) * D;
+  const int Tp = (int)((T + KT - 1) / KT * KT);
+  v_transpose_kernel<<<dim3((uint32_t)(Tp / 64), (uint32_t)(n_kv * D / 64)), 256, 0, st>>>(
+      qkv, (int)T, ld, (n_q + n_kv) * D, Tp, vt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rep = n_q / n_kv, n_hg = (rep + 3) / 4;
+  const int nqb = (int)((T + QB - 1) / QB);
+  const float c_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  attention_kernel<<<dim3((uint32_t)(nqb * n_kv * n_hg)), 256, 0, st>>>(
+      qkv, vt, out, (int)T, ld, n_q, n_kv, Tp, n_hg, c_log2);
+  return hipGetLastError();
+}
+
+}  // namespace fp8moe

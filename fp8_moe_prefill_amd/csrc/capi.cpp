@@ -11,10 +11,12 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 constexpr int64_t kMaxGroupedK = 16384;
+constexpr int32_t kHeadDim = 128;
+constexpr int32_t kMaxHeads = 4096;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -53,6 +55,11 @@ size_t fp8moe_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c) {
   if (op == FP8MOE_OP_ROUTE_PERMUTE) {
     if (a < 1 || b < 1 || b > kMaxE || c < 1 || c > b || c > kMaxK) return (size_t)-1;
     return fp8moe::route_workspace_bytes(a, (int32_t)b);
+  }
+  if (op == FP8MOE_OP_ATTENTION) {
+    if (a < 1 || a >= (int64_t(1) << 31) || b < 1 || b > kMaxHeads || c != kHeadDim)
+      return (size_t)-1;
+    return fp8moe::attention_workspace_bytes(a, (int32_t)b);
   }
   return (size_t)-1;
 }
@@ -176,6 +183,50 @@ int32_t moe_unpermute_combine(const void* y, int32_t y_dtype, const int32_t* pos
     if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
   return launch_status(fp8moe::launch_combine(y, y_dtype, pos, weights, T, k, H, out_dtype, out,
                                               static_cast<hipStream_t>(stream)));
+}
+
+int32_t fp8moe_rmsnorm(const void* x, const void* delta, int64_t T, int64_t H, double eps,
+                       void* x_out, void* y, void* stream) {
+  if (!x || !y || (delta && !x_out)) return FP8MOE_ERR_NULL;
+  if (T < 1 || H < 8 || H % 8 != 0 || T >= (int64_t(1) << 31) || H >= (int64_t(1) << 31) ||
+      T > (int64_t(1) << 40) / H)
+    return FP8MOE_ERR_SHAPE;
+  if (!(eps >= 0.0)) return FP8MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(y) || (delta && (!aligned16(delta) || !aligned16(x_out))))
+    return FP8MOE_ERR_ALIGN;
+  return launch_status(fp8moe::launch_rmsnorm(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(delta), T, H, eps,
+      static_cast<uint16_t*>(delta ? x_out : nullptr), static_cast<uint16_t*>(y),
+      static_cast<hipStream_t>(stream)));
+}
+
+int32_t fp8moe_bf16_gemm(const void* a, const void* w, int64_t M, int64_t N, int64_t K,
+                         float* out, void* stream) {
+  if (!a || !w || !out) return FP8MOE_ERR_NULL;
+  if (M < 1 || N < 1 || K < 64 || K % 64 != 0) return FP8MOE_ERR_SHAPE;
+  if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31))
+    return FP8MOE_ERR_SHAPE;
+  if (((M + 127) / 128) * ((N + 127) / 128) >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(out)) return FP8MOE_ERR_ALIGN;
+  return launch_status(fp8moe::launch_bf16_gemm(static_cast<const uint16_t*>(a),
+                                                 static_cast<const uint16_t*>(w), M, N, K, out,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int32_t fp8moe_causal_attention(const void* qkv, int64_t T, int32_t n_q, int32_t n_kv,
+                                int32_t head_dim, void* out, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (!qkv || !out || !ws) return FP8MOE_ERR_NULL;
+  if (head_dim != kHeadDim) return FP8MOE_ERR_SHAPE;
+  if (T < 1 || n_kv < 1 || n_q < 1 || n_q > kMaxHeads || n_q % n_kv != 0)
+    return FP8MOE_ERR_SHAPE;
+  if ((int64_t)(n_q + 2 * n_kv) * head_dim * T >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
+  if (!aligned16(qkv) || !aligned16(out) || !aligned16(ws)) return FP8MOE_ERR_ALIGN;
+  if (ws_bytes < fp8moe::attention_workspace_bytes(T, n_kv)) return FP8MOE_ERR_WORKSPACE;
+  return launch_status(fp8moe::launch_attention(static_cast<const uint16_t*>(qkv), T, n_q, n_kv,
+                                                static_cast<uint16_t*>(out),
+                                                static_cast<uint16_t*>(ws),
+                                                static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

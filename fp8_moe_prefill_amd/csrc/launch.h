@@ -45,4 +45,13 @@ hipError_t launch_combine(const void* y, int32_t y_dtype, const int32_t* pos, co
                           int64_t T, int32_t k, int64_t H, int32_t out_dtype, void* out,
                           hipStream_t st);
 
+// Depth-stack support kernels.
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* delta, int64_t T, int64_t H,
+                          double eps, uint16_t* x_out, uint16_t* y, hipStream_t st);
+hipError_t launch_bf16_gemm(const uint16_t* a, const uint16_t* w, int64_t M, int64_t N,
+                            int64_t K, float* out, hipStream_t st);
+size_t attention_workspace_bytes(int64_t T, int32_t n_kv);
+hipError_t launch_attention(const uint16_t* qkv, int64_t T, int32_t n_q, int32_t n_kv,
+                            uint16_t* out, uint16_t* vt, hipStream_t st);
+
 }  // namespace fp8moe

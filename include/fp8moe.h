@@ -14,12 +14,19 @@
  *   fp8_dense_gemm           W8A8 GEMM with per-tensor activation and weight scales
  *   moe_unpermute_combine    weighted sum of each token's k expert rows
  *
+ * and, for the depth stack those layers sit in ([P1] section 3):
+ *
+ *   fp8moe_rmsnorm           residual add + RMSNorm, bf16 in and out
+ *   fp8moe_bf16_gemm         bf16 x bf16 -> fp32 GEMM (router, LM head)
+ *   fp8moe_causal_attention  causal grouped-query attention, bf16 in and out
+ *
  * Sources (by page title and section):
  *   [P1] "FP8 grouped-expert prefill with on-chip int4-to-e4m3 dequant"
  *        (octopusresearch.org), section 1 Contribution.
  *   [P2] FreeToken PR #389 "load-time per-tensor FP8 dense projections (W8A8 via
  *        _scaled_mm)", sections "What this adds" and "Limits".
  *   [P4] memra-engine fp8_ffi module docs (docs.rs), module text and struct Fp8Scratch.
+ *   [P1] section 3 also names the depth stacks (L = 8 and 12) the note measures.
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers, row-major, densely packed, owned by the
@@ -71,6 +78,7 @@ extern "C" {
 /* ops for fp8moe_workspace_bytes */
 #define FP8MOE_OP_QUANT_ACT 0
 #define FP8MOE_OP_ROUTE_PERMUTE 1
+#define FP8MOE_OP_ATTENTION 2
 
 /* Version of this ABI (bumped on any signature change). */
 int32_t fp8moe_abi_version(void);
@@ -82,6 +90,7 @@ const char* fp8moe_status_str(int32_t status);
  * fp8moe_workspace_bytes -- device scratch an entry point needs.
  *   op = FP8MOE_OP_QUANT_ACT:      a = M, b = K, c = group (128 or 0)
  *   op = FP8MOE_OP_ROUTE_PERMUTE:  a = T, b = E, c = k
+ *   op = FP8MOE_OP_ATTENTION:      a = T, b = n_kv, c = head_dim (128)
  * Returns 0 for an op that needs none, (size_t)-1 for invalid arguments.
  */
 size_t fp8moe_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c);
@@ -245,6 +254,61 @@ int32_t fp8_dense_gemm(const uint8_t* a, const float* a_scale_blk, const uint8_t
 int32_t moe_unpermute_combine(const void* y, int32_t y_dtype, const int32_t* pos,
                               const float* weights, int64_t T, int32_t k, int64_t H,
                               int32_t out_dtype, void* out, void* stream);
+
+/*
+ * fp8moe_rmsnorm -- residual add and RMSNorm of one depth-stack block boundary.
+ *
+ * [P1] sections 1 and 3: the FP8 projections and grouped experts run inside a stack of
+ * pre-norm transformer layers with RMSNorm; the pages print no formula, so the plain
+ * one is used, with unit gain:
+ *   delta == NULL:  y = bf16(x / sqrt(mean(x^2) + eps))
+ *   delta != NULL:  x_out = bf16(x + delta), then y = bf16(x_out / sqrt(mean(x_out^2) + eps))
+ * Both roundings are single roundings (round to nearest even) of the exact value, up to
+ * the fp64 summation order of the mean.
+ *
+ *   x        bf16 [T, H]
+ *   delta    NULL, or bf16 [T, H] added to x
+ *   eps      added to the mean square (the stack uses 1e-6)
+ *   x_out    out (only with delta), bf16 [T, H]; may be x itself (in-place update)
+ *   y        out, bf16 [T, H]; must not overlap x, delta or x_out
+ * Constraints: T >= 1, H >= 8, H % 8 == 0, T*H < 2^40, eps >= 0.
+ */
+int32_t fp8moe_rmsnorm(const void* x, const void* delta, int64_t T, int64_t H, double eps,
+                       void* x_out, void* y, void* stream);
+
+/*
+ * fp8moe_bf16_gemm -- out = a . w^T in fp32 from bf16 operands (fp32 accumulation).
+ *
+ * [P1] section 1 gates the stack on its final logits; [P2] "Limits": the LM head stays
+ * bf16. Used for the router logits and the LM head.
+ *
+ *   a    bf16 [M, K]
+ *   w    bf16 [N, K]
+ *   out  fp32 [M, N]
+ * Constraints: M >= 1, N >= 1, K >= 64, K % 64 == 0, M, N, K < 2^31,
+ * ceil(M/128) * ceil(N/128) < 2^31.
+ */
+int32_t fp8moe_bf16_gemm(const void* a, const void* w, int64_t M, int64_t N, int64_t K,
+                         float* out, void* stream);
+
+/*
+ * fp8moe_causal_attention -- causal grouped-query attention over a fused qkv tensor.
+ *
+ * [P1] sections 1 and 3: the attention core between the FP8 q/k/v and o projections
+ * stays bf16. Reading used: no rotary embedding; query head h reads kv head
+ * h / (n_q / n_kv); o[t, h] = sum_{s <= t} softmax_s(q[t, h] . k[s, kv] / sqrt(d)) v[s, kv]
+ * with scores, softmax and the sum in fp32 and the weights rounded to bf16 for the
+ * product with v (their row sum uses the same rounded weights).
+ *
+ *   qkv   bf16 [T, (n_q + 2 n_kv) * d]: row t = [q heads | k heads | v heads], head-major
+ *   out   out, bf16 [T, n_q * d], head-major
+ *   ws    workspace of fp8moe_workspace_bytes(FP8MOE_OP_ATTENTION, T, n_kv, d) bytes
+ *         (v transposed per kv head)
+ * Constraints: T >= 1, d == 128, n_kv >= 1, n_q % n_kv == 0, (n_q + 2 n_kv) * d * T < 2^31.
+ */
+int32_t fp8moe_causal_attention(const void* qkv, int64_t T, int32_t n_q, int32_t n_kv,
+                                int32_t head_dim, void* out, void* ws, size_t ws_bytes,
+                                void* stream);
 
 #ifdef __cplusplus
 }

@@ -40,13 +40,17 @@ def rmsnorm(x: np.ndarray) -> np.ndarray:
     return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + EPS)
 
 
-def causal_gqa_attention(q, k, v, n_q, n_kv, d):
-    """q [T, n_q*d], k/v [T, n_kv*d] -> [T, n_q*d], float64."""
+def causal_gqa_attention(q, k, v, n_q, n_kv, d, with_bound=False):
+    """q [T, n_q*d], k/v [T, n_kv*d] -> [T, n_q*d], float64.
+
+    With ``with_bound`` also returns sum_s p[t, s] * |v[s]| per output element (the
+    magnitude the attention weights' rounding errors scale with)."""
     T = q.shape[0]
     q = np.asarray(q, np.float64).reshape(T, n_q, d)
     k = np.asarray(k, np.float64).reshape(T, n_kv, d)
     v = np.asarray(v, np.float64).reshape(T, n_kv, d)
     out = np.empty((T, n_q, d))
+    bound = np.empty((T, n_q, d)) if with_bound else None
     mask = np.tril(np.ones((T, T), dtype=bool))
     rep = n_q // n_kv
     for h in range(n_q):
@@ -57,6 +61,10 @@ def causal_gqa_attention(q, k, v, n_q, n_kv, d):
         p = np.exp(s)
         p /= p.sum(axis=1, keepdims=True)
         out[:, h, :] = p @ v[:, kv, :]
+        if with_bound:
+            bound[:, h, :] = p @ np.abs(v[:, kv, :])
+    if with_bound:
+        return out.reshape(T, n_q * d), bound.reshape(T, n_q * d)
     return out.reshape(T, n_q * d)
 
 

@@ -39,13 +39,15 @@ def test_header_declares_the_five_entry_points():
                  "fp8_dense_gemm", "moe_unpermute_combine"]:
         assert name in fns
     assert "fp8moe_workspace_bytes" in fns and "fp8moe_status_str" in fns
+    for name in ["fp8moe_rmsnorm", "fp8moe_bf16_gemm", "fp8moe_causal_attention"]:
+        assert name in fns
 
 
 def test_every_declared_symbol_is_exported(lib):
     raw = ctypes.CDLL(LIB)
     for name in declared_functions():
         assert hasattr(raw, name), name
-    assert lib.fp8moe_abi_version() == 2
+    assert lib.fp8moe_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -179,3 +181,44 @@ def test_binding_refuses_host_tensors():
     import fp8_moe_prefill_amd as f
     with pytest.raises(ValueError):
         f.fp8_quant_act(torch.zeros((4, 128), dtype=torch.bfloat16))
+
+
+def test_attention_workspace_query(lib):
+    bad = ctypes.c_size_t(-1).value
+    assert lib.fp8moe_workspace_bytes(2, 2048, 4, 128) == 4 * 128 * 2048 * 2
+    assert lib.fp8moe_workspace_bytes(2, 100, 2, 128) == 2 * 128 * 128 * 2  # T padded to 64
+    assert lib.fp8moe_workspace_bytes(2, 100, 2, 64) == bad  # head_dim must be 128
+    assert lib.fp8moe_workspace_bytes(2, 0, 2, 128) == bad
+
+
+def test_rmsnorm_validation(lib):
+    f = lib.fp8moe_rmsnorm
+    assert f(None, None, 4, 64, 1e-6, None, P, None) == NULL
+    assert f(P, P, 4, 64, 1e-6, None, P, None) == NULL  # delta without x_out
+    assert f(P, None, 0, 64, 1e-6, None, P, None) == SHAPE
+    assert f(P, None, 4, 60, 1e-6, None, P, None) == SHAPE  # H % 8
+    assert f(P, None, 4, 64, -1.0, None, P, None) == SHAPE
+    assert f(P, None, 4, 64, float("nan"), None, P, None) == SHAPE
+    assert f(U, None, 4, 64, 1e-6, None, P, None) == ALIGN
+    assert f(P, U, 4, 64, 1e-6, P, P, None) == ALIGN
+
+
+def test_bf16_gemm_validation(lib):
+    f = lib.fp8moe_bf16_gemm
+    assert f(None, P, 4, 4, 64, P, None) == NULL
+    assert f(P, P, 0, 4, 64, P, None) == SHAPE
+    assert f(P, P, 4, 0, 64, P, None) == SHAPE
+    assert f(P, P, 4, 4, 96, P, None) == SHAPE  # K % 64
+    assert f(P, P, 4, 4, 64, U, None) == ALIGN
+
+
+def test_attention_validation(lib):
+    f = lib.fp8moe_causal_attention
+    n = 4 * 128 * 64 * 2
+    assert f(None, 64, 16, 4, 128, P, P, n, None) == NULL
+    assert f(P, 64, 16, 4, 64, P, P, n, None) == SHAPE   # head_dim
+    assert f(P, 64, 16, 3, 128, P, P, n, None) == SHAPE  # n_q % n_kv
+    assert f(P, 0, 16, 4, 128, P, P, n, None) == SHAPE
+    assert f(P, 64, 16, 4, 128, U, P, n, None) == ALIGN
+    assert f(P, 64, 16, 4, 128, P, P, n - 1, None) == WS
+
