@@ -11,7 +11,13 @@ Prints one JSON line: MoE prefill tokens/s for the whole layer, plus the rooflin
 dominant kernel (the grouped gate|up GEMM, FP8 MFMA bound) measured with HIP events on the
 launch stream inside the timed region, and the CPU oracle timed on a bounded sample.
 
+The line also carries the depth stack (T=2048, L=8 by default, --stack 12 or 0): prefill
+tokens/s of the whole forward (L layers of W8A8 q/k/v/o, causal GQA attention, router and
+FP8 MoE, then the bf16 LM head), with its time against the sum of its parts' MFMA
+rooflines (FP8 parts at the FP8 peak, bf16 parts at the bf16 peak).
+
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] [--dense]
+                    [--stack {0,8,12}]
 """
 
 from __future__ import annotations
@@ -27,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "grouped FP8 expert GEMM TFLOP/s (% FP8 MFMA peak); MoE prefill tokens/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_gate_up_moe_prefill_traffic.json")
@@ -42,6 +49,8 @@ def _parse():
     ap.add_argument("--dense", action="store_true",
                     help="also time the W8A8 dense projections (2048 x 4096 x {6144, 4096})")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--stack", type=int, default=8, choices=[0, 8, 12],
+                    help="also time the depth stack of this many layers (0: skip)")
     return ap.parse_args()
 
 
@@ -86,6 +95,66 @@ def cpu_baseline(n_tokens: int, min_seconds: float = 10.0, max_reps: int = 5):
             "kind": "oracle",
             "sample": f"the NumPy fp64 oracle MoE layer on the first {n_tokens} of the 4096 "
                       f"tokens (all 64 experts), {reps} runs, {total:.1f} s"}
+
+
+def stack_flops(c):
+    """Algorithmic FLOP of one stack forward, split by MFMA dtype: FP8 (q/k/v/o, experts)
+    and bf16 (causal attention, router, LM head)."""
+    T, H, d = c.T, c.H, c.head_dim
+    nqkv = (c.n_q + 2 * c.n_kv) * d
+    fp8 = 2.0 * T * H * nqkv + 2.0 * T * c.n_q * d * H + 6.0 * T * c.k * H * c.I
+    attn = 4.0 * d * (T * (T + 1) / 2) * c.n_q  # q.k and p.v over the causal pairs
+    bf16 = attn + 2.0 * T * H * c.E
+    head = 2.0 * T * H * c.V
+    return c.L * fp8, c.L * bf16 + head
+
+
+def bench_stack(L: int, warmup: int, steps: int):
+    """The depth stack forward (T=2048): prefill tokens/s, per-layer and LM-head times."""
+    import numpy as np
+    import torch
+
+    import fp8_moe_prefill_amd as f
+    from synth import CONFIGS, stack_inputs
+
+    c = CONFIGS[f"stack_L{L}"]
+    dev = torch.device("cuda:0")
+    inp = stack_inputs(c)
+    stack = f.DepthStack.from_host(inp, c.n_q, c.n_kv, c.head_dim, c.k, dev)
+    x0 = torch.from_numpy(inp["x0"].view(np.int16)).to(dev).view(torch.bfloat16)
+    del inp
+    runner = f.StackRunner(stack, c.T, dev)
+    for _ in range(max(warmup, 1)):
+        runner.run(x0)
+    torch.cuda.synchronize()
+
+    def evp():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    t0, t1 = evp()
+    t0.record()
+    for _ in range(steps):
+        runner.run(x0)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    # one more forward with per-part events (not part of the timed loop above)
+    ev = {"layer": ([torch.cuda.Event(enable_timing=True) for _ in range(L)],
+                    [torch.cuda.Event(enable_timing=True) for _ in range(L)]),
+          "lm_head": evp()}
+    runner.run(x0, events=ev)
+    torch.cuda.synchronize()
+    layer_us = [ev["layer"][0][i].elapsed_time(ev["layer"][1][i]) * 1e3 for i in range(L)]
+    head_us = ev["lm_head"][0].elapsed_time(ev["lm_head"][1]) * 1e3
+    f8, b16 = stack_flops(c)
+    roof_us = (f8 / PEAK_FP8_TFLOPS + b16 / PEAK_BF16_TFLOPS) / 1e6
+    return {"workload": f"stack_L{L}: {L} layers, T={c.T}, hidden {c.H}, {c.n_q}/{c.n_kv} heads "
+                        f"of {c.head_dim}, W8A8 q/k/v/o, causal GQA attention, FP8 MoE "
+                        f"(E={c.E}, top-{c.k}, I={c.I}), bf16 LM head V={c.V}",
+            "prefill_tokens_per_s": c.T / (ms * 1e-3), "ms_per_forward": ms, "steps": steps,
+            "layer_us_mean": float(np.mean(layer_us)), "lm_head_us": head_us,
+            "tflops": (f8 + b16) / (ms * 1e-3) / 1e12,
+            "roofline_us": roof_us, "frac_roofline": roof_us / (ms * 1e3)}
 
 
 def main():
@@ -186,6 +255,9 @@ def main():
             fl = 2.0 * x.shape[0] * w.shape[0] * x.shape[1]
             res[wn] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12}
         out["dense_w8a8"] = res
+
+    if args.stack:
+        out["stack"] = bench_stack(args.stack, args.warmup, min(args.steps, 20))
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_tokens)

@@ -8,8 +8,8 @@
 //
 // gfx950 design (one pass over the keys with a running max, so the T x T score matrix never
 // leaves registers):
-// * a workgroup owns one kv head, 32 queries and four query heads of that kv head's group,
-//   one per wave; the K tile and the transposed V tile of 64 keys are staged once in LDS
+// * a workgroup owns one kv head, 16 queries and four query heads of that kv head's group,
+//   one per wave (small query blocks: more workgroups in flight for the causal imbalance); the K tile and the transposed V tile of 64 keys are staged once in LDS
 //   (double-buffered, next tile's global loads in flight during the MFMAs) and shared by
 //   the four waves;
 // * each wave computes S^T = K Q^T (v_mfma_f32_16x16x32_bf16, keys as rows), so a lane's
@@ -29,7 +29,8 @@ namespace fp8moe {
 namespace {
 
 constexpr int D = 128;        // head dim
-constexpr int QB = 32;        // queries per workgroup (two 16-query MFMA tiles per wave)
+constexpr int NQT = 1;        // 16-query MFMA tiles per wave
+constexpr int QB = 16 * NQT;  // queries per workgroup
 constexpr int KT = 64;        // keys per tile
 constexpr int KS = D * 2 + 16;   // K tile row stride in LDS (bytes): 256 + 16 pad
 constexpr int VS = KT * 2 + 16;  // V^T tile row stride in LDS (bytes): 128 + 16 pad
@@ -75,9 +76,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   const int nkt = min(q0 + QB - 1, T - 1) / KT + 1;
 
   // Q fragments: lane (g, c16) holds query q0 + 16 qt + c16, dims 32 kk + 8 g .. +7
-  bf16x8_t qf[2][4];
+  bf16x8_t qf[NQT][4];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < NQT; ++qt) {
     const int t = min(q0 + 16 * qt + c16, T - 1);
     const uint16_t* src = qkv + (int64_t)t * ld + h * D + 8 * g;
 #pragma unroll
@@ -108,12 +109,14 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
     }
   };
 
-  v4f o[2][8];
+  v4f o[NQT][8];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[qt][dt] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+  float m_run[NQT], l_part[NQT];
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) m_run[qt] = -INFINITY, l_part[qt] = 0.f;
 
   load_tile(0);
   store_tile(0);
@@ -125,26 +128,26 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
     if (more) load_tile(kt + 1);
 
     // S^T[key 16 s + 4 g + r][query 16 qt + c16], s = 16-key subtile
-    v4f st[2][4];
+    v4f st[NQT][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) st[qt][s] = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int qt = 0; qt < NQT; ++qt) st[qt][s] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const bf16x8_t a = as_bf16x8(
             *reinterpret_cast<const uint4*>(&sK[cur][(16 * s + c16) * KS + kk * 64 + g * 16]));
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        for (int qt = 0; qt < NQT; ++qt)
           st[qt][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qt][kk], st[qt][s], 0, 0, 0);
       }
     }
 
     // online softmax in the log2 domain; only the last tile can hold keys past a query
     const bool diag = kt == nkt - 1;
-    bf16x8_t pb[2][2], pl[2][2];
+    bf16x8_t pb[NQT][2], pl[NQT][2];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < NQT; ++qt) {
       const int qi = q0 + 16 * qt + c16;
       float mx = -INFINITY;
 #pragma unroll
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
         const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (32 * c + 16 + 4 * g) * 2);
         const bf16x8_t a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
+        for (int qt = 0; qt < NQT; ++qt) {
           o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qt][c], o[qt][dt], 0, 0, 0);
           o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[qt][c], o[qt][dt], 0, 0, 0);
         }
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
 
   if (!live) return;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < NQT; ++qt) {
     float l = l_part[qt];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);

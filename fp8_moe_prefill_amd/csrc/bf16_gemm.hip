@@ -6,8 +6,8 @@
 // keeps the LM head in bf16. The router that feeds the top-k selection and the LM head are
 // therefore plain bf16 GEMMs with fp32 accumulation and fp32 output.
 //
-// gfx950 design: both operands K-contiguous ("TN"). Workgroup tile 128 x 128, 4 waves in a
-// 2 x 2 grid of 64 x 64, each 4 x 4 tiles of v_mfma_f32_16x16x32_bf16. One K step is 64
+// gfx950 design: both operands K-contiguous ("TN"). For N > 128: workgroup tile 128 x 128,
+// 4 waves in a 2 x 2 grid of 64 x 64, each 4 x 4 tiles of v_mfma_f32_16x16x32_bf16. One K step is 64
 // elements (128 bytes per row), staged through XOR-swizzled LDS, double-buffered with one
 // barrier per step; the next step's global loads are in flight during the MFMAs.
 #include "common.h"
@@ -121,10 +121,75 @@ __global__ __launch_bounds__(256, 2) void bf16_gemm_kernel(const uint16_t* __res
     }
 }
 
+// Narrow outputs (N <= 128, the router): a workgroup owns 16 rows and all N columns, its
+// four waves split K (interleaved 32-wide steps) and add their partial tiles in a fixed
+// order through LDS. Operands come straight from global memory (the N x K weight stays in
+// L2); the 128 x 128 tiling above would leave most of the chip idle for such shapes.
+template <int NT>
+__global__ __launch_bounds__(256) void bf16_gemm_narrow_kernel(const uint16_t* __restrict__ A,
+                                                               const uint16_t* __restrict__ W,
+                                                               int M, int N, int K,
+                                                               float* __restrict__ out) {
+  __shared__ v4f part[4][NT][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int m0 = blockIdx.x * 16;
+  const uint16_t* a = A + (int64_t)min(m0 + c16, M - 1) * K + 8 * g;
+  const uint16_t* w[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) w[t] = W + (int64_t)min(16 * t + c16, N - 1) * K + 8 * g;
+  v4f acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int k = 32 * wv; k < K; k += 128) {
+    const bf16x8_t av = as_bf16x8(*reinterpret_cast<const uint4*>(a + k));
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          av, as_bf16x8(*reinterpret_cast<const uint4*>(w[t] + k)), acc[t], 0, 0, 0);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) part[wv][t][lane] = acc[t];
+  __syncthreads();
+  if (wv != 0) return;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    v4f sum = part[0][t][lane];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) sum += part[q][t][lane];
+    const int col = 16 * t + c16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + 4 * g + r;
+      if (row < M && col < N) out[(int64_t)row * N + col] = sum[r];
+    }
+  }
+}
+
+template <int NT>
+hipError_t launch_narrow(const uint16_t* a, const uint16_t* w, int64_t M, int64_t N, int64_t K,
+                         float* out, hipStream_t st) {
+  bf16_gemm_narrow_kernel<NT><<<dim3((uint32_t)((M + 15) / 16)), 256, 0, st>>>(
+      a, w, (int)M, (int)N, (int)K, out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_bf16_gemm(const uint16_t* a, const uint16_t* w, int64_t M, int64_t N,
                             int64_t K, float* out, hipStream_t st) {
+  switch ((N + 15) / 16) {
+    case 1: return launch_narrow<1>(a, w, M, N, K, out, st);
+    case 2: return launch_narrow<2>(a, w, M, N, K, out, st);
+    case 3: return launch_narrow<3>(a, w, M, N, K, out, st);
+    case 4: return launch_narrow<4>(a, w, M, N, K, out, st);
+    case 5: return launch_narrow<5>(a, w, M, N, K, out, st);
+    case 6: return launch_narrow<6>(a, w, M, N, K, out, st);
+    case 7: return launch_narrow<7>(a, w, M, N, K, out, st);
+    case 8: return launch_narrow<8>(a, w, M, N, K, out, st);
+    default: break;
+  }
   const int NTM = (int)((M + TM - 1) / TM), NTN = (int)((N + TN - 1) / TN);
   bf16_gemm_kernel<<<dim3((uint32_t)(NTM * NTN)), 256, 0, st>>>(a, w, (int)M, (int)N, (int)K,
                                                                 NTN, out);

@@ -94,7 +94,8 @@ def test_rmsnorm_bit_exact(T, H):
 # ------------------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (300, 200, 320), (2048, 64, 2048), (129, 257, 192)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (300, 200, 320), (2048, 64, 2048), (129, 257, 192),
+                                   (77, 100, 128), (33, 128, 4160)])
 def test_bf16_gemm_bound(M, N, K):
     import fp8_moe_prefill_amd as f
     rng = np.random.default_rng(M + 7 * N + 13 * K)
@@ -105,12 +106,14 @@ def test_bf16_gemm_bound(M, N, K):
     check_close(host(out), A @ W.T, gemm_bound(np.abs(A) @ np.abs(W).T), "bf16 gemm")
 
 
-def test_bf16_gemm_integer_exact():
+@pytest.mark.parametrize("N", [144, 64])
+def test_bf16_gemm_integer_exact(N):
     """Integer operands in -4..4 with K = 384: every partial sum is an integer below 2^24,
-    so fp32 accumulation is exact in any order and the GPU result must equal a @ w^T."""
+    so fp32 accumulation is exact in any order and the GPU result must equal a @ w^T
+    (N = 64 takes the narrow-output path)."""
     import fp8_moe_prefill_amd as f
     rng = np.random.default_rng(5)
-    M, N, K = 200, 144, 384
+    M, K = 200, 384
     a = bf16_bits_from_f32(rng.integers(-4, 5, (M, K)).astype(np.float32))
     w = bf16_bits_from_f32(rng.integers(-4, 5, (N, K)).astype(np.float32))
     out = f.bf16_gemm(dev(a), dev(w))
