@@ -162,6 +162,8 @@ int32_t fp8_dense_gemm(const uint8_t* a, const float* a_scale_blk, const uint8_t
   if (M < 1 || M >= (int64_t(1) << 31) || N < 16 || N % 16 != 0 || N >= (int64_t(1) << 31))
     return FP8MOE_ERR_SHAPE;
   if (K < 128 || K % 128 != 0 || K >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
+  // per-lane 32-bit byte offsets into A and W
+  if (M * K >= (int64_t(1) << 32) || N * K >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;
   const void* ptrs[] = {a, a_scale_blk, w, w_scale, out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
@@ -207,6 +209,8 @@ int32_t fp8moe_bf16_gemm(const void* a, const void* w, int64_t M, int64_t N, int
   if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) || K >= (int64_t(1) << 31))
     return FP8MOE_ERR_SHAPE;
   if (((M + 127) / 128) * ((N + 127) / 128) >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
+  // per-lane 32-bit byte offsets into a and w
+  if (2 * M * K >= (int64_t(1) << 32) || 2 * N * K >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;
   if (!aligned16(a) || !aligned16(w) || !aligned16(out)) return FP8MOE_ERR_ALIGN;
   return launch_status(fp8moe::launch_bf16_gemm(static_cast<const uint16_t*>(a),
                                                  static_cast<const uint16_t*>(w), M, N, K, out,

@@ -100,4 +100,18 @@ __device__ __forceinline__ uint32_t xcd_contiguous(uint32_t bid, uint32_t nblock
   return x * per + (x < rem ? x : rem) + i;
 }
 
+// Logical tile L of an NTM x NTN tile grid, in groups of up to 8 tile rows swept
+// column-block by column-block: consecutive L (which run side by side on one XCD, see
+// xcd_contiguous) then cover a compact block of 8 x 8 tiles whose A rows and W columns
+// stay in that XCD's L2, instead of one tile row against 64 different weight blocks.
+__device__ __forceinline__ void grouped_tile(uint32_t L, int NTM, int NTN, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const uint32_t per_group = (uint32_t)(GM * NTN);
+  const int first = (int)(L / per_group) * GM;
+  const int gm = min(NTM - first, GM);
+  const int r = (int)(L % per_group);
+  tm = first + r % gm;
+  tn = r / gm;
+}
+
 }  // namespace fp8moe

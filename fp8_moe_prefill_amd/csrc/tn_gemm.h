@@ -1,0 +1,213 @@
+// out[M, N] = scale * (A[M, K] . W[N, K]^T) with both operands K-contiguous ("TN"), for
+// e4m3 x e4m3 (the W8A8 projections, fp8_dense_gemm) and bf16 x bf16 (the stack's LM head,
+// fp8moe_bf16_gemm).
+//
+// gfx950 design:
+// * Workgroup tile 128 x 128, 4 waves in a 2 x 2 grid of 64 x 64 (4 x 4 MFMA tiles each).
+//   One K step is 128 bytes of each row: one v_mfma_f32_16x16x128_f8f6f4 per 16 x 16 tile
+//   for e4m3, two v_mfma_f32_16x16x32_bf16 for bf16.
+// * Both operands go straight from global memory into LDS (LDS DMA, no VGPR staging, no
+//   LDS writes by the waves), each DMA instruction copying 8 whole 128-byte lines (8 rows
+//   of one K step) into 1 KB of LDS; the 16-byte chunks of a row are XOR-swizzled so that
+//   the MFMA operand reads (row c of a 16-row tile, chunk 2 g + half for lane g * 16 + c)
+//   are free of bank conflicts.
+// * A ring of STAGES steps in LDS: the loads of step ks + STAGES - 1 are issued right after
+//   the barrier that frees their slot and stream in while step ks is computed; each wave
+//   waits for its own loads by count, and the barrier publishes them.
+// * Tiles are dealt to XCDs in contiguous ranges and walked in 8 x 8 blocks, so the A rows
+//   and W columns of the tiles in flight on an XCD stay in its L2.
+// * Output columns are interleaved so that each lane holds four consecutive columns of a
+//   row: column tile s of a wave covers columns 4 * c + s of its 64, and a lane writes them
+//   with one 8-byte (bf16) or 16-byte (fp32) store.
+#pragma once
+
+#include "common.h"
+#include "lds_dma.h"
+
+namespace fp8moe {
+namespace tn {
+
+constexpr int TM = 128, TN = 128;  // tile rows and columns
+constexpr int KSTEP = 128;         // bytes of K per step
+constexpr int BLK = 1024;          // one operand block: 64 lanes x 16 bytes
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+template <int STAGES>
+struct Smem {
+  uint8_t a[STAGES][16 * BLK];  // 8 row tiles x 2 halves
+  uint8_t b[STAGES][16 * BLK];  // 8 column tiles x 2 halves
+};
+
+__device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// LDS holds each operand tile as 128 rows of 128 bytes (one K step), the 16-byte chunk c of
+// row r at position c ^ sw(r): any 16 consecutive rows then read one chunk each without
+// bank conflicts.
+__device__ __forceinline__ int sw(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// W's LDS row rho holds global column col_of(rho) of the tile: wave wn's column tile s,
+// lane c reads row 64 wn + 16 s + c, which is column 64 wn + 4 c + s, so each lane ends up
+// with four consecutive output columns.
+__device__ __forceinline__ int col_of(int rho) {
+  return 64 * (rho >> 6) + 4 * (rho & 15) + ((rho >> 4) & 3);
+}
+
+// IN_BF16: operands are bf16 (K counts elements, 2 bytes each), else e4m3 bytes.
+// OUT_BF16: bf16 output (round to nearest even), else fp32.
+// scale_a / scale_w: the e4m3 path multiplies by scale_a[2] * scale_w[0] (the activation
+// scale block and the weight scale, both on the device); the bf16 path takes no scale.
+template <bool IN_BF16, bool OUT_BF16, int STAGES>
+__global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restrict__ A,
+                                                         const uint8_t* __restrict__ W, int M,
+                                                         int N, int row_bytes, int NTM,
+                                                         int NTN,
+                                                         const float* __restrict__ scale_a,
+                                                         const float* __restrict__ scale_w,
+                                                         void* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) Smem<STAGES> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int g = lane >> 4, c16 = lane & 15;
+  const int wm = wv >> 1, wn = wv & 1;
+  const uint32_t L = xcd_contiguous(blockIdx.x, gridDim.x);
+  int tm, tn;
+  grouped_tile(L, NTM, NTN, tm, tn);
+  const int m0 = tm * TM, n0 = tn * TN;
+  const int KS = row_bytes / KSTEP;
+
+  // DMA duty: 32 instructions per step (16 for the 128 rows of A, 16 for the 128 columns
+  // of W), 8 per wave; waves 0-1 load A, waves 2-3 load W. Instruction j of an operand
+  // copies its rows 8 (j % 16) .. + 7 as whole 128-byte lines: lane l takes row
+  // 8 (j % 16) + l / 8 and writes LDS position l % 8 of it, holding the line's 16-byte
+  // chunk (l % 8) ^ sw(row) (see lds_pos). voff[j] is that byte offset at K step 0.
+  const uint8_t* src = wv < 2 ? A : W;
+  uint32_t voff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int rho = 8 * (8 * (wv & 1) + j) + (lane >> 3);  // LDS row of this lane
+    int row;
+    if (wv < 2) row = min(m0 + rho, M - 1);
+    else row = min(n0 + col_of(rho), N - 1);
+    const int chunk = (lane & 7) ^ sw(rho);
+    voff[j] = (uint32_t)row * (uint32_t)row_bytes + 16u * (uint32_t)chunk;
+  }
+  auto issue = [&](int ks) {
+    const int st = ks % STAGES;
+    uint8_t* dst = (wv < 2 ? sm.a[st] : sm.b[st]) + (wv & 1) * 8 * BLK;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma16(src, voff[j] + (uint32_t)(ks * KSTEP), dst + j * BLK);
+  };
+  // operand reads: tile T (16 rows), half h: row 16 T + c16, chunk 2 g + h
+  const int x = sw(c16);
+  const int rd0 = c16 * KSTEP + (((2 * g) ^ x) << 4);
+  const int rd1 = c16 * KSTEP + (((2 * g + 1) ^ x) << 4);
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc[t][s] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < KS) issue(p);
+
+  for (int ks = 0; ks < KS; ++ks) {
+    // this step's blocks are in: only the steps issued after it may still be in flight
+    if (STAGES == 3 && ks + 1 < KS) wait_loads<8>();
+    else wait_loads<0>();
+    lds_barrier();  // every wave's loads of step ks landed; slot (ks - 1) % STAGES is free
+    if (ks + STAGES - 1 < KS) issue(ks + STAGES - 1);
+    const uint8_t* sa = sm.a[ks % STAGES];
+    const uint8_t* sb = sm.b[ks % STAGES];
+    if (IN_BF16) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8_t aop[4], bop[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          bop[s] = __builtin_bit_cast(bf16x8_t, lds16(sb + (4 * wn + s) * 16 * KSTEP + (h ? rd1 : rd0)));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          aop[t] = __builtin_bit_cast(bf16x8_t, lds16(sa + (4 * wm + t) * 16 * KSTEP + (h ? rd1 : rd0)));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[t], bop[s], acc[t][s], 0, 0, 0);
+      }
+    } else {
+      // all operands of the step first (16 reads in flight), then the 16 MFMAs
+      v8i aop[4], bop[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 lo = lds16(sb + (4 * wn + s) * 16 * KSTEP + rd0);
+        const uint4 hi = lds16(sb + (4 * wn + s) * 16 * KSTEP + rd1);
+        bop[s] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint4 lo = lds16(sa + (4 * wm + t) * 16 * KSTEP + rd0);
+        const uint4 hi = lds16(sa + (4 * wm + t) * 16 * KSTEP + rd1);
+        aop[t] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc[t][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop[t], bop[s], acc[t][s],
+                                                                       0, 0, 0, 0, 0, 0);
+    }
+  }
+
+  const float scale = IN_BF16 ? 1.f : scale_a[2] * scale_w[0];
+  const int c0 = n0 + 64 * wn + 4 * c16;
+  const bool vec = (c0 + 3 < N) && ((N & 3) == 0);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + 64 * wm + 16 * t + 4 * g + r;
+      if (row >= M) continue;
+      const float v0 = acc[t][0][r] * scale, v1 = acc[t][1][r] * scale;
+      const float v2 = acc[t][2][r] * scale, v3 = acc[t][3][r] * scale;
+      const int64_t o = (int64_t)row * N + c0;
+      if (OUT_BF16) {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(out) + o;
+        if (vec) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(bf16x2(v0, v1), bf16x2(v2, v3));
+        } else {
+          const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            if (c0 + s < N) dst[s] = (uint16_t)f32_to_bf16(v[s]);
+        }
+      } else {
+        float* dst = reinterpret_cast<float*>(out) + o;
+        if (vec) {
+          *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
+        } else {
+          const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            if (c0 + s < N) dst[s] = v[s];
+        }
+      }
+    }
+}
+
+// Enqueue the kernel over ceil(M/128) x ceil(N/128) tiles; row_bytes = bytes per row of K.
+template <bool IN_BF16, bool OUT_BF16, int STAGES>
+hipError_t launch(const uint8_t* a, const uint8_t* w, int64_t M, int64_t N, int64_t row_bytes,
+                  const float* scale_a, const float* scale_w, void* out, hipStream_t st) {
+  const int NTM = (int)((M + TM - 1) / TM), NTN = (int)((N + TN - 1) / TN);
+  tn_gemm_kernel<IN_BF16, OUT_BF16, STAGES><<<dim3((uint32_t)(NTM * NTN)), 256, 0, st>>>(
+      a, w, (int)M, (int)N, (int)row_bytes, NTM, NTN, scale_a, scale_w, out);
+  return hipGetLastError();
+}
+
+}  // namespace tn
+}  // namespace fp8moe

@@ -232,7 +232,7 @@ int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales,
  *   w            e4m3 [N, K]
  *   w_scale      fp32[1] on the device, s_w
  *   out          [M, N] fp32 or bf16 (RNE) per out_dtype
- * Constraints: M >= 1, N % 16 == 0, K % 128 == 0.
+ * Constraints: M >= 1, N % 16 == 0, K % 128 == 0, M*K < 2^32, N*K < 2^32.
  */
 int32_t fp8_dense_gemm(const uint8_t* a, const float* a_scale_blk, const uint8_t* w,
                        const float* w_scale, int64_t M, int64_t N, int64_t K,
@@ -286,7 +286,7 @@ int32_t fp8moe_rmsnorm(const void* x, const void* delta, int64_t T, int64_t H, d
  *   w    bf16 [N, K]
  *   out  fp32 [M, N]
  * Constraints: M >= 1, N >= 1, K >= 64, K % 64 == 0, M, N, K < 2^31,
- * ceil(M/128) * ceil(N/128) < 2^31.
+ * ceil(M/128) * ceil(N/128) < 2^31, 2*M*K < 2^32, 2*N*K < 2^32.
  */
 int32_t fp8moe_bf16_gemm(const void* a, const void* w, int64_t M, int64_t N, int64_t K,
                          float* out, void* stream);
