@@ -3,7 +3,7 @@ oracle alone: ``python -m tests.golden.make_stack_golden`` (minutes of CPU per s
 
 The whole-stack oracle takes minutes, too long to rerun inside a GPU test, and its full
 logits (T x V fp32) are too large to store. What is stored, per stack, in
-``stack_<name>.npz``:
+``<name>.npz``:
 
 * ``rows``: 8 token positions spread over the sequence (first and last included), and
   ``row_logits``: the oracle's logits at those rows, as fp16 (relative rounding 2^-11,
@@ -40,7 +40,7 @@ N_ROWS = 8
 
 
 def golden_path(name: str) -> str:
-    return os.path.join(HERE, f"stack_{name}.npz")
+    return os.path.join(HERE, f"{name}.npz")
 
 
 def sample_rows(T: int) -> np.ndarray:
