@@ -21,7 +21,8 @@
 //   from LDS; the output accumulators are again per query;
 // * V is transposed once per layer into a [n_kv][d][T_pad] workspace by a small kernel
 //   (zero-filled past T), so V^T tiles load as contiguous rows.
-// Workgroups of the latest query blocks (most keys) are launched first.
+// Workgroups are paired heavy with light (see the rank mapping) against the causal
+// imbalance.
 #include "common.h"
 #include "launch.h"
 
@@ -33,11 +34,28 @@ constexpr int NQT = 1;        // 16-query MFMA tiles per wave
 constexpr int QB = 16 * NQT;  // queries per workgroup
 constexpr int KT = 64;        // keys per tile
 constexpr int KS = D * 2 + 16;   // K tile row stride in LDS (bytes): 256 + 16 pad
-constexpr int VS = KT * 2 + 16;  // V^T tile row stride in LDS (bytes): 128 + 16 pad
+constexpr int VS = KT * 2;       // V^T tile row stride in LDS (bytes): 64 keys, no pad
+// V^T tile rows are XOR-swizzled in 8-byte slots (4 keys): slot s of row d sits at
+// position s ^ (d % 16), so the 16 rows one operand read touches hit distinct banks.
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// max / sum of v over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes that hold the
+// same query): two lane-swap instructions of gfx950, no LDS round trip
+__device__ __forceinline__ float max4q(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4q(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // [T, ld] column block of V (kv head j) -> vt[j][d][t], zero for t in [T, Tp)
 __global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ qkv,
@@ -66,8 +84,16 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   const int rep = n_q / n_kv;
   const int nqb = (T + QB - 1) / QB;
   const int per_qb = n_kv * n_hg;
-  const int qb = nqb - 1 - (int)(blockIdx.x / per_qb);  // latest query blocks first
-  const int rest = (int)(blockIdx.x % per_qb);
+  // Work ranks by weight: rank 0 = the latest query block (most keys). The first half of
+  // the grid takes ranks 0, 1, ... and the second half the lightest first, so the two
+  // workgroups that share a CU (blocks b and b + half are dispatched to the same slot
+  // position) carry one heavy and one light block: every CU gets about the same number
+  // of key tiles.
+  const int nblk = (int)gridDim.x, half = (nblk + 1) / 2;
+  const int b = (int)blockIdx.x;
+  const int rank = b < half ? b : nblk - 1 - (b - half);
+  const int qb = nqb - 1 - rank / per_qb;
+  const int rest = rank % per_qb;
   const int j = rest / n_hg, hg = rest % n_hg;
   const int hr = hg * 4 + wv;               // head within the kv group
   const bool live = hr < rep;               // a wave past the group's heads only helps load
@@ -105,7 +131,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i;
       *reinterpret_cast<uint4*>(&sK[buf][(c >> 4) * KS + (c & 15) * 16]) = rk[i];
-      *reinterpret_cast<uint4*>(&sV[buf][(c >> 3) * VS + (c & 7) * 16]) = rv[i];
+      // 16-byte chunk j of row d holds slots 2j, 2j + 1: they land as chunk j ^ (sg / 2),
+      // in swapped order when sg is odd
+      const int d = c >> 3, sg = d & 15;
+      const uint4 v = (sg & 1) ? make_uint4(rv[i].z, rv[i].w, rv[i].x, rv[i].y) : rv[i];
+      *reinterpret_cast<uint4*>(&sV[buf][d * VS + ((c & 7) ^ (sg >> 1)) * 16]) = v;
     }
   };
 
@@ -159,10 +189,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
           st[qt][s][r] = v;
           mx = fmaxf(mx, v);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max4q(mx);
       const float m_new = fmaxf(m_run[qt], mx);
-      const float alpha = exp2f(m_run[qt] - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
       m_run[qt] = m_new;
       float ls = 0.f;
 #pragma unroll
@@ -171,15 +200,17 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
         for (int r = 0; r < 4; ++r) {
           // p enters P.V as hi + lo, two bf16 terms (about 16 significant bits): the
           // product keeps fp32-level accuracy on the bf16 matrix cores
-          const float p = exp2f(st[qt][s][r] - m_new);
+          const float p = __builtin_amdgcn_exp2f(st[qt][s][r] - m_new);
           const __bf16 hi = (__bf16)p;
           ls += p;
           pb[qt][s >> 1][4 * (s & 1) + r] = hi;
           pl[qt][s >> 1][4 * (s & 1) + r] = (__bf16)(p - (float)hi);
         }
       l_part[qt] = l_part[qt] * alpha + ls;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {  // uniform: some query's max moved
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[qt][dt] *= alpha;
+        for (int dt = 0; dt < 8; ++dt) o[qt][dt] *= alpha;
+      }
     }
 
     // O^T[d 16 dt + 4 g + r][query 16 qt + c16] += V^T P^T over two 32-key steps; the key
@@ -190,8 +221,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
       const uint8_t* vrow = &sV[cur][(16 * dt + c16) * VS];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (32 * c + 4 * g) * 2);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (32 * c + 16 + 4 * g) * 2);
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + ((8 * c + g) ^ c16) * 8);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + ((8 * c + 4 + g) ^ c16) * 8);
         const bf16x8_t a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
@@ -208,9 +239,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   if (!live) return;
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
-    float l = l_part[qt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = sum4q(l_part[qt]);
     const int qi = q0 + 16 * qt + c16;
     if (qi >= T) continue;
     const float inv = 1.f / l;

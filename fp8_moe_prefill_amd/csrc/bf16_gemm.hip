@@ -22,15 +22,17 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // Narrow outputs (N <= 128, the router): a workgroup owns 16 rows and all N columns, its
-// four waves split K (interleaved 32-wide steps) and add their partial tiles in a fixed
-// order through LDS. Operands come straight from global memory (the N x K weight stays in
-// L2); 128 x 128 tiles would leave most of the chip idle for such shapes.
+// NWN waves split K (interleaved 32-wide steps, so each wave has only a few loads to wait
+// for) and add their partial tiles in a fixed order through LDS. Operands come straight
+// from global memory (the N x K weight stays in L2); 128 x 128 tiles would leave most of
+// the chip idle for such shapes.
+constexpr int NWN = 16;
 template <int NT>
-__global__ __launch_bounds__(256) void bf16_gemm_narrow_kernel(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(NWN * 64) void bf16_gemm_narrow_kernel(const uint16_t* __restrict__ A,
                                                                const uint16_t* __restrict__ W,
                                                                int M, int N, int K,
                                                                float* __restrict__ out) {
-  __shared__ v4f part[4][NT][64];
+  __shared__ v4f part[NWN][NT][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int m0 = blockIdx.x * 16;
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(256) void bf16_gemm_narrow_kernel(const uint16_t* _
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-  for (int k = 32 * wv; k < K; k += 128) {
+  for (int k = 32 * wv; k < K; k += 32 * NWN) {
     const bf16x8_t av = as_bf16x8(*reinterpret_cast<const uint4*>(a + k));
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(256) void bf16_gemm_narrow_kernel(const uint16_t* _
   for (int t = 0; t < NT; ++t) {
     v4f sum = part[0][t][lane];
 #pragma unroll
-    for (int q = 1; q < 4; ++q) sum += part[q][t][lane];
+    for (int q = 1; q < NWN; ++q) sum += part[q][t][lane];
     const int col = 16 * t + c16;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(256) void bf16_gemm_narrow_kernel(const uint16_t* _
 template <int NT>
 hipError_t launch_narrow(const uint16_t* a, const uint16_t* w, int64_t M, int64_t N, int64_t K,
                          float* out, hipStream_t st) {
-  bf16_gemm_narrow_kernel<NT><<<dim3((uint32_t)((M + 15) / 16)), 256, 0, st>>>(
+  bf16_gemm_narrow_kernel<NT><<<dim3((uint32_t)((M + 15) / 16)), NWN * 64, 0, st>>>(
       a, w, (int)M, (int)N, (int)K, out);
   return hipGetLastError();
 }

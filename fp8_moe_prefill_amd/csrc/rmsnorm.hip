@@ -7,11 +7,12 @@
 // normalised activations stored in bf16.
 //
 // One wave per row. The sum of squares of the bf16 values (each square exact in fp64) is
-// accumulated in fp64, and the quotient x / sqrt(mean + eps) is formed in fp64 and rounded
-// once to bf16, so the result is the correctly rounded bf16 of the exact expression up to
-// the fp64 summation order. The residual add x + delta of two bf16 values is exact in fp64
-// and is rounded once to bf16 the same way. Memory-bound: 2 bytes read per element (4 with
-// the residual), 2 written (4 with the residual).
+// accumulated in fp64, x / sqrt(mean + eps) is formed in fp64 (as x times the row's fp64
+// reciprocal) and rounded once to bf16: the correctly rounded bf16 of the exact value
+// except when that value lies within a few fp64 ulps of a bf16 rounding midpoint. The
+// residual add x + delta of two bf16 values is exact in fp64 and is rounded once to bf16
+// the same way. Memory-bound: 2 bytes read per element (4 with the residual), 2 written
+// (4 with the residual).
 #include "common.h"
 #include "launch.h"
 
@@ -87,14 +88,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* x, const u
     for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
   }
   ss = wave_sum_f64(ss);
-  const double rms = sqrt(ss / (double)H + eps);
+  const double inv = 1.0 / sqrt(ss / (double)H + eps);
   for (int c = lane; c < nch; c += 64) {
     // the same lane wrote this chunk of x_out above, so it reads its own store
     const uint4 w = delta ? xo[c] : xr[c];
     double v[8];
     unpack8(w, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = v[i] / rms;
+    for (int i = 0; i < 8; ++i) v[i] = v[i] * inv;
     yr[c] = pack8(v);
   }
 }
