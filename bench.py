@@ -17,7 +17,7 @@ FP8 MoE, then the bf16 LM head), with its time against the sum of its parts' MFM
 rooflines (FP8 parts at the FP8 peak, bf16 parts at the bf16 peak).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] [--dense]
-                    [--stack {0,8,12}]
+                    [--stack {0,8,12}] [--stack-only]
 """
 
 from __future__ import annotations
@@ -51,6 +51,8 @@ def _parse():
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--stack", type=int, default=8, choices=[0, 8, 12],
                     help="also time the depth stack of this many layers (0: skip)")
+    ap.add_argument("--stack-only", action="store_true",
+                    help="time only the depth stack (for profiling it alone)")
     return ap.parse_args()
 
 
@@ -163,6 +165,17 @@ def main():
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU expert-parallel path is not built", file=sys.stderr)
         sys.exit(2)
+
+    if args.stack_only:
+        st = bench_stack(args.stack or 8, args.warmup, args.steps)
+        print(json.dumps({"metric": "depth stack prefill tokens/s", "value":
+                          st["prefill_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                          "steps": st["steps"], "warmup": args.warmup,
+                          "ms_per_step": st["ms_per_forward"], "higher_is_better": True,
+                          "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
+                          "data": "synthetic", "config": {"workload": st["workload"]},
+                          "stack": st}))
+        return
 
     import numpy as np
     import torch
