@@ -21,13 +21,21 @@ namespace fp8moe {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// The base address is wave-uniform by contract; readfirstlane makes that explicit to the
+// compiler (a no-op when it already holds the value in SGPRs).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, const void* lds) {
   asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1\n\ts_nop 0"
-               :: "v"(voff), "s"(base), "{m0}"(lds_addr(lds)) : "memory");
+               :: "v"(voff), "s"(uniform_ptr(base)), "{m0}"(lds_addr(lds)) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, const void* lds) {
   asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1\n\ts_nop 0"
-               :: "v"(voff), "s"(base), "{m0}"(lds_addr(lds)) : "memory");
+               :: "v"(voff), "s"(uniform_ptr(base)), "{m0}"(lds_addr(lds)) : "memory");
 }
 
 // Waits and barriers of the pipeline. They are compiler memory barriers ("memory"
