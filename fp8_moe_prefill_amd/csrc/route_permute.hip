@@ -8,10 +8,11 @@
 //
 // Design: a stable counting sort with no order-dependent atomics, so every output is a
 // pure function of the logits.
-//   1. topk_hist:  one wave per token selects the top k by (logit desc, expert asc), one
-//                  wave argmax (DPP within rows, v_readlane across them) per pick; a
-//                  workgroup owns a chunk of 16 tokens and counts its pairs per expert in
-//                  LDS (integer adds commute).
+//   1. topk_hist:  one wave per token selects the top k by (logit desc, expert asc): each
+//                  pick is the wave maximum of a 64-bit key (order-preserving logit bits,
+//                  then the inverted expert index) reduced with DPP only; a workgroup owns
+//                  a chunk of 16 tokens and counts its pairs per expert in LDS (integer
+//                  adds commute).
 //   2. chunk_scan: one workgroup per expert scans that expert's per-chunk counts.
 //   3. scatter:    one workgroup per chunk recomputes the expert offsets (a scan over E),
 //                  ranks each pair among the chunk's earlier pairs of the same expert and
@@ -43,47 +44,49 @@ __device__ __forceinline__ int block_inclusive_scan256(int v, int* tmp /*[4]*/) 
   return v + add;
 }
 
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// Orderable 64-bit key of (logit, expert): a larger key is a larger logit, then a lower
+// expert index. The float's bits map to an unsigned order (negatives flipped, -0 taken as
+// +0); -inf keys stay above 0, the key of a taken expert.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  uint32_t b = __float_as_uint(v);
+  if ((b << 1) == 0u) b = 0u;  // -0 ranks as +0 (they compare equal)
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(~e);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int key_index(uint64_t k) { return (int)~(uint32_t)k; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max64(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, 0xF, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
 }
 
-// value of lane - o within the same 16-lane row; lanes below o keep `old`
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float old, float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL,
-                                                    0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int old, int v) {
-  return __builtin_amdgcn_update_dpp(old, v, CTRL, 0xF, 0xF, false);
-}
-
-// Best (value desc, index asc) over the wave, returned in SGPRs. Within each 16-lane row
-// four DPP row_shr steps carry the row's best into its last lane; the four row winners
-// are then compared through v_readlane on the scalar unit. No LDS round trips.
-__device__ __forceinline__ void wave_argmax(float v, int i, float& bv, int& bi) {
-  float ov = dpp_f<0x111>(v, v); int oi = dpp_i<0x111>(i, i);  // row_shr:1
-  if (better(ov, oi, v, i)) { v = ov; i = oi; }
-  ov = dpp_f<0x112>(v, v); oi = dpp_i<0x112>(i, i);            // row_shr:2
-  if (better(ov, oi, v, i)) { v = ov; i = oi; }
-  ov = dpp_f<0x114>(v, v); oi = dpp_i<0x114>(i, i);            // row_shr:4
-  if (better(ov, oi, v, i)) { v = ov; i = oi; }
-  ov = dpp_f<0x118>(v, v); oi = dpp_i<0x118>(i, i);            // row_shr:8
-  if (better(ov, oi, v, i)) { v = ov; i = oi; }
-  bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
-  bi = __builtin_amdgcn_readlane(i, 15);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) {
-    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r + 15));
-    const int ri = __builtin_amdgcn_readlane(i, 16 * r + 15);
-    if (better(rv, ri, bv, bi)) { bv = rv; bi = ri; }
-  }
+// Largest key of the wave, as a wave-uniform value: row_shr steps carry each 16-lane
+// row's maximum into its last lane, row_bcast:15 and row_bcast:31 carry them into lane
+// 63; all VALU, no branches.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = dpp_max64<0x111>(k);  // row_shr:1
+  k = dpp_max64<0x112>(k);  // row_shr:2
+  k = dpp_max64<0x114>(k);  // row_shr:4
+  k = dpp_max64<0x118>(k);  // row_shr:8
+  k = dpp_max64<0x142>(k);  // row_bcast:15
+  k = dpp_max64<0x143>(k);  // row_bcast:31
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Top-k of each token and the per-chunk expert histogram. A workgroup owns a chunk of
 // kRouteChunk tokens; each wave takes kRouteChunk/4 of them, loads all their logits first
 // (lane e holds experts e, e+64, ...), then picks the k best one at a time: a per-lane
-// best over the lane's untaken experts, the wave argmax, and the winner marked taken.
+// best key over the lane's untaken experts, the wave maximum, and the winner's key cleared.
 template <int NJ>  // experts per lane: E <= 64 * NJ
 __global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict__ logits,
                                                         int64_t T, int E, int k,
@@ -111,24 +114,25 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict_
   for (int u = 0; u < TPW; ++u) {
     const int64_t t = (int64_t)blockIdx.x * kRouteChunk + wv * TPW + u;
     if (t >= T) break;  // wave-uniform
-    uint32_t taken = 0;
+    // keys of this lane's experts; a taken expert's key becomes 0
+    uint64_t key[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      key[j] = e < E ? topk_key(v[u][j], e) : 0;
+    }
     float my_v = -INFINITY, top_v = 0.f;
     int my_i = 0;
     for (int s = 0; s < k; ++s) {
-      float lv = -INFINITY;
-      int li = 0x7FFFFFFF;
+      uint64_t best = key[0];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int e = lane + 64 * j;
-        if (e < E && !((taken >> j) & 1u) && better(v[u][j], e, lv, li)) {
-          lv = v[u][j];
-          li = e;
-        }
-      }
-      float bv;
-      int bi;
-      wave_argmax(lv, li, bv, bi);
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      for (int j = 1; j < NJ; ++j) best = key[j] > best ? key[j] : best;
+      const uint64_t w = wave_max_key(best);
+      const int bi = key_index(w);
+      const float bv = key_value(w);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        if (bi == lane + 64 * j) key[j] = 0;
       if (lane == s) {
         my_v = bv;
         my_i = bi;
