@@ -71,12 +71,18 @@ __device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Max over the 16 lanes that share (lane / 16).
+// Max over the 16 lanes that share (lane / 16), in every one of them: four DPP row
+// rotations (by 1, 2, 4, 8 lanes within the 16-lane row), VALU only.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
+                                                    0xF, 0xF, false));
+}
 __device__ __forceinline__ float max16(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
+  v = fmaxf(v, dpp_row<0x121>(v));  // row_ror:1
+  v = fmaxf(v, dpp_row<0x122>(v));  // row_ror:2
+  v = fmaxf(v, dpp_row<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp_row<0x128>(v));  // row_ror:8
   return v;
 }
 

@@ -7,9 +7,10 @@
 // cast launch above 64k elements, chosen by shape only).
 // Scale rule amax/448: memra-engine fp8_ffi module docs.
 //
-// Both modes are HBM-bound streaming kernels: each thread reads 16 bytes (8 bf16) and
-// writes 8 bytes; a 128-group is the 16 consecutive lanes of a quarter wave, so its amax
-// is a 4-step cross-lane reduction with no LDS and no host synchronisation.
+// Both modes are HBM-bound streaming kernels: each thread reads 16-byte chunks (8 bf16),
+// four of them in flight at once, and writes 8 bytes per chunk; a 128-group is the 16
+// consecutive lanes of a quarter wave, so its amax is a 4-step cross-lane reduction with
+// no LDS and no host synchronisation.
 #include "common.h"
 #include "launch.h"
 
@@ -43,21 +44,34 @@ __device__ __forceinline__ uint2 encode8(const F8& f, float inv) {
   return r;
 }
 
-// One thread per 8 consecutive elements; 16 threads per 128-group.
+// Chunks of 8 consecutive elements per thread: kChunks of them, a whole grid apart, all
+// loaded before any is processed (more loads in flight per thread hide the HBM latency);
+// the 16 consecutive lanes of a quarter wave hold one 128-group.
+constexpr int kChunks = 4;
 __global__ __launch_bounds__(256) void quant_group_kernel(const uint4* __restrict__ x,
-                                                          int64_t nthreads,
+                                                          int64_t nchunks,
                                                           uint2* __restrict__ q,
                                                           float* __restrict__ scales) {
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  bool valid = i < nthreads;  // nthreads is a multiple of 16: groups are all-or-nothing
-  uint4 u = valid ? x[i] : make_uint4(0, 0, 0, 0);
-  F8 f = unpack8(u);
-  float m = max16(amax8(f));
-  float s, inv;
-  scale_pair(m, s, inv);
-  if (valid) {
-    q[i] = encode8(f, inv);
-    if ((threadIdx.x & 15) == 0) scales[i >> 4] = s;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint4 u[kChunks];
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const int64_t i = i0 + j * stride;
+    // nchunks and stride are multiples of 16: groups are all-or-nothing
+    u[j] = i < nchunks ? x[i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const int64_t i = i0 + j * stride;
+    const F8 f = unpack8(u[j]);
+    const float m = max16(amax8(f));
+    float s, inv;
+    scale_pair(m, s, inv);
+    if (i < nchunks) {
+      q[i] = encode8(f, inv);
+      if ((threadIdx.x & 15) == 0) scales[i >> 4] = s;
+    }
   }
 }
 
@@ -96,9 +110,15 @@ __global__ __launch_bounds__(256) void quant_tensor_amax_kernel(const uint4* __r
                                                                float* __restrict__ partials) {
   __shared__ float red[4];
   float m = 0.f;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks;
-       i += (int64_t)gridDim.x * 256)
-    m = fmaxf(m, amax8(unpack8(x[i])));
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks; i += kChunks * stride) {
+    uint4 u[kChunks];
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j)
+      u[j] = i + j * stride < nchunks ? x[i + j * stride] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) m = fmaxf(m, amax8(unpack8(u[j])));
+  }
   float r = block_max(m, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = r;
 }
@@ -118,19 +138,26 @@ __global__ __launch_bounds__(256) void quant_tensor_cast_kernel(const uint4* __r
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     block[0] = amax; block[1] = inv; block[2] = s; block[3] = 0.f;
   }
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks;
-       i += (int64_t)gridDim.x * 256)
-    q[i] = encode8(unpack8(x[i]), inv);
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunks; i += kChunks * stride) {
+    uint4 u[kChunks];
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j)
+      u[j] = i + j * stride < nchunks ? x[i + j * stride] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j)
+      if (i + j * stride < nchunks) q[i + j * stride] = encode8(unpack8(u[j]), inv);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_quant_group(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
                               float* scales, hipStream_t st) {
-  int64_t nthreads = M * K / 8;
-  int64_t blocks = (nthreads + 255) / 256;
+  const int64_t nchunks = M * K / 8;
+  const int64_t blocks = (nchunks + 256 * kChunks - 1) / (256 * kChunks);
   quant_group_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, st>>>(
-      reinterpret_cast<const uint4*>(x), nthreads, reinterpret_cast<uint2*>(q), scales);
+      reinterpret_cast<const uint4*>(x), nchunks, reinterpret_cast<uint2*>(q), scales);
   return hipGetLastError();
 }
 
@@ -148,7 +175,7 @@ hipError_t launch_quant_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* 
   quant_tensor_amax_kernel<<<npart, 256, 0, st>>>(xv, nchunks, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int64_t cast_blocks = (nchunks + 255) / 256;
+  int64_t cast_blocks = (nchunks + 256 * kChunks - 1) / (256 * kChunks);
   if (cast_blocks > 8192) cast_blocks = 8192;
   quant_tensor_cast_kernel<<<(uint32_t)cast_blocks, 256, 0, st>>>(xv, nchunks, partials, npart,
                                                                   qv, block);
