@@ -111,6 +111,46 @@ def stack_flops(c):
     return c.L * fp8, c.L * bf16 + head
 
 
+# FreeToken PR #389, "Why": per-rank decode projections (N x K) at M = 1, 8, 16
+DECODE_SHAPES = [(6656, 2560), (2560, 3072), (8192, 2560)]
+ROT_DECODE = 16
+
+
+def bench_decode(steps: int = 20):
+    """W8A8 at decode sizes: the weight-streaming path, HBM-bound. Sixteen copies of the
+    weight (272-336 MB, more than the 256 MB Infinity Cache) are rotated so every launch
+    streams its weight from HBM; achieved GB/s counts weights + activations + output once."""
+    import torch
+
+    import fp8_moe_prefill_amd as f
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(0)
+    res = {}
+    for (N, K) in DECODE_SHAPES:
+        w = (torch.randn((N, K), generator=g) * 0.02).to(torch.bfloat16).to(dev)
+        wq, sw = f.quantize_weight(w)
+        ws = [(wq.clone(), sw.clone()) for _ in range(ROT_DECODE)]
+        for M in (1, 8, 16):
+            x = torch.randn((M, K), generator=g).to(torch.bfloat16).to(dev)
+            xq, blk = f.fp8_quant_act(x, 0)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            for i in range(3):
+                f.fp8_dense_gemm(xq, blk, ws[i % ROT_DECODE][0], ws[i % ROT_DECODE][1], out=y)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for i in range(steps):
+                f.fp8_dense_gemm(xq, blk, ws[i % ROT_DECODE][0], ws[i % ROT_DECODE][1], out=y)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / steps * 1e3
+            nbytes = N * K + M * K + 2 * M * N
+            res[f"M{M}_N{N}_K{K}"] = {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+                                      "frac_hbm": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    return res
+
+
 def bench_stack(L: int, warmup: int, steps: int):
     """The depth stack forward (T=2048): prefill tokens/s, per-layer and LM-head times."""
     import numpy as np
@@ -269,6 +309,7 @@ def main():
             res[wn] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12}
         out["dense_w8a8"] = res
 
+    out["decode_w8a8"] = bench_decode()
     if args.stack:
         out["stack"] = bench_stack(args.stack, args.warmup, min(args.steps, 20))
 

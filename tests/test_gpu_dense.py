@@ -70,3 +70,22 @@ def test_full_size_sampled(which):
     cols = rng.integers(0, y.shape[1], 3000)
     ref, b = dense_w8a8_entries(rq, rblk[2], wq, sw[0], rows, cols)
     check_close(y[rows, cols].astype(np.float64), ref, gemm_bound(b), f"dense {which}")
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+@pytest.mark.parametrize("N,K", [(6656, 2560), (2560, 3072), (8192, 2560)])
+def test_decode_shapes(M, N, K):
+    """The decode shapes of FreeToken PR #389, "Why" (per-rank projections at M = 1, 8, 16):
+    the small-M weight-streaming path, every output within the bound, bf16 = RNE(fp32)."""
+    rng = np.random.default_rng(M * 7 + N + K)
+    x = bf16_bits_from_f32(rng.standard_normal((M, K)).astype(np.float32))
+    w = bf16_bits_from_f32((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    y, xq, blk, wq, sw = _gpu(x, w)
+    rq, rblk = quant_tensor_bf16(x)
+    rwq, rsw = quantize_weight(w)
+    assert_bytes_equal(xq, rq, "activation codes")
+    assert_bytes_equal(wq, rwq, "weight codes")
+    ref, b = dense_w8a8(rq, rblk[2], rwq, rsw, with_bound=True)
+    check_close(y, ref, gemm_bound(b), f"decode M={M} N={N} K={K}")
+    yb = _gpu(x, w, torch.bfloat16)[0]
+    assert_bytes_equal(yb, bf16_bits(round_bf16(y.astype(np.float64))), "bf16 = RNE(fp32)")
