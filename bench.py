@@ -309,6 +309,24 @@ def main():
             res[wn] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12}
         out["dense_w8a8"] = res
 
+    # decode regime of the same layer: 16 tokens (128 routed rows, one or two per expert)
+    # against the same three rotated banks; the whole bank is read once per layer
+    Td = 16
+    rd = f.MoELayerRunner(Td, c.H, c.E, c.k, c.I, dev)
+    for i in range(3):
+        rd.run(xs[i % ROT][:Td], lgs[i % ROT][:Td], banks[i % ROT])
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(30):
+        rd.run(xs[i % ROT][:Td], lgs[i % ROT][:Td], banks[i % ROT])
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / 30 * 1e3
+    bank_bytes = 3 * c.E * c.H * c.I // 2 + 3 * c.E * c.H * c.I * 4 // 128
+    out["decode_moe"] = {"tokens": Td, "us_per_layer": us,
+                         "bank_GBps": bank_bytes / (us * 1e-6) / 1e9,
+                         "frac_hbm": bank_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
     out["decode_w8a8"] = bench_decode()
     if args.stack:
         out["stack"] = bench_stack(args.stack, args.warmup, min(args.steps, 20))

@@ -32,8 +32,11 @@ def _gpu_layer(cfg, T=None):
     return c, inp, out, st
 
 
-def test_tiny_layer_all_outputs():
-    c, inp, out, st = _gpu_layer("moe_tiny")
+@pytest.mark.parametrize("cfg,T", [("moe_tiny", None), ("moe_prefill", 1), ("moe_prefill", 16)])
+def test_layer_all_outputs(cfg, T):
+    """The tiny layer, and the config-3 layer at decode token counts (one or two rows per
+    expert: the grouped GEMM's few-rows regime)."""
+    c, inp, out, st = _gpu_layer(cfg, T=T)
     ref = moe_layer(inp["x"], inp["logits"], inp["w_gu"], inp["s_gu"], inp["w_dn"],
                     inp["s_dn"], c.k)
     assert_bytes_equal(host(st["xq"]), ref["xq"], "xq")
