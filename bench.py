@@ -51,6 +51,8 @@ def _parse():
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--stack", type=int, default=8, choices=[0, 8, 12],
                     help="also time the depth stack of this many layers (0: skip)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-regime timings (16-token layer, M <= 16 projections)")
     ap.add_argument("--stack-only", action="store_true",
                     help="time only the depth stack (for profiling it alone)")
     return ap.parse_args()
@@ -309,17 +311,34 @@ def main():
             res[wn] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12}
         out["dense_w8a8"] = res
 
-    # decode regime of the same layer: 16 tokens (128 routed rows, one or two per expert)
-    # against the same three rotated banks; the whole bank is read once per layer
+    if not args.no_decode:
+        out.update(bench_decode_regime(c, xs, lgs, banks, dev))
+    if args.stack:
+        out["stack"] = bench_stack(args.stack, args.warmup, min(args.steps, 20))
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+    print(json.dumps(out))
+
+
+def bench_decode_regime(c, xs, lgs, banks, dev) -> dict:
+    """Decode regime of the same layer: 16 tokens (128 routed rows, one or two per expert)
+    against the same rotated banks, the whole bank read once per layer; plus the M <= 16
+    W8A8 projections."""
+    import torch
+
+    import fp8_moe_prefill_amd as f
+
+    out = {}
     Td = 16
     rd = f.MoELayerRunner(Td, c.H, c.E, c.k, c.I, dev)
     for i in range(3):
-        rd.run(xs[i % ROT][:Td], lgs[i % ROT][:Td], banks[i % ROT])
+        rd.run(xs[i % len(banks)][:Td], lgs[i % len(banks)][:Td], banks[i % len(banks)])
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     a.record()
     for i in range(30):
-        rd.run(xs[i % ROT][:Td], lgs[i % ROT][:Td], banks[i % ROT])
+        rd.run(xs[i % len(banks)][:Td], lgs[i % len(banks)][:Td], banks[i % len(banks)])
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) / 30 * 1e3
@@ -328,12 +347,7 @@ def main():
                          "bank_GBps": bank_bytes / (us * 1e-6) / 1e9,
                          "frac_hbm": bank_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
     out["decode_w8a8"] = bench_decode()
-    if args.stack:
-        out["stack"] = bench_stack(args.stack, args.warmup, min(args.steps, 20))
-
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
-    print(json.dumps(out))
+    return out
 
 
 if __name__ == "__main__":
