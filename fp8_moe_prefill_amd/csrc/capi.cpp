@@ -141,6 +141,8 @@ int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales, const i
   if (sorted && k_route < 1) return FP8MOE_ERR_SHAPE;
   if (R * K >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;  // 32-bit A row offsets
   if (N * (K / 2) >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;  // 32-bit offsets in one expert
+  // 32-bit tile indexing: (128-row tiles, one more per expert) x (256-column tiles)
+  if (((R + 127) / 128 + E) * ((N + 255) / 256) >= (int64_t(1) << 28)) return FP8MOE_ERR_SHAPE;
   const void* ptrs[] = {a, a_scales, w, w_scales, offsets, out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FP8MOE_ERR_ALIGN;

@@ -175,6 +175,8 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   __shared__ Stage ring[2];
   __shared__ int s_mstart[kMaxExperts + 1];  // m-tiles before expert e
   __shared__ int s_tmp[NW];
+  __shared__ int s_part[kMaxExperts];  // experts with a small (front) or tiny (back) last m-tile
+  __shared__ int s_npart;              // tiny count << 11 | small count
   __shared__ int s_src[NW][RPW];  // pair ids of the rows each wave stages for the next tile
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -185,57 +187,90 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   const int NB = N / 16;  // 16-column blocks of the bank
   const int kshift = (k_route & (k_route - 1)) == 0 ? __builtin_ctz(k_route) : -1;
 
-  // ---- m-tiles per expert, prefix-summed (4 experts per thread, E <= 1024)
+  // ---- m-tiles per expert. An expert's rows split into 128-row m-tiles. Its last m-tile
+  // is "small" when it has at most 64 rows (it runs 4 of the 8 row tiles) and "tiny" with
+  // at most 16 (1 row tile); the others are "whole". s_mstart[e] = whole m-tiles before
+  // expert e; s_part lists the experts with a small last m-tile from the front (entry i =
+  // the i-th such expert) and those with a tiny one from the back (entry 1023 - i), at
+  // most one per expert, so 1024 entries hold both. 4 experts per thread, E <= 1024.
   {
     constexpr int EPT = kMaxExperts / NT_THREADS;
-    int loc[EPT], sum = 0;
+    int nwh[EPT], cls[EPT], sum_w = 0, sum_p = 0;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const int e = tid * EPT + j;
       const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-      loc[j] = c > 0 ? (c + BM - 1) / BM : 0;
-      sum += loc[j];
+      const int rem = c % BM;
+      cls[j] = rem == 0 ? 0 : rem <= 16 ? 2048 : rem <= BM / 2 ? 1 : 0;  // tiny << 11 | small
+      nwh[j] = c / BM + (rem > BM / 2 ? 1 : 0);
+      sum_w += nwh[j];
+      sum_p += cls[j];
     }
-    int run = block_inclusive_scan(sum, s_tmp) - sum;
+    int run_w = block_inclusive_scan(sum_w, s_tmp) - sum_w;
+    int run_p = block_inclusive_scan(sum_p, s_tmp) - sum_p;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const int e = tid * EPT + j;
-      run += loc[j];
-      if (e < E) s_mstart[e + 1] = run;
+      if (e < E && cls[j] == 1) s_part[run_p & 2047] = e;
+      if (e < E && cls[j] == 2048) s_part[kMaxExperts - 1 - (run_p >> 11)] = e;
+      run_w += nwh[j];
+      run_p += cls[j];
+      if (e < E) s_mstart[e + 1] = run_w;
+      if (e == E - 1) s_npart = run_p;
     }
     if (tid == 0) s_mstart[0] = 0;
     __syncthreads();
   }
 
-  // ---- this workgroup's tiles. Logical tile L = m-tile * NT + n-tile; XCD x (workgroups
-  // x, x + nx, ...) owns the contiguous range [b_x, e_x) and its workgroups take every
-  // nwg_x-th tile of it.
-  const int64_t ntiles = (int64_t)__builtin_amdgcn_readfirstlane(s_mstart[E]) * NT;
+  // ---- this workgroup's work units. Tiles are (m-tile, n-tile) pairs, n-tile fastest.
+  // Whole, small and tiny tiles are dealt separately so that every XCD gets an even share
+  // of each: XCD x (workgroups x, x + nx, ...) owns a contiguous range of each class,
+  // lists them whole first, then small, then tiny, and its workgroups take every
+  // nwg_x-th entry of that list. (The launcher keeps the tile count below 2^28, so 32-bit
+  // tile indices do not overflow.)
+  const int npart = __builtin_amdgcn_readfirstlane(s_npart);
+  const int n_whole = __builtin_amdgcn_readfirstlane(s_mstart[E]) * NT;
+  const int n_small = (npart & 2047) * NT, n_tiny = (npart >> 11) * NT;
   const int nx = min(8, (int)gridDim.x);
   const int x = (int)blockIdx.x % nx, u = (int)blockIdx.x / nx;
   const int nwg_x = ((int)gridDim.x - x + nx - 1) / nx;
-  const int64_t b_x = ntiles * x / nx, e_x = ntiles * (x + 1) / nx;
-  const int64_t first = b_x + u;
-  const int my_tiles = first < e_x ? (int)((e_x - 1 - first) / nwg_x + 1) : 0;
-  if (my_tiles == 0) return;  // uniform
-  const int total_steps = my_tiles * G;
+  const int wb_x = n_whole * x / nx, nw_x = n_whole * (x + 1) / nx - wb_x;
+  const int sb_x = n_small * x / nx, ns_x = n_small * (x + 1) / nx - sb_x;
+  const int tb_x = n_tiny * x / nx, nt_x = n_tiny * (x + 1) / nx - tb_x;
 
-  auto tile_of = [&](int j) {
-    const int64_t L = first + (int64_t)j * nwg_x;
-    const int mt = (int)(L / NT);
+  auto tile_of = [&](int j) {  // j-th unit of this workgroup: entry u + j * nwg_x
+    const int l = u + j * nwg_x;
     TileDesc d;
-    d.nt = (int)(L - (int64_t)mt * NT);
-    int lo = 0, hi = E;  // s_mstart[lo] <= mt < s_mstart[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (__builtin_amdgcn_readfirstlane(s_mstart[mid]) <= mt) lo = mid;
-      else hi = mid;
+    if (l < nw_x) {
+      const int L = wb_x + l, mt = L / NT;
+      d.nt = L - mt * NT;
+      int lo = 0, hi = E;  // s_mstart[lo] <= mt < s_mstart[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (__builtin_amdgcn_readfirstlane(s_mstart[mid]) <= mt) lo = mid;
+        else hi = mid;
+      }
+      d.e = lo;
+      d.row_begin =
+          sload(offsets + lo) + (mt - __builtin_amdgcn_readfirstlane(s_mstart[lo])) * BM;
+    } else {
+      const bool small = l < nw_x + ns_x;
+      const int L = small ? sb_x + (l - nw_x) : tb_x + (l - nw_x - ns_x), i = L / NT;
+      d.nt = L - i * NT;
+      d.e = __builtin_amdgcn_readfirstlane(s_part[small ? i : kMaxExperts - 1 - i]);
+      d.row_begin = sload(offsets + d.e) +
+                    (__builtin_amdgcn_readfirstlane(s_mstart[d.e + 1]) -
+                     __builtin_amdgcn_readfirstlane(s_mstart[d.e])) * BM;
     }
-    d.e = lo;
-    d.row_begin = sload(offsets + lo) + (mt - __builtin_amdgcn_readfirstlane(s_mstart[lo])) * BM;
-    d.rows = min(BM, sload(offsets + lo + 1) - d.row_begin);
+    d.rows = min(BM, sload(offsets + d.e + 1) - d.row_begin);
     return d;
   };
+  // units [0, j_small) are whole, [j_small, j_tiny) small, [j_tiny, my_tiles) tiny
+  auto units_below = [&](int n) { return n > u ? (n - u + nwg_x - 1) / nwg_x : 0; };
+  const int j_small = units_below(nw_x), j_tiny = units_below(nw_x + ns_x);
+  const int my_tiles = units_below(nw_x + ns_x + nt_x);
+  if (my_tiles == 0) return;  // uniform
+  const int total_steps = my_tiles * G;
 
   // Columns. In the prepacked bank, block b of 16 columns holds bank columns
   // 64*(b/4) + 4*i + b%4 (i = 0..15), so MFMA tile s of a wave reading block 4k + s gives
@@ -353,9 +388,9 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   // MFMA of step i-2 (already complete), so the matrix core and the VALU work side by
   // side; a sched_barrier after every step pins that interleaving. The first group of a
   // tile initialises the accumulators (no separate zeroing).
-  auto group = [&](auto first_tag, const Stage& cur) {
+  auto group = [&](auto first_tag, auto tmax_tag, const Stage& cur) {
     constexpr bool FIRST = decltype(first_tag)::value;
-    constexpr int tmax = BM / 16;
+    constexpr int tmax = decltype(tmax_tag)::value;
     const uint8_t* ta = cur.a;
     const uint8_t* tb = cur.b + wv * BW_BYTES;
     const float* ra = cur.ra;
@@ -437,13 +472,17 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
       // each lane holds 4 consecutive output columns (tiles s = 0..3) of rows t*16 + 4q + r:
       // 16 lanes cover 64 consecutive columns of a row, so every store instruction writes
       // whole 128 B (bf16) or 256 B (fp32) row segments, straight from registers
+      // (q4 is opaque to the compiler, so the row indices below are formed here and not
+      // hoisted out of the tile loops, where they would stay live across the main loop)
+      int q4 = 4 * q;
+      asm volatile("" : "+v"(q4));
       const int col0 = nt * WCOLS_WG + wv * WCOLS + 4 * c16;
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
         if (t8 >= tmax) break;  // uniform
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = t8 * 16 + 4 * q + r;
+          const int row = t8 * 16 + q4 + r;
           if (row < rows && col0 < N) {
             const int64_t o = (int64_t)(row_begin + row) * N + col0;
             if (OUT_BF16)
@@ -533,21 +572,25 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   // compute. Tiles are consecutive runs of G groups; the first group of a tile initialises
   // the accumulators, the epilogue follows its last group.
   int s = 0;
-  auto step = [&](auto first_tag) {
+  auto step = [&](auto first_tag, auto tmax_tag) {
     const int stage = s & 1;
     const bool more = s + 1 < total_steps;
     if (more) dma_group(s + 1, ring[stage ^ 1]);
-    group(first_tag, ring[stage]);
+    group(first_tag, tmax_tag, ring[stage]);
     wait_all_loads();  // own loads of group s+1 landed
     if (more) row_sums(ring[stage ^ 1]);
     lds_barrier();
     ++s;
   };
-  for (int j = 0; j < my_tiles; ++j) {
-    step(std::true_type{});
-    for (int g = 1; g < G; ++g) step(std::false_type{});
-    epilogue(tile_of(j), ring[(s + 1) & 1]);
-  }
+  auto unit = [&](int j, auto tmax_tag) {
+    const TileDesc cur = tile_of(j);  // before the accumulators are live
+    step(std::true_type{}, tmax_tag);
+    for (int g = 1; g < G; ++g) step(std::false_type{}, tmax_tag);
+    epilogue(cur, ring[(s + 1) & 1]);
+  };
+  for (int j = 0; j < j_small; ++j) unit(j, std::integral_constant<int, 8>{});
+  for (int j = j_small; j < j_tiny; ++j) unit(j, std::integral_constant<int, 4>{});
+  for (int j = j_tiny; j < my_tiles; ++j) unit(j, std::integral_constant<int, 1>{});
 }
 
 int cu_count() {
@@ -576,6 +619,7 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const in
   // SwiGLU: a tile covers 128 h columns (gate and up); otherwise 256 output columns
   const int NT = epilogue == FP8MOE_EPI_SWIGLU_QUANT ? (int)((N / 2 + 127) / 128)
                                                      : (int)((N + WCOLS_WG - 1) / WCOLS_WG);
+  if (mtiles * NT >= (int64_t(1) << 28)) return hipErrorInvalidValue;  // 32-bit tile indexing
   const int64_t grid = std::min<int64_t>(2 * (int64_t)cu_count(), mtiles * NT);
   const int a_rows = (int)(sorted ? R / k_route : R);
   dim3 g((uint32_t)grid), block(NT_THREADS);

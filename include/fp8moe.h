@@ -210,8 +210,8 @@ int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t
  *              (group 128) into out = e4m3 [R, I] and out_scales = fp32 [I/128, R],
  *              group-major like a_scales (ready to be the next GEMM's a_scales)
  * Constraints: R >= 0 (R = 0 is a no-op), 1 <= E <= 1024, K % 128 == 0,
- * 128 <= K <= 16384, R*K < 2^32, N*K/2 < 2^32; STORE: N % 64 == 0; SWIGLU_QUANT:
- * N % 256 == 0.
+ * 128 <= K <= 16384, R*K < 2^32, N*K/2 < 2^32, (ceil(R/128) + E) * ceil(N/256) < 2^28;
+ * STORE: N % 64 == 0; SWIGLU_QUANT: N % 256 == 0.
  */
 int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales,
                                 const int32_t* sorted, int32_t k_route, const uint8_t* w,
