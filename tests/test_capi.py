@@ -136,6 +136,8 @@ def test_grouped_gemm_validation(lib):
     assert _gg(lib, out=U) == ALIGN
     assert _gg(lib, R=0) == OK  # empty input is a no-op; nothing is launched
     assert _gg(lib, R=64, N=1 << 20, K=16384) == SHAPE  # N*K/2 >= 2^32
+    # (ceil(R/128) + E) * ceil(N/256) >= 2^28: tile indices would not fit 32 bits
+    assert _gg(lib, R=(1 << 25) - 128, N=(1 << 24) - 256, K=128) == SHAPE
 
 
 def _pack(lib, w=P, s=P, E=4, N=64, K=256, wp=P, sp=P):
