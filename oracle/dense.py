@@ -9,6 +9,11 @@ the accumulator. So
     y[m, n] = (s_a * s_w) * sum_k dec(qa[m, k]) * dec(qw[n, k])
 
 with both operands K-contiguous (a "TN" GEMM), computed here in float64.
+
+Row-wise variant (FreeToken PR #389, "Limits": row-wise activation scales, measured there
+against the per-tensor route): the activation carries one scale per row, so
+
+    y[m, n] = (s_a[m] * s_w) * sum_k dec(qa[m, k]) * dec(qw[n, k]).
 """
 
 from __future__ import annotations
@@ -40,6 +45,28 @@ def dense_w8a8_entries(a_codes, a_scale, w_codes, w_scale, rows, cols):
     b = np.empty(len(rows))
     for m, (i, n) in enumerate(zip(rows, cols)):
         a = e4m3_decode(a_codes[i]) * float(a_scale)
+        w = e4m3_decode(w_codes[n]) * float(w_scale)
+        y[m] = float(a @ w)
+        b[m] = float(np.abs(a) @ np.abs(w))
+    return y, b
+
+
+def dense_w8a8_rowwise(a_codes, a_scales, w_codes, w_scale, with_bound=False):
+    """Row-wise variant: a_scales is fp32 [M], one activation scale per row."""
+    a = e4m3_decode(a_codes) * np.asarray(a_scales, dtype=np.float64)[:, None]
+    w = e4m3_decode(w_codes) * float(w_scale)
+    y = a @ w.T
+    if with_bound:
+        return y, np.abs(a) @ np.abs(w).T
+    return y
+
+
+def dense_w8a8_rowwise_entries(a_codes, a_scales, w_codes, w_scale, rows, cols):
+    """Selected outputs of the row-wise variant and their bounds, one at a time."""
+    y = np.empty(len(rows))
+    b = np.empty(len(rows))
+    for m, (i, n) in enumerate(zip(rows, cols)):
+        a = e4m3_decode(a_codes[i]) * float(a_scales[i])
         w = e4m3_decode(w_codes[n]) * float(w_scale)
         y[m] = float(a @ w)
         b[m] = float(np.abs(a) @ np.abs(w))

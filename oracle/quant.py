@@ -1,6 +1,6 @@
 """Dynamic activation quantisation to e4m3 -- oracle side (test infrastructure).
 
-Two granularities:
+Three granularities:
 
 * per (token, 128-wide K group): the FP8 grouped-expert prefill note, section 1 ("a
   per-(token, group) activation scale folded into the accumulator path"); this feeds the
@@ -8,7 +8,11 @@ Two granularities:
 * per tensor: FreeToken PR #389, "What this adds" (a dynamic per-tensor activation
   scale: an amax pass, then the cast), and the memra-engine ``fp8_ffi`` docs (module
   text: one scalar scale amax/448); this feeds the dense W8A8 projections and is also the
-  load-time weight quantiser ("e4m3 with one fp32 scale each").
+  load-time weight quantiser ("e4m3 with one fp32 scale each");
+* per row (token): FreeToken PR #389, "Limits", measures row-wise activation scales as
+  the alternative to the per-tensor one (one outlier channel in one row then sets the
+  scale of that row only). The pages print no row-wise formula; reading: the per-tensor
+  rule below applied to each row on its own.
 
 Arithmetic, all in fp32 as the scale block of ``fp8_ffi``'s ``Fp8Scratch`` is fp32:
   amax  = max |x| over the group (exact; NaN elements are skipped)
@@ -63,6 +67,20 @@ def quant_tensor(x: np.ndarray):
     _, s, inv = _scale_pair(amax)
     q = e4m3_encode((x * inv).astype(np.float32))
     return q, np.array([amax, inv, s, 0.0], dtype=np.float32)
+
+
+def quant_row(x: np.ndarray):
+    """fp32 activations [M, K] -> (e4m3 codes [M, K], fp32 scales [M]): one scale per row
+    (FreeToken PR #389, "Limits": row-wise scales), each row quantised by the per-tensor
+    rule."""
+    x = np.asarray(x, dtype=np.float32)
+    _, s, inv = _scale_pair(_amax(x, axis=1))
+    q = e4m3_encode((x * inv[:, None]).astype(np.float32))
+    return q, s
+
+
+def quant_row_bf16(x_bits: np.ndarray):
+    return quant_row(bf16_to_f32(x_bits))
 
 
 def quant_group_bf16(x_bits: np.ndarray, group: int = GROUP):

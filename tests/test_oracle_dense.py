@@ -5,15 +5,19 @@
 * numpy matmul on operands dequantised independently (torch's e4m3 decode) at
   M = 1, 16, 300 -- the shapes of FreeToken PR #389's "Testing" section;
 * the per-tensor weight quantiser keeps the weight within e4m3 tolerance (the PR's
-  "loader round trip within e4m3 tolerance").
+  "loader round trip within e4m3 tolerance");
+* row-wise variant: numpy matmul with each row's scale; equal row scales give the
+  per-tensor projection; scaling one row's scale scales that output row only; brute force
+  (Python float loops) on a tiny case.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from oracle.dense import dense_w8a8, dense_w8a8_entries, quantize_weight
-from oracle.quant import quant_tensor_bf16
+from oracle.dense import (dense_w8a8, dense_w8a8_entries, dense_w8a8_rowwise,
+                          dense_w8a8_rowwise_entries, quantize_weight)
+from oracle.quant import quant_row_bf16, quant_tensor_bf16
 from synth import CONFIGS, bf16_bits_from_f32, dense_inputs, f32_from_bf16_bits
 
 DEC = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(
@@ -59,3 +63,48 @@ def test_weight_round_trip_within_e4m3_tolerance():
     sub = np.abs(wf) < 2.0 ** -6 * float(sw)
     tol = np.where(sub, 2.0 ** -10 * float(sw), 2.0 ** -4 * np.abs(wf)) * (1 + 1e-6)
     assert np.all(np.abs(deq - wf) <= tol + 1e-30)
+
+
+@pytest.mark.parametrize("M", [1, 16, 300])
+def test_rowwise_vs_matmul_and_per_tensor(M):
+    c = CONFIGS["dense_w8a8"]
+    inp = dense_inputs(c, M=M)
+    w = inp["w_qkv"][:64, :512]
+    x = inp["x"][:, :512]
+    wq, sw = quantize_weight(w)
+    qa, sa = quant_row_bf16(x)
+    y, b = dense_w8a8_rowwise(qa, sa, wq, sw, with_bound=True)
+    ref = np.matmul(DEC[qa] * sa.astype(np.float64)[:, None], (DEC[wq] * float(sw)).T)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+    rows = np.arange(M) % M
+    cols = np.arange(M) % 64
+    ye, be = dense_w8a8_rowwise_entries(qa, sa, wq, sw, rows, cols)
+    assert np.allclose(ye, ref[rows, cols], rtol=1e-12, atol=1e-12)
+    assert np.all(b >= np.abs(y) - 1e-12)
+    # equal row scales: the per-tensor projection
+    s0 = np.float32(0.0123)
+    assert np.array_equal(dense_w8a8_rowwise(qa, np.full(M, s0, np.float32), wq, sw),
+                          dense_w8a8(qa, s0, wq, sw))
+    # one row's scale doubled: that output row doubles, the others stay
+    s2 = sa.copy()
+    s2[M // 2] *= 2
+    y2 = dense_w8a8_rowwise(qa, s2, wq, sw)
+    assert np.array_equal(y2[M // 2], 2 * y[M // 2])
+    assert np.array_equal(np.delete(y2, M // 2, 0), np.delete(y, M // 2, 0))
+
+
+def test_rowwise_brute_force():
+    rng = np.random.default_rng(5)
+    qa = rng.integers(0, 256, (3, 128)).astype(np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0  # no NaN codes
+    qw = rng.integers(0, 256, (5, 128)).astype(np.uint8)
+    qw[(qw & 0x7F) == 0x7F] = 0
+    sa = np.float32([0.5, 3.0, 1e-3])
+    sw = np.float32(0.25)
+    y = dense_w8a8_rowwise(qa, sa, qw, sw)
+    for m in range(3):
+        for n in range(5):
+            acc = 0.0
+            for k in range(128):
+                acc += float(DEC[qa[m, k]]) * float(DEC[qw[n, k]])
+            assert abs(y[m, n] - float(sa[m]) * float(sw) * acc) <= 1e-12 * max(1.0, abs(acc))

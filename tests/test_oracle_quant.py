@@ -6,14 +6,16 @@
 * closed-form error bound: |x - dec(q) * s| <= 2^-4 |x| in e4m3's normal range and
   <= 2^-10 s in the subnormal range (half a code spacing), up to fp32 scale rounding;
 * library cross-check: torch computes x * inv in fp32 and casts with its own e4m3 encoder;
-* per-tensor mode on a single group equals group mode; the scale block layout.
+* per-tensor mode on a single group equals group mode; the scale block layout;
+* row-wise mode: torch's fp32 multiply and e4m3 cast with each row's own amax; a single
+  row equals per-tensor mode; rows a power of two apart share codes, scales exactly.
 """
 
 import numpy as np
 import torch
 
 from oracle.codec import e4m3_decode
-from oracle.quant import AMAX_FLOOR, quant_group, quant_group_bf16, quant_tensor
+from oracle.quant import AMAX_FLOOR, quant_group, quant_group_bf16, quant_row, quant_tensor
 from synth import CONFIGS, bf16_bits_from_f32, f32_from_bf16_bits, moe_inputs
 
 
@@ -89,3 +91,31 @@ def test_nan_policy():
     x2[0, 3] = 0.0
     q2, s2 = quant_group(x2)
     assert s[0, 0] == s2[0, 0]  # NaN does not take part in amax
+
+
+def test_row_wise_matches_torch_per_row_rule():
+    # FreeToken PR #389 "Limits": row-wise scales; torch's own fp32 multiply and e4m3 cast
+    # of every row with that row's amax
+    x = _x(7, (37, 384))
+    x[3, 5] = 300.0  # an outlier channel sets the scale of its own row only
+    x[11] = 0.0      # an all-zero row takes the floor
+    q, s = quant_row(x)
+    xt = torch.from_numpy(x.copy())
+    amax = xt.abs().amax(dim=1, keepdim=True).clamp_min(1e-12)
+    inv = torch.tensor(448.0, dtype=torch.float32) / amax
+    ref = torch.clamp(xt * inv, -448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(q, ref.numpy())
+    assert np.array_equal(s, (amax / 448.0).reshape(-1).numpy())
+    assert s[3] == np.float32(300.0) / np.float32(448.0) and np.all(q[11] == 0)
+
+
+def test_row_wise_single_row_is_per_tensor_and_rows_scale_exactly():
+    x = _x(8, (1, 256))
+    qr, sr = quant_row(x)
+    qt, blk = quant_tensor(x)
+    assert np.array_equal(qr, qt) and sr[0] == blk[2]
+    # rows that differ by a power of two share their codes; their scales differ by it
+    rows = np.concatenate([x * np.float32(2.0 ** j) for j in (-3, 0, 5)])
+    q3, s3 = quant_row(rows)
+    assert all(np.array_equal(q3[i], qt[0]) for i in range(3))
+    assert np.array_equal(s3, blk[2] * np.float32([2.0 ** -3, 1.0, 2.0 ** 5]))
