@@ -309,6 +309,18 @@ def main():
             us = a.elapsed_time(b) / 20 * 1e3
             fl = 2.0 * x.shape[0] * w.shape[0] * x.shape[1]
             res[wn] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12}
+            # row-wise activation scales (one per token) on the same projection
+            xr, sr = f.fp8_quant_act(x, f.QUANT_ROW)
+            yr = f.fp8_dense_gemm_rowwise(xr, sr, wq, sw)
+            for _ in range(3):
+                f.fp8_dense_gemm_rowwise(xr, sr, wq, sw, out=yr)
+            a.record()
+            for _ in range(20):
+                f.fp8_dense_gemm_rowwise(xr, sr, wq, sw, out=yr)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / 20 * 1e3
+            res[wn + "_rowwise"] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12}
         out["dense_w8a8"] = res
 
     if not args.no_decode:

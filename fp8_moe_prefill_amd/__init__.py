@@ -3,12 +3,13 @@
 The computation lives in ``libfp8moe.so`` (hand-written HIP kernels behind a C ABI,
 declared in ``include/fp8moe.h``). This package is its thin binding plus the composition
 of the calls into an MoE layer, a W8A8 projection and the depth stack around them. Importing it fails if the library
-has not been built (``python -m fp8_moe_prefill_amd.build``).
+has not been built (``python fp8_moe_prefill_amd/build.py``).
 """
 
 from ._lib import (  # noqa: F401
-    DTYPE_BF16, DTYPE_F32, EPI_STORE, EPI_SWIGLU_QUANT, GROUP, Fp8MoeError, LIB_PATH,
-    abi_version, bf16_gemm, causal_attention, fp8_dense_gemm, fp8_grouped_expert_gemm,
+    DTYPE_BF16, DTYPE_F32, EPI_STORE, EPI_SWIGLU_QUANT, GROUP, QUANT_ROW, Fp8MoeError,
+    LIB_PATH, abi_version, bf16_gemm, causal_attention, fp8_dense_gemm, fp8_dense_gemm_rowwise,
+    fp8_grouped_expert_gemm,
     fp8_quant_act, moe_route_permute, moe_unpermute_combine, pack_expert_bank, rmsnorm,
     workspace_bytes,
 )

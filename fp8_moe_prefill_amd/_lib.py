@@ -17,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfp8moe.so")
 
 GROUP = 128
+QUANT_ROW = -1  # fp8_quant_act group: one scale per row
 DTYPE_F32, DTYPE_BF16 = 0, 1
 EPI_STORE, EPI_SWIGLU_QUANT = 0, 1
 OP_QUANT_ACT, OP_ROUTE_PERMUTE, OP_ATTENTION = 0, 1, 2
@@ -42,6 +43,8 @@ SIGNATURES = {
                                        _c_void_p, _c_void_p, _c_void_p]),
     "fp8_dense_gemm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i32,
                               _c_void_p, _c_void_p]),
+    "fp8_dense_gemm_rowwise": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64,
+                                      _i32, _c_void_p, _c_void_p]),
     "moe_unpermute_combine": (_i32, [_c_void_p, _i32, _c_void_p, _c_void_p, _i64, _i32, _i64,
                                      _i32, _c_void_p, _c_void_p]),
     "fp8moe_rmsnorm": (_i32, [_c_void_p, _c_void_p, _i64, _i64, ctypes.c_double, _c_void_p,
@@ -54,7 +57,7 @@ SIGNATURES = {
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
-        raise ImportError(f"{path} is missing: build it with `python -m fp8_moe_prefill_amd.build`")
+        raise ImportError(f"{path} is missing: build it with `python fp8_moe_prefill_amd/build.py`")
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
@@ -127,13 +130,14 @@ def abi_version() -> int:
 
 def fp8_quant_act(x: torch.Tensor, group: int = GROUP, q=None, scales=None, ws=None,
                   stream=None):
-    """bf16 [M, K] -> (e4m3 codes uint8 [M, K], fp32 scales [M, K/128] or block[4])."""
+    """bf16 [M, K] -> (e4m3 codes uint8 [M, K], fp32 scales: [M, K/128] for group=128,
+    block[4] for group=0, [M] for group=QUANT_ROW)."""
     _dev(x, "x", torch.bfloat16)
     M, K = x.shape
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if scales is None:
-        shape = (M, K // GROUP) if group == GROUP else (4,)
+        shape = (M, K // GROUP) if group == GROUP else (M,) if group == QUANT_ROW else (4,)
         scales = torch.empty(shape, dtype=torch.float32, device=x.device)
     nbytes = workspace_bytes(OP_QUANT_ACT, M, K, group)
     wsb = _workspace(nbytes, x.device, ws)
@@ -253,6 +257,26 @@ def fp8_dense_gemm(a, a_scale_blk, w, w_scale, out_dtype=torch.bfloat16, out=Non
     _check("fp8_dense_gemm", _lib.fp8_dense_gemm(_ptr(a), _ptr(a_scale_blk), _ptr(w),
                                                  _ptr(w_scale), M, N, K, _dt(out.dtype),
                                                  _ptr(out), _stream(stream)))
+    return out
+
+
+def fp8_dense_gemm_rowwise(a, a_scales, w, w_scale, out_dtype=torch.bfloat16, out=None,
+                           stream=None):
+    """e4m3 [M, K] x e4m3 [N, K]^T with one activation scale per row (a_scales fp32 [M])
+    and s_w = w_scale[0]."""
+    _dev(a, "a", torch.uint8)
+    _dev(w, "w", torch.uint8)
+    _dev(a_scales, "a_scales", torch.float32)
+    _dev(w_scale, "w_scale", torch.float32)
+    M, K = a.shape
+    N = w.shape[0]
+    if a_scales.numel() != M:
+        raise ValueError(f"a_scales has {a_scales.numel()} elements, expected {M}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check("fp8_dense_gemm_rowwise",
+           _lib.fp8_dense_gemm_rowwise(_ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scale), M, N, K,
+                                       _dt(out.dtype), _ptr(out), _stream(stream)))
     return out
 
 

@@ -1,7 +1,8 @@
 """Build the HIP library ``libfp8moe.so`` in-tree for gfx950 with hipcc.
 
-Usage: ``python -m fp8_moe_prefill_amd.build`` (or ``build()`` from Python). Every call
-recompiles; objects go to ``fp8_moe_prefill_amd/_build/`` and the library next to this file.
+Usage: ``python fp8_moe_prefill_amd/build.py`` (or ``build()`` of ``__graft_entry__``). Every
+call recompiles; objects go to ``fp8_moe_prefill_amd/_build/`` and the library next to this
+file. It imports nothing from the package, so it runs while the library is stale or absent.
 """
 
 from __future__ import annotations

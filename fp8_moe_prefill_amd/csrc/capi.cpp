@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 constexpr int64_t kMaxGroupedK = 16384;
@@ -49,7 +49,8 @@ const char* fp8moe_status_str(int32_t status) {
 
 size_t fp8moe_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c) {
   if (op == FP8MOE_OP_QUANT_ACT) {
-    if (a < 1 || b < 1 || (c != 0 && c != FP8MOE_GROUP)) return (size_t)-1;
+    if (a < 1 || b < 1 || (c != 0 && c != FP8MOE_GROUP && c != FP8MOE_QUANT_ROW))
+      return (size_t)-1;
     return quant_ws(a, b, (int32_t)c);
   }
   if (op == FP8MOE_OP_ROUTE_PERMUTE) {
@@ -67,9 +68,12 @@ size_t fp8moe_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c) {
 int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int32_t group, uint8_t* q,
                       float* scales, void* ws, size_t ws_bytes, void* stream) {
   if (!x || !q || !scales) return FP8MOE_ERR_NULL;
-  if (group != 0 && group != FP8MOE_GROUP) return FP8MOE_ERR_UNSUPPORTED;
+  if (group != 0 && group != FP8MOE_GROUP && group != FP8MOE_QUANT_ROW)
+    return FP8MOE_ERR_UNSUPPORTED;
   if (M < 1 || K < 1 || M > (int64_t(1) << 40) / K) return FP8MOE_ERR_SHAPE;
   if (group == FP8MOE_GROUP && K % FP8MOE_GROUP != 0) return FP8MOE_ERR_SHAPE;
+  if (group == FP8MOE_QUANT_ROW && (K % 8 != 0 || M >= (int64_t(1) << 31)))
+    return FP8MOE_ERR_SHAPE;
   if (group == 0 && (M * K) % 8 != 0) return FP8MOE_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(q) || !aligned16(scales)) return FP8MOE_ERR_ALIGN;
   size_t need = quant_ws(M, K, group);
@@ -78,6 +82,8 @@ int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int32_t group, uint8_
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   if (group == FP8MOE_GROUP) return launch_status(fp8moe::launch_quant_group(xb, M, K, q, scales, st));
+  if (group == FP8MOE_QUANT_ROW)
+    return launch_status(fp8moe::launch_quant_row(xb, M, K, q, scales, st));
   return launch_status(
       fp8moe::launch_quant_tensor(xb, M * K, q, scales, static_cast<float*>(ws), st));
 }
@@ -171,6 +177,24 @@ int32_t fp8_dense_gemm(const uint8_t* a, const float* a_scale_blk, const uint8_t
     if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
   return launch_status(fp8moe::launch_dense_gemm(a, a_scale_blk, w, w_scale, M, N, K, out_dtype,
                                                  out, static_cast<hipStream_t>(stream)));
+}
+
+int32_t fp8_dense_gemm_rowwise(const uint8_t* a, const float* a_scales, const uint8_t* w,
+                               const float* w_scale, int64_t M, int64_t N, int64_t K,
+                               int32_t out_dtype, void* out, void* stream) {
+  if (out_dtype != FP8MOE_DTYPE_F32 && out_dtype != FP8MOE_DTYPE_BF16)
+    return FP8MOE_ERR_UNSUPPORTED;
+  if (!a || !a_scales || !w || !w_scale || !out) return FP8MOE_ERR_NULL;
+  if (M < 1 || M >= (int64_t(1) << 31) || N < 16 || N % 16 != 0 || N >= (int64_t(1) << 31))
+    return FP8MOE_ERR_SHAPE;
+  if (K < 128 || K % 128 != 0 || K >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
+  if (M * K >= (int64_t(1) << 32) || N * K >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;
+  const void* ptrs[] = {a, a_scales, w, w_scale, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
+  return launch_status(fp8moe::launch_dense_gemm_rowwise(a, a_scales, w, w_scale, M, N, K,
+                                                         out_dtype, out,
+                                                         static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_unpermute_combine(const void* y, int32_t y_dtype, const int32_t* pos,

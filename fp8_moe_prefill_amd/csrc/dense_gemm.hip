@@ -10,6 +10,10 @@
 // (tn_gemm.h: 128 x 128 tiles, operands DMA'd into LDS); decode shapes (M <= 16) take the
 // weight-streaming kernel below (memra-engine fp8_ffi module text draws the same line
 // between prefill, m >= 16, and decode).
+//
+// Row-wise variant (fp8_dense_gemm_rowwise): FreeToken PR #389, "Limits" -- one activation
+// scale per row, y = (s_a[m] * s_w) * (qa . qw^T); the same kernels with the scale product
+// formed per output row in the epilogue.
 #include "common.h"
 #include "launch.h"
 #include "tn_gemm.h"
@@ -29,7 +33,8 @@ constexpr int kDenseStages = 2;
 constexpr int kGemvWaves = 8;
 constexpr int kGemvUnroll = 4;
 
-template <bool OUT_BF16>
+// a_blk: the per-tensor scale block (s_a = a_blk[2]), or with ROW_SCALE the per-row scales
+template <bool OUT_BF16, bool ROW_SCALE>
 __global__ __launch_bounds__(kGemvWaves * 64) void dense_gemv_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ a_blk,
     const uint8_t* __restrict__ W, const float* __restrict__ w_scale, int M, int N, int K,
@@ -71,14 +76,14 @@ __global__ __launch_bounds__(kGemvWaves * 64) void dense_gemv_kernel(
   v4f sum = part[0][lane];
 #pragma unroll
   for (int j = 1; j < kGemvWaves; ++j) sum += part[j][lane];
-  const float scale = a_blk[2] * w_scale[0];
+  const float sw0 = w_scale[0];
   const int n = n0 + c16;
   // lane (g, c16) holds out[m = 4g + r][n0 + c16]
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * g + r;
     if (m < M && n < N) {
-      const float v = sum[r] * scale;
+      const float v = sum[r] * ((ROW_SCALE ? a_blk[m] : a_blk[2]) * sw0);
       if (OUT_BF16)
         reinterpret_cast<uint16_t*>(out)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(v);
       else
@@ -87,24 +92,37 @@ __global__ __launch_bounds__(kGemvWaves * 64) void dense_gemv_kernel(
   }
 }
 
+template <bool ROW_SCALE>
+hipError_t launch_dense(const uint8_t* a, const float* a_s, const uint8_t* w,
+                        const float* w_scale, int64_t M, int64_t N, int64_t K,
+                        int32_t out_dtype, void* out, hipStream_t st) {
+  if (M <= 16) {  // by shape only, never by values
+    const dim3 grid((uint32_t)((N + 15) / 16)), block(kGemvWaves * 64);
+    if (out_dtype == FP8MOE_DTYPE_BF16)
+      dense_gemv_kernel<true, ROW_SCALE><<<grid, block, 0, st>>>(a, a_s, w, w_scale, (int)M,
+                                                                 (int)N, (int)K, out);
+    else
+      dense_gemv_kernel<false, ROW_SCALE><<<grid, block, 0, st>>>(a, a_s, w, w_scale, (int)M,
+                                                                  (int)N, (int)K, out);
+    return hipGetLastError();
+  }
+  if (out_dtype == FP8MOE_DTYPE_BF16)
+    return tn::launch<false, true, kDenseStages, ROW_SCALE>(a, w, M, N, K, a_s, w_scale, out, st);
+  return tn::launch<false, false, kDenseStages, ROW_SCALE>(a, w, M, N, K, a_s, w_scale, out, st);
+}
+
 }  // namespace
 
 hipError_t launch_dense_gemm(const uint8_t* a, const float* a_blk, const uint8_t* w,
                              const float* w_scale, int64_t M, int64_t N, int64_t K,
                              int32_t out_dtype, void* out, hipStream_t st) {
-  if (M <= 16) {  // by shape only, never by values
-    const dim3 grid((uint32_t)((N + 15) / 16)), block(kGemvWaves * 64);
-    if (out_dtype == FP8MOE_DTYPE_BF16)
-      dense_gemv_kernel<true><<<grid, block, 0, st>>>(a, a_blk, w, w_scale, (int)M, (int)N,
-                                                      (int)K, out);
-    else
-      dense_gemv_kernel<false><<<grid, block, 0, st>>>(a, a_blk, w, w_scale, (int)M, (int)N,
-                                                       (int)K, out);
-    return hipGetLastError();
-  }
-  if (out_dtype == FP8MOE_DTYPE_BF16)
-    return tn::launch<false, true, kDenseStages>(a, w, M, N, K, a_blk, w_scale, out, st);
-  return tn::launch<false, false, kDenseStages>(a, w, M, N, K, a_blk, w_scale, out, st);
+  return launch_dense<false>(a, a_blk, w, w_scale, M, N, K, out_dtype, out, st);
+}
+
+hipError_t launch_dense_gemm_rowwise(const uint8_t* a, const float* a_scales, const uint8_t* w,
+                                     const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                     int32_t out_dtype, void* out, hipStream_t st) {
+  return launch_dense<true>(a, a_scales, w, w_scale, M, N, K, out_dtype, out, st);
 }
 
 }  // namespace fp8moe

@@ -15,6 +15,8 @@ namespace fp8moe {
 constexpr int64_t kQuantFusedMax = 65536;
 constexpr int kQuantPartials = 1024;  // max workgroups of the per-tensor amax pass
 
+hipError_t launch_quant_row(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* scales,
+                            hipStream_t st);
 hipError_t launch_quant_group(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
                               float* scales, hipStream_t st);
 hipError_t launch_quant_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* block,
@@ -37,6 +39,9 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const in
                                int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
                                float* out_scales, hipStream_t st);
 
+hipError_t launch_dense_gemm_rowwise(const uint8_t* a, const float* a_scales, const uint8_t* w,
+                                     const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                     int32_t out_dtype, void* out, hipStream_t st);
 hipError_t launch_dense_gemm(const uint8_t* a, const float* a_blk, const uint8_t* w,
                              const float* w_scale, int64_t M, int64_t N, int64_t K,
                              int32_t out_dtype, void* out, hipStream_t st);

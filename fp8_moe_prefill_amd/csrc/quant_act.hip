@@ -5,6 +5,8 @@
 // Per-tensor mode: one scale for the whole tensor -- FreeToken PR #389, "What this adds"
 // (an amax pass, then the cast; one fused launch for small tensors, a reduction plus a
 // cast launch above 64k elements, chosen by shape only).
+// Row mode: one scale per row (token) -- FreeToken PR #389, "Limits" (row-wise activation
+// scales, measured there against the per-tensor route).
 // Scale rule amax/448: memra-engine fp8_ffi module docs.
 //
 // Both modes are HBM-bound streaming kernels: each thread reads 16-byte chunks (8 bf16),
@@ -150,7 +152,32 @@ __global__ __launch_bounds__(256) void quant_tensor_cast_kernel(const uint4* __r
   }
 }
 
+// Row mode: one workgroup per row. The row's amax is a block reduction; the cast pass
+// reads the row again (a few KB, still in the caches), so HBM sees it once.
+__global__ __launch_bounds__(256) void quant_row_kernel(const uint4* __restrict__ x,
+                                                       int64_t nch, uint2* __restrict__ q,
+                                                       float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const uint4* xr = x + row * nch;
+  uint2* qr = q + row * nch;
+  float m = 0.f;
+  for (int64_t c = threadIdx.x; c < nch; c += 256) m = fmaxf(m, amax8(unpack8(xr[c])));
+  const float amax = block_max(m, red);
+  float s, inv;
+  scale_pair(amax, s, inv);
+  if (threadIdx.x == 0) scales[row] = s;
+  for (int64_t c = threadIdx.x; c < nch; c += 256) qr[c] = encode8(unpack8(xr[c]), inv);
+}
+
 }  // namespace
+
+hipError_t launch_quant_row(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* scales,
+                            hipStream_t st) {
+  quant_row_kernel<<<dim3((uint32_t)M), dim3(256), 0, st>>>(
+      reinterpret_cast<const uint4*>(x), K / 8, reinterpret_cast<uint2*>(q), scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_group(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
                               float* scales, hipStream_t st) {

@@ -56,8 +56,9 @@ __device__ __forceinline__ int col_of(int rho) {
 // IN_BF16: operands are bf16 (K counts elements, 2 bytes each), else e4m3 bytes.
 // OUT_BF16: bf16 output (round to nearest even), else fp32.
 // scale_a / scale_w: the e4m3 path multiplies by scale_a[2] * scale_w[0] (the activation
-// scale block and the weight scale, both on the device); the bf16 path takes no scale.
-template <bool IN_BF16, bool OUT_BF16, int STAGES>
+// scale block and the weight scale, both on the device), or with ROW_SCALE by
+// scale_a[row] * scale_w[0] (one activation scale per row); the bf16 path takes no scale.
+template <bool IN_BF16, bool OUT_BF16, int STAGES, bool ROW_SCALE = false>
 __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restrict__ A,
                                                          const uint8_t* __restrict__ W, int M,
                                                          int N, int row_bytes, int NTM,
@@ -108,6 +109,16 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc[t][s] = (v4f){0.f, 0.f, 0.f, 0.f};
+  // per-row activation scales of this lane's 16 output rows, loaded now so that their
+  // latency is hidden behind the main loop
+  float row_scale[4][4];
+  if (ROW_SCALE) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        row_scale[t][r] = scale_a[min(m0 + 64 * wm + 16 * t + 4 * g + r, M - 1)];
+  }
 
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
@@ -163,7 +174,8 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
     }
   }
 
-  const float scale = IN_BF16 ? 1.f : scale_a[2] * scale_w[0];
+  const float sw0 = IN_BF16 ? 1.f : scale_w[0];
+  const float tensor_scale = IN_BF16 || ROW_SCALE ? sw0 : scale_a[2] * sw0;
   const int c0 = n0 + 64 * wn + 4 * c16;
   const bool vec = (c0 + 3 < N) && ((N & 3) == 0);
 #pragma unroll
@@ -172,6 +184,7 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
     for (int r = 0; r < 4; ++r) {
       const int row = m0 + 64 * wm + 16 * t + 4 * g + r;
       if (row >= M) continue;
+      const float scale = ROW_SCALE ? row_scale[t][r] * sw0 : tensor_scale;
       const float v0 = acc[t][0][r] * scale, v1 = acc[t][1][r] * scale;
       const float v2 = acc[t][2][r] * scale, v3 = acc[t][3][r] * scale;
       const int64_t o = (int64_t)row * N + c0;
@@ -200,11 +213,11 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
 }
 
 // Enqueue the kernel over ceil(M/128) x ceil(N/128) tiles; row_bytes = bytes per row of K.
-template <bool IN_BF16, bool OUT_BF16, int STAGES>
+template <bool IN_BF16, bool OUT_BF16, int STAGES, bool ROW_SCALE = false>
 hipError_t launch(const uint8_t* a, const uint8_t* w, int64_t M, int64_t N, int64_t row_bytes,
                   const float* scale_a, const float* scale_w, void* out, hipStream_t st) {
   const int NTM = (int)((M + TM - 1) / TM), NTN = (int)((N + TN - 1) / TN);
-  tn_gemm_kernel<IN_BF16, OUT_BF16, STAGES><<<dim3((uint32_t)(NTM * NTN)), 256, 0, st>>>(
+  tn_gemm_kernel<IN_BF16, OUT_BF16, STAGES, ROW_SCALE><<<dim3((uint32_t)(NTM * NTN)), 256, 0, st>>>(
       a, w, (int)M, (int)N, (int)row_bytes, NTM, NTN, scale_a, scale_w, out);
   return hipGetLastError();
 }

@@ -14,6 +14,10 @@
  *   fp8_dense_gemm           W8A8 GEMM with per-tensor activation and weight scales
  *   moe_unpermute_combine    weighted sum of each token's k expert rows
  *
+ * quantisation variants of those ([P2] "Limits"):
+ *
+ *   fp8_dense_gemm_rowwise   W8A8 GEMM with one activation scale per row
+ *
  * and, for the depth stack those layers sit in ([P1] section 3):
  *
  *   fp8moe_rmsnorm           residual add + RMSNorm, bf16 in and out
@@ -68,6 +72,7 @@ extern "C" {
 
 /* ---- enums ------------------------------------------------------------------- */
 #define FP8MOE_GROUP 128             /* the K-group of every group-wise scale        */
+#define FP8MOE_QUANT_ROW (-1)        /* fp8_quant_act group: one scale per row        */
 
 #define FP8MOE_DTYPE_F32 0
 #define FP8MOE_DTYPE_BF16 1
@@ -88,7 +93,7 @@ const char* fp8moe_status_str(int32_t status);
 
 /*
  * fp8moe_workspace_bytes -- device scratch an entry point needs.
- *   op = FP8MOE_OP_QUANT_ACT:      a = M, b = K, c = group (128 or 0)
+ *   op = FP8MOE_OP_QUANT_ACT:      a = M, b = K, c = group (128, 0 or FP8MOE_QUANT_ROW)
  *   op = FP8MOE_OP_ROUTE_PERMUTE:  a = T, b = E, c = k
  *   op = FP8MOE_OP_ATTENTION:      a = T, b = n_kv, c = head_dim (128)
  * Returns 0 for an op that needs none, (size_t)-1 for invalid arguments.
@@ -104,17 +109,19 @@ size_t fp8moe_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c);
  *
  *   x       bf16 [M, K]
  *   group   FP8MOE_GROUP (128): one scale per (row, 128 consecutive columns);
- *           0: one scale for the whole tensor
+ *           0: one scale for the whole tensor;
+ *           FP8MOE_QUANT_ROW: one scale per row ([P2] "Limits": row-wise scales)
  *   q       out, e4m3 [M, K]
  *   scales  out; group=128: fp32 [M, K/128], scale of (row m, group g) at m*K/128 + g;
- *           group=0: fp32[4] = {amax, 448/a, a/448, 0} with a = max(amax, 1e-12)
+ *           group=0: fp32[4] = {amax, 448/a, a/448, 0} with a = max(amax, 1e-12);
+ *           FP8MOE_QUANT_ROW: fp32 [M], the scale a/448 of each row
  *   ws      workspace of fp8moe_workspace_bytes(FP8MOE_OP_QUANT_ACT, M, K, group)
  *           bytes (may be NULL if that is 0)
  * Arithmetic (fp32): a = max(max|x| over the group, 1e-12); s = a/448 and
  * inv = 448/a, both correctly rounded; q = e4m3(x * inv). NaN inputs encode to 0x7F
  * and are skipped by the amax.
  * Constraints: M >= 1, K >= 1; group=128 needs K % 128 == 0; group=0 needs
- * M*K % 8 == 0.
+ * M*K % 8 == 0; FP8MOE_QUANT_ROW needs K % 8 == 0 and M < 2^31.
  */
 int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int32_t group, uint8_t* q,
                       float* scales, void* ws, size_t ws_bytes, void* stream);
@@ -237,6 +244,22 @@ int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales,
 int32_t fp8_dense_gemm(const uint8_t* a, const float* a_scale_blk, const uint8_t* w,
                        const float* w_scale, int64_t M, int64_t N, int64_t K,
                        int32_t out_dtype, void* out, void* stream);
+
+/*
+ * fp8_dense_gemm_rowwise -- W8A8 projection with one activation scale per row,
+ * y[m, n] = (s_a[m] * s_w) * (qa[m] . qw[n]).
+ *
+ * [P2] "Limits": row-wise activation scales, measured there against the per-tensor route
+ * (the same shapes, GEMM only).
+ *
+ *   a          e4m3 [M, K] (from fp8_quant_act with group = FP8MOE_QUANT_ROW)
+ *   a_scales   fp32 [M] on the device, s_a of each row
+ *   w, w_scale, out, out_dtype: as fp8_dense_gemm
+ * Constraints: as fp8_dense_gemm.
+ */
+int32_t fp8_dense_gemm_rowwise(const uint8_t* a, const float* a_scales, const uint8_t* w,
+                               const float* w_scale, int64_t M, int64_t N, int64_t K,
+                               int32_t out_dtype, void* out, void* stream);
 
 /*
  * moe_unpermute_combine -- out[t, :] = sum_{j=0..k-1} weights[t, j] * y[pos[t*k+j], :]

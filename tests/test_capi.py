@@ -28,7 +28,7 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        pytest.fail(f"{LIB} not built (python -m fp8_moe_prefill_amd.build)")
+        pytest.fail(f"{LIB} not built (python fp8_moe_prefill_amd/build.py)")
     from fp8_moe_prefill_amd._lib import load_library
     return load_library(LIB)
 
@@ -39,7 +39,8 @@ def test_header_declares_the_five_entry_points():
                  "fp8_dense_gemm", "moe_unpermute_combine"]:
         assert name in fns
     assert "fp8moe_workspace_bytes" in fns and "fp8moe_status_str" in fns
-    for name in ["fp8moe_rmsnorm", "fp8moe_bf16_gemm", "fp8moe_causal_attention"]:
+    for name in ["fp8moe_rmsnorm", "fp8moe_bf16_gemm", "fp8moe_causal_attention",
+                 "fp8_dense_gemm_rowwise"]:
         assert name in fns
 
 
@@ -47,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
     raw = ctypes.CDLL(LIB)
     for name in declared_functions():
         assert hasattr(raw, name), name
-    assert lib.fp8moe_abi_version() == 3
+    assert lib.fp8moe_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -60,6 +61,7 @@ def test_workspace_queries(lib):
     assert lib.fp8moe_workspace_bytes(0, 64, 256, 128) == 0
     assert lib.fp8moe_workspace_bytes(0, 2048, 4096, 0) == 4096
     assert lib.fp8moe_workspace_bytes(0, 8, 8, 0) == 0  # fused single-workgroup path
+    assert lib.fp8moe_workspace_bytes(0, 2048, 4096, -1) == 0  # row mode needs none
     n = lib.fp8moe_workspace_bytes(1, 4096, 64, 8)
     assert n >= (4096 // 16) * 64 * 4 and n % 256 == 0
     bad = ctypes.c_size_t(-1).value
@@ -83,6 +85,9 @@ def test_quant_act_validation(lib):
     assert f(U, 4, 128, 128, P, P, None, 0, None) == ALIGN
     assert f(P, 2048, 4096, 0, P, P, None, 0, None) == WS
     assert f(P, 2048, 4096, 0, P, P, P, 100, None) == WS
+    assert f(P, 4, 100, -1, P, P, None, 0, None) == SHAPE  # row mode: K % 8
+    assert f(P, 4, 96, -1, U, P, None, 0, None) == ALIGN
+    assert f(P, 4, 96, -2, P, P, None, 0, None) == UNSUP
 
 
 def _route(lib, logits=P, T=16, E=8, k=2, ws=P, ws_bytes=1 << 20, xq=None, xs=None, H=0,
@@ -165,6 +170,17 @@ def test_dense_gemm_validation(lib):
     assert f(P, P, P, P, 16, 24, 128, 0, P, None) == SHAPE
     assert f(P, P, P, P, 16, 64, 96, 0, P, None) == SHAPE
     assert f(P, P, U, P, 16, 64, 128, 0, P, None) == ALIGN
+
+
+def test_dense_gemm_rowwise_validation(lib):
+    f = lib.fp8_dense_gemm_rowwise
+    assert f(P, P, P, P, 16, 64, 128, 5, P, None) == UNSUP
+    assert f(P, None, P, P, 16, 64, 128, 0, P, None) == NULL
+    assert f(P, P, P, P, 0, 64, 128, 0, P, None) == SHAPE
+    assert f(P, P, P, P, 16, 24, 128, 0, P, None) == SHAPE
+    assert f(P, P, P, P, 16, 64, 96, 0, P, None) == SHAPE
+    assert f(P, P, P, P, 1 << 21, 64, 4096, 0, P, None) == SHAPE  # M*K >= 2^32
+    assert f(P, U, P, P, 16, 64, 128, 0, P, None) == ALIGN
 
 
 def test_combine_validation(lib):

@@ -1,4 +1,5 @@
-"""fp8_dense_gemm (and the per-tensor quantiser feeding it) on the GPU vs the oracle.
+"""fp8_dense_gemm (and the per-tensor quantiser feeding it) on the GPU vs the oracle,
+and the row-wise variant fp8_dense_gemm_rowwise (FreeToken PR #389, "Limits").
 
 Shapes: M = 1, 16, 300 (FreeToken PR #389, "Testing": the op against the dequantised
 weight at M=1/16/300) and the full 2048 x 4096 x {6144, 4096} projections, sampled.
@@ -8,9 +9,10 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.dense import dense_w8a8, dense_w8a8_entries, quantize_weight
+from oracle.dense import (dense_w8a8, dense_w8a8_entries, dense_w8a8_rowwise,
+                          dense_w8a8_rowwise_entries, quantize_weight)
 from oracle.numeric import bf16_bits, round_bf16
-from oracle.quant import quant_tensor_bf16
+from oracle.quant import quant_row_bf16, quant_tensor_bf16
 from oracle.tol import check_close, gemm_bound
 from synth import CONFIGS, bf16_bits_from_f32, dense_inputs
 from tests.gpu_util import assert_bytes_equal, dev, host
@@ -89,3 +91,43 @@ def test_decode_shapes(M, N, K):
     check_close(y, ref, gemm_bound(b), f"decode M={M} N={N} K={K}")
     yb = _gpu(x, w, torch.bfloat16)[0]
     assert_bytes_equal(yb, bf16_bits(round_bf16(y.astype(np.float64))), "bf16 = RNE(fp32)")
+
+
+def _gpu_rowwise(x_bits, w_bits, out_dtype=torch.float32):
+    import fp8_moe_prefill_amd as f
+    wq, sw = f.quantize_weight(dev(w_bits))
+    xq, sa = f.fp8_quant_act(dev(x_bits), f.QUANT_ROW)
+    y = f.fp8_dense_gemm_rowwise(xq, sa, wq, sw, out_dtype)
+    torch.cuda.synchronize()
+    return host(y), host(xq), host(sa), host(wq), host(sw)
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 300])
+def test_rowwise_small_m(M):
+    """Row-wise scales at M = 1 / 8 / 16 (the weight-streaming path) and 300 (tiles, ragged
+    last row tile), N = 528 (ragged last column tile), on the outlier-channel activations."""
+    inp = dense_inputs(CONFIGS["dense_w8a8"], M=M)
+    w = inp["w_qkv"][:528]
+    y, xq, sa, wq, sw = _gpu_rowwise(inp["x"], w)
+    rq, rs = quant_row_bf16(inp["x"])
+    assert_bytes_equal(xq, rq, "activation codes")
+    assert_bytes_equal(sa.view(np.uint32), rs.view(np.uint32), "row scales")
+    ref, b = dense_w8a8_rowwise(rq, rs, wq, sw[0], with_bound=True)
+    check_close(y.astype(np.float64), ref, gemm_bound(b), f"rowwise M={M}")
+    yb = _gpu_rowwise(inp["x"], w, torch.bfloat16)[0]
+    assert_bytes_equal(yb, bf16_bits(round_bf16(y.astype(np.float64))), "bf16 = RNE(fp32)")
+
+
+@pytest.mark.parametrize("which", ["w_qkv", "w_o"])
+def test_rowwise_full_size_sampled(which):
+    inp = dense_inputs(CONFIGS["dense_w8a8"])
+    x = inp["x"] if which == "w_qkv" else inp["x_o"]
+    y, xq, sa, wq, sw = _gpu_rowwise(x, inp[which])
+    rq, rs = quant_row_bf16(x)
+    assert_bytes_equal(xq, rq, "activation codes")
+    assert_bytes_equal(sa.view(np.uint32), rs.view(np.uint32), "row scales")
+    rng = np.random.default_rng(6)
+    rows = rng.integers(0, y.shape[0], 3000)
+    cols = rng.integers(0, y.shape[1], 3000)
+    ref, b = dense_w8a8_rowwise_entries(rq, rs, wq, sw[0], rows, cols)
+    check_close(y[rows, cols].astype(np.float64), ref, gemm_bound(b), f"rowwise {which}")

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.quant import quant_group_bf16, quant_tensor_bf16
+from oracle.quant import quant_group_bf16, quant_row_bf16, quant_tensor_bf16
 from synth import CONFIGS, bf16_bits_from_f32, dense_inputs, moe_inputs
 from tests.gpu_util import assert_bytes_equal, dev, host
 
@@ -127,3 +127,32 @@ def test_repeat_runs_identical():
     a = _run_group(x)
     b = _run_group(x)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def _run_row(x_bits):
+    import fp8_moe_prefill_amd as f
+    q, s = f.fp8_quant_act(dev(x_bits), f.QUANT_ROW)
+    torch.cuda.synchronize()
+    return host(q), host(s)
+
+
+@pytest.mark.parametrize("M,K", [(1, 8), (1, 4096), (7, 200), (300, 4096), (2048, 4096),
+                                 (5, 16384)])
+def test_row_mode(M, K):
+    """One scale per row (FreeToken PR #389, "Limits"): ragged K (not a multiple of 128),
+    one-row and full 2048 x 4096 tensors, rows spanning 4 decades, an all-zero row, a -0
+    row and an outlier channel confined to its row."""
+    rng = np.random.default_rng(M + K)
+    x = (rng.standard_normal((M, K)) * np.exp(rng.uniform(-5, 4, (M, 1)))).astype(np.float32)
+    if M > 3:
+        x[1] = 0.0
+        x[2, K // 3] = 3000.0
+    xb = bf16_bits_from_f32(x)
+    if M > 3:
+        xb[3] = 0x8000
+    q, s = _run_row(xb)
+    rq, rs = quant_row_bf16(xb)
+    assert_bytes_equal(q, rq, "codes")
+    assert_bytes_equal(s.view(np.uint32), rs.view(np.uint32), "scales")
+    if M > 3:
+        assert np.all(q[1] == 0) and np.all(q[3] == 0x80)
