@@ -12,7 +12,12 @@ Three granularities:
 * per row (token): FreeToken PR #389, "Limits", measures row-wise activation scales as
   the alternative to the per-tensor one (one outlier channel in one row then sets the
   scale of that row only). The pages print no row-wise formula; reading: the per-tensor
-  rule below applied to each row on its own.
+  rule below applied to each row on its own;
+* per 128 x 128 weight block: the memra-engine fp8_ffi docs name a block-128 e4m3 weight
+  class (QT_F8_E4M3_BLK, "the Qwen-official FP8 class": e4m3 weights with their own grid
+  of block scales, read in place by a per-block FP8 tile). Reading: one scale per
+  (128-row, 128-column) block of the [N, K] weight, found by the same rule; the last
+  row block may be shorter when N is not a multiple of 128.
 
 Arithmetic, all in fp32 as the scale block of ``fp8_ffi``'s ``Fp8Scratch`` is fp32:
   amax  = max |x| over the group (exact; NaN elements are skipped)
@@ -77,6 +82,30 @@ def quant_row(x: np.ndarray):
     _, s, inv = _scale_pair(_amax(x, axis=1))
     q = e4m3_encode((x * inv[:, None]).astype(np.float32))
     return q, s
+
+
+def quant_block128(w: np.ndarray):
+    """fp32 weight [N, K] (K % 128 == 0) -> (e4m3 codes [N, K], fp32 block scales
+    [ceil(N/128), K/128]): each 128 x 128 block quantised by the per-tensor rule
+    (memra-engine fp8_ffi docs, the block-128 e4m3 class)."""
+    w = np.asarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert K % GROUP == 0
+    NB, G = -(-N // GROUP), K // GROUP
+    q = np.empty((N, K), dtype=np.uint8)
+    scales = np.empty((NB, G), dtype=np.float32)
+    for nb in range(NB):
+        for g in range(G):
+            blk = w[nb * GROUP:(nb + 1) * GROUP, g * GROUP:(g + 1) * GROUP]
+            _, s, inv = _scale_pair(_amax(blk.reshape(-1), axis=0))
+            q[nb * GROUP:(nb + 1) * GROUP, g * GROUP:(g + 1) * GROUP] = e4m3_encode(
+                (blk * inv).astype(np.float32))
+            scales[nb, g] = s
+    return q, scales
+
+
+def quant_block128_bf16(w_bits: np.ndarray):
+    return quant_block128(bf16_to_f32(w_bits))
 
 
 def quant_row_bf16(x_bits: np.ndarray):

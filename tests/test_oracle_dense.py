@@ -8,7 +8,9 @@
   "loader round trip within e4m3 tolerance");
 * row-wise variant: numpy matmul with each row's scale; equal row scales give the
   per-tensor projection; scaling one row's scale scales that output row only; brute force
-  (Python float loops) on a tiny case.
+  (Python float loops) on a tiny case;
+* block-128 variant: the same sum taken as scaled per-group partial products; uniform
+  scales reduce it to the row-wise projection; brute force across a block boundary.
 """
 
 import numpy as np
@@ -108,3 +110,57 @@ def test_rowwise_brute_force():
             for k in range(128):
                 acc += float(DEC[qa[m, k]]) * float(DEC[qw[n, k]])
             assert abs(y[m, n] - float(sa[m]) * float(sw) * acc) <= 1e-12 * max(1.0, abs(acc))
+
+
+def _block_case(M, N, K, seed):
+    from oracle.quant import quant_block128_bf16, quant_group_bf16
+    rng = np.random.default_rng(seed)
+    x = bf16_bits_from_f32((rng.standard_normal((M, K)) * rng.uniform(0.1, 10, (M, 1))).astype(np.float32))
+    w = bf16_bits_from_f32((rng.standard_normal((N, K)) * 0.02 * rng.uniform(0.2, 5, (N, 1))).astype(np.float32))
+    qa, sa = quant_group_bf16(x)
+    qw, sw = quant_block128_bf16(w)
+    return qa, sa, qw, sw
+
+
+def test_block_gemm_group_partials():
+    """Block-128 variant against a different order of the same sum: per-K-group partial
+    products of the decoded codes (torch's e4m3 decode), each scaled by its row's group
+    scale and its column's block scale, then summed over the groups."""
+    from oracle.dense import block_gemm, block_gemm_entries
+    M, N, K = 37, 200, 384
+    qa, sa, qw, sw = _block_case(M, N, K, 3)
+    y, b = block_gemm(qa, sa, qw, sw, with_bound=True)
+    ref = np.zeros((M, N))
+    for g in range(K // 128):
+        part = DEC[qa[:, 128 * g:128 * (g + 1)]] @ DEC[qw[:, 128 * g:128 * (g + 1)]].T
+        ref += part * sa[:, g:g + 1].astype(np.float64) * np.repeat(sw[:, g].astype(np.float64), 128)[:N][None, :]
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-14)
+    rows = np.arange(50) % M
+    cols = (np.arange(50) * 7) % N
+    ye, be = block_gemm_entries(qa, sa, qw, sw, rows, cols)
+    assert np.allclose(ye, ref[rows, cols], rtol=1e-12, atol=1e-14)
+    assert np.all(b >= np.abs(y) - 1e-12)
+
+
+def test_block_gemm_uniform_scales_is_rowwise():
+    from oracle.dense import block_gemm
+    M, N, K = 9, 256, 256
+    qa, _, qw, _ = _block_case(M, N, K, 4)
+    sa_row = np.float32([0.5, 2, 3, 1e-3, 7, 0.25, 1, 1, 4])
+    sa = np.repeat(sa_row[:, None], K // 128, axis=1)
+    sw = np.full((2, 2), np.float32(0.125))
+    assert np.allclose(block_gemm(qa, sa, qw, sw), dense_w8a8_rowwise(qa, sa_row, qw, np.float32(0.125)),
+                       rtol=1e-13, atol=0)
+
+
+def test_block_gemm_brute_force():
+    from oracle.dense import block_gemm
+    M, N, K = 2, 130, 256
+    qa, sa, qw, sw = _block_case(M, N, K, 5)
+    y = block_gemm(qa, sa, qw, sw)
+    for m in range(M):
+        for n in (0, 1, 127, 128, 129):
+            acc = 0.0
+            for k in range(K):
+                acc += float(DEC[qa[m, k]]) * float(sa[m, k // 128]) * float(DEC[qw[n, k]]) * float(sw[n // 128, k // 128])
+            assert abs(y[m, n] - acc) <= 1e-12 * max(1.0, abs(acc))

@@ -8,7 +8,9 @@
 * library cross-check: torch computes x * inv in fp32 and casts with its own e4m3 encoder;
 * per-tensor mode on a single group equals group mode; the scale block layout;
 * row-wise mode: torch's fp32 multiply and e4m3 cast with each row's own amax; a single
-  row equals per-tensor mode; rows a power of two apart share codes, scales exactly.
+  row equals per-tensor mode; rows a power of two apart share codes, scales exactly;
+* block-128 weights: torch's cast with each 128 x 128 block's amax (ragged last row
+  block); a single block equals per-tensor mode; blocks are independent.
 """
 
 import numpy as np
@@ -119,3 +121,36 @@ def test_row_wise_single_row_is_per_tensor_and_rows_scale_exactly():
     q3, s3 = quant_row(rows)
     assert all(np.array_equal(q3[i], qt[0]) for i in range(3))
     assert np.array_equal(s3, blk[2] * np.float32([2.0 ** -3, 1.0, 2.0 ** 5]))
+
+
+def test_block128_matches_torch_per_block_rule():
+    # memra-engine fp8_ffi docs: the block-128 e4m3 weight class, one scale per 128 x 128
+    # block; torch's fp32 multiply and e4m3 cast with each block's amax. N = 200: the last
+    # row block has 72 rows.
+    from oracle.quant import quant_block128
+    w = _x(9, (200, 384)) * np.float32(0.05)
+    w[150, 300] = 1000.0  # an outlier sets the scale of its own block only
+    q, s = quant_block128(w)
+    assert s.shape == (2, 3)
+    wt = torch.from_numpy(np.vstack([w, np.zeros((56, 384), np.float32)]).copy())
+    blocks = wt.reshape(2, 128, 3, 128).permute(0, 2, 1, 3)
+    amax = blocks.abs().amax(dim=(2, 3), keepdim=True).clamp_min(1e-12)
+    inv = torch.tensor(448.0, dtype=torch.float32) / amax
+    ref = torch.clamp(blocks * inv, -448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    ref = ref.permute(0, 2, 1, 3).reshape(256, 384)[:200]
+    assert np.array_equal(q, ref.numpy())
+    assert np.array_equal(s, (amax / 448.0).reshape(2, 3).numpy())
+    assert s[1, 2] == np.float32(1000.0) / np.float32(448.0)
+
+
+def test_block128_single_block_is_per_tensor_and_blocks_are_independent():
+    from oracle.quant import quant_block128
+    w = _x(10, (128, 256))
+    q, s = quant_block128(w)
+    for g in range(2):
+        qt, blk = quant_tensor(w[:, 128 * g:128 * (g + 1)])
+        assert np.array_equal(q[:, 128 * g:128 * (g + 1)], qt) and s[0, g] == blk[2]
+    w2 = w.copy()
+    w2[:, 128:] *= np.float32(2.0 ** 7)
+    q2, s2 = quant_block128(w2)
+    assert np.array_equal(q2, q) and s2[0, 0] == s[0, 0] and s2[0, 1] == s[0, 1] * 2 ** 7
