@@ -321,6 +321,19 @@ def main():
             torch.cuda.synchronize()
             us = a.elapsed_time(b) / 20 * 1e3
             res[wn + "_rowwise"] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12}
+            # block-128 e4m3 weights with per-(token, 128) activation scales
+            wb, wbs = f.fp8_quant_weight_block128(w)
+            xg, xgs = f.fp8_quant_act(x, 128)
+            yb = f.fp8_block_gemm(xg, xgs, wb, wbs)
+            for _ in range(3):
+                f.fp8_block_gemm(xg, xgs, wb, wbs, out=yb)
+            a.record()
+            for _ in range(20):
+                f.fp8_block_gemm(xg, xgs, wb, wbs, out=yb)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / 20 * 1e3
+            res[wn + "_block128"] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12}
         out["dense_w8a8"] = res
 
     if not args.no_decode:

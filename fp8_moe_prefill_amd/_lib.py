@@ -45,6 +45,10 @@ SIGNATURES = {
                               _c_void_p, _c_void_p]),
     "fp8_dense_gemm_rowwise": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64,
                                       _i32, _c_void_p, _c_void_p]),
+    "fp8_block_gemm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i32,
+                              _c_void_p, _c_void_p]),
+    "fp8_quant_weight_block128": (_i32, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p,
+                                         _c_void_p]),
     "moe_unpermute_combine": (_i32, [_c_void_p, _i32, _c_void_p, _c_void_p, _i64, _i32, _i64,
                                      _i32, _c_void_p, _c_void_p]),
     "fp8moe_rmsnorm": (_i32, [_c_void_p, _c_void_p, _i64, _i64, ctypes.c_double, _c_void_p,
@@ -277,6 +281,41 @@ def fp8_dense_gemm_rowwise(a, a_scales, w, w_scale, out_dtype=torch.bfloat16, ou
     _check("fp8_dense_gemm_rowwise",
            _lib.fp8_dense_gemm_rowwise(_ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scale), M, N, K,
                                        _dt(out.dtype), _ptr(out), _stream(stream)))
+    return out
+
+
+def fp8_quant_weight_block128(w, q=None, scales=None, stream=None):
+    """bf16 weight [N, K] -> (e4m3 codes [N, K], fp32 block scales [ceil(N/128), K/128])."""
+    _dev(w, "w", torch.bfloat16)
+    N, K = w.shape
+    if q is None:
+        q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(((N + 127) // 128, K // GROUP), dtype=torch.float32, device=w.device)
+    _check("fp8_quant_weight_block128",
+           _lib.fp8_quant_weight_block128(_ptr(w), N, K, _ptr(q), _ptr(scales), _stream(stream)))
+    return q, scales
+
+
+def fp8_block_gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16, out=None, stream=None):
+    """e4m3 [M, K] (scales fp32 [M, K/128]) x block-128 e4m3 [N, K] (scales fp32
+    [ceil(N/128), K/128])."""
+    _dev(a, "a", torch.uint8)
+    _dev(w, "w", torch.uint8)
+    _dev(a_scales, "a_scales", torch.float32)
+    _dev(w_scales, "w_scales", torch.float32)
+    M, K = a.shape
+    N = w.shape[0]
+    if a_scales.shape != (M, K // GROUP):
+        raise ValueError(f"a_scales has shape {tuple(a_scales.shape)}, expected {(M, K // GROUP)}")
+    if w_scales.shape != ((N + 127) // 128, K // GROUP):
+        raise ValueError(f"w_scales has shape {tuple(w_scales.shape)}, expected "
+                         f"{((N + 127) // 128, K // GROUP)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check("fp8_block_gemm", _lib.fp8_block_gemm(_ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scales),
+                                                 M, N, K, _dt(out.dtype), _ptr(out),
+                                                 _stream(stream)))
     return out
 
 

@@ -197,6 +197,35 @@ int32_t fp8_dense_gemm_rowwise(const uint8_t* a, const float* a_scales, const ui
                                                          static_cast<hipStream_t>(stream)));
 }
 
+int32_t fp8_block_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
+                       const float* w_scales, int64_t M, int64_t N, int64_t K, int32_t out_dtype,
+                       void* out, void* stream) {
+  if (out_dtype != FP8MOE_DTYPE_F32 && out_dtype != FP8MOE_DTYPE_BF16)
+    return FP8MOE_ERR_UNSUPPORTED;
+  if (!a || !a_scales || !w || !w_scales || !out) return FP8MOE_ERR_NULL;
+  if (M < 1 || M >= (int64_t(1) << 31) || N < 16 || N % 16 != 0 || N >= (int64_t(1) << 31))
+    return FP8MOE_ERR_SHAPE;
+  if (K < 128 || K % 128 != 0 || K >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
+  if (M * K >= (int64_t(1) << 32) || N * K >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;
+  if (K > 16384) return FP8MOE_ERR_SHAPE;  // a tile stages its block scales of all K steps
+  const void* ptrs[] = {a, a_scales, w, w_scales, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
+  return launch_status(fp8moe::launch_block_gemm(a, a_scales, w, w_scales, M, N, K, out_dtype,
+                                                 out, static_cast<hipStream_t>(stream)));
+}
+
+int32_t fp8_quant_weight_block128(const void* w, int64_t N, int64_t K, uint8_t* q,
+                                  float* scales, void* stream) {
+  if (!w || !q || !scales) return FP8MOE_ERR_NULL;
+  if (N < 1 || N >= (int64_t(1) << 31) || K < 128 || K % 128 != 0 || K >= (int64_t(1) << 31))
+    return FP8MOE_ERR_SHAPE;
+  if ((N + 127) / 128 >= 65536 || K / 128 >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(scales)) return FP8MOE_ERR_ALIGN;
+  return launch_status(fp8moe::launch_quant_block128(static_cast<const uint16_t*>(w), N, K, q,
+                                                     scales, static_cast<hipStream_t>(stream)));
+}
+
 int32_t moe_unpermute_combine(const void* y, int32_t y_dtype, const int32_t* pos,
                               const float* weights, int64_t T, int32_t k, int64_t H,
                               int32_t out_dtype, void* out, void* stream) {

@@ -42,6 +42,11 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const in
 hipError_t launch_dense_gemm_rowwise(const uint8_t* a, const float* a_scales, const uint8_t* w,
                                      const float* w_scale, int64_t M, int64_t N, int64_t K,
                                      int32_t out_dtype, void* out, hipStream_t st);
+hipError_t launch_block_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
+                             const float* w_scales, int64_t M, int64_t N, int64_t K,
+                             int32_t out_dtype, void* out, hipStream_t st);
+hipError_t launch_quant_block128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q,
+                                 float* scales, hipStream_t st);
 hipError_t launch_dense_gemm(const uint8_t* a, const float* a_blk, const uint8_t* w,
                              const float* w_scale, int64_t M, int64_t N, int64_t K,
                              int32_t out_dtype, void* out, hipStream_t st);

@@ -7,6 +7,9 @@
 // cast launch above 64k elements, chosen by shape only).
 // Row mode: one scale per row (token) -- FreeToken PR #389, "Limits" (row-wise activation
 // scales, measured there against the per-tensor route).
+// Block-128 weights (fp8_quant_weight_block128): one scale per 128 x 128 block of an
+// [N, K] weight -- the block-128 e4m3 class of the memra-engine fp8_ffi docs, made at load
+// time.
 // Scale rule amax/448: memra-engine fp8_ffi module docs.
 //
 // Both modes are HBM-bound streaming kernels: each thread reads 16-byte chunks (8 bf16),
@@ -170,7 +173,44 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint4* __restrict_
   for (int64_t c = threadIdx.x; c < nch; c += 256) qr[c] = encode8(unpack8(xr[c]), inv);
 }
 
+// Block-128 weights: one workgroup per 128 x 128 block. Its 2048 chunks of 8 bf16 (128
+// rows x 16 chunks) are held in registers, 8 per thread, across the block's amax
+// reduction and the cast; rows past N (the last row block of a ragged N) are skipped.
+__global__ __launch_bounds__(256) void quant_block128_kernel(const uint4* __restrict__ w,
+                                                            int N, int K,
+                                                            uint2* __restrict__ q,
+                                                            float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int nb = blockIdx.y, g = blockIdx.x, G = K / 128;
+  const int64_t rs = K / 8;  // chunks per row
+  uint4 u[8];
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = threadIdx.x + 256 * j, row = nb * 128 + (c >> 4);
+    u[j] = row < N ? w[(int64_t)row * rs + g * 16 + (c & 15)] : make_uint4(0, 0, 0, 0);
+    m = fmaxf(m, amax8(unpack8(u[j])));
+  }
+  const float amax = block_max(m, red);
+  float s, inv;
+  scale_pair(amax, s, inv);
+  if (threadIdx.x == 0) scales[nb * G + g] = s;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = threadIdx.x + 256 * j, row = nb * 128 + (c >> 4);
+    if (row < N) q[(int64_t)row * rs + g * 16 + (c & 15)] = encode8(unpack8(u[j]), inv);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quant_block128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q,
+                                 float* scales, hipStream_t st) {
+  const dim3 grid((uint32_t)(K / 128), (uint32_t)((N + 127) / 128));
+  quant_block128_kernel<<<grid, dim3(256), 0, st>>>(reinterpret_cast<const uint4*>(w), (int)N,
+                                                   (int)K, reinterpret_cast<uint2*>(q), scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_row(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* scales,
                             hipStream_t st) {

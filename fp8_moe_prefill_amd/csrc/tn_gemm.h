@@ -19,6 +19,14 @@
 // * Output columns are interleaved so that each lane holds four consecutive columns of a
 //   row: column tile s of a wave covers columns 4 * c + s of its 64, and a lane writes them
 //   with one 8-byte (bf16) or 16-byte (fp32) store.
+// * BLOCK (block-128 e4m3 weights with one scale per 128 x 128 block, activations with one
+//   scale per row and 128-wide K group): a K step is exactly one scale group, so each
+//   step's MFMAs start from zero and their results are folded into the fp32 accumulators
+//   with the step's scale products (row scale x block scale). The tile's 128 columns are
+//   one weight block, so the block scale is a single scalar per step; the 128 row scales of
+//   the step ride the same LDS DMA stream as the A tile, and the tile's block scales of all
+//   K steps sit in LDS from the start. A step issues its 16 MFMAs, then the 64 folds; the
+//   other wave on the SIMD keeps the matrix core busy meanwhile.
 #pragma once
 
 #include "common.h"
@@ -30,6 +38,7 @@ namespace tn {
 constexpr int TM = 128, TN = 128;  // tile rows and columns
 constexpr int KSTEP = 128;         // bytes of K per step
 constexpr int BLK = 1024;          // one operand block: 64 lanes x 16 bytes
+constexpr int kMaxBlockSteps = 128;  // BLOCK: K <= 16384
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
@@ -37,6 +46,8 @@ template <int STAGES>
 struct Smem {
   uint8_t a[STAGES][16 * BLK];  // 8 row tiles x 2 halves
   uint8_t b[STAGES][16 * BLK];  // 8 column tiles x 2 halves
+  float as[STAGES][TM];         // BLOCK: the step's scales of the tile's 128 rows
+  float ws[kMaxBlockSteps];     // BLOCK: the tile's weight-block scale of every K step
 };
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -57,8 +68,10 @@ __device__ __forceinline__ int col_of(int rho) {
 // OUT_BF16: bf16 output (round to nearest even), else fp32.
 // scale_a / scale_w: the e4m3 path multiplies by scale_a[2] * scale_w[0] (the activation
 // scale block and the weight scale, both on the device), or with ROW_SCALE by
-// scale_a[row] * scale_w[0] (one activation scale per row); the bf16 path takes no scale.
-template <bool IN_BF16, bool OUT_BF16, int STAGES, bool ROW_SCALE = false>
+// scale_a[row] * scale_w[0] (one activation scale per row); with BLOCK, scale_a is fp32
+// [M, K/128] (per row and K group) and scale_w fp32 [ceil(N/128), K/128] (per weight
+// block), folded per K step; the bf16 path takes no scale.
+template <bool IN_BF16, bool OUT_BF16, int STAGES, bool ROW_SCALE = false, bool BLOCK = false>
 __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restrict__ A,
                                                          const uint8_t* __restrict__ W, int M,
                                                          int N, int row_bytes, int NTM,
@@ -93,11 +106,23 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
     const int chunk = (lane & 7) ^ sw(rho);
     voff[j] = (uint32_t)row * (uint32_t)row_bytes + 16u * (uint32_t)chunk;
   }
+  static_assert(!BLOCK || (!IN_BF16 && !ROW_SCALE && STAGES == 2),
+                "block scales: e4m3 operands, two stages (the waits count all loads)");
+  // BLOCK: waves 0 and 1 also stage the step's scales of rows 64 wv .. 64 wv + 63 (the
+  // activation scales are [M, KS], one per row and K step)
+  const uint32_t soff = BLOCK && wv < 2
+                            ? (uint32_t)min(m0 + 64 * wv + lane, M - 1) * (uint32_t)KS * 4u
+                            : 0u;
+  // BLOCK: the tile's 128 columns are one weight block; its scales of all K steps go to
+  // LDS once (published by the first step's barrier)
+  if (BLOCK)
+    for (int k = tid; k < KS; k += 256) sm.ws[k] = scale_w[(n0 / TN) * KS + k];
   auto issue = [&](int ks) {
     const int st = ks % STAGES;
     uint8_t* dst = (wv < 2 ? sm.a[st] : sm.b[st]) + (wv & 1) * 8 * BLK;
 #pragma unroll
     for (int j = 0; j < 8; ++j) dma16(src, voff[j] + (uint32_t)(ks * KSTEP), dst + j * BLK);
+    if (BLOCK && wv < 2) dma4(scale_a, soff + 4u * (uint32_t)ks, &sm.as[st][64 * wv]);
   };
   // operand reads: tile T (16 rows), half h: row 16 T + c16, chunk 2 g + h
   const int x = sw(c16);
@@ -148,6 +173,41 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
           for (int s = 0; s < 4; ++s)
             acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[t], bop[s], acc[t][s], 0, 0, 0);
       }
+    } else if (BLOCK) {
+      v8i aop[4], bop[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 lo = lds16(sb + (4 * wn + s) * 16 * KSTEP + rd0);
+        const uint4 hi = lds16(sb + (4 * wn + s) * 16 * KSTEP + rd1);
+        bop[s] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint4 lo = lds16(sa + (4 * wm + t) * 16 * KSTEP + rd0);
+        const uint4 hi = lds16(sa + (4 * wm + t) * 16 * KSTEP + rd1);
+        aop[t] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      // scale products of this lane's rows 64 wm + 16 t + 4 g + r for this step
+      const float swb = sm.ws[ks];
+      float sc[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&sm.as[ks % STAGES][64 * wm + 16 * t + 4 * g]);
+        sc[t][0] = a4.x * swb; sc[t][1] = a4.y * swb; sc[t][2] = a4.z * swb; sc[t][3] = a4.w * swb;
+      }
+      const v4f zero = {0.f, 0.f, 0.f, 0.f};
+      v4f pb[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pb[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop[i >> 2], bop[i & 3], zero,
+                                                                 0, 0, 0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[i >> 2][i & 3][r] = fmaf(pb[i][r], sc[i >> 2][r], acc[i >> 2][i & 3][r]);
     } else {
       // all operands of the step first (16 reads in flight), then the 16 MFMAs
       v8i aop[4], bop[4];
@@ -174,8 +234,8 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
     }
   }
 
-  const float sw0 = IN_BF16 ? 1.f : scale_w[0];
-  const float tensor_scale = IN_BF16 || ROW_SCALE ? sw0 : scale_a[2] * sw0;
+  const float sw0 = IN_BF16 || BLOCK ? 1.f : scale_w[0];
+  const float tensor_scale = IN_BF16 || ROW_SCALE || BLOCK ? sw0 : scale_a[2] * sw0;
   const int c0 = n0 + 64 * wn + 4 * c16;
   const bool vec = (c0 + 3 < N) && ((N & 3) == 0);
 #pragma unroll
@@ -213,11 +273,12 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
 }
 
 // Enqueue the kernel over ceil(M/128) x ceil(N/128) tiles; row_bytes = bytes per row of K.
-template <bool IN_BF16, bool OUT_BF16, int STAGES, bool ROW_SCALE = false>
+template <bool IN_BF16, bool OUT_BF16, int STAGES, bool ROW_SCALE = false, bool BLOCK = false>
 hipError_t launch(const uint8_t* a, const uint8_t* w, int64_t M, int64_t N, int64_t row_bytes,
                   const float* scale_a, const float* scale_w, void* out, hipStream_t st) {
   const int NTM = (int)((M + TM - 1) / TM), NTN = (int)((N + TN - 1) / TN);
-  tn_gemm_kernel<IN_BF16, OUT_BF16, STAGES, ROW_SCALE><<<dim3((uint32_t)(NTM * NTN)), 256, 0, st>>>(
+  tn_gemm_kernel<IN_BF16, OUT_BF16, STAGES, ROW_SCALE, BLOCK>
+      <<<dim3((uint32_t)(NTM * NTN)), 256, 0, st>>>(
       a, w, (int)M, (int)N, (int)row_bytes, NTM, NTN, scale_a, scale_w, out);
   return hipGetLastError();
 }

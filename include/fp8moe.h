@@ -14,9 +14,11 @@
  *   fp8_dense_gemm           W8A8 GEMM with per-tensor activation and weight scales
  *   moe_unpermute_combine    weighted sum of each token's k expert rows
  *
- * quantisation variants of those ([P2] "Limits"):
+ * quantisation variants of those ([P2] "Limits"; [P4] the block-128 e4m3 class):
  *
- *   fp8_dense_gemm_rowwise   W8A8 GEMM with one activation scale per row
+ *   fp8_dense_gemm_rowwise     W8A8 GEMM with one activation scale per row
+ *   fp8_quant_weight_block128  bf16 weight -> e4m3 codes + one fp32 scale per 128 x 128
+ *   fp8_block_gemm             e4m3 GEMM on block-128 weights, per-(row, 128) activations
  *
  * and, for the depth stack those layers sit in ([P1] section 3):
  *
@@ -260,6 +262,42 @@ int32_t fp8_dense_gemm(const uint8_t* a, const float* a_scale_blk, const uint8_t
 int32_t fp8_dense_gemm_rowwise(const uint8_t* a, const float* a_scales, const uint8_t* w,
                                const float* w_scale, int64_t M, int64_t N, int64_t K,
                                int32_t out_dtype, void* out, void* stream);
+
+/*
+ * fp8_quant_weight_block128 -- load-time quantisation of a weight to the block-128 e4m3
+ * class: one fp32 scale per 128 x 128 block.
+ *
+ * [P4] fp8_blk_mmq_native_enabled / st_e4m3_blk_enabled: the block-128 e4m3 weight class
+ * ("the Qwen-official FP8 class") with its own grid of block scales, read in place.
+ *
+ *   w       bf16 [N, K]
+ *   q       out, e4m3 [N, K]
+ *   scales  out, fp32 [ceil(N/128), K/128]; block (nb, g) covers rows 128 nb .. 128 nb + 127
+ *           (fewer in the last row block when N % 128 != 0) and columns 128 g .. 128 g + 127
+ * Arithmetic: fp8_quant_act's rule over each block. Constraints: N >= 1, K % 128 == 0,
+ * ceil(N/128) < 65536.
+ */
+int32_t fp8_quant_weight_block128(const void* w, int64_t N, int64_t K, uint8_t* q,
+                                  float* scales, void* stream);
+
+/*
+ * fp8_block_gemm -- e4m3 GEMM on block-128 weights:
+ *   y[m, n] = sum_g s_a[m, g] * s_w[n / 128, g] * (qa[m, 128 g ..] . qw[n, 128 g ..]).
+ *
+ * [P4]: the block-128 e4m3 weight class read natively by a per-block FP8 tile. The pages do
+ * not give the activation scaling of that path; this takes the per-(row, 128-wide K group)
+ * scales of fp8_quant_act with group = 128 ([P1] section 1), so both scales are constant
+ * inside every 128-wide K group and are folded into the fp32 accumulator group by group.
+ *
+ *   a          e4m3 [M, K] (fp8_quant_act, group = 128)
+ *   a_scales   fp32 [M, K/128] (fp8_quant_act's group-mode layout)
+ *   w          e4m3 [N, K], w_scales fp32 [ceil(N/128), K/128] (fp8_quant_weight_block128)
+ *   out        [M, N] fp32 or bf16 (RNE) per out_dtype
+ * Constraints: as fp8_dense_gemm, and K <= 16384.
+ */
+int32_t fp8_block_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
+                       const float* w_scales, int64_t M, int64_t N, int64_t K, int32_t out_dtype,
+                       void* out, void* stream);
 
 /*
  * moe_unpermute_combine -- out[t, :] = sum_{j=0..k-1} weights[t, j] * y[pos[t*k+j], :]

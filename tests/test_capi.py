@@ -40,7 +40,7 @@ def test_header_declares_the_five_entry_points():
         assert name in fns
     assert "fp8moe_workspace_bytes" in fns and "fp8moe_status_str" in fns
     for name in ["fp8moe_rmsnorm", "fp8moe_bf16_gemm", "fp8moe_causal_attention",
-                 "fp8_dense_gemm_rowwise"]:
+                 "fp8_dense_gemm_rowwise", "fp8_block_gemm", "fp8_quant_weight_block128"]:
         assert name in fns
 
 
@@ -181,6 +181,26 @@ def test_dense_gemm_rowwise_validation(lib):
     assert f(P, P, P, P, 16, 64, 96, 0, P, None) == SHAPE
     assert f(P, P, P, P, 1 << 21, 64, 4096, 0, P, None) == SHAPE  # M*K >= 2^32
     assert f(P, U, P, P, 16, 64, 128, 0, P, None) == ALIGN
+
+
+def test_block_gemm_validation(lib):
+    f = lib.fp8_block_gemm
+    assert f(P, P, P, P, 16, 64, 128, 5, P, None) == UNSUP
+    assert f(P, P, P, None, 16, 64, 128, 0, P, None) == NULL
+    assert f(P, P, P, P, 0, 64, 128, 0, P, None) == SHAPE
+    assert f(P, P, P, P, 16, 24, 128, 0, P, None) == SHAPE
+    assert f(P, P, P, P, 16, 64, 200, 0, P, None) == SHAPE
+    assert f(P, P, P, U, 16, 64, 128, 0, P, None) == ALIGN
+    assert f(P, P, P, P, 16, 64, 16384 + 128, 0, P, None) == SHAPE
+
+
+def test_quant_weight_block128_validation(lib):
+    f = lib.fp8_quant_weight_block128
+    assert f(None, 64, 128, P, P, None) == NULL
+    assert f(P, 0, 128, P, P, None) == SHAPE
+    assert f(P, 64, 100, P, P, None) == SHAPE
+    assert f(P, 128 * 65536, 128, P, P, None) == SHAPE  # row-block grid limit
+    assert f(P, 64, 128, P, U, None) == ALIGN
 
 
 def test_combine_validation(lib):

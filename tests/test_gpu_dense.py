@@ -131,3 +131,68 @@ def test_rowwise_full_size_sampled(which):
     cols = rng.integers(0, y.shape[1], 3000)
     ref, b = dense_w8a8_rowwise_entries(rq, rs, wq, sw[0], rows, cols)
     check_close(y[rows, cols].astype(np.float64), ref, gemm_bound(b), f"rowwise {which}")
+
+
+def _gpu_block(x_bits, w_bits, out_dtype=torch.float32):
+    import fp8_moe_prefill_amd as f
+    wq, ws = f.fp8_quant_weight_block128(dev(w_bits))
+    xq, xs = f.fp8_quant_act(dev(x_bits), 128)
+    y = f.fp8_block_gemm(xq, xs, wq, ws, out_dtype)
+    torch.cuda.synchronize()
+    return host(y), host(xq), host(xs), host(wq), host(ws)
+
+
+def _block_weight(N, K, seed):
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((N, K)) * 0.02 * rng.uniform(0.2, 5, (N, 1)) * rng.uniform(0.5, 2, (1, K))
+    return bf16_bits_from_f32(w.astype(np.float32))
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 300])
+def test_block128_small_m(M):
+    """Block-128 weights (memra-engine fp8_ffi docs): codes and block scales bit-exact; the
+    GEMM at M = 1 / 8 / 16 (weight-streaming path) and 300 (tiles), N = 528 (a ragged last
+    weight block of 16 rows), K = 4096, within the fp32 accumulation bound."""
+    from oracle.dense import block_gemm
+    from oracle.quant import quant_block128_bf16, quant_group_bf16
+    inp = dense_inputs(CONFIGS["dense_w8a8"], M=M)
+    w = _block_weight(528, 4096, M)
+    y, xq, xs, wq, ws = _gpu_block(inp["x"], w)
+    rq, rs = quant_group_bf16(inp["x"])
+    rwq, rws = quant_block128_bf16(w)
+    assert_bytes_equal(xq, rq, "activation codes")
+    assert_bytes_equal(wq, rwq, "weight codes")
+    assert_bytes_equal(ws.view(np.uint32), rws.view(np.uint32), "block scales")
+    ref, b = block_gemm(rq, rs, rwq, rws, with_bound=True)
+    check_close(y.astype(np.float64), ref, gemm_bound(b), f"block128 M={M}")
+    yb = _gpu_block(inp["x"], w, torch.bfloat16)[0]
+    assert_bytes_equal(yb, bf16_bits(round_bf16(y.astype(np.float64))), "bf16 = RNE(fp32)")
+
+
+@pytest.mark.parametrize("which", ["w_qkv", "w_o"])
+def test_block128_full_size_sampled(which):
+    from oracle.dense import block_gemm_entries
+    from oracle.quant import quant_group_bf16
+    inp = dense_inputs(CONFIGS["dense_w8a8"])
+    x = inp["x"] if which == "w_qkv" else inp["x_o"]
+    y, xq, xs, wq, ws = _gpu_block(x, inp[which])
+    rq, rs = quant_group_bf16(x)
+    assert_bytes_equal(xq, rq, "activation codes")
+    rng = np.random.default_rng(7)
+    rows = rng.integers(0, y.shape[0], 3000)
+    cols = rng.integers(0, y.shape[1], 3000)
+    ref, b = block_gemm_entries(rq, rs, wq, ws, rows, cols)
+    check_close(y[rows, cols].astype(np.float64), ref, gemm_bound(b), f"block128 {which}")
+
+
+def test_block128_quant_ragged_and_outliers():
+    from oracle.quant import quant_block128_bf16
+    w = _block_weight(200, 384, 11)
+    w[150, 300] = 0x447A  # 1000.0 in bf16: the outlier sets its own block's scale only
+    w[5] = 0x8000  # a -0 row
+    import fp8_moe_prefill_amd as f
+    q, s = f.fp8_quant_weight_block128(dev(w))
+    torch.cuda.synchronize()
+    rq, rs = quant_block128_bf16(w)
+    assert_bytes_equal(host(q), rq, "codes")
+    assert_bytes_equal(host(s).view(np.uint32), rs.view(np.uint32), "block scales")
