@@ -51,6 +51,8 @@ def _parse():
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--stack", type=int, default=8, choices=[0, 8, 12],
                     help="also time the depth stack of this many layers (0: skip)")
+    ap.add_argument("--no-mxfp4", action="store_true",
+                    help="skip the layer with MXFP4 activations")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-regime timings (16-token layer, M <= 16 projections)")
     ap.add_argument("--stack-only", action="store_true",
@@ -336,6 +338,8 @@ def main():
             res[wn + "_block128"] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12}
         out["dense_w8a8"] = res
 
+    if not args.no_mxfp4:
+        out["mxfp4_act"] = bench_mxfp4_layer(c, xs, lgs, args.warmup, min(args.steps, 30), dev)
     if not args.no_decode:
         out.update(bench_decode_regime(c, xs, lgs, banks, dev))
     if args.stack:
@@ -344,6 +348,39 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
     print(json.dumps(out))
+
+
+def bench_mxfp4_layer(c, xs, lgs, warmup, steps, dev) -> dict:
+    """The same layer with MXFP4 activations into gate|up (E2M1 codes, one E8M0 scale per
+    32, applied by the MFMA): per-stage times and the gate|up rate."""
+    import numpy as np
+    import torch
+
+    import fp8_moe_prefill_amd as f
+    from synth import moe_inputs
+
+    banks = [f.ExpertBank.from_host(moe_inputs(c, seed=r), dev, act="mxfp4")
+             for r in range(len(xs))]
+    runner = f.MoELayerRunner(c.T, c.H, c.E, c.k, c.I, dev, act="mxfp4")
+    n = len(xs)
+    for i in range(warmup):
+        runner.run(xs[i % n], lgs[i % n], banks[i % n])
+    stages = f.MoELayerRunner.STAGES
+    ev = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for s in stages} for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(steps):
+        runner.run(xs[i % n], lgs[i % n], banks[i % n], events=ev[i])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    per = {s: float(np.mean([e[s][0].elapsed_time(e[s][1]) for e in ev])) * 1e3 for s in stages}
+    flop_gu = 4.0 * c.T * c.k * c.H * c.I
+    tf = flop_gu / (per["gate_up"] * 1e-6) / 1e12
+    return {"tokens_per_s": c.T / (ms * 1e-3), "ms_per_step": ms, "stages_us": per,
+            "gate_up_tflops": tf, "gate_up_frac_fp8_peak": tf / PEAK_FP8_TFLOPS}
 
 
 def bench_decode_regime(c, xs, lgs, banks, dev) -> dict:

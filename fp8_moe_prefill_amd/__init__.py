@@ -9,7 +9,8 @@ has not been built (``python fp8_moe_prefill_amd/build.py``).
 from ._lib import (  # noqa: F401
     DTYPE_BF16, DTYPE_F32, EPI_STORE, EPI_SWIGLU_QUANT, GROUP, QUANT_ROW, Fp8MoeError,
     LIB_PATH, abi_version, bf16_gemm, causal_attention, fp8_dense_gemm, fp8_dense_gemm_rowwise,
-    fp8_block_gemm, fp8_grouped_expert_gemm, fp8_quant_weight_block128,
+    fp8_block_gemm, fp8_grouped_expert_gemm, fp8_quant_weight_block128, mxfp4_grouped_expert_gemm,
+    mxfp4_quant_act,
     fp8_quant_act, moe_route_permute, moe_unpermute_combine, pack_expert_bank, rmsnorm,
     workspace_bytes,
 )

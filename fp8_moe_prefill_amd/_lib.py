@@ -49,6 +49,12 @@ SIGNATURES = {
                               _c_void_p, _c_void_p]),
     "fp8_quant_weight_block128": (_i32, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p,
                                          _c_void_p]),
+    "mxfp4_quant_act": (_i32, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "fp8moe_pack_expert_bank_mxfp4": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p,
+                                             _c_void_p, _c_void_p]),
+    "mxfp4_grouped_expert_gemm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
+                                         _c_void_p, _c_void_p, _i64, _i32, _i64, _i64, _i32,
+                                         _i32, _c_void_p, _c_void_p, _c_void_p]),
     "moe_unpermute_combine": (_i32, [_c_void_p, _i32, _c_void_p, _c_void_p, _i64, _i32, _i64,
                                      _i32, _c_void_p, _c_void_p]),
     "fp8moe_rmsnorm": (_i32, [_c_void_p, _c_void_p, _i64, _i64, ctypes.c_double, _c_void_p,
@@ -192,10 +198,12 @@ def moe_route_permute(logits: torch.Tensor, k: int, xq=None, xs=None, out=None, 
     return r
 
 
-def pack_expert_bank(w: torch.Tensor, w_scales: torch.Tensor, out=None, stream=None):
+def pack_expert_bank(w: torch.Tensor, w_scales: torch.Tensor, out=None, stream=None,
+                     mxfp4: bool = False):
     """Canonical bank (packed int4 [E, N, K/2], low nibble = even k; fp32 scales
     [E, N, K/128]) -> the grouped GEMM's layout: (bank bytes, kept as a [E, N, K/2] uint8
-    tensor, and scales [E, K/128, N])."""
+    tensor, and scales [E, K/128, N]). ``mxfp4``: the K order of the MXFP4-activation
+    GEMM (``mxfp4_grouped_expert_gemm``)."""
     _dev(w, "w", torch.uint8)
     _dev(w_scales, "w_scales", torch.float32)
     E, N, Kh = w.shape
@@ -204,8 +212,9 @@ def pack_expert_bank(w: torch.Tensor, w_scales: torch.Tensor, out=None, stream=N
         out = (torch.empty_like(w),
                torch.empty((E, K // GROUP, N), dtype=torch.float32, device=w.device))
     wp, sp = out
-    _check("fp8moe_pack_expert_bank", _lib.fp8moe_pack_expert_bank(
-        _ptr(w), _ptr(w_scales), E, N, K, _ptr(wp), _ptr(sp), _stream(stream)))
+    name = "fp8moe_pack_expert_bank_mxfp4" if mxfp4 else "fp8moe_pack_expert_bank"
+    _check(name, getattr(_lib, name)(_ptr(w), _ptr(w_scales), E, N, K, _ptr(wp), _ptr(sp),
+                                     _stream(stream)))
     return wp, sp
 
 
@@ -215,13 +224,34 @@ def fp8_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=
     """Grouped expert GEMM on a bank from ``pack_expert_bank`` (w [E, N, K/2] bytes,
     w_scales [E, K/128, N]); a_scales are group-major [K/128, R]. STORE -> out [R, N];
     SWIGLU_QUANT -> (codes [R, N/2], scales [N/256, R], group-major)."""
+    return _grouped(a, a_scales, w, w_scales, offsets, R, epilogue, out_dtype, sorted_, k_route,
+                    out, out_scales, stream, False)
+
+
+def mxfp4_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=EPI_STORE,
+                              out_dtype=torch.float32, sorted_=None, k_route: int = 1,
+                              out=None, out_scales=None, stream=None):
+    """The grouped expert GEMM with MXFP4 activations: a = codes [rows, K/2] from
+    ``mxfp4_quant_act``, a_scales = [K/128, R] 32-bit words (four E8M0 bytes each,
+    group-major: ``moe_route_permute``'s xs_perm of the quantiser's scales viewed as
+    [rows, K/128] words); the bank from ``pack_expert_bank(..., mxfp4=True)``."""
+    return _grouped(a, a_scales, w, w_scales, offsets, R, epilogue, out_dtype, sorted_, k_route,
+                    out, out_scales, stream, True)
+
+
+def _grouped(a, a_scales, w, w_scales, offsets, R, epilogue, out_dtype, sorted_, k_route, out,
+             out_scales, stream, a_fp4):
     _dev(a, "a", torch.uint8)
-    _dev(a_scales, "a_scales", torch.float32)
+    _dev(a_scales, "a_scales")
+    if a_scales.element_size() != 4:
+        raise ValueError("a_scales must hold 32-bit elements")
     _dev(w, "w", torch.uint8)
     _dev(w_scales, "w_scales", torch.float32)
     _dev(offsets, "offsets", torch.int32)
     E, N, Kh = w.shape
     K = Kh * 2
+    if a.shape[1] != (K // 2 if a_fp4 else K):
+        raise ValueError(f"a has {a.shape[1]} bytes per row, expected {K // 2 if a_fp4 else K}")
     if tuple(a_scales.shape) != (K // GROUP, R):
         raise ValueError(f"a_scales must be [K/128, R] = {(K // GROUP, R)}, "
                          f"got {tuple(a_scales.shape)}")
@@ -242,10 +272,24 @@ def fp8_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=
         if out is None:
             out = torch.empty((R, N), dtype=out_dtype, device=dev)
         dt = _dt(out.dtype)
-    _check("fp8_grouped_expert_gemm", _lib.fp8_grouped_expert_gemm(
+    name = "mxfp4_grouped_expert_gemm" if a_fp4 else "fp8_grouped_expert_gemm"
+    _check(name, getattr(_lib, name)(
         _ptr(a), _ptr(a_scales), _ptr(sorted_), k_route, _ptr(w), _ptr(w_scales), _ptr(offsets),
         R, E, N, K, epilogue, dt, _ptr(out), _ptr(out_scales), _stream(stream)))
     return (out, out_scales) if epilogue == EPI_SWIGLU_QUANT else out
+
+
+def mxfp4_quant_act(x: torch.Tensor, q=None, scales=None, stream=None):
+    """bf16 [M, K] -> (MXFP4 codes uint8 [M, K/2], E8M0 scale bytes uint8 [M, K/32])."""
+    _dev(x, "x", torch.bfloat16)
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _check("mxfp4_quant_act", _lib.mxfp4_quant_act(_ptr(x), M, K, _ptr(q), _ptr(scales),
+                                                   _stream(stream)))
+    return q, scales
 
 
 def fp8_dense_gemm(a, a_scale_blk, w, w_scale, out_dtype=torch.bfloat16, out=None, stream=None):

@@ -17,6 +17,14 @@
 // Its 16 bytes at 16 * (16h + i) hold column n(c, i), k = 128g + 32h + 0..31, as four
 // little-endian words; byte b of word j holds k0 + b in the low nibble and k0 + 4 + b in
 // the high nibble (k0 = 128g + 32h + 8j). Scales: [E][K/128][N].
+//
+// FP4-activation layout (the bank for MXFP4 activations): an FP4 operand lane of the
+// gfx950 MFMA holds its 32 values at K positions {b .. b + 15} and {b + 32 .. b + 47} of
+// the 128 (b = 64 (q % 2) + 16 (q / 2) for lane block q), and its E8M0 scale covers just
+// those. With each lane holding one MX block (32 consecutive K) of the activations, the
+// weights must present logical K chunk (16 values) pi(c) = c / 2 + 4 (c % 2) at the
+// MFMA's K chunk c: so lane block h holds logical k = 128g + 16h + 0..15 and then
+// 128g + 64 + 16h + 0..15 (k0 = 128g + 16h + 64 (j / 2) + 8 (j % 2)).
 #include "common.h"
 #include "launch.h"
 
@@ -24,6 +32,7 @@ namespace fp8moe {
 namespace {
 
 // one thread per output 32-bit word
+template <bool FP4_LAYOUT>
 __global__ __launch_bounds__(256) void pack_bank_kernel(const uint32_t* __restrict__ w,
                                                         uint32_t* __restrict__ out,
                                                         int64_t words, int N, int K) {
@@ -37,7 +46,8 @@ __global__ __launch_bounds__(256) void pack_bank_kernel(const uint32_t* __restri
   const int cb = (int)(ecb % NB);
   const int64_t e = ecb / NB;
   const int n = 64 * (cb >> 2) + 4 * (lane & 15) + (cb & 3);
-  const int k0 = g * kGroup + (lane >> 4) * 32 + j * 8;
+  const int h = lane >> 4;
+  const int k0 = g * kGroup + (FP4_LAYOUT ? 16 * h + 64 * (j >> 1) + 8 * (j & 1) : 32 * h + 8 * j);
   // canonical k0 .. k0+7 are the 4 bytes at k0/2: k0 + m sits at bits 4m of this word
   const uint32_t c = w[((e * N + n) * (int64_t)(K / 2) + k0 / 2) >> 2];
   uint32_t r = 0;
@@ -65,11 +75,18 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const float* __restric
 }  // namespace
 
 hipError_t launch_pack_bank(const uint8_t* w, const float* w_scales, int64_t E, int64_t N,
-                            int64_t K, uint8_t* w_packed, float* ws_packed, hipStream_t st) {
+                            int64_t K, uint8_t* w_packed, float* ws_packed, hipStream_t st,
+                            bool fp4_layout) {
   const int64_t words = E * N * (K / 8);
-  pack_bank_kernel<<<dim3((uint32_t)((words + 255) / 256)), 256, 0, st>>>(
-      reinterpret_cast<const uint32_t*>(w), reinterpret_cast<uint32_t*>(w_packed), words,
-      (int)N, (int)K);
+  const dim3 grid((uint32_t)((words + 255) / 256));
+  if (fp4_layout)
+    pack_bank_kernel<true><<<grid, 256, 0, st>>>(reinterpret_cast<const uint32_t*>(w),
+                                                 reinterpret_cast<uint32_t*>(w_packed), words,
+                                                 (int)N, (int)K);
+  else
+    pack_bank_kernel<false><<<grid, 256, 0, st>>>(reinterpret_cast<const uint32_t*>(w),
+                                                  reinterpret_cast<uint32_t*>(w_packed), words,
+                                                  (int)N, (int)K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t ns = E * N * (K / kGroup);

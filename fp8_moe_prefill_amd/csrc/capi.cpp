@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 4;
+constexpr int32_t kAbiVersion = 5;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 constexpr int64_t kMaxGroupedK = 16384;
@@ -112,9 +112,9 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, 
       static_cast<hipStream_t>(stream)));
 }
 
-int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t E, int64_t N,
-                                int64_t K, uint8_t* w_packed, float* w_scales_packed,
-                                void* stream) {
+namespace {
+int32_t pack_bank(const uint8_t* w, const float* w_scales, int64_t E, int64_t N, int64_t K,
+                  uint8_t* w_packed, float* w_scales_packed, void* stream, bool fp4_layout) {
   if (!w || !w_scales || !w_packed || !w_scales_packed) return FP8MOE_ERR_NULL;
   if (E < 1 || E > kMaxE) return FP8MOE_ERR_SHAPE;
   if (N < 64 || N % 64 != 0 || N >= (int64_t(1) << 24)) return FP8MOE_ERR_SHAPE;
@@ -124,14 +124,28 @@ int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t
   for (const void* p : ptrs)
     if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
   return launch_status(fp8moe::launch_pack_bank(w, w_scales, E, N, K, w_packed, w_scales_packed,
-                                                static_cast<hipStream_t>(stream)));
+                                                static_cast<hipStream_t>(stream), fp4_layout));
+}
+}  // namespace
+
+int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t E, int64_t N,
+                                int64_t K, uint8_t* w_packed, float* w_scales_packed,
+                                void* stream) {
+  return pack_bank(w, w_scales, E, N, K, w_packed, w_scales_packed, stream, false);
 }
 
-int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,
-                                int32_t k_route, const uint8_t* w, const float* w_scales,
-                                const int32_t* offsets, int64_t R, int32_t E, int64_t N,
-                                int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
-                                float* out_scales, void* stream) {
+int32_t fp8moe_pack_expert_bank_mxfp4(const uint8_t* w, const float* w_scales, int64_t E,
+                                      int64_t N, int64_t K, uint8_t* w_packed,
+                                      float* w_scales_packed, void* stream) {
+  return pack_bank(w, w_scales, E, N, K, w_packed, w_scales_packed, stream, true);
+}
+
+namespace {
+int32_t grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,
+                     int32_t k_route, const uint8_t* w, const float* w_scales,
+                     const int32_t* offsets, int64_t R, int32_t E, int64_t N, int64_t K,
+                     int32_t epilogue, int32_t out_dtype, void* out, float* out_scales,
+                     void* stream, bool a_fp4) {
   if (epilogue != FP8MOE_EPI_STORE && epilogue != FP8MOE_EPI_SWIGLU_QUANT)
     return FP8MOE_ERR_UNSUPPORTED;
   if (epilogue == FP8MOE_EPI_STORE && out_dtype != FP8MOE_DTYPE_F32 &&
@@ -158,7 +172,37 @@ int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales, const i
   return launch_status(fp8moe::launch_grouped_gemm(a, a_scales, sorted, k_route, w, w_scales,
                                                    offsets, R, E, N, K, epilogue, out_dtype,
                                                    out, out_scales,
-                                                   static_cast<hipStream_t>(stream)));
+                                                   static_cast<hipStream_t>(stream), a_fp4));
+}
+}  // namespace
+
+int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,
+                                int32_t k_route, const uint8_t* w, const float* w_scales,
+                                const int32_t* offsets, int64_t R, int32_t E, int64_t N,
+                                int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
+                                float* out_scales, void* stream) {
+  return grouped_gemm(a, a_scales, sorted, k_route, w, w_scales, offsets, R, E, N, K, epilogue,
+                      out_dtype, out, out_scales, stream, false);
+}
+
+int32_t mxfp4_grouped_expert_gemm(const uint8_t* a, const uint32_t* a_scales,
+                                  const int32_t* sorted, int32_t k_route, const uint8_t* w,
+                                  const float* w_scales, const int32_t* offsets, int64_t R,
+                                  int32_t E, int64_t N, int64_t K, int32_t epilogue,
+                                  int32_t out_dtype, void* out, float* out_scales,
+                                  void* stream) {
+  return grouped_gemm(a, reinterpret_cast<const float*>(a_scales), sorted, k_route, w, w_scales,
+                      offsets, R, E, N, K, epilogue, out_dtype, out, out_scales, stream, true);
+}
+
+int32_t mxfp4_quant_act(const void* x, int64_t M, int64_t K, uint8_t* q, uint8_t* scales,
+                        void* stream) {
+  if (!x || !q || !scales) return FP8MOE_ERR_NULL;
+  if (M < 1 || K < 32 || K % 32 != 0 || M > (int64_t(1) << 40) / K) return FP8MOE_ERR_SHAPE;
+  if (M * K / 8 >= (int64_t(1) << 31) * 256) return FP8MOE_ERR_SHAPE;  // grid size
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scales)) return FP8MOE_ERR_ALIGN;
+  return launch_status(fp8moe::launch_quant_mxfp4(static_cast<const uint16_t*>(x), M, K, q,
+                                                  scales, static_cast<hipStream_t>(stream)));
 }
 
 int32_t fp8_dense_gemm(const uint8_t* a, const float* a_scale_blk, const uint8_t* w,

@@ -129,6 +129,18 @@ __device__ __forceinline__ v8i lds_a_operand(const uint8_t* tile, int r, int q) 
                (int)hi.w};
 }
 
+// FP4 (MXFP4) A tile: 64 bytes per row and group, two rows per 128-byte line (line
+// L = r / 2 holds chunks c' = 4 (r % 2) + c, c = 0..3 the 16-byte chunks of row r), chunk
+// c' of line L at position c' ^ ((L / 2) % 4): the 16 rows one ds_read_b128 touches (same
+// c) then sit in 16 distinct 16-byte bank groups. Lane (q, row) of the MFMA reads chunk q
+// of its row: the 32 E2M1 values of block q (K = 32 q .. 32 q + 31 of the group).
+__device__ __forceinline__ int a4_pos(int L, int cc) { return cc ^ ((L >> 1) & 3); }
+__device__ __forceinline__ v8i lds_a4_operand(const uint8_t* tile, int r, int q) {
+  const int L = r >> 1;
+  const uint4 v = *reinterpret_cast<const uint4*>(&tile[L * 128 + (a4_pos(L, 4 * (r & 1) + q) << 4)]);
+  return (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+}
+
 __device__ __forceinline__ float dpp_xor1(float v) {  // value of lane ^ 1 (quad_perm 1,0,3,2)
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
@@ -166,7 +178,11 @@ struct TileDesc {
   int e, row_begin, rows, nt;
 };
 
-template <int EPI, bool OUT_BF16>
+// AF4: the activations are MXFP4 (E2M1 codes, two per byte, with one E8M0 scale per 32
+// consecutive K, four per row and group as one 32-bit word in As), and the bank is packed
+// in the matching K order (pack_bank with the FP4 layout). The MFMA applies the
+// activation scales itself, so the fold is one FMA by the weight scale.
+template <int EPI, bool OUT_BF16, bool AF4 = false>
 __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As,
     const int32_t* __restrict__ sorted, int k_route, int a_rows, const uint8_t* __restrict__ W,
@@ -311,7 +327,9 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   fetch_rows(pend);
   wait_all_loads();
 
-  uint32_t a_off32[RPW / 8] = {}, as_off32 = 0, ws_off32 = 0;
+  constexpr int A_DMA = AF4 ? RPW / 16 : RPW / 8;  // A tile DMA instructions per wave
+  const int a_row_bytes = AF4 ? K / 2 : K;
+  uint32_t a_off32[A_DMA] = {}, as_off32 = 0, ws_off32 = 0;
   uint32_t b_blk[4] = {0, 0, 0, 0};  // byte offset of this wave's 4 column blocks in its expert
   const uint8_t* w_exp = W;
   const float* ws_exp = Ws;
@@ -323,8 +341,18 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
       // a new tile enters the stream: set up its sources from the prefetched descriptor
       const TileDesc t = pend;
 #pragma unroll
-      for (int j = 0; j < RPW / 8; ++j) {
-        const int rl = 8 * j + (lane >> 3);  // row (of this wave's RPW) staged by this lane
+      for (int j = 0; j < A_DMA; ++j) {
+        // row (of this wave's RPW) and 16-byte chunk staged by this lane
+        int rl, c;
+        if (AF4) {
+          const int L = wv * (RPW / 2) + 8 * j + (lane >> 3);  // LDS line of the tile
+          const int cc = a4_pos(L, lane & 7);                   // chunk held at slot lane & 7
+          rl = 2 * L + (cc >> 2) - wv * RPW;
+          c = cc & 3;
+        } else {
+          rl = 8 * j + (lane >> 3);
+          c = (lane & 7) ^ a_swz(rl);
+        }
         int src;
         if (sorted) {
           const int p = s_src[wv][rl];
@@ -333,8 +361,7 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
           src = t.row_begin + min(wv * RPW + rl, t.rows - 1);
         }
         src = max(min(src, a_rows - 1), 0);
-        const int c = (lane & 7) ^ a_swz(rl);
-        a_off32[j] = (uint32_t)src * (uint32_t)K + (uint32_t)(c * 16);
+        a_off32[j] = (uint32_t)src * (uint32_t)a_row_bytes + (uint32_t)(c * 16);
       }
       as_off32 =
           (uint32_t)max(min(t.row_begin + min(wv * RPW + (lane & (RPW - 1)), t.rows - 1), R - 1), 0) * 4u;
@@ -353,9 +380,9 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
       pend = tile_of(jd + 1);
       fetch_rows(pend);
     }
-    const uint8_t* ag = A + gd * kGroup;
+    const uint8_t* ag = A + gd * (AF4 ? kGroup / 2 : kGroup);
 #pragma unroll
-    for (int j = 0; j < RPW / 8; ++j) dma16(ag, a_off32[j], st.a + (wv * (RPW / 8) + j) * 1024);
+    for (int j = 0; j < A_DMA; ++j) dma16(ag, a_off32[j], st.a + (wv * A_DMA + j) * 1024);
     uint8_t* sb = st.b + wv * BW_BYTES;
 #pragma unroll
     for (int s = 0; s < 4; ++s) dma16(w_exp + b_blk[s] + gd * kBlockBytes, lane16, sb + s * 1024);
@@ -368,12 +395,25 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   const v8i ones = {(int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes,
                     (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  // AF4: this lane's E8M0 scale for A row r (block q) of stage st, in bits 7..0
+  auto a4_scale = [&](const Stage& st, int r) {
+    return (int)(__float_as_uint(st.as[r]) >> (8 * q));
+  };
   auto row_sums = [&](Stage& st) {
 #pragma unroll
     for (int h = 0; h < RPW / 16; ++h) {
       const int r0 = wv * RPW + h * 16;
-      v4f pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lds_a_operand(st.a, r0 + c16, q),
-                                                                ones, zero, 0, 0, 0, 0, 0, 0);
+      v4f pr;
+      if (AF4)  // MXFP4 rows, scaled by the MFMA (the ones operand's scale is 2^0)
+        pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            lds_a4_operand(st.a, r0 + c16, q), ones, zero, 4, 0, 0, a4_scale(st, r0 + c16), 0,
+            127);
+      else
+        pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lds_a_operand(st.a, r0 + c16, q),
+                                                              ones, zero, 0, 0, 0, 0, 0, 0);
+      // the MFMA reads every lane's operands (and, scaled, every lane's scale): pin it here,
+      // with all lanes active, so that it is not sunk into the one-lane-per-row store below
+      asm volatile("" : "+v"(pr));
       if (c16 == 0)
         *reinterpret_cast<float4*>(&st.ra[r0 + 4 * q]) =
             make_float4(pr[0] * -0.015625f, pr[1] * -0.015625f, pr[2] * -0.015625f,
@@ -410,18 +450,33 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
     v8i aop[2];
     v4f seed[2];
     float4 sa[2];
-    aop[0] = lds_a_operand(ta, c16, q);
+    int sx[2];  // AF4: the E8M0 scale of this lane's A row and block, per row tile
+    auto a_op = [&](int r) { return AF4 ? lds_a4_operand(ta, r, q) : lds_a_operand(ta, r, q); };
+    aop[0] = a_op(c16);
     {
       const float4 c4 = *reinterpret_cast<const float4*>(&ra[4 * q]);
       seed[0] = (v4f){c4.x, c4.y, c4.z, c4.w};
     }
-    sa[0] = *reinterpret_cast<const float4*>(&sag[4 * q]);
+    if (AF4) sx[0] = a4_scale(cur, c16);
+    else sa[0] = *reinterpret_cast<const float4*>(&sag[4 * q]);
     v4f pb[3];
 
     auto fold = [&](int i) {
       const int t = i >> 2, s = i & 3;
-      const float4 a4 = sa[t & 1];
       const v4f p = pb[i % 3];
+      if (AF4) {  // the activation scales are already inside P
+        if (FIRST) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[t][s][r] = p[r] * sw[s];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[t][s][r] = fmaf(p[r], sw[s], acc[t][s][r]);
+        }
+        asm volatile("" : "+v"(acc[t][s][0]), "+v"(acc[t][s][1]), "+v"(acc[t][s][2]),
+                     "+v"(acc[t][s][3]));
+        return;
+      }
+      const float4 a4 = sa[t & 1];
       if (FIRST) {
         acc[t][s][0] = p[0] * (a4.x * sw[s]);
         acc[t][s][1] = p[1] * (a4.y * sw[s]);
@@ -444,14 +499,19 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
       const int t = i >> 2, s = i & 3;
       if (t < tmax) {  // uniform
         if (s == 0 && t + 1 < tmax) {  // A operand and seed of the next row tile
-          aop[(t + 1) & 1] = lds_a_operand(ta, (t + 1) * 16 + c16, q);
+          aop[(t + 1) & 1] = a_op((t + 1) * 16 + c16);
           const float4 c4 = *reinterpret_cast<const float4*>(&ra[(t + 1) * 16 + 4 * q]);
           seed[(t + 1) & 1] = (v4f){c4.x, c4.y, c4.z, c4.w};
+          if (AF4) sx[(t + 1) & 1] = a4_scale(cur, (t + 1) * 16 + c16);
         }
-        if (s == 2 && t + 1 < tmax)  // A scales of the next row tile (tile t-1's folds are done)
+        if (!AF4 && s == 2 && t + 1 < tmax)  // A scales of the next row tile (tile t-1's folds are done)
           sa[(t + 1) & 1] = *reinterpret_cast<const float4*>(&sag[(t + 1) * 16 + 4 * q]);
-        pb[i % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop[t & 1], bop[s],
-                                                                     seed[t & 1], 0, 0, 0, 0, 0, 0);
+        if (AF4)
+          pb[i % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              aop[t & 1], bop[s], seed[t & 1], 4, 0, 0, sx[t & 1], 0, 127);
+        else
+          pb[i % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              aop[t & 1], bop[s], seed[t & 1], 0, 0, 0, 0, 0, 0);
       }
       if (i >= 2 && ((i - 2) >> 2) < tmax) fold(i - 2);
       __builtin_amdgcn_sched_barrier(0);
@@ -609,11 +669,13 @@ int cu_count() {
 
 }  // namespace
 
-hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,
-                               int32_t k_route, const uint8_t* w, const float* w_scales,
-                               const int32_t* offsets, int64_t R, int32_t E, int64_t N,
-                               int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
-                               float* out_scales, hipStream_t st) {
+namespace {
+template <bool AF4>
+hipError_t launch_grouped(const uint8_t* a, const float* a_scales, const int32_t* sorted,
+                          int32_t k_route, const uint8_t* w, const float* w_scales,
+                          const int32_t* offsets, int64_t R, int32_t E, int64_t N, int64_t K,
+                          int32_t epilogue, int32_t out_dtype, void* out, float* out_scales,
+                          hipStream_t st) {
   if (R == 0) return hipSuccess;
   const int64_t mtiles = (R + BM - 1) / BM + E;  // bound on the m-tiles over all experts
   // SwiGLU: a tile covers 128 h columns (gate and up); otherwise 256 output columns
@@ -624,18 +686,31 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const in
   const int a_rows = (int)(sorted ? R / k_route : R);
   dim3 g((uint32_t)grid), block(NT_THREADS);
   if (epilogue == FP8MOE_EPI_SWIGLU_QUANT)
-    grouped_gemm_kernel<FP8MOE_EPI_SWIGLU_QUANT, false><<<g, block, 0, st>>>(
+    grouped_gemm_kernel<FP8MOE_EPI_SWIGLU_QUANT, false, AF4><<<g, block, 0, st>>>(
         a, a_scales, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N, (int)K,
         NT, out, out_scales);
   else if (out_dtype == FP8MOE_DTYPE_BF16)
-    grouped_gemm_kernel<FP8MOE_EPI_STORE, true><<<g, block, 0, st>>>(
+    grouped_gemm_kernel<FP8MOE_EPI_STORE, true, AF4><<<g, block, 0, st>>>(
         a, a_scales, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N, (int)K,
         NT, out, nullptr);
   else
-    grouped_gemm_kernel<FP8MOE_EPI_STORE, false><<<g, block, 0, st>>>(
+    grouped_gemm_kernel<FP8MOE_EPI_STORE, false, AF4><<<g, block, 0, st>>>(
         a, a_scales, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N, (int)K,
         NT, out, nullptr);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,
+                               int32_t k_route, const uint8_t* w, const float* w_scales,
+                               const int32_t* offsets, int64_t R, int32_t E, int64_t N,
+                               int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
+                               float* out_scales, hipStream_t st, bool a_fp4) {
+  if (a_fp4)
+    return launch_grouped<true>(a, a_scales, sorted, k_route, w, w_scales, offsets, R, E, N, K,
+                                epilogue, out_dtype, out, out_scales, st);
+  return launch_grouped<false>(a, a_scales, sorted, k_route, w, w_scales, offsets, R, E, N, K,
+                               epilogue, out_dtype, out, out_scales, st);
 }
 
 }  // namespace fp8moe

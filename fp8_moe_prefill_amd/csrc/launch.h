@@ -15,6 +15,8 @@ namespace fp8moe {
 constexpr int64_t kQuantFusedMax = 65536;
 constexpr int kQuantPartials = 1024;  // max workgroups of the per-tensor amax pass
 
+hipError_t launch_quant_mxfp4(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
+                              uint8_t* scales, hipStream_t st);
 hipError_t launch_quant_row(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* scales,
                             hipStream_t st);
 hipError_t launch_quant_group(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
@@ -31,13 +33,13 @@ hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32
                                 uint8_t* xq_perm, float* xs_perm, void* ws, hipStream_t st);
 
 hipError_t launch_pack_bank(const uint8_t* w, const float* w_scales, int64_t E, int64_t N,
-                            int64_t K, uint8_t* w_packed, float* ws_packed, hipStream_t st);
+                            int64_t K, uint8_t* w_packed, float* ws_packed, hipStream_t st, bool fp4_layout = false);
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,
                                int32_t k_route, const uint8_t* w, const float* w_scales,
                                const int32_t* offsets, int64_t R, int32_t E, int64_t N,
                                int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
-                               float* out_scales, hipStream_t st);
+                               float* out_scales, hipStream_t st, bool a_fp4 = false);
 
 hipError_t launch_dense_gemm_rowwise(const uint8_t* a, const float* a_scales, const uint8_t* w,
                                      const float* w_scale, int64_t M, int64_t N, int64_t K,

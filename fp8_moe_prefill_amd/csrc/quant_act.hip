@@ -7,6 +7,8 @@
 // cast launch above 64k elements, chosen by shape only).
 // Row mode: one scale per row (token) -- FreeToken PR #389, "Limits" (row-wise activation
 // scales, measured there against the per-tensor route).
+// MXFP4 (mxfp4_quant_act): E2M1 codes with one E8M0 scale per 32 consecutive elements --
+// the FP4 activations of DeepGEMM issue 338, in the OCP MX v1.0 MXFP4 format.
 // Block-128 weights (fp8_quant_weight_block128): one scale per 128 x 128 block of an
 // [N, K] weight -- the block-128 e4m3 class of the memra-engine fp8_ffi docs, made at load
 // time.
@@ -202,7 +204,53 @@ __global__ __launch_bounds__(256) void quant_block128_kernel(const uint4* __rest
   }
 }
 
+// MXFP4: one thread per 8 elements, four consecutive lanes per 32-element block. The
+// shared exponent is floor(log2(amax)) - 2 clamped to [-127, 127], read straight from
+// amax's exponent field (E8M0 byte = field - 2, clamped to [0, 254]; zero and subnormal
+// maxima give 0); v / 2^e is an exact multiply, and the E2M1 code of its magnitude is the
+// count of the rounding thresholds it passes (a midpoint counts toward the even code).
+__device__ __forceinline__ uint32_t e2m1_code(float v, float inv) {
+  const float a = fabsf(v * inv);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  const bool neg = (__float_as_uint(v) >> 31) && !(v != v);  // NaN encodes to +0
+  return m | (neg ? 8u : 0u);
+}
+
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint4* __restrict__ x,
+                                                         int64_t nchunks,
+                                                         uint32_t* __restrict__ q,
+                                                         uint8_t* __restrict__ scales) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  // nchunks is a multiple of 4 and so is every block's first chunk: a quad of lanes is
+  // either wholly in range or wholly out
+  const uint4 u = i < nchunks ? x[i] : make_uint4(0, 0, 0, 0);
+  const F8 f = unpack8(u);
+  float m = amax8(f);
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  const int field = (int)((__float_as_uint(m) >> 23) & 0xFF);
+  const uint32_t b = (uint32_t)min(max(field - 2, 0), 254);
+  const float inv = __uint_as_float((254u - b) << 23);  // 2^-(b - 127), b <= 252 here
+  if (i < nchunks) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= e2m1_code(f.v[j], inv) << (4 * j);
+    q[i] = w;
+    if ((threadIdx.x & 3) == 0) scales[i >> 2] = (uint8_t)b;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quant_mxfp4(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
+                              uint8_t* scales, hipStream_t st) {
+  const int64_t nchunks = M * K / 8;
+  quant_mxfp4_kernel<<<dim3((uint32_t)((nchunks + 255) / 256)), dim3(256), 0, st>>>(
+      reinterpret_cast<const uint4*>(x), nchunks, reinterpret_cast<uint32_t*>(q), scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_block128(const uint16_t* w, int64_t N, int64_t K, uint8_t* q,
                                  float* scales, hipStream_t st) {

@@ -245,7 +245,9 @@ __global__ __launch_bounds__(256) void gather_scales_kernel(const int32_t* __res
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (j < R * G) {
     const int64_t g = j / R, row = j - g * R;
-    xs_perm[j] = xs[(int64_t)(sorted[row] / k) * G + g];
+    // copied as 32-bit words: the same gather serves fp32 scales and packed E8M0 bytes
+    reinterpret_cast<uint32_t*>(xs_perm)[j] =
+        reinterpret_cast<const uint32_t*>(xs)[(int64_t)(sorted[row] / k) * G + g];
   }
 }
 

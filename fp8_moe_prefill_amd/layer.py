@@ -43,19 +43,25 @@ class ExpertBank:
     def H(self) -> int:
         return self.w_dn.shape[1]
 
-    @staticmethod
-    def from_canonical(w_gu, s_gu, w_dn, s_dn, stream=None) -> "ExpertBank":
-        """Canonical device tensors (packed int4 [E, N, K/2], low nibble = even k; scales
-        [E, N, K/128]) -> the packed layout (one-time, at load)."""
-        gu = _lib.pack_expert_bank(w_gu, s_gu, stream=stream)
-        dn = _lib.pack_expert_bank(w_dn, s_dn, stream=stream)
-        return ExpertBank(gu[0], gu[1], dn[0], dn[1])
+    act: str = "e4m3"
 
     @staticmethod
-    def from_host(d: dict, device) -> "ExpertBank":
+    def from_canonical(w_gu, s_gu, w_dn, s_dn, stream=None, act: str = "e4m3") -> "ExpertBank":
+        """Canonical device tensors (packed int4 [E, N, K/2], low nibble = even k; scales
+        [E, N, K/128]) -> the packed layout (one-time, at load). ``act="mxfp4"``: the
+        gate|up bank in the K order of the MXFP4-activation GEMM (the down GEMM's
+        activations stay e4m3)."""
+        if act not in ("e4m3", "mxfp4"):
+            raise ValueError(f"act must be 'e4m3' or 'mxfp4', got {act!r}")
+        gu = _lib.pack_expert_bank(w_gu, s_gu, stream=stream, mxfp4=act == "mxfp4")
+        dn = _lib.pack_expert_bank(w_dn, s_dn, stream=stream)
+        return ExpertBank(gu[0], gu[1], dn[0], dn[1], act)
+
+    @staticmethod
+    def from_host(d: dict, device, act: str = "e4m3") -> "ExpertBank":
         """Canonical host arrays w_gu, s_gu, w_dn, s_dn -> a packed bank on ``device``."""
         t = [torch.from_numpy(d[n]).to(device) for n in ("w_gu", "s_gu", "w_dn", "s_dn")]
-        return ExpertBank.from_canonical(*t)
+        return ExpertBank.from_canonical(*t, act=act)
 
 
 def moe_layer(x: torch.Tensor, logits: torch.Tensor, bank: ExpertBank, k: int,
@@ -65,11 +71,16 @@ def moe_layer(x: torch.Tensor, logits: torch.Tensor, bank: ExpertBank, k: int,
     With ``keep`` the intermediate tensors are returned too (for parity checks)."""
     T = x.shape[0]
     R = T * k
-    xq, xs = _lib.fp8_quant_act(x, _lib.GROUP, stream=stream)
-    rt = _lib.moe_route_permute(logits, k, xs=xs, stream=stream)
-    hq, hs = _lib.fp8_grouped_expert_gemm(xq, rt["xs_perm"], bank.w_gu, bank.s_gu,
-                                          rt["offsets"], R, _lib.EPI_SWIGLU_QUANT,
-                                          sorted_=rt["sorted"], k_route=k, stream=stream)
+    if bank.act == "mxfp4":  # MXFP4 activations into gate|up (bank packed for them)
+        xq, xs = _lib.mxfp4_quant_act(x, stream=stream)
+        rt = _lib.moe_route_permute(logits, k, xs=xs.view(torch.float32), stream=stream)
+        gemm = _lib.mxfp4_grouped_expert_gemm
+    else:
+        xq, xs = _lib.fp8_quant_act(x, _lib.GROUP, stream=stream)
+        rt = _lib.moe_route_permute(logits, k, xs=xs, stream=stream)
+        gemm = _lib.fp8_grouped_expert_gemm
+    hq, hs = gemm(xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"], R,
+                  _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=k, stream=stream)
     y = _lib.fp8_grouped_expert_gemm(hq, hs, bank.w_dn, bank.s_dn, rt["offsets"], R,
                                      _lib.EPI_STORE, out_dtype=torch.bfloat16, stream=stream)
     out = _lib.moe_unpermute_combine(y, rt["pos"], rt["weights"], torch.bfloat16, stream=stream)
@@ -100,13 +111,18 @@ class MoELayerRunner:
 
     STAGES = ("quant", "route", "gate_up", "down", "combine")
 
-    def __init__(self, T: int, H: int, E: int, k: int, I: int, device):
+    def __init__(self, T: int, H: int, E: int, k: int, I: int, device, act: str = "e4m3"):
         R = T * k
         self.T, self.H, self.E, self.k, self.I, self.R = T, H, E, k, I, R
+        self.act = act
         dev = torch.device(device)
         u8, f32, i32 = torch.uint8, torch.float32, torch.int32
-        self.xq = torch.empty((T, H), dtype=u8, device=dev)
-        self.xs = torch.empty((T, H // _lib.GROUP), dtype=f32, device=dev)
+        if act == "mxfp4":  # codes [T, H/2]; E8M0 bytes [T, H/32] = [T, H/128] words
+            self.xq = torch.empty((T, H // 2), dtype=u8, device=dev)
+            self.xs = torch.empty((T, H // 32), dtype=u8, device=dev)
+        else:
+            self.xq = torch.empty((T, H), dtype=u8, device=dev)
+            self.xs = torch.empty((T, H // _lib.GROUP), dtype=f32, device=dev)
         self.route = dict(ids=torch.empty((T, k), dtype=i32, device=dev),
                           weights=torch.empty((T, k), dtype=f32, device=dev),
                           offsets=torch.empty(E + 1, dtype=i32, device=dev),
@@ -128,17 +144,24 @@ class MoELayerRunner:
                 ev[name][i].record()
 
         rt = self.route
+        mx = self.act == "mxfp4"
+        if bank.act != self.act:
+            raise ValueError(f"bank packed for {bank.act} activations, runner for {self.act}")
         mark("quant", 0)
-        _lib.fp8_quant_act(x, _lib.GROUP, q=self.xq, scales=self.xs, stream=stream)
+        if mx:
+            _lib.mxfp4_quant_act(x, q=self.xq, scales=self.xs, stream=stream)
+        else:
+            _lib.fp8_quant_act(x, _lib.GROUP, q=self.xq, scales=self.xs, stream=stream)
         mark("quant", 1)
         mark("route", 0)
-        _lib.moe_route_permute(logits, self.k, xs=self.xs, out=rt, ws=self.ws, stream=stream)
+        _lib.moe_route_permute(logits, self.k, xs=self.xs.view(torch.float32), out=rt,
+                               ws=self.ws, stream=stream)
         mark("route", 1)
         mark("gate_up", 0)
-        _lib.fp8_grouped_expert_gemm(self.xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"],
-                                     self.R, _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"],
-                                     k_route=self.k, out=self.hq, out_scales=self.hs,
-                                     stream=stream)
+        gemm = _lib.mxfp4_grouped_expert_gemm if mx else _lib.fp8_grouped_expert_gemm
+        gemm(self.xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"], self.R,
+             _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k, out=self.hq,
+             out_scales=self.hs, stream=stream)
         mark("gate_up", 1)
         mark("down", 0)
         _lib.fp8_grouped_expert_gemm(self.hq, self.hs, bank.w_dn, bank.s_dn, rt["offsets"],

@@ -19,6 +19,9 @@
  *   fp8_dense_gemm_rowwise     W8A8 GEMM with one activation scale per row
  *   fp8_quant_weight_block128  bf16 weight -> e4m3 codes + one fp32 scale per 128 x 128
  *   fp8_block_gemm             e4m3 GEMM on block-128 weights, per-(row, 128) activations
+ *   mxfp4_quant_act            bf16 activations -> MXFP4 (E2M1 codes + E8M0 scale per 32)
+ *   fp8moe_pack_expert_bank_mxfp4  the expert bank packed for MXFP4 activations
+ *   mxfp4_grouped_expert_gemm  the grouped expert GEMM with MXFP4 activations
  *
  * and, for the depth stack those layers sit in ([P1] section 3):
  *
@@ -31,6 +34,8 @@
  *        (octopusresearch.org), section 1 Contribution.
  *   [P2] FreeToken PR #389 "load-time per-tensor FP8 dense projections (W8A8 via
  *        _scaled_mm)", sections "What this adds" and "Limits".
+ *   [P3] DeepGEMM issue 338 "FP4 activations for fp8_fp4_mega_moe" (E2M1 activations to
+ *        halve the dispatch buffer and run an MXF4 main loop).
  *   [P4] memra-engine fp8_ffi module docs (docs.rs), module text and struct Fp8Scratch.
  *   [P1] section 3 also names the depth stacks (L = 8 and 12) the note measures.
  *
@@ -298,6 +303,59 @@ int32_t fp8_quant_weight_block128(const void* w, int64_t N, int64_t K, uint8_t* 
 int32_t fp8_block_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
                        const float* w_scales, int64_t M, int64_t N, int64_t K, int32_t out_dtype,
                        void* out, void* stream);
+
+/*
+ * mxfp4_quant_act -- bf16 activations -> MXFP4: E2M1 codes with one E8M0 scale per 32
+ * consecutive elements.
+ *
+ * [P3]: E2M1 activations (packed by a pre-dispatch kernel) for an MXF4 main loop. The
+ * pages give no formula; this is the OCP Microscaling (MX) v1.0 MXFP4 definition:
+ * e = floor(log2(max |x| over the 32)) - 2 clamped to [-127, 127] (an all-zero block
+ * takes -127), scale byte e + 127, code = E2M1(x / 2^e) rounded to nearest with ties to
+ * the even code and magnitudes above 6 saturating to 6. The sign of zero is kept; NaN
+ * inputs are skipped by the maximum and encode to +0; inputs are otherwise finite.
+ *
+ *   x       bf16 [M, K]
+ *   q       out, [M, K/2] bytes: element 2i in the low nibble of byte i (bit 3 = sign)
+ *   scales  out, [M, K/32] E8M0 bytes. With K % 128 == 0 the four bytes of a
+ *           (row, 128-column group) form one 32-bit word, so moe_route_permute gathers
+ *           them as its fp32 `xs` ([M, K/128] words) into the group-major layout that
+ *           mxfp4_grouped_expert_gemm reads.
+ * Constraints: M >= 1, K % 32 == 0.
+ */
+int32_t mxfp4_quant_act(const void* x, int64_t M, int64_t K, uint8_t* q, uint8_t* scales,
+                        void* stream);
+
+/*
+ * fp8moe_pack_expert_bank_mxfp4 -- fp8moe_pack_expert_bank for the MXFP4-activation GEMM:
+ * the same blocks and scales, with the 16-value K chunks of every 128-group in the order
+ * the gfx950 MFMA pairs with an FP4 operand (chunk c of the MFMA's K holds logical chunk
+ * c / 2 + 4 (c % 2)). Arguments and constraints as fp8moe_pack_expert_bank.
+ */
+int32_t fp8moe_pack_expert_bank_mxfp4(const uint8_t* w, const float* w_scales, int64_t E,
+                                      int64_t N, int64_t K, uint8_t* w_packed,
+                                      float* w_scales_packed, void* stream);
+
+/*
+ * mxfp4_grouped_expert_gemm -- fp8_grouped_expert_gemm with MXFP4 activations ([P3]: FP4
+ * E2M1 activations into the grouped expert GEMM; [P1] section 1 for the rest):
+ *   y[i, n] = sum_g s_w[e, g, n] * sum_{k in g} x(a[i, k]) * q[e, n, k],
+ * x(a) = E2M1 value * 2^(its block's E8M0 byte - 127). The MFMA applies the activation
+ * block scales itself; the weight scale is folded per 128-group as in the e4m3 GEMM.
+ *
+ *   a          MXFP4 codes [rows, K/2] (mxfp4_quant_act), rows in token order when `sorted`
+ *              is given (gathered on the fly), else already grouped
+ *   a_scales   uint32 [K/128, R]: the four E8M0 bytes of (grouped row, 128-group) as one
+ *              word, group-major (moe_route_permute's xs_perm of mxfp4_quant_act's scales)
+ *   w, w_scales  from fp8moe_pack_expert_bank_mxfp4
+ *   everything else as fp8_grouped_expert_gemm (epilogues, output layouts, constraints)
+ */
+int32_t mxfp4_grouped_expert_gemm(const uint8_t* a, const uint32_t* a_scales,
+                                  const int32_t* sorted, int32_t k_route, const uint8_t* w,
+                                  const float* w_scales, const int32_t* offsets, int64_t R,
+                                  int32_t E, int64_t N, int64_t K, int32_t epilogue,
+                                  int32_t out_dtype, void* out, float* out_scales,
+                                  void* stream);
 
 /*
  * moe_unpermute_combine -- out[t, :] = sum_{j=0..k-1} weights[t, j] * y[pos[t*k+j], :]

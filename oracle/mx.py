@@ -139,3 +139,27 @@ def grouped_gemm_fp4act_rows(a_codes, a_scales, w_packed, w_scales, offsets, row
         y[m] = float(np.dot(a, w))
         b[m] = float(np.dot(np.abs(a), np.abs(w)))
     return y, b
+
+
+def moe_layer_mxfp4(x_bits, logits, w_gu, s_gu, w_dn, s_dn, k):
+    """The MoE layer with MXFP4 activations into the gate|up GEMM (DeepGEMM issue 338's
+    FP4 dispatch); every other stage as ``moe.moe_layer``: routing, the SwiGLU and its
+    e4m3 requantisation, the down GEMM, the combine."""
+    from .moe import combine, grouped_gemm, swiglu_quant
+    from .numeric import round_bf16
+    from .route import group_pairs, permute_rows, topk_route
+
+    E = w_gu.shape[0]
+    xq, xs = quant_mxfp4_bf16(x_bits)
+    ids, w = topk_route(logits, k)
+    offsets, sorted_, pos = group_pairs(ids, E)
+    aq = permute_rows(xq, sorted_, k)
+    as_ = permute_rows(xs, sorted_, k)
+    y_gu = grouped_gemm_fp4act(aq, as_, w_gu, s_gu, offsets)
+    hq, hs, h = swiglu_quant(y_gu)
+    y_dn = grouped_gemm(hq, hs, w_dn, s_dn, offsets)
+    y_dn_bf16 = round_bf16(y_dn)
+    out = combine(y_dn_bf16, pos, w)
+    return dict(xq=xq, xs=xs, ids=ids, w=w, offsets=offsets, sorted=sorted_, pos=pos,
+                aq=aq, as_=as_, y_gu=y_gu, h=h, hq=hq, hs=hs, y_dn=y_dn,
+                y_dn_bf16=y_dn_bf16, out=out)

@@ -40,7 +40,8 @@ def test_header_declares_the_five_entry_points():
         assert name in fns
     assert "fp8moe_workspace_bytes" in fns and "fp8moe_status_str" in fns
     for name in ["fp8moe_rmsnorm", "fp8moe_bf16_gemm", "fp8moe_causal_attention",
-                 "fp8_dense_gemm_rowwise", "fp8_block_gemm", "fp8_quant_weight_block128"]:
+                 "fp8_dense_gemm_rowwise", "fp8_block_gemm", "fp8_quant_weight_block128",
+                 "mxfp4_quant_act", "fp8moe_pack_expert_bank_mxfp4", "mxfp4_grouped_expert_gemm"]:
         assert name in fns
 
 
@@ -48,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
     raw = ctypes.CDLL(LIB)
     for name in declared_functions():
         assert hasattr(raw, name), name
-    assert lib.fp8moe_abi_version() == 4
+    assert lib.fp8moe_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -201,6 +202,24 @@ def test_quant_weight_block128_validation(lib):
     assert f(P, 64, 100, P, P, None) == SHAPE
     assert f(P, 128 * 65536, 128, P, P, None) == SHAPE  # row-block grid limit
     assert f(P, 64, 128, P, U, None) == ALIGN
+
+
+def test_mxfp4_validation(lib):
+    q = lib.mxfp4_quant_act
+    assert q(None, 4, 64, P, P, None) == NULL
+    assert q(P, 0, 64, P, P, None) == SHAPE
+    assert q(P, 4, 48, P, P, None) == SHAPE  # K % 32
+    assert q(P, 4, 64, P, U, None) == ALIGN
+    pk = lib.fp8moe_pack_expert_bank_mxfp4
+    assert pk(None, P, 4, 64, 256, P, P, None) == NULL
+    assert pk(P, P, 4, 24, 256, P, P, None) == SHAPE
+    assert pk(P, P, 4, 64, 100, P, P, None) == SHAPE
+    g = lib.mxfp4_grouped_expert_gemm
+    assert g(P, P, None, 1, P, P, P, 256, 8, 512, 256, 2, 0, P, P, None) == UNSUP
+    assert g(None, P, None, 1, P, P, P, 256, 8, 512, 256, 0, 0, P, P, None) == NULL
+    assert g(P, P, None, 1, P, P, P, 256, 8, 512, 100, 0, 0, P, P, None) == SHAPE
+    assert g(P, P, None, 1, P, P, P, 256, 8, 512, 256, 0, 0, U, P, None) == ALIGN
+    assert g(P, P, None, 1, P, P, P, 0, 8, 512, 256, 0, 0, P, P, None) == OK
 
 
 def test_combine_validation(lib):

@@ -100,3 +100,36 @@ def test_layer_repeat_runs_identical():
         a, b = host(st1[n]), host(st2[n])
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), n
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg,T", [("moe_tiny", None), ("moe_prefill", 16), ("moe_prefill", None)])
+def test_layer_mxfp4_activations(cfg, T):
+    """The layer with MXFP4 activations into gate|up (DeepGEMM issue 338's FP4 dispatch):
+    codes, scale bytes and routing bit-exact; the down GEMM and the combine on the GPU's own
+    intermediates within their bounds; the output against the oracle's MXFP4 layer."""
+    import fp8_moe_prefill_amd as f
+    from oracle.mx import moe_layer_mxfp4, unpack_fp4
+    c = CONFIGS[cfg]
+    inp = moe_inputs(c, T=T)
+    bank = f.ExpertBank.from_host(inp, "cuda:0", act="mxfp4")
+    out, st = f.moe_layer(dev(inp["x"]), dev(inp["logits"]), bank, c.k, keep=True)
+    torch.cuda.synchronize()
+    ref = moe_layer_mxfp4(inp["x"], inp["logits"], inp["w_gu"], inp["s_gu"], inp["w_dn"],
+                          inp["s_dn"], c.k)
+    assert_bytes_equal(unpack_fp4(host(st["xq"])), ref["xq"], "codes")
+    assert_bytes_equal(host(st["xs"]), ref["xs"], "E8M0 scales")
+    for key in ("ids", "offsets", "sorted", "pos"):
+        assert_bytes_equal(host(st[key]), ref[key], key)
+    hq, hs = host(st["hq"]), np.ascontiguousarray(host(st["hs"]).T)
+    if cfg == "moe_tiny":
+        y_ref, b = grouped_gemm(hq, hs, inp["w_dn"], inp["s_dn"], ref["offsets"], with_bound=True)
+        y = bf16_values(st["y"])
+        check_close(y, y_ref, gemm_bound(b) + half_ulp_bf16(y_ref), "down (bf16 out)")
+    else:
+        rng = np.random.default_rng(21)
+        rows = rng.integers(0, hq.shape[0], 2000)
+        cols = rng.integers(0, c.H, 2000)
+        y_ref, b = grouped_gemm_rows(hq, hs, inp["w_dn"], inp["s_dn"], ref["offsets"], rows, cols)
+        y = bf16_values(st["y"])[rows, cols]
+        check_close(y, y_ref, gemm_bound(b) + half_ulp_bf16(y_ref), "down sampled")
+    assert cosine(bf16_values(out), ref["out"]) > 0.999

@@ -112,3 +112,31 @@ def test_grouped_gemm_equals_e4m3_path_on_shared_values():
     y_hi = grouped_gemm_fp4act(codes, sc2, w_packed, w_scales, offsets) - grouped_gemm_fp4act(codes2, sc2, w_packed, w_scales, offsets)
     y_lo = grouped_gemm_fp4act(codes, sc, w_packed, w_scales, offsets) - grouped_gemm_fp4act(codes2, sc, w_packed, w_scales, offsets)
     assert np.allclose(y_hi, 8 * y_lo, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_with_exactly_representable_activations():
+    """Activations that MXFP4 holds exactly (E2M1 values times one power of two per
+    32-block, each block's maximum 4 or 6 times it): the codes decode back to the input
+    bit for bit, the gate|up GEMM equals the routed input times the dequantised bank (no
+    quantisation at all), and the routing equals the e4m3 layer's."""
+    from oracle.moe import dequant_bank, moe_layer
+    from oracle.mx import moe_layer_mxfp4
+    from synth import CONFIGS, bf16_bits_from_f32, moe_inputs
+    c = CONFIGS["moe_tiny"]
+    inp = moe_inputs(c)
+    rng = np.random.default_rng(3)
+    vals = np.array(TABLE)[rng.integers(0, 8, (c.T, c.H))] * rng.choice([-1, 1], (c.T, c.H))
+    vals[:, ::32] = rng.choice([4.0, 6.0], (c.T, c.H // 32))
+    pw = np.exp2(rng.integers(-6, 7, (c.T, c.H // 32))).repeat(32, axis=1)
+    x = (vals * pw).astype(np.float32)
+    xb = bf16_bits_from_f32(x)
+    a = moe_layer_mxfp4(xb, inp["logits"], inp["w_gu"], inp["s_gu"], inp["w_dn"], inp["s_dn"], c.k)
+    assert np.array_equal(dequant_mxfp4(a["xq"], a["xs"]), x.astype(np.float64))
+    xp = x.astype(np.float64)[a["sorted"] // c.k]
+    for e in range(c.E):
+        lo, hi = a["offsets"][e], a["offsets"][e + 1]
+        want = xp[lo:hi] @ dequant_bank(inp["w_gu"][e], inp["s_gu"][e]).T
+        assert np.allclose(a["y_gu"][lo:hi], want, rtol=1e-12, atol=1e-9)
+    b = moe_layer(xb, inp["logits"], inp["w_gu"], inp["s_gu"], inp["w_dn"], inp["s_dn"], c.k)
+    for key in ("ids", "offsets", "sorted", "pos"):
+        assert np.array_equal(a[key], b[key])
