@@ -31,16 +31,16 @@ SIGNATURES = {
     "fp8moe_abi_version": (_i32, []),
     "fp8moe_status_str": (ctypes.c_char_p, [_i32]),
     "fp8moe_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64]),
-    "fp8_quant_act": (_i32, [_c_void_p, _i64, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _sz,
-                             _c_void_p]),
+    "fp8_quant_act": (_i32, [_c_void_p, _i64, _i64, _i32, _c_void_p, _c_void_p, _c_void_p,
+                             _c_void_p, _sz, _c_void_p]),
     "moe_route_permute": (_i32, [_c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
-                                 _c_void_p, _c_void_p, _sz, _c_void_p]),
+                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
     "fp8moe_pack_expert_bank": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p,
                                        _c_void_p, _c_void_p]),
-    "fp8_grouped_expert_gemm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
-                                       _c_void_p, _c_void_p, _i64, _i32, _i64, _i64, _i32, _i32,
-                                       _c_void_p, _c_void_p, _c_void_p]),
+    "fp8_grouped_expert_gemm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
+                                       _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i64, _i64,
+                                       _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "fp8_dense_gemm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i32,
                               _c_void_p, _c_void_p]),
     "fp8_dense_gemm_rowwise": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64,
@@ -54,7 +54,7 @@ SIGNATURES = {
                                              _c_void_p, _c_void_p]),
     "mxfp4_grouped_expert_gemm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
                                          _c_void_p, _c_void_p, _i64, _i32, _i64, _i64, _i32,
-                                         _i32, _c_void_p, _c_void_p, _c_void_p]),
+                                         _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "moe_unpermute_combine": (_i32, [_c_void_p, _i32, _c_void_p, _c_void_p, _i64, _i32, _i64,
                                      _i32, _c_void_p, _c_void_p]),
     "fp8moe_rmsnorm": (_i32, [_c_void_p, _c_void_p, _i64, _i64, ctypes.c_double, _c_void_p,
@@ -139,9 +139,10 @@ def abi_version() -> int:
 
 
 def fp8_quant_act(x: torch.Tensor, group: int = GROUP, q=None, scales=None, ws=None,
-                  stream=None):
+                  stream=None, sums=None, with_sums: bool = False):
     """bf16 [M, K] -> (e4m3 codes uint8 [M, K], fp32 scales: [M, K/128] for group=128,
-    block[4] for group=0, [M] for group=QUANT_ROW)."""
+    block[4] for group=0, [M] for group=QUANT_ROW). With ``with_sums`` (group=128) also the
+    code sums fp32 [M, K/128]: (q, scales, sums)."""
     _dev(x, "x", torch.bfloat16)
     M, K = x.shape
     if q is None:
@@ -149,19 +150,23 @@ def fp8_quant_act(x: torch.Tensor, group: int = GROUP, q=None, scales=None, ws=N
     if scales is None:
         shape = (M, K // GROUP) if group == GROUP else (M,) if group == QUANT_ROW else (4,)
         scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    if with_sums and sums is None:
+        sums = torch.empty((M, K // GROUP), dtype=torch.float32, device=x.device)
     nbytes = workspace_bytes(OP_QUANT_ACT, M, K, group)
     wsb = _workspace(nbytes, x.device, ws)
     _check("fp8_quant_act", _lib.fp8_quant_act(_ptr(x), M, K, group, _ptr(q), _ptr(scales),
-                                               _ptr(wsb), nbytes, _stream(stream)))
-    return q, scales
+                                               _ptr(sums), _ptr(wsb), nbytes, _stream(stream)))
+    return (q, scales, sums) if sums is not None else (q, scales)
 
 
 def moe_route_permute(logits: torch.Tensor, k: int, xq=None, xs=None, out=None, ws=None,
-                      stream=None) -> dict:
-    """fp32 logits [T, E] -> dict(ids, weights, offsets, sorted, pos[, xq_perm][, xs_perm]).
+                      stream=None, xsum=None) -> dict:
+    """fp32 logits [T, E] -> dict(ids, weights, offsets, sorted, pos[, xq_perm][, xs_perm]
+    [, xsum_perm]).
 
     ``xq`` (e4m3 [T, H]) is gathered into xq_perm [T*k, H]; ``xs`` (fp32 [T, H/128]) into
-    xs_perm [H/128, T*k], group-major. Either may be given alone."""
+    xs_perm [H/128, T*k], group-major; ``xsum`` (the code sums, fp32 [T, H/128], only with
+    ``xs``) into xsum_perm of the same layout as xs_perm. xq and xs may be given alone."""
     _dev(logits, "logits", torch.float32)
     T, E = logits.shape
     dev = logits.device
@@ -185,16 +190,23 @@ def moe_route_permute(logits: torch.Tensor, k: int, xq=None, xs=None, out=None, 
         _dev(xs, "xs", torch.float32)
         H = xs.shape[1] * GROUP
         xs_perm = buf("xs_perm", (H // GROUP, T * k), torch.float32)
+    xsum_perm = None
+    if xsum is not None:
+        _dev(xsum, "xsum", torch.float32)
+        xsum_perm = buf("xsum_perm", (H // GROUP, T * k), torch.float32)
     nbytes = workspace_bytes(OP_ROUTE_PERMUTE, T, E, k)
     wsb = _workspace(nbytes, dev, ws)
     _check("moe_route_permute", _lib.moe_route_permute(
         _ptr(logits), T, E, k, _ptr(ids), _ptr(w), _ptr(offsets), _ptr(sorted_), _ptr(pos),
-        _ptr(xq), _ptr(xs), H, _ptr(xq_perm), _ptr(xs_perm), _ptr(wsb), nbytes, _stream(stream)))
+        _ptr(xq), _ptr(xs), H, _ptr(xq_perm), _ptr(xs_perm), _ptr(xsum), _ptr(xsum_perm),
+        _ptr(wsb), nbytes, _stream(stream)))
     r = dict(ids=ids, weights=w, offsets=offsets, sorted=sorted_, pos=pos)
     if xq is not None:
         r.update(xq_perm=xq_perm)
     if xs is not None:
         r.update(xs_perm=xs_perm)
+    if xsum is not None:
+        r.update(xsum_perm=xsum_perm)
     return r
 
 
@@ -220,27 +232,32 @@ def pack_expert_bank(w: torch.Tensor, w_scales: torch.Tensor, out=None, stream=N
 
 def fp8_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=EPI_STORE,
                             out_dtype=torch.float32, sorted_=None, k_route: int = 1, out=None,
-                            out_scales=None, stream=None):
+                            out_scales=None, stream=None, a_sums=None, out_sums=None,
+                            with_sums: bool = False):
     """Grouped expert GEMM on a bank from ``pack_expert_bank`` (w [E, N, K/2] bytes,
     w_scales [E, K/128, N]); a_scales are group-major [K/128, R]. STORE -> out [R, N];
-    SWIGLU_QUANT -> (codes [R, N/2], scales [N/256, R], group-major)."""
+    SWIGLU_QUANT -> (codes [R, N/2], scales [N/256, R], group-major), plus the code sums
+    [N/256, R] of the quantised output when ``out_sums`` or ``with_sums`` is given.
+    ``a_sums`` (optional, group-major [K/128, R]) are the per-(row, K group) sums of the
+    decoded activation codes; without them the kernel forms them itself."""
     return _grouped(a, a_scales, w, w_scales, offsets, R, epilogue, out_dtype, sorted_, k_route,
-                    out, out_scales, stream, False)
+                    out, out_scales, stream, False, a_sums, out_sums, with_sums)
 
 
 def mxfp4_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=EPI_STORE,
                               out_dtype=torch.float32, sorted_=None, k_route: int = 1,
-                              out=None, out_scales=None, stream=None):
+                              out=None, out_scales=None, stream=None, out_sums=None,
+                              with_sums: bool = False):
     """The grouped expert GEMM with MXFP4 activations: a = codes [rows, K/2] from
     ``mxfp4_quant_act``, a_scales = [K/128, R] 32-bit words (four E8M0 bytes each,
     group-major: ``moe_route_permute``'s xs_perm of the quantiser's scales viewed as
     [rows, K/128] words); the bank from ``pack_expert_bank(..., mxfp4=True)``."""
     return _grouped(a, a_scales, w, w_scales, offsets, R, epilogue, out_dtype, sorted_, k_route,
-                    out, out_scales, stream, True)
+                    out, out_scales, stream, True, None, out_sums, with_sums)
 
 
 def _grouped(a, a_scales, w, w_scales, offsets, R, epilogue, out_dtype, sorted_, k_route, out,
-             out_scales, stream, a_fp4):
+             out_scales, stream, a_fp4, a_sums, out_sums, with_sums):
     _dev(a, "a", torch.uint8)
     _dev(a_scales, "a_scales")
     if a_scales.element_size() != 4:
@@ -267,16 +284,33 @@ def _grouped(a, a_scales, w, w_scales, offsets, R, epilogue, out_dtype, sorted_,
             out = torch.empty((R, I), dtype=torch.uint8, device=dev)
         if out_scales is None:
             out_scales = torch.empty((I // GROUP, R), dtype=torch.float32, device=dev)
+        if with_sums and out_sums is None:
+            out_sums = torch.empty((I // GROUP, R), dtype=torch.float32, device=dev)
         dt = DTYPE_F32
     else:
+        if out_sums is not None or with_sums:
+            raise ValueError("output code sums come only with the SwiGLU epilogue")
         if out is None:
             out = torch.empty((R, N), dtype=out_dtype, device=dev)
         dt = _dt(out.dtype)
-    name = "mxfp4_grouped_expert_gemm" if a_fp4 else "fp8_grouped_expert_gemm"
-    _check(name, getattr(_lib, name)(
-        _ptr(a), _ptr(a_scales), _ptr(sorted_), k_route, _ptr(w), _ptr(w_scales), _ptr(offsets),
-        R, E, N, K, epilogue, dt, _ptr(out), _ptr(out_scales), _stream(stream)))
-    return (out, out_scales) if epilogue == EPI_SWIGLU_QUANT else out
+    if a_sums is not None:
+        _dev(a_sums, "a_sums", torch.float32)
+        if tuple(a_sums.shape) != (K // GROUP, R):
+            raise ValueError(f"a_sums must be [K/128, R] = {(K // GROUP, R)}, "
+                             f"got {tuple(a_sums.shape)}")
+    if a_fp4:
+        _check("mxfp4_grouped_expert_gemm", _lib.mxfp4_grouped_expert_gemm(
+            _ptr(a), _ptr(a_scales), _ptr(sorted_), k_route, _ptr(w), _ptr(w_scales),
+            _ptr(offsets), R, E, N, K, epilogue, dt, _ptr(out), _ptr(out_scales),
+            _ptr(out_sums), _stream(stream)))
+    else:
+        _check("fp8_grouped_expert_gemm", _lib.fp8_grouped_expert_gemm(
+            _ptr(a), _ptr(a_scales), _ptr(a_sums), _ptr(sorted_), k_route, _ptr(w),
+            _ptr(w_scales), _ptr(offsets), R, E, N, K, epilogue, dt, _ptr(out),
+            _ptr(out_scales), _ptr(out_sums), _stream(stream)))
+    if epilogue != EPI_SWIGLU_QUANT:
+        return out
+    return (out, out_scales, out_sums) if out_sums is not None else (out, out_scales)
 
 
 def mxfp4_quant_act(x: torch.Tensor, q=None, scales=None, stream=None):

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 5;
+constexpr int32_t kAbiVersion = 6;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 constexpr int64_t kMaxGroupedK = 16384;
@@ -66,10 +66,12 @@ size_t fp8moe_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c) {
 }
 
 int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int32_t group, uint8_t* q,
-                      float* scales, void* ws, size_t ws_bytes, void* stream) {
+                      float* scales, float* sums, void* ws, size_t ws_bytes, void* stream) {
   if (!x || !q || !scales) return FP8MOE_ERR_NULL;
   if (group != 0 && group != FP8MOE_GROUP && group != FP8MOE_QUANT_ROW)
     return FP8MOE_ERR_UNSUPPORTED;
+  if (sums && group != FP8MOE_GROUP) return FP8MOE_ERR_UNSUPPORTED;  // group sums only
+  if (sums && !aligned16(sums)) return FP8MOE_ERR_ALIGN;
   if (M < 1 || K < 1 || M > (int64_t(1) << 40) / K) return FP8MOE_ERR_SHAPE;
   if (group == FP8MOE_GROUP && K % FP8MOE_GROUP != 0) return FP8MOE_ERR_SHAPE;
   if (group == FP8MOE_QUANT_ROW && (K % 8 != 0 || M >= (int64_t(1) << 31)))
@@ -81,7 +83,8 @@ int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int32_t group, uint8_
   if (need > 0 && !aligned16(ws)) return FP8MOE_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  if (group == FP8MOE_GROUP) return launch_status(fp8moe::launch_quant_group(xb, M, K, q, scales, st));
+  if (group == FP8MOE_GROUP)
+    return launch_status(fp8moe::launch_quant_group(xb, M, K, q, scales, sums, st));
   if (group == FP8MOE_QUANT_ROW)
     return launch_status(fp8moe::launch_quant_row(xb, M, K, q, scales, st));
   return launch_status(
@@ -91,12 +94,17 @@ int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int32_t group, uint8_
 int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* ids,
                           float* weights, int32_t* offsets, int32_t* sorted, int32_t* pos,
                           const uint8_t* xq, const float* xs, int64_t H, uint8_t* xq_perm,
-                          float* xs_perm, void* ws, size_t ws_bytes, void* stream) {
+                          float* xs_perm, const float* xsum, float* xsum_perm, void* ws,
+                          size_t ws_bytes, void* stream) {
   if (!logits || !ids || !weights || !offsets || !sorted || !pos || !ws) return FP8MOE_ERR_NULL;
   // the row gather (xq -> xq_perm) and the scale gather (xs -> xs_perm) are independent
-  // options, each all-or-nothing
+  // options, each all-or-nothing; the code-sum gather (xsum -> xsum_perm) rides the scale
+  // gather
   if ((xq != nullptr) != (xq_perm != nullptr)) return FP8MOE_ERR_NULL;
   if ((xs != nullptr) != (xs_perm != nullptr)) return FP8MOE_ERR_NULL;
+  if ((xsum != nullptr) != (xsum_perm != nullptr)) return FP8MOE_ERR_NULL;
+  if (xsum && !xs) return FP8MOE_ERR_NULL;
+  if (xsum && (!aligned16(xsum) || !aligned16(xsum_perm))) return FP8MOE_ERR_ALIGN;
   const bool rows = xq != nullptr, scales = xs != nullptr;
   if (T < 1 || E < 1 || E > kMaxE || k < 1 || k > E || k > kMaxK) return FP8MOE_ERR_SHAPE;
   if (T * (int64_t)k >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
@@ -108,8 +116,8 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, 
   if (scales && (!aligned16(xs) || !aligned16(xs_perm))) return FP8MOE_ERR_ALIGN;
   if (ws_bytes < fp8moe::route_workspace_bytes(T, E)) return FP8MOE_ERR_WORKSPACE;
   return launch_status(fp8moe::launch_route_permute(
-      logits, T, E, k, ids, weights, offsets, sorted, pos, xq, xs, H, xq_perm, xs_perm, ws,
-      static_cast<hipStream_t>(stream)));
+      logits, T, E, k, ids, weights, offsets, sorted, pos, xq, xs, H, xq_perm, xs_perm, xsum,
+      xsum_perm, ws, static_cast<hipStream_t>(stream)));
 }
 
 namespace {
@@ -141,11 +149,11 @@ int32_t fp8moe_pack_expert_bank_mxfp4(const uint8_t* w, const float* w_scales, i
 }
 
 namespace {
-int32_t grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,
-                     int32_t k_route, const uint8_t* w, const float* w_scales,
-                     const int32_t* offsets, int64_t R, int32_t E, int64_t N, int64_t K,
-                     int32_t epilogue, int32_t out_dtype, void* out, float* out_scales,
-                     void* stream, bool a_fp4) {
+int32_t grouped_gemm(const uint8_t* a, const float* a_scales, const float* a_sums,
+                     const int32_t* sorted, int32_t k_route, const uint8_t* w,
+                     const float* w_scales, const int32_t* offsets, int64_t R, int32_t E,
+                     int64_t N, int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
+                     float* out_scales, float* out_sums, void* stream, bool a_fp4) {
   if (epilogue != FP8MOE_EPI_STORE && epilogue != FP8MOE_EPI_SWIGLU_QUANT)
     return FP8MOE_ERR_UNSUPPORTED;
   if (epilogue == FP8MOE_EPI_STORE && out_dtype != FP8MOE_DTYPE_F32 &&
@@ -168,21 +176,25 @@ int32_t grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* sor
     if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
   if ((sorted && !aligned16(sorted)) || (out_scales && !aligned16(out_scales)))
     return FP8MOE_ERR_ALIGN;
+  if ((a_sums && !aligned16(a_sums)) || (out_sums && !aligned16(out_sums)))
+    return FP8MOE_ERR_ALIGN;
+  if (out_sums && epilogue != FP8MOE_EPI_SWIGLU_QUANT) return FP8MOE_ERR_UNSUPPORTED;
   if (R == 0) return FP8MOE_OK;
-  return launch_status(fp8moe::launch_grouped_gemm(a, a_scales, sorted, k_route, w, w_scales,
-                                                   offsets, R, E, N, K, epilogue, out_dtype,
-                                                   out, out_scales,
+  return launch_status(fp8moe::launch_grouped_gemm(a, a_scales, a_sums, sorted, k_route, w,
+                                                   w_scales, offsets, R, E, N, K, epilogue,
+                                                   out_dtype, out, out_scales, out_sums,
                                                    static_cast<hipStream_t>(stream), a_fp4));
 }
 }  // namespace
 
-int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,
-                                int32_t k_route, const uint8_t* w, const float* w_scales,
-                                const int32_t* offsets, int64_t R, int32_t E, int64_t N,
-                                int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
-                                float* out_scales, void* stream) {
-  return grouped_gemm(a, a_scales, sorted, k_route, w, w_scales, offsets, R, E, N, K, epilogue,
-                      out_dtype, out, out_scales, stream, false);
+int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales, const float* a_sums,
+                                const int32_t* sorted, int32_t k_route, const uint8_t* w,
+                                const float* w_scales, const int32_t* offsets, int64_t R,
+                                int32_t E, int64_t N, int64_t K, int32_t epilogue,
+                                int32_t out_dtype, void* out, float* out_scales,
+                                float* out_sums, void* stream) {
+  return grouped_gemm(a, a_scales, a_sums, sorted, k_route, w, w_scales, offsets, R, E, N, K,
+                      epilogue, out_dtype, out, out_scales, out_sums, stream, false);
 }
 
 int32_t mxfp4_grouped_expert_gemm(const uint8_t* a, const uint32_t* a_scales,
@@ -190,9 +202,10 @@ int32_t mxfp4_grouped_expert_gemm(const uint8_t* a, const uint32_t* a_scales,
                                   const float* w_scales, const int32_t* offsets, int64_t R,
                                   int32_t E, int64_t N, int64_t K, int32_t epilogue,
                                   int32_t out_dtype, void* out, float* out_scales,
-                                  void* stream) {
-  return grouped_gemm(a, reinterpret_cast<const float*>(a_scales), sorted, k_route, w, w_scales,
-                      offsets, R, E, N, K, epilogue, out_dtype, out, out_scales, stream, true);
+                                  float* out_sums, void* stream) {
+  return grouped_gemm(a, reinterpret_cast<const float*>(a_scales), nullptr, sorted, k_route, w,
+                      w_scales, offsets, R, E, N, K, epilogue, out_dtype, out, out_scales,
+                      out_sums, stream, true);
 }
 
 int32_t mxfp4_quant_act(const void* x, int64_t M, int64_t K, uint8_t* q, uint8_t* scales,

@@ -86,6 +86,35 @@ __device__ __forceinline__ float max16(float v) {
   return v;
 }
 
+// sum over the 16 lanes of a row, every lane ends with the sum (a fixed association order
+// for each lane, so the value a given lane holds is deterministic)
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_row<0x121>(v);  // row_ror:1
+  v += dpp_row<0x122>(v);  // row_ror:2
+  v += dpp_row<0x124>(v);  // row_ror:4
+  v += dpp_row<0x128>(v);  // row_ror:8
+  return v;
+}
+
+// sum over each aligned group of 8 lanes, every lane of the group ends with the sum (all
+// lanes of the row must be active)
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_row<0xB1>(v);   // quad_perm [1,0,3,2]: the lane beside
+  v += dpp_row<0x4E>(v);   // quad_perm [2,3,0,1]: the other pair of the quad
+  v += dpp_row<0x141>(v);  // row_half_mirror: the other quad of the 8
+  return v;
+}
+
+// sum of the values of 8 e4m3 codes (two words), in a fixed order
+__device__ __forceinline__ float e4m3_sum8(uint32_t lo, uint32_t hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+  const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+  return ((a.x + a.y) + (b.x + b.y)) + ((c.x + c.y) + (d.x + d.y));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;

@@ -182,12 +182,17 @@ struct TileDesc {
 // consecutive K, four per row and group as one 32-bit word in As), and the bank is packed
 // in the matching K order (pack_bank with the FP4 layout). The MFMA applies the
 // activation scales itself, so the fold is one FMA by the weight scale.
-template <int EPI, bool OUT_BF16, bool AF4 = false>
+//
+// SUMS: the per-(row, K group) sums of the decoded A codes come in Asum (group-major like
+// As) and seed the accumulators directly; otherwise the kernel forms them on the matrix
+// core from the staged tile.
+template <int EPI, bool OUT_BF16, bool AF4, bool SUMS>
 __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ As,
+    const uint8_t* __restrict__ A, const float* __restrict__ As, const float* __restrict__ Asum,
     const int32_t* __restrict__ sorted, int k_route, int a_rows, const uint8_t* __restrict__ W,
     const float* __restrict__ Ws, const int32_t* __restrict__ offsets, int R, int E, int N,
-    int K, int NT, void* __restrict__ out, float* __restrict__ out_scales) {
+    int K, int NT, void* __restrict__ out, float* __restrict__ out_scales,
+    float* __restrict__ out_sums) {
   __shared__ Stage ring[2];
   __shared__ int s_mstart[kMaxExperts + 1];  // m-tiles before expert e
   __shared__ int s_tmp[NW];
@@ -388,6 +393,8 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
     for (int s = 0; s < 4; ++s) dma16(w_exp + b_blk[s] + gd * kBlockBytes, lane16, sb + s * 1024);
     dma4(ws_exp + (int64_t)gd * N, ws_off32, st.ws + wv * WCOLS);
     if (lane < RPW) dma4(As + (int64_t)gd * R, as_off32, st.as + wv * RPW);
+    // given code sums replace the in-kernel row sums: they land where the seeds go
+    if (SUMS && lane < RPW) dma4(Asum + (int64_t)gd * R, as_off32, st.ra + wv * RPW);
   };
 
   // sum of this wave's 16-row tile of the A tile of stage st -> st.ra as -sum/64, the
@@ -400,6 +407,10 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
     return (int)(__float_as_uint(st.as[r]) >> (8 * q));
   };
   auto row_sums = [&](Stage& st) {
+    if constexpr (SUMS) {  // this wave's rows' sums arrived with its own loads: sum -> seed
+      if (lane < RPW) st.ra[wv * RPW + lane] *= -0.015625f;
+      return;
+    }
 #pragma unroll
     for (int h = 0; h < RPW / 16; ++h) {
       const int r0 = wv * RPW + h * 16;
@@ -610,11 +621,17 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
       }
       lds_barrier();
       uint8_t* o8 = reinterpret_cast<uint8_t*>(out);
-      for (int i = tid; i < BM * 8; i += NT_THREADS) {
+      static_assert(BM * 8 % NT_THREADS == 0, "every lane takes part in every pass (sum8)");
+      for (int i = tid; i < BM * 8; i += NT_THREADS) {  // the 8 lanes i .. i + 7 share a row
         const int row = i >> 3, ch = i & 7;
+        const uint4 c = *reinterpret_cast<const uint4*>(&s_codes[row * 128 + ch * 16]);
         if (row < rows && hcol < I)
-          *reinterpret_cast<uint4*>(&o8[(int64_t)(row_begin + row) * I + hcol + ch * 16]) =
-              *reinterpret_cast<const uint4*>(&s_codes[row * 128 + ch * 16]);
+          *reinterpret_cast<uint4*>(&o8[(int64_t)(row_begin + row) * I + hcol + ch * 16]) = c;
+        if (out_sums) {  // the row's 128 code values summed (the down GEMM's offset seed)
+          const float v = sum8(e4m3_sum8(c.x, c.y) + e4m3_sum8(c.z, c.w));
+          if (ch == 0 && row < rows && hcol < I)
+            out_sums[(int64_t)(hcol / kGroup) * R + row_begin + row] = v;
+        }
       }
       lds_barrier();
     }
@@ -670,12 +687,12 @@ int cu_count() {
 }  // namespace
 
 namespace {
-template <bool AF4>
-hipError_t launch_grouped(const uint8_t* a, const float* a_scales, const int32_t* sorted,
-                          int32_t k_route, const uint8_t* w, const float* w_scales,
-                          const int32_t* offsets, int64_t R, int32_t E, int64_t N, int64_t K,
-                          int32_t epilogue, int32_t out_dtype, void* out, float* out_scales,
-                          hipStream_t st) {
+template <bool AF4, bool SUMS>
+hipError_t launch_grouped(const uint8_t* a, const float* a_scales, const float* a_sums,
+                          const int32_t* sorted, int32_t k_route, const uint8_t* w,
+                          const float* w_scales, const int32_t* offsets, int64_t R, int32_t E,
+                          int64_t N, int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
+                          float* out_scales, float* out_sums, hipStream_t st) {
   if (R == 0) return hipSuccess;
   const int64_t mtiles = (R + BM - 1) / BM + E;  // bound on the m-tiles over all experts
   // SwiGLU: a tile covers 128 h columns (gate and up); otherwise 256 output columns
@@ -686,31 +703,38 @@ hipError_t launch_grouped(const uint8_t* a, const float* a_scales, const int32_t
   const int a_rows = (int)(sorted ? R / k_route : R);
   dim3 g((uint32_t)grid), block(NT_THREADS);
   if (epilogue == FP8MOE_EPI_SWIGLU_QUANT)
-    grouped_gemm_kernel<FP8MOE_EPI_SWIGLU_QUANT, false, AF4><<<g, block, 0, st>>>(
-        a, a_scales, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N, (int)K,
-        NT, out, out_scales);
+    grouped_gemm_kernel<FP8MOE_EPI_SWIGLU_QUANT, false, AF4, SUMS><<<g, block, 0, st>>>(
+        a, a_scales, a_sums, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N,
+        (int)K, NT, out, out_scales, out_sums);
   else if (out_dtype == FP8MOE_DTYPE_BF16)
-    grouped_gemm_kernel<FP8MOE_EPI_STORE, true, AF4><<<g, block, 0, st>>>(
-        a, a_scales, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N, (int)K,
-        NT, out, nullptr);
+    grouped_gemm_kernel<FP8MOE_EPI_STORE, true, AF4, SUMS><<<g, block, 0, st>>>(
+        a, a_scales, a_sums, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N,
+        (int)K, NT, out, nullptr, nullptr);
   else
-    grouped_gemm_kernel<FP8MOE_EPI_STORE, false, AF4><<<g, block, 0, st>>>(
-        a, a_scales, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N, (int)K,
-        NT, out, nullptr);
+    grouped_gemm_kernel<FP8MOE_EPI_STORE, false, AF4, SUMS><<<g, block, 0, st>>>(
+        a, a_scales, a_sums, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N,
+        (int)K, NT, out, nullptr, nullptr);
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,
-                               int32_t k_route, const uint8_t* w, const float* w_scales,
-                               const int32_t* offsets, int64_t R, int32_t E, int64_t N,
-                               int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
-                               float* out_scales, hipStream_t st, bool a_fp4) {
+hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const float* a_sums,
+                               const int32_t* sorted, int32_t k_route, const uint8_t* w,
+                               const float* w_scales, const int32_t* offsets, int64_t R,
+                               int32_t E, int64_t N, int64_t K, int32_t epilogue,
+                               int32_t out_dtype, void* out, float* out_scales,
+                               float* out_sums, hipStream_t st, bool a_fp4) {
   if (a_fp4)
-    return launch_grouped<true>(a, a_scales, sorted, k_route, w, w_scales, offsets, R, E, N, K,
-                                epilogue, out_dtype, out, out_scales, st);
-  return launch_grouped<false>(a, a_scales, sorted, k_route, w, w_scales, offsets, R, E, N, K,
-                               epilogue, out_dtype, out, out_scales, st);
+    return launch_grouped<true, false>(a, a_scales, nullptr, sorted, k_route, w, w_scales,
+                                       offsets, R, E, N, K, epilogue, out_dtype, out,
+                                       out_scales, out_sums, st);
+  if (a_sums)
+    return launch_grouped<false, true>(a, a_scales, a_sums, sorted, k_route, w, w_scales,
+                                       offsets, R, E, N, K, epilogue, out_dtype, out,
+                                       out_scales, out_sums, st);
+  return launch_grouped<false, false>(a, a_scales, nullptr, sorted, k_route, w, w_scales,
+                                      offsets, R, E, N, K, epilogue, out_dtype, out, out_scales,
+                                      out_sums, st);
 }
 
 }  // namespace fp8moe

@@ -20,7 +20,7 @@ hipError_t launch_quant_mxfp4(const uint16_t* x, int64_t M, int64_t K, uint8_t* 
 hipError_t launch_quant_row(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, float* scales,
                             hipStream_t st);
 hipError_t launch_quant_group(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
-                              float* scales, hipStream_t st);
+                              float* scales, float* sums, hipStream_t st);
 hipError_t launch_quant_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* block,
                                float* partials, hipStream_t st);
 
@@ -30,16 +30,18 @@ size_t route_workspace_bytes(int64_t T, int32_t E);
 hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
                                 int32_t* ids, float* w, int32_t* offsets, int32_t* sorted,
                                 int32_t* pos, const uint8_t* xq, const float* xs, int64_t H,
-                                uint8_t* xq_perm, float* xs_perm, void* ws, hipStream_t st);
+                                uint8_t* xq_perm, float* xs_perm, const float* xsum,
+                                float* xsum_perm, void* ws, hipStream_t st);
 
 hipError_t launch_pack_bank(const uint8_t* w, const float* w_scales, int64_t E, int64_t N,
                             int64_t K, uint8_t* w_packed, float* ws_packed, hipStream_t st, bool fp4_layout = false);
 
-hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* sorted,
-                               int32_t k_route, const uint8_t* w, const float* w_scales,
-                               const int32_t* offsets, int64_t R, int32_t E, int64_t N,
-                               int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
-                               float* out_scales, hipStream_t st, bool a_fp4 = false);
+hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const float* a_sums,
+                               const int32_t* sorted, int32_t k_route, const uint8_t* w,
+                               const float* w_scales, const int32_t* offsets, int64_t R,
+                               int32_t E, int64_t N, int64_t K, int32_t epilogue,
+                               int32_t out_dtype, void* out, float* out_scales,
+                               float* out_sums, hipStream_t st, bool a_fp4 = false);
 
 hipError_t launch_dense_gemm_rowwise(const uint8_t* a, const float* a_scales, const uint8_t* w,
                                      const float* w_scale, int64_t M, int64_t N, int64_t K,

@@ -58,7 +58,8 @@ constexpr int kChunks = 4;
 __global__ __launch_bounds__(256) void quant_group_kernel(const uint4* __restrict__ x,
                                                           int64_t nchunks,
                                                           uint2* __restrict__ q,
-                                                          float* __restrict__ scales) {
+                                                          float* __restrict__ scales,
+                                                          float* __restrict__ sums) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   uint4 u[kChunks];
@@ -75,9 +76,15 @@ __global__ __launch_bounds__(256) void quant_group_kernel(const uint4* __restric
     const float m = max16(amax8(f));
     float s, inv;
     scale_pair(m, s, inv);
+    const uint2 c = encode8(f, inv);
+    // optional: the sum of the group's code values (the grouped GEMM's offset seed)
+    const float gs = sums ? sum16(e4m3_sum8(c.x, c.y)) : 0.f;
     if (i < nchunks) {
-      q[i] = encode8(f, inv);
-      if ((threadIdx.x & 15) == 0) scales[i >> 4] = s;
+      q[i] = c;
+      if ((threadIdx.x & 15) == 0) {
+        scales[i >> 4] = s;
+        if (sums) sums[i >> 4] = gs;
+      }
     }
   }
 }
@@ -268,11 +275,11 @@ hipError_t launch_quant_row(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
 }
 
 hipError_t launch_quant_group(const uint16_t* x, int64_t M, int64_t K, uint8_t* q,
-                              float* scales, hipStream_t st) {
+                              float* scales, float* sums, hipStream_t st) {
   const int64_t nchunks = M * K / 8;
   const int64_t blocks = (nchunks + 256 * kChunks - 1) / (256 * kChunks);
   quant_group_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, st>>>(
-      reinterpret_cast<const uint4*>(x), nchunks, reinterpret_cast<uint2*>(q), scales);
+      reinterpret_cast<const uint4*>(x), nchunks, reinterpret_cast<uint2*>(q), scales, sums);
   return hipGetLastError();
 }
 

@@ -238,16 +238,21 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const int32_t* __restr
 
 // Scales of grouped row i, group-major: xs_perm[g * R + i] = xs[(sorted[i] / k) * G + g].
 // One thread per (g, i), consecutive threads on consecutive grouped rows.
+// [T, G] per-token values -> [G, R] group-major in grouped row order, for the scales and,
+// when given, the code sums in the same pass
 __global__ __launch_bounds__(256) void gather_scales_kernel(const int32_t* __restrict__ sorted,
                                                             int k, int64_t R, int64_t G,
                                                             const float* __restrict__ xs,
-                                                            float* __restrict__ xs_perm) {
+                                                            float* __restrict__ xs_perm,
+                                                            const float* __restrict__ xsum,
+                                                            float* __restrict__ xsum_perm) {
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (j < R * G) {
     const int64_t g = j / R, row = j - g * R;
+    const int64_t src = (int64_t)(sorted[row] / k) * G + g;
     // copied as 32-bit words: the same gather serves fp32 scales and packed E8M0 bytes
-    reinterpret_cast<uint32_t*>(xs_perm)[j] =
-        reinterpret_cast<const uint32_t*>(xs)[(int64_t)(sorted[row] / k) * G + g];
+    reinterpret_cast<uint32_t*>(xs_perm)[j] = reinterpret_cast<const uint32_t*>(xs)[src];
+    if (xsum) xsum_perm[j] = xsum[src];
   }
 }
 
@@ -262,7 +267,8 @@ size_t route_workspace_bytes(int64_t T, int32_t E) {
 hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
                                 int32_t* ids, float* w, int32_t* offsets, int32_t* sorted,
                                 int32_t* pos, const uint8_t* xq, const float* xs, int64_t H,
-                                uint8_t* xq_perm, float* xs_perm, void* ws, hipStream_t st) {
+                                uint8_t* xq_perm, float* xs_perm, const float* xsum,
+                                float* xsum_perm, void* ws, hipStream_t st) {
   int64_t C = (T + kRouteChunk - 1) / kRouteChunk;
   int32_t* cnt = static_cast<int32_t*>(ws);
   int32_t* tot = cnt + C * E;
@@ -290,7 +296,7 @@ hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32
   if (xs != nullptr) {
     const int64_t n = R * (H / kGroup);
     gather_scales_kernel<<<dim3((uint32_t)((n + 255) / 256)), 256, 0, st>>>(
-        sorted, k, R, H / kGroup, xs, xs_perm);
+        sorted, k, R, H / kGroup, xs, xs_perm, xsum, xsum_perm);
     e = hipGetLastError();
   }
   return e;

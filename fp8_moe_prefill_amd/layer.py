@@ -73,19 +73,26 @@ def moe_layer(x: torch.Tensor, logits: torch.Tensor, bank: ExpertBank, k: int,
     R = T * k
     if bank.act == "mxfp4":  # MXFP4 activations into gate|up (bank packed for them)
         xq, xs = _lib.mxfp4_quant_act(x, stream=stream)
+        xsum = None
         rt = _lib.moe_route_permute(logits, k, xs=xs.view(torch.float32), stream=stream)
-        gemm = _lib.mxfp4_grouped_expert_gemm
+        hq, hs, hsum = _lib.mxfp4_grouped_expert_gemm(
+            xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"], R, _lib.EPI_SWIGLU_QUANT,
+            sorted_=rt["sorted"], k_route=k, stream=stream, with_sums=True)
     else:
-        xq, xs = _lib.fp8_quant_act(x, _lib.GROUP, stream=stream)
-        rt = _lib.moe_route_permute(logits, k, xs=xs, stream=stream)
-        gemm = _lib.fp8_grouped_expert_gemm
-    hq, hs = gemm(xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"], R,
-                  _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=k, stream=stream)
+        # the quantiser also emits each (token, 128) group's code sum; the grouped GEMMs
+        # take those in place of forming them from the tiles
+        xq, xs, xsum = _lib.fp8_quant_act(x, _lib.GROUP, stream=stream, with_sums=True)
+        rt = _lib.moe_route_permute(logits, k, xs=xs, xsum=xsum, stream=stream)
+        hq, hs, hsum = _lib.fp8_grouped_expert_gemm(
+            xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"], R, _lib.EPI_SWIGLU_QUANT,
+            sorted_=rt["sorted"], k_route=k, stream=stream, a_sums=rt["xsum_perm"],
+            with_sums=True)
     y = _lib.fp8_grouped_expert_gemm(hq, hs, bank.w_dn, bank.s_dn, rt["offsets"], R,
-                                     _lib.EPI_STORE, out_dtype=torch.bfloat16, stream=stream)
+                                     _lib.EPI_STORE, out_dtype=torch.bfloat16, stream=stream,
+                                     a_sums=hsum)
     out = _lib.moe_unpermute_combine(y, rt["pos"], rt["weights"], torch.bfloat16, stream=stream)
     if keep:
-        return out, dict(xq=xq, xs=xs, hq=hq, hs=hs, y=y, **rt)
+        return out, dict(xq=xq, xs=xs, xsum=xsum, hq=hq, hs=hs, hsum=hsum, y=y, **rt)
     return out
 
 
@@ -123,16 +130,20 @@ class MoELayerRunner:
         else:
             self.xq = torch.empty((T, H), dtype=u8, device=dev)
             self.xs = torch.empty((T, H // _lib.GROUP), dtype=f32, device=dev)
+            self.xsum = torch.empty((T, H // _lib.GROUP), dtype=f32, device=dev)
         self.route = dict(ids=torch.empty((T, k), dtype=i32, device=dev),
                           weights=torch.empty((T, k), dtype=f32, device=dev),
                           offsets=torch.empty(E + 1, dtype=i32, device=dev),
                           sorted=torch.empty(R, dtype=i32, device=dev),
                           pos=torch.empty(R, dtype=i32, device=dev),
                           xs_perm=torch.empty((H // _lib.GROUP, R), dtype=f32, device=dev))
+        if act != "mxfp4":
+            self.route["xsum_perm"] = torch.empty((H // _lib.GROUP, R), dtype=f32, device=dev)
         nws = _lib.workspace_bytes(_lib.OP_ROUTE_PERMUTE, T, E, k)
         self.ws = torch.empty(max(nws, 256), dtype=u8, device=dev)
         self.hq = torch.empty((R, I), dtype=u8, device=dev)
         self.hs = torch.empty((I // _lib.GROUP, R), dtype=f32, device=dev)
+        self.hsum = torch.empty((I // _lib.GROUP, R), dtype=f32, device=dev)
         self.y = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
@@ -151,21 +162,30 @@ class MoELayerRunner:
         if mx:
             _lib.mxfp4_quant_act(x, q=self.xq, scales=self.xs, stream=stream)
         else:
-            _lib.fp8_quant_act(x, _lib.GROUP, q=self.xq, scales=self.xs, stream=stream)
+            _lib.fp8_quant_act(x, _lib.GROUP, q=self.xq, scales=self.xs, sums=self.xsum,
+                               stream=stream)
         mark("quant", 1)
         mark("route", 0)
         _lib.moe_route_permute(logits, self.k, xs=self.xs.view(torch.float32), out=rt,
-                               ws=self.ws, stream=stream)
+                               ws=self.ws, stream=stream, xsum=None if mx else self.xsum)
         mark("route", 1)
         mark("gate_up", 0)
-        gemm = _lib.mxfp4_grouped_expert_gemm if mx else _lib.fp8_grouped_expert_gemm
-        gemm(self.xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"], self.R,
-             _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k, out=self.hq,
-             out_scales=self.hs, stream=stream)
+        if mx:
+            _lib.mxfp4_grouped_expert_gemm(
+                self.xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"], self.R,
+                _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k, out=self.hq,
+                out_scales=self.hs, out_sums=self.hsum, stream=stream)
+        else:
+            _lib.fp8_grouped_expert_gemm(
+                self.xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"], self.R,
+                _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k, out=self.hq,
+                out_scales=self.hs, out_sums=self.hsum, stream=stream,
+                a_sums=rt["xsum_perm"])
         mark("gate_up", 1)
         mark("down", 0)
         _lib.fp8_grouped_expert_gemm(self.hq, self.hs, bank.w_dn, bank.s_dn, rt["offsets"],
-                                     self.R, _lib.EPI_STORE, out=self.y, stream=stream)
+                                     self.R, _lib.EPI_STORE, out=self.y, stream=stream,
+                                     a_sums=self.hsum)
         mark("down", 1)
         mark("combine", 0)
         _lib.moe_unpermute_combine(self.y, rt["pos"], rt["weights"], out=self.out,

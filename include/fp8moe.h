@@ -122,6 +122,10 @@ size_t fp8moe_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c);
  *   scales  out; group=128: fp32 [M, K/128], scale of (row m, group g) at m*K/128 + g;
  *           group=0: fp32[4] = {amax, 448/a, a/448, 0} with a = max(amax, 1e-12);
  *           FP8MOE_QUANT_ROW: fp32 [M], the scale a/448 of each row
+ *   sums    optional out (group=128 only, else NULL): fp32 [M, K/128], the sum of the
+ *           e4m3 code values of each (row, group), sum_k e4m3(q[m, k]) unscaled, in a fixed
+ *           order in fp32. fp8_grouped_expert_gemm takes them (gathered into grouped order
+ *           by moe_route_permute) in place of summing the rows itself.
  *   ws      workspace of fp8moe_workspace_bytes(FP8MOE_OP_QUANT_ACT, M, K, group)
  *           bytes (may be NULL if that is 0)
  * Arithmetic (fp32): a = max(max|x| over the group, 1e-12); s = a/448 and
@@ -131,7 +135,7 @@ size_t fp8moe_workspace_bytes(int32_t op, int64_t a, int64_t b, int64_t c);
  * M*K % 8 == 0; FP8MOE_QUANT_ROW needs K % 8 == 0 and M < 2^31.
  */
 int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int32_t group, uint8_t* q,
-                      float* scales, void* ws, size_t ws_bytes, void* stream);
+                      float* scales, float* sums, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_route_permute -- top-k routing and grouping of the routed (token, expert) pairs.
@@ -155,6 +159,8 @@ int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int32_t group, uint8_
  *   xs, xs_perm    optional pair (both NULL or both set): fp32 scales [T, H/128] gathered
  *                  into grouped order, GROUP-MAJOR: xs_perm[g * T*k + i] is the scale of
  *                  group g of grouped row i (the layout fp8_grouped_expert_gemm reads)
+ *   xsum, xsum_perm  optional pair, only with xs: fp32 code sums [T, H/128] (from
+ *                  fp8_quant_act) gathered like the scales into [H/128, T*k]
  *   H              row width of xq / xs (needed when either pair is set)
  *   ws       workspace of fp8moe_workspace_bytes(FP8MOE_OP_ROUTE_PERMUTE, T, E, k)
  * Constraints: T >= 1, 1 <= E <= 1024, 1 <= k <= min(E, 32), T*k < 2^31;
@@ -164,8 +170,8 @@ int32_t fp8_quant_act(const void* x, int64_t M, int64_t K, int32_t group, uint8_
 int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
                           int32_t* ids, float* weights, int32_t* offsets, int32_t* sorted,
                           int32_t* pos, const uint8_t* xq, const float* xs, int64_t H,
-                          uint8_t* xq_perm, float* xs_perm, void* ws, size_t ws_bytes,
-                          void* stream);
+                          uint8_t* xq_perm, float* xs_perm, const float* xsum,
+                          float* xsum_perm, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * fp8moe_pack_expert_bank -- one-time repacking of a packed-int4 expert bank (and its
@@ -212,6 +218,11 @@ int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t
  *   a          e4m3 [Ra, K]  (Ra = R without `sorted`, Ra = R / k_route with it)
  *   a_scales   fp32 [K/128, R], group-major: the scale of group g of grouped row i is
  *              a_scales[g * R + i]
+ *   a_sums     NULL, or fp32 [K/128, R] group-major: the sums of the e4m3 code values of
+ *              each (grouped row, group) (fp8_quant_act's sums, gathered, or a previous
+ *              SWIGLU_QUANT launch's out_sums). The kernel otherwise sums the rows itself
+ *              on the matrix core (one extra MFMA per 16 rows and group), a sum that may
+ *              drop the lowest bits of tiny codes; both ways stay within the error bound.
  *   sorted     NULL, or int32 [R] pair ids from moe_route_permute
  *   k_route    experts per token (used only with `sorted`)
  *   w          the bank as laid out by fp8moe_pack_expert_bank
@@ -222,17 +233,20 @@ int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t
  *              FP8MOE_EPI_SWIGLU_QUANT: N = 2I with gate columns 0..I-1 and up columns
  *              I..2I-1; h = silu(gate) * up in fp32 is quantised like fp8_quant_act
  *              (group 128) into out = e4m3 [R, I] and out_scales = fp32 [I/128, R],
- *              group-major like a_scales (ready to be the next GEMM's a_scales)
+ *              group-major like a_scales (ready to be the next GEMM's a_scales), and,
+ *              when out_sums is not NULL, the code sums of h into out_sums = fp32
+ *              [I/128, R] (ready to be the next GEMM's a_sums); out_sums must be NULL
+ *              with STORE
  * Constraints: R >= 0 (R = 0 is a no-op), 1 <= E <= 1024, K % 128 == 0,
  * 128 <= K <= 16384, R*K < 2^32, N*K/2 < 2^32, (ceil(R/128) + E) * ceil(N/256) < 2^28;
  * STORE: N % 64 == 0; SWIGLU_QUANT: N % 256 == 0.
  */
 int32_t fp8_grouped_expert_gemm(const uint8_t* a, const float* a_scales,
-                                const int32_t* sorted, int32_t k_route, const uint8_t* w,
-                                const float* w_scales, const int32_t* offsets, int64_t R,
-                                int32_t E, int64_t N, int64_t K, int32_t epilogue,
-                                int32_t out_dtype, void* out, float* out_scales,
-                                void* stream);
+                                const float* a_sums, const int32_t* sorted, int32_t k_route,
+                                const uint8_t* w, const float* w_scales,
+                                const int32_t* offsets, int64_t R, int32_t E, int64_t N,
+                                int64_t K, int32_t epilogue, int32_t out_dtype, void* out,
+                                float* out_scales, float* out_sums, void* stream);
 
 /*
  * fp8_dense_gemm -- W8A8 projection y = (s_a * s_w) * (qa . qw^T).
@@ -348,14 +362,15 @@ int32_t fp8moe_pack_expert_bank_mxfp4(const uint8_t* w, const float* w_scales, i
  *   a_scales   uint32 [K/128, R]: the four E8M0 bytes of (grouped row, 128-group) as one
  *              word, group-major (moe_route_permute's xs_perm of mxfp4_quant_act's scales)
  *   w, w_scales  from fp8moe_pack_expert_bank_mxfp4
- *   everything else as fp8_grouped_expert_gemm (epilogues, output layouts, constraints)
+ *   everything else as fp8_grouped_expert_gemm (epilogues, output layouts including
+ *   out_sums, constraints); there is no a_sums (the kernel sums the scaled rows itself)
  */
 int32_t mxfp4_grouped_expert_gemm(const uint8_t* a, const uint32_t* a_scales,
                                   const int32_t* sorted, int32_t k_route, const uint8_t* w,
                                   const float* w_scales, const int32_t* offsets, int64_t R,
                                   int32_t E, int64_t N, int64_t K, int32_t epilogue,
                                   int32_t out_dtype, void* out, float* out_scales,
-                                  void* stream);
+                                  float* out_sums, void* stream);
 
 /*
  * moe_unpermute_combine -- out[t, :] = sum_{j=0..k-1} weights[t, j] * y[pos[t*k+j], :]

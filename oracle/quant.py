@@ -104,6 +104,19 @@ def quant_block128(w: np.ndarray):
     return q, scales
 
 
+def code_sums(q: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """e4m3 codes [M, K] -> float64 [M, K/group]: the sum of the decoded (unscaled) codes in
+    each group. Not a quantity the pages name: the library can emit it beside the codes so
+    that a GEMM on an offset-coded int4 weight (w = u - 8 with u >= 0) recovers
+    sum_k a_k w_k as sum_k a_k u_k - 8 sum_k a_k without forming the second sum itself.
+    Definition only: decode, then add, in float64 (exact for any 128 e4m3 values)."""
+    from .codec import e4m3_decode
+    q = np.asarray(q, dtype=np.uint8)
+    M, K = q.shape
+    assert K % group == 0
+    return e4m3_decode(q).reshape(M, K // group, group).sum(axis=2)
+
+
 def quant_block128_bf16(w_bits: np.ndarray):
     return quant_block128(bf16_to_f32(w_bits))
 

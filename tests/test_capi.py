@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
     raw = ctypes.CDLL(LIB)
     for name in declared_functions():
         assert hasattr(raw, name), name
-    assert lib.fp8moe_abi_version() == 5
+    assert lib.fp8moe_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -78,23 +78,27 @@ U = 0x1004  # misaligned
 
 def test_quant_act_validation(lib):
     f = lib.fp8_quant_act
-    assert f(None, 4, 128, 128, P, P, None, 0, None) == NULL
-    assert f(P, 4, 128, 64, P, P, None, 0, None) == UNSUP
-    assert f(P, 0, 128, 128, P, P, None, 0, None) == SHAPE
-    assert f(P, 4, 100, 128, P, P, None, 0, None) == SHAPE
-    assert f(P, 3, 3, 0, P, P, None, 0, None) == SHAPE  # M*K % 8
-    assert f(U, 4, 128, 128, P, P, None, 0, None) == ALIGN
-    assert f(P, 2048, 4096, 0, P, P, None, 0, None) == WS
-    assert f(P, 2048, 4096, 0, P, P, P, 100, None) == WS
-    assert f(P, 4, 100, -1, P, P, None, 0, None) == SHAPE  # row mode: K % 8
-    assert f(P, 4, 96, -1, U, P, None, 0, None) == ALIGN
-    assert f(P, 4, 96, -2, P, P, None, 0, None) == UNSUP
+    assert f(None, 4, 128, 128, P, P, None, None, 0, None) == NULL
+    assert f(P, 4, 128, 64, P, P, None, None, 0, None) == UNSUP
+    assert f(P, 0, 128, 128, P, P, None, None, 0, None) == SHAPE
+    assert f(P, 4, 100, 128, P, P, None, None, 0, None) == SHAPE
+    assert f(P, 3, 3, 0, P, P, None, None, 0, None) == SHAPE  # M*K % 8
+    assert f(U, 4, 128, 128, P, P, None, None, 0, None) == ALIGN
+    assert f(P, 2048, 4096, 0, P, P, None, None, 0, None) == WS
+    assert f(P, 2048, 4096, 0, P, P, None, P, 100, None) == WS
+    assert f(P, 4, 100, -1, P, P, None, None, 0, None) == SHAPE  # row mode: K % 8
+    assert f(P, 4, 96, -1, U, P, None, None, 0, None) == ALIGN
+    assert f(P, 4, 96, -2, P, P, None, None, 0, None) == UNSUP
+    # code sums come only with the per-(token, 128) mode
+    assert f(P, 4, 128, 0, P, P, P, None, 0, None) == UNSUP
+    assert f(P, 4, 128, -1, P, P, P, None, 0, None) == UNSUP
+    assert f(P, 4, 128, 128, P, P, U, None, 0, None) == ALIGN
 
 
 def _route(lib, logits=P, T=16, E=8, k=2, ws=P, ws_bytes=1 << 20, xq=None, xs=None, H=0,
-           xqp=None, xsp=None, ids=P):
-    return lib.moe_route_permute(logits, T, E, k, ids, P, P, P, P, xq, xs, H, xqp, xsp, ws,
-                                 ws_bytes, None)
+           xqp=None, xsp=None, ids=P, xsum=None, xsump=None):
+    return lib.moe_route_permute(logits, T, E, k, ids, P, P, P, P, xq, xs, H, xqp, xsp, xsum,
+                                 xsump, ws, ws_bytes, None)
 
 
 def test_route_validation(lib):
@@ -115,12 +119,15 @@ def test_route_validation(lib):
     assert _route(lib, xs=P, xsp=U, H=256) == ALIGN
     assert _route(lib, ids=U) == ALIGN
     assert _route(lib, ws_bytes=16) == WS
+    assert _route(lib, xs=P, xsp=P, H=256, xsum=P) == NULL  # the sum pair comes together
+    assert _route(lib, xsum=P, xsump=P) == NULL  # and only with the scale gather
+    assert _route(lib, xs=P, xsp=P, H=256, xsum=P, xsump=U) == ALIGN
 
 
 def _gg(lib, a=P, R=256, E=8, N=512, K=256, epi=0, dt=0, out_scales=P, sorted_=None, kr=1,
-        out=P):
-    return lib.fp8_grouped_expert_gemm(a, P, sorted_, kr, P, P, P, R, E, N, K, epi, dt, out,
-                                       out_scales, None)
+        out=P, a_sums=None, out_sums=None):
+    return lib.fp8_grouped_expert_gemm(a, P, a_sums, sorted_, kr, P, P, P, R, E, N, K, epi, dt,
+                                       out, out_scales, out_sums, None)
 
 
 def test_grouped_gemm_validation(lib):
@@ -144,6 +151,9 @@ def test_grouped_gemm_validation(lib):
     assert _gg(lib, R=64, N=1 << 20, K=16384) == SHAPE  # N*K/2 >= 2^32
     # (ceil(R/128) + E) * ceil(N/256) >= 2^28: tile indices would not fit 32 bits
     assert _gg(lib, R=(1 << 25) - 128, N=(1 << 24) - 256, K=128) == SHAPE
+    assert _gg(lib, out_sums=P) == UNSUP  # output code sums only with SwiGLU
+    assert _gg(lib, a_sums=U) == ALIGN
+    assert _gg(lib, epi=1, out_sums=U) == ALIGN
 
 
 def _pack(lib, w=P, s=P, E=4, N=64, K=256, wp=P, sp=P):
@@ -215,11 +225,12 @@ def test_mxfp4_validation(lib):
     assert pk(P, P, 4, 24, 256, P, P, None) == SHAPE
     assert pk(P, P, 4, 64, 100, P, P, None) == SHAPE
     g = lib.mxfp4_grouped_expert_gemm
-    assert g(P, P, None, 1, P, P, P, 256, 8, 512, 256, 2, 0, P, P, None) == UNSUP
-    assert g(None, P, None, 1, P, P, P, 256, 8, 512, 256, 0, 0, P, P, None) == NULL
-    assert g(P, P, None, 1, P, P, P, 256, 8, 512, 100, 0, 0, P, P, None) == SHAPE
-    assert g(P, P, None, 1, P, P, P, 256, 8, 512, 256, 0, 0, U, P, None) == ALIGN
-    assert g(P, P, None, 1, P, P, P, 0, 8, 512, 256, 0, 0, P, P, None) == OK
+    assert g(P, P, None, 1, P, P, P, 256, 8, 512, 256, 2, 0, P, P, None, None) == UNSUP
+    assert g(None, P, None, 1, P, P, P, 256, 8, 512, 256, 0, 0, P, P, None, None) == NULL
+    assert g(P, P, None, 1, P, P, P, 256, 8, 512, 100, 0, 0, P, P, None, None) == SHAPE
+    assert g(P, P, None, 1, P, P, P, 256, 8, 512, 256, 0, 0, U, P, None, None) == ALIGN
+    assert g(P, P, None, 1, P, P, P, 0, 8, 512, 256, 0, 0, P, P, None, None) == OK
+    assert g(P, P, None, 1, P, P, P, 256, 8, 512, 256, 0, 0, P, P, P, None) == UNSUP
 
 
 def test_combine_validation(lib):

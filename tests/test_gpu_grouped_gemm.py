@@ -250,3 +250,101 @@ def test_pack_expert_bank_layout():
                                     got[e, n, kk] = nib - 16 if nib >= 8 else nib
     assert np.array_equal(got, q)
     assert np.array_equal(ps, np.transpose(ws, (0, 2, 1)))
+
+
+def _sums_gm(aq):
+    """Oracle code sums of the grouped rows, group-major fp32 on the device."""
+    from oracle.quant import code_sums
+    return _gm(code_sums(aq).astype(np.float32))
+
+
+@pytest.mark.parametrize("counts,K,N", [
+    ([0, 37, 130, 1, 200], 256, 512),
+    ([5, 0, 0, 261, 17, 64, 0, 9], 1024, 320),
+])
+def test_store_with_given_code_sums(counts, K, N):
+    """a_sums in place of the in-kernel sums: within the same bound of the oracle. (Not bit
+    for bit the result without them: the sum the kernel forms on the matrix core is not
+    always the exact sum of the 128 codes, the given one is.)"""
+    f = _lib()
+    aq, as_, wp, ws, off = _problem(counts, K, N, seed=K + N + 1)
+    w, s = _bank(wp, ws)
+    args = (dev(aq), _gm(as_), w, s, dev(off), aq.shape[0], f.EPI_STORE, torch.float32)
+    y1 = host(f.fp8_grouped_expert_gemm(*args, a_sums=_sums_gm(aq)))
+    torch.cuda.synchronize()
+    ref, b = grouped_gemm(aq, as_, wp, ws, off, with_bound=True)
+    check_close(y1.astype(np.float64), ref, gemm_bound(b), "grouped gemm with a_sums")
+
+
+def test_integer_operands_exact_with_given_sums():
+    """The exactness case above with the sums given: every term is an integer, so the
+    result must be exact."""
+    f = _lib()
+    rng = np.random.default_rng(4)
+    R, K, N = 200, 512, 128
+    aq = e4m3_encode(rng.integers(-16, 17, size=(R, K)).astype(np.float64))
+    as_ = np.ones((R, K // 128), np.float32)
+    wp = rng.integers(0, 256, size=(3, N, K // 2), dtype=np.uint8)
+    ws = np.ones((3, N, K // 128), np.float32)
+    off = np.array([0, 60, 61, R], np.int32)
+    w, s = _bank(wp, ws)
+    y = host(f.fp8_grouped_expert_gemm(dev(aq), _gm(as_), w, s, dev(off), R, f.EPI_STORE,
+                                       torch.float32, a_sums=_sums_gm(aq)))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.astype(np.float64), grouped_gemm(aq, as_, wp, ws, off))
+
+
+def test_wrong_code_sums_change_the_result():
+    """The kernel really reads a_sums: sums off by one unit shift the outputs (the offset
+    term of the int4 weights), so the result differs from the one with the right sums."""
+    f = _lib()
+    aq, as_, wp, ws, off = _problem([200, 56], 256, 256, seed=21)
+    w, s = _bank(wp, ws)
+    args = (dev(aq), _gm(as_), w, s, dev(off), aq.shape[0], f.EPI_STORE, torch.float32)
+    from oracle.quant import code_sums
+    bad = _gm((code_sums(aq) + 1.0).astype(np.float32))
+    y0 = host(f.fp8_grouped_expert_gemm(*args, a_sums=_sums_gm(aq)))
+    y1 = host(f.fp8_grouped_expert_gemm(*args, a_sums=bad))
+    torch.cuda.synchronize()
+    assert not np.array_equal(y0, y1)
+
+
+@pytest.mark.parametrize("cfg", ["moe_tiny", "moe_prefill"])
+def test_swiglu_epilogue_code_sums(cfg):
+    """Gate|up with given input sums and the SwiGLU epilogue's optional output sums: the
+    codes and scales pass the SwiGLU check against the same kernel's fp32 accumulators
+    (also run with the given sums); each output sum is the sum of the decoded output codes
+    of its (row, 128 group) to fp32 summation accuracy; and the down GEMM fed those sums
+    stays within the bound of the oracle on those codes."""
+    c = CONFIGS[cfg]
+    inp = moe_inputs(c)
+    f = _lib()
+    from oracle.codec import e4m3_decode
+    from oracle.quant import code_sums
+    xq, xs = quant_group_bf16(inp["x"])
+    ids, _ = topk_route(inp["logits"], c.k)
+    off, sorted_, _ = group_pairs(ids, c.E)
+    R = c.T * c.k
+    w, s = _bank(inp["w_gu"], inp["s_gu"])
+    args = (dev(xq), _gm(permute_rows(xs, sorted_, c.k)), w, s, dev(off), R)
+    kw = dict(sorted_=dev(sorted_), k_route=c.k,
+              a_sums=_sums_gm(permute_rows(xq, sorted_, c.k)))
+    hq, hs, hsum = f.fp8_grouped_expert_gemm(*args, f.EPI_SWIGLU_QUANT, **kw, with_sums=True)
+    y32 = f.fp8_grouped_expert_gemm(*args, f.EPI_STORE, torch.float32, **kw)
+    torch.cuda.synchronize()
+    codes = host(hq)
+    _swiglu_check(codes, np.ascontiguousarray(host(hs).T), host(y32))
+    ref = code_sums(codes).T
+    err = np.abs(host(hsum).astype(np.float64) - ref)
+    bound = 8 * 2.0 ** -24 * np.abs(e4m3_decode(codes)).reshape(R, -1, 128).sum(-1).T
+    assert np.all(err <= bound), err.max()
+    wd, sd = _bank(inp["w_dn"], inp["s_dn"])
+    y = host(f.fp8_grouped_expert_gemm(hq, hs, wd, sd, dev(off), R, f.EPI_STORE, torch.float32,
+                                       a_sums=hsum))
+    torch.cuda.synchronize()
+    hs_rows = np.ascontiguousarray(host(hs).T)
+    rng = np.random.default_rng(13)
+    rows = rng.integers(0, R, 3000)
+    cols = rng.integers(0, c.H, 3000)
+    dref, db = grouped_gemm_rows(codes, hs_rows, inp["w_dn"], inp["s_dn"], off, rows, cols)
+    check_close(y[rows, cols].astype(np.float64), dref, gemm_bound(db), "down with given sums")

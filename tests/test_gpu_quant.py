@@ -156,3 +156,49 @@ def test_row_mode(M, K):
     assert_bytes_equal(s.view(np.uint32), rs.view(np.uint32), "scales")
     if M > 3:
         assert np.all(q[1] == 0) and np.all(q[3] == 0x80)
+
+
+def _sum_bound(q):
+    """fp32 summation of one group: error <= 8 * 2^-24 * sum |dec(code)| (depth-7 tree)."""
+    from oracle.codec import e4m3_decode
+    M, K = q.shape
+    return 8 * 2.0 ** -24 * np.abs(e4m3_decode(q)).reshape(M, K // 128, 128).sum(-1)
+
+
+@pytest.mark.parametrize("cfg", ["moe_tiny", "moe_prefill"])
+def test_group_mode_code_sums(cfg):
+    """The optional per-(token, 128) code sums: the codes and scales are unchanged by asking
+    for them, and each sum is the sum of that group's decoded codes (the oracle's codes,
+    which the GPU's equal bit for bit), to fp32 summation accuracy."""
+    import fp8_moe_prefill_amd as f
+    from oracle.quant import code_sums
+    x = moe_inputs(CONFIGS[cfg])["x"]
+    q, s, sm = f.fp8_quant_act(dev(x), 128, with_sums=True)
+    torch.cuda.synchronize()
+    rq, rs = quant_group_bf16(x)
+    assert_bytes_equal(host(q), rq, "codes")
+    assert_bytes_equal(host(s).view(np.uint32), rs.view(np.uint32), "scales")
+    err = np.abs(host(sm).astype(np.float64) - code_sums(rq))
+    assert np.all(err <= _sum_bound(rq)), err.max()
+
+
+def test_code_sums_extremes():
+    """Groups at the format's edges: all +448 (sum 57344, above 2^15 so fp32 partial sums
+    round), all zero, alternating signs, and one outlier per group."""
+    import fp8_moe_prefill_amd as f
+    from oracle.quant import code_sums
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((64, 1024)).astype(np.float32)
+    x[0] = 7.0
+    x[1] = 0.0
+    x[2, 0::2], x[2, 1::2] = 3.0, -3.0
+    x[3:, ::128] = 1000.0
+    xb = bf16_bits_from_f32(x)
+    q, s, sm = f.fp8_quant_act(dev(xb), 128, with_sums=True)
+    torch.cuda.synchronize()
+    rq, _ = quant_group_bf16(xb)
+    assert_bytes_equal(host(q), rq, "codes")
+    ref = code_sums(rq)
+    err = np.abs(host(sm).astype(np.float64) - ref)
+    assert np.all(err <= _sum_bound(rq)), err.max()
+    assert np.all(host(sm)[0] == 57344.0) and np.all(host(sm)[1] == 0.0)

@@ -96,3 +96,24 @@ def test_repeat_runs_identical():
     b = _gpu_route(logits, c.k)
     for n in a:
         assert np.array_equal(a[n].view(np.uint8), b[n].view(np.uint8)), n
+
+
+def test_code_sum_gather():
+    """xsum rides the scale gather: xsum_perm[g, r] = xsum[sorted[r] // k, g], bit-exact, with
+    the scales' gather unchanged beside it."""
+    import fp8_moe_prefill_amd as f
+    c = CONFIGS["moe_tiny"]
+    from synth.inputs import router_logits
+    logits = router_logits(c.seed, f"{c.name}.logits", c.T, c.E, c.zipf_s)
+    rng = np.random.default_rng(3)
+    G = 4
+    xs = rng.uniform(0.01, 1, (c.T, G)).astype(np.float32)
+    xsum = rng.standard_normal((c.T, G)).astype(np.float32) * 100
+    r = f.moe_route_permute(dev(logits), c.k, xs=dev(xs), xsum=dev(xsum))
+    torch.cuda.synchronize()
+    ids, _ = topk_route(logits, c.k)
+    _, sorted_, _ = group_pairs(ids, c.E)
+    assert_bytes_equal(host(r["xs_perm"]), np.ascontiguousarray(permute_rows(xs, sorted_, c.k).T),
+                       "xs_perm")
+    assert_bytes_equal(host(r["xsum_perm"]),
+                       np.ascontiguousarray(permute_rows(xsum, sorted_, c.k).T), "xsum_perm")

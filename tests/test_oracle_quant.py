@@ -154,3 +154,37 @@ def test_block128_single_block_is_per_tensor_and_blocks_are_independent():
     w2[:, 128:] *= np.float32(2.0 ** 7)
     q2, s2 = quant_block128(w2)
     assert np.array_equal(q2, q) and s2[0, 0] == s[0, 0] and s2[0, 1] == s[0, 1] * 2 ** 7
+
+
+def test_code_sums_closed_forms():
+    """Sum of decoded codes per (row, 128 group): constant codes give 128 x value, a code
+    beside its negation cancels, and a single nonzero code lands in its own (row, group)
+    cell only (catches a transposed or mis-strided reshape)."""
+    from oracle.quant import code_sums
+    ones = np.full((3, 256), 0x38, np.uint8)  # e4m3 1.0
+    assert np.array_equal(code_sums(ones), np.full((3, 2), 128.0))
+    top = np.full((1, 128), 0x7E, np.uint8)  # e4m3 448 (largest finite)
+    assert code_sums(top)[0, 0] == 448.0 * 128
+    rng = np.random.default_rng(1)
+    c = rng.integers(0, 0x7F, size=(4, 64), dtype=np.uint8)
+    pair = np.empty((4, 128), np.uint8)
+    pair[:, 0::2] = c
+    pair[:, 1::2] = c | 0x80
+    assert np.array_equal(code_sums(pair), np.zeros((4, 1)))
+    for m, k, code, val in [(0, 5, 0x40, 2.0), (2, 300, 0xC8, -4.0), (1, 511, 0x01, 2.0 ** -9)]:
+        q = np.zeros((3, 512), np.uint8)
+        q[m, k] = code
+        ref = np.zeros((3, 4))
+        ref[m, k // 128] = val
+        assert np.array_equal(code_sums(q), ref)
+
+
+def test_code_sums_match_torch_float8_decode():
+    import torch
+    from oracle.quant import code_sums
+    rng = np.random.default_rng(2)
+    q = rng.integers(0, 256, size=(16, 384), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0  # drop NaN codes
+    t = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64)
+    ref = t.reshape(16, 3, 128).sum(-1).numpy()
+    assert np.allclose(code_sums(q), ref, rtol=0, atol=1e-9)
