@@ -7,9 +7,10 @@ intermediate 768, packed-int4 experts with group-128 scales). Inputs are synthet
 already resident in HBM; three copies of the weight bank and of the inputs are rotated so
 the 151 MB bank cannot stay in the 256 MB Infinity Cache between steps.
 
-Prints one JSON line: MoE prefill tokens/s for the whole layer, plus the roofline of the
-dominant kernel (the grouped gate|up GEMM, FP8 MFMA bound) measured with HIP events on the
-launch stream inside the timed region, and the CPU oracle timed on a bounded sample.
+Prints one JSON line: MoE prefill tokens/s for the whole layer (K steps timed with nothing
+between the launches), plus the roofline of the dominant kernel (the grouped gate|up GEMM,
+FP8 MFMA bound) from HIP events around each stage on the launch stream over a second pass
+of the same K steps, and the CPU oracle timed on a bounded sample.
 
 The line also carries the depth stack (T=2048, L=8 by default, --stack 12 or 0): prefill
 tokens/s of the whole forward (L layers of W8A8 q/k/v/o, causal GQA attention, router and
@@ -243,19 +244,7 @@ def main():
         runner.run(xs[i % ROT], lgs[i % ROT], banks[i % ROT])
     torch.cuda.synchronize()
 
-    stages = f.MoELayerRunner.STAGES
-    ev = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for s in stages} for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        runner.run(xs[i % ROT], lgs[i % ROT], banks[i % ROT], events=ev[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    per = {s: float(np.mean([e[s][0].elapsed_time(e[s][1]) for e in ev])) for s in stages}
+    ms_step, per = time_layer(runner, xs, lgs, banks, args.steps)
 
     flop_gu = 4.0 * R * c.H * c.I
     flop_dn = 2.0 * R * c.I * c.H
@@ -350,6 +339,33 @@ def main():
     print(json.dumps(out))
 
 
+def time_layer(runner, xs, lgs, banks, steps):
+    """(ms per layer step, {stage: ms}). The steps are timed twice: first with nothing
+    between the launches but the launches themselves (the step time; a HIP event recorded
+    between kernels costs several microseconds of GPU time here), then again with a pair of
+    events around each stage on the launch stream (the per-stage and per-kernel times)."""
+    import numpy as np
+    import torch
+
+    n = len(xs)
+    stages = runner.STAGES
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        runner.run(xs[i % n], lgs[i % n], banks[i % n])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / steps
+    ev = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for s in stages} for _ in range(steps)]
+    for i in range(steps):
+        runner.run(xs[i % n], lgs[i % n], banks[i % n], events=ev[i])
+    torch.cuda.synchronize()
+    per = {s: float(np.mean([e[s][0].elapsed_time(e[s][1]) for e in ev])) for s in stages}
+    return ms_step, per
+
+
 def bench_mxfp4_layer(c, xs, lgs, warmup, steps, dev) -> dict:
     """The same layer with MXFP4 activations into gate|up (E2M1 codes, one E8M0 scale per
     32, applied by the MFMA): per-stage times and the gate|up rate."""
@@ -365,18 +381,8 @@ def bench_mxfp4_layer(c, xs, lgs, warmup, steps, dev) -> dict:
     n = len(xs)
     for i in range(warmup):
         runner.run(xs[i % n], lgs[i % n], banks[i % n])
-    stages = f.MoELayerRunner.STAGES
-    ev = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for s in stages} for _ in range(steps)]
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for i in range(steps):
-        runner.run(xs[i % n], lgs[i % n], banks[i % n], events=ev[i])
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
-    per = {s: float(np.mean([e[s][0].elapsed_time(e[s][1]) for e in ev])) * 1e3 for s in stages}
+    ms, per = time_layer(runner, xs, lgs, banks, steps)
+    per = {s: v * 1e3 for s, v in per.items()}
     flop_gu = 4.0 * c.T * c.k * c.H * c.I
     tf = flop_gu / (per["gate_up"] * 1e-6) / 1e12
     return {"tokens_per_s": c.T / (ms * 1e-3), "ms_per_step": ms, "stages_us": per,

@@ -235,7 +235,10 @@ def fp8_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=
                             out_scales=None, stream=None, a_sums=None, out_sums=None,
                             with_sums: bool = False):
     """Grouped expert GEMM on a bank from ``pack_expert_bank`` (w [E, N, K/2] bytes,
-    w_scales [E, K/128, N]); a_scales are group-major [K/128, R]. STORE -> out [R, N];
+    w_scales [E, K/128, N]). Without ``sorted_`` the rows are in grouped order and a_scales
+    (and a_sums) are group-major [K/128, R]; with it the rows are gathered from token order
+    (a = [T, K] with T = R / k_route) and a_scales (and a_sums) are the per-token
+    [T, K/128] arrays the quantiser writes. STORE -> out [R, N];
     SWIGLU_QUANT -> (codes [R, N/2], scales [N/256, R], group-major), plus the code sums
     [N/256, R] of the quantised output when ``out_sums`` or ``with_sums`` is given.
     ``a_sums`` (optional, group-major [K/128, R]) are the per-(row, K group) sums of the
@@ -249,9 +252,9 @@ def mxfp4_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogu
                               out=None, out_scales=None, stream=None, out_sums=None,
                               with_sums: bool = False):
     """The grouped expert GEMM with MXFP4 activations: a = codes [rows, K/2] from
-    ``mxfp4_quant_act``, a_scales = [K/128, R] 32-bit words (four E8M0 bytes each,
-    group-major: ``moe_route_permute``'s xs_perm of the quantiser's scales viewed as
-    [rows, K/128] words); the bank from ``pack_expert_bank(..., mxfp4=True)``."""
+    ``mxfp4_quant_act``, a_scales = 32-bit words of four E8M0 bytes each: the quantiser's
+    scales viewed as [rows, K/128] words when gathering through ``sorted_``, else
+    group-major [K/128, R]; the bank from ``pack_expert_bank(..., mxfp4=True)``."""
     return _grouped(a, a_scales, w, w_scales, offsets, R, epilogue, out_dtype, sorted_, k_route,
                     out, out_scales, stream, True, None, out_sums, with_sums)
 
@@ -269,9 +272,11 @@ def _grouped(a, a_scales, w, w_scales, offsets, R, epilogue, out_dtype, sorted_,
     K = Kh * 2
     if a.shape[1] != (K // 2 if a_fp4 else K):
         raise ValueError(f"a has {a.shape[1]} bytes per row, expected {K // 2 if a_fp4 else K}")
-    if tuple(a_scales.shape) != (K // GROUP, R):
-        raise ValueError(f"a_scales must be [K/128, R] = {(K // GROUP, R)}, "
-                         f"got {tuple(a_scales.shape)}")
+    # rows gathered through `sorted`: per-token scales (and sums) [T, K/128], as the
+    # quantiser writes them; otherwise group-major [K/128, R] in grouped row order
+    s_shape = (R // k_route, K // GROUP) if sorted_ is not None else (K // GROUP, R)
+    if tuple(a_scales.shape) != s_shape:
+        raise ValueError(f"a_scales must be {s_shape}, got {tuple(a_scales.shape)}")
     if tuple(w_scales.shape) != (E, K // GROUP, N):
         raise ValueError(f"w_scales must be [E, K/128, N] = {(E, K // GROUP, N)}, "
                          f"got {tuple(w_scales.shape)}")
@@ -295,9 +300,8 @@ def _grouped(a, a_scales, w, w_scales, offsets, R, epilogue, out_dtype, sorted_,
         dt = _dt(out.dtype)
     if a_sums is not None:
         _dev(a_sums, "a_sums", torch.float32)
-        if tuple(a_sums.shape) != (K // GROUP, R):
-            raise ValueError(f"a_sums must be [K/128, R] = {(K // GROUP, R)}, "
-                             f"got {tuple(a_sums.shape)}")
+        if tuple(a_sums.shape) != s_shape:
+            raise ValueError(f"a_sums must be {s_shape}, got {tuple(a_sums.shape)}")
     if a_fp4:
         _check("mxfp4_grouped_expert_gemm", _lib.mxfp4_grouped_expert_gemm(
             _ptr(a), _ptr(a_scales), _ptr(sorted_), k_route, _ptr(w), _ptr(w_scales),

@@ -18,9 +18,10 @@
 //   u * 2^-9 (the subnormals and the first normal binade share the spacing 2^-9), so the
 //   offset nibble u = n ^ 8 = q + 8 (q the int4 value) IS the e4m3 code of (q + 8) * 2^-9.
 //   The +8 is removed inside the MFMA: its accumulator input is seeded with
-//   -8 * 2^-9 * sum_k a_k for that row and group, and that row sum is itself one MFMA of
-//   the A tile against a constant all-ones operand (one extra MFMA per 16 rows per group,
-//   +3%). The 2^9 is folded into the weight scale (exact). The prepacked bank stores the
+//   -8 * 2^-9 * sum_k a_k for that row and group. That row sum is given (the quantiser,
+//   or a previous SwiGLU epilogue, emits it beside the codes), or else formed here as one
+//   MFMA of the A tile against a constant all-ones operand (one extra MFMA per 16 rows per
+//   group). The 2^9 is folded into the weight scale (exact). The prepacked bank stores the
 //   nibbles of a 32-bit word so that its low nibbles are four consecutive k and its high
 //   nibbles the next four: a byte split gives K-ordered e4m3 bytes with no permutes.
 // * Tile 128 rows x 256 accumulator columns per workgroup, 4 waves side by side along N
@@ -28,7 +29,8 @@
 //   lane), two workgroups per CU (two waves per SIMD, one from each). Per K group a tile
 //   stages 16 KB of A and 16 KB of packed B for 8.4 MFLOP. A (e4m3 rows, gathered from token order through `sorted` when given),
 //   each wave's packed B slice (one contiguous 1 KB block per 16 columns in the prepacked
-//   bank) and both scale vectors (contiguous per group in their group-major layouts) go
+//   bank) and both scale vectors (the activation scales per row: by token when the rows
+//   are gathered, else contiguous per group in the group-major layout) go
 //   straight from global memory into LDS (LDS DMA, no VGPR staging) through two stages:
 //   the next group streams in while the current one is computed, one barrier per group.
 // * Persistent: the grid is two workgroups per CU and each walks its list of
@@ -368,8 +370,14 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
         src = max(min(src, a_rows - 1), 0);
         a_off32[j] = (uint32_t)src * (uint32_t)a_row_bytes + (uint32_t)(c * 16);
       }
-      as_off32 =
-          (uint32_t)max(min(t.row_begin + min(wv * RPW + (lane & (RPW - 1)), t.rows - 1), R - 1), 0) * 4u;
+      if (sorted) {  // per-token scales and sums, row-major [a_rows, G]: the token's row
+        const int p = s_src[wv][lane & (RPW - 1)];
+        const int tok = max(min(kshift >= 0 ? (p >> kshift) : (p / k_route), a_rows - 1), 0);
+        as_off32 = (uint32_t)tok * (uint32_t)G * 4u;
+      } else {  // group-major [G, R] in grouped row order
+        as_off32 = (uint32_t)max(
+            min(t.row_begin + min(wv * RPW + (lane & (RPW - 1)), t.rows - 1), R - 1), 0) * 4u;
+      }
       ws_off32 = (uint32_t)ws_col(t.nt, lane) * 4u;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -392,9 +400,12 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s) dma16(w_exp + b_blk[s] + gd * kBlockBytes, lane16, sb + s * 1024);
     dma4(ws_exp + (int64_t)gd * N, ws_off32, st.ws + wv * WCOLS);
-    if (lane < RPW) dma4(As + (int64_t)gd * R, as_off32, st.as + wv * RPW);
+    // group gd of the rows' scales (and sums): column gd of the per-token arrays, or row gd
+    // of the group-major ones
+    const int64_t as_base = sorted ? (int64_t)gd : (int64_t)gd * R;
+    if (lane < RPW) dma4(As + as_base, as_off32, st.as + wv * RPW);
     // given code sums replace the in-kernel row sums: they land where the seeds go
-    if (SUMS && lane < RPW) dma4(Asum + (int64_t)gd * R, as_off32, st.ra + wv * RPW);
+    if (SUMS && lane < RPW) dma4(Asum + as_base, as_off32, st.ra + wv * RPW);
   };
 
   // sum of this wave's 16-row tile of the A tile of stage st -> st.ra as -sum/64, the

@@ -10,9 +10,9 @@
 // pure function of the logits.
 //   1. topk_hist:  one wave per token selects the top k by (logit desc, expert asc): each
 //                  pick is the wave maximum of a 64-bit key (order-preserving logit bits,
-//                  then the inverted expert index) reduced with DPP only; a workgroup owns
-//                  a chunk of 16 tokens and counts its pairs per expert in LDS (integer
-//                  adds commute).
+//                  then the inverted expert index) reduced with DPP only; a workgroup of
+//                  16 waves owns a chunk of 16 tokens and counts its pairs per expert in
+//                  LDS (integer adds commute).
 //   2. chunk_scan: one workgroup per expert scans that expert's per-chunk counts.
 //   3. scatter:    one workgroup per chunk recomputes the expert offsets (a scan over E),
 //                  ranks each pair among the chunk's earlier pairs of the same expert and
@@ -84,42 +84,28 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
 }
 
 // Top-k of each token and the per-chunk expert histogram. A workgroup owns a chunk of
-// kRouteChunk tokens; each wave takes kRouteChunk/4 of them, loads all their logits first
-// (lane e holds experts e, e+64, ...), then picks the k best one at a time: a per-lane
-// best key over the lane's untaken experts, the wave maximum, and the winner's key cleared.
+// kRouteChunk tokens, one wave per token (the k picks of a token are a dependent chain,
+// so the tokens of a chunk run side by side); lane e holds experts e, e+64, ... The wave
+// picks the k best one at a time: a per-lane best key over the lane's untaken experts,
+// the wave maximum, and the winner's key cleared.
 template <int NJ>  // experts per lane: E <= 64 * NJ
-__global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict__ logits,
-                                                        int64_t T, int E, int k,
-                                                        int32_t* __restrict__ ids,
-                                                        float* __restrict__ wts,
-                                                        int32_t* __restrict__ cnt) {
-  constexpr int TPW = kRouteChunk / 4;  // tokens per wave
+__global__ __launch_bounds__(kRouteChunk * 64) void topk_hist_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ wts, int32_t* __restrict__ cnt) {
   __shared__ int hist[kMaxE];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  for (int e = threadIdx.x; e < E; e += kRouteChunk * 64) hist[e] = 0;
   __syncthreads();
-
-  float v[TPW][NJ];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int64_t t = (int64_t)blockIdx.x * kRouteChunk + wv * TPW + u;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = lane + 64 * j;
-      const float lv = (t < T && e < E) ? logits[t * E + e] : -INFINITY;
-      v[u][j] = lv != lv ? -INFINITY : lv;  // NaN ranks as -inf: every pick stays a valid expert
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int64_t t = (int64_t)blockIdx.x * kRouteChunk + wv * TPW + u;
-    if (t >= T) break;  // wave-uniform
+  const int64_t t = (int64_t)blockIdx.x * kRouteChunk + wv;
+  if (t < T) {  // wave-uniform
     // keys of this lane's experts; a taken expert's key becomes 0
     uint64_t key[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j;
-      key[j] = e < E ? topk_key(v[u][j], e) : 0;
+      float lv = e < E ? logits[t * E + e] : -INFINITY;
+      if (lv != lv) lv = -INFINITY;  // NaN ranks as -inf: every pick stays a valid expert
+      key[j] = e < E ? topk_key(lv, e) : 0;
     }
     float my_v = -INFINITY, top_v = 0.f;
     int my_i = 0;
@@ -151,7 +137,8 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(const float* __restrict_
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) cnt[(int64_t)blockIdx.x * E + e] = hist[e];
+  for (int e = threadIdx.x; e < E; e += kRouteChunk * 64)
+    cnt[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
 // One workgroup per expert: exclusive scan of its count over the chunks (in place) and
@@ -272,13 +259,13 @@ hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32
   int64_t C = (T + kRouteChunk - 1) / kRouteChunk;
   int32_t* cnt = static_cast<int32_t*>(ws);
   int32_t* tot = cnt + C * E;
-  const dim3 grid((uint32_t)C);
+  const dim3 grid((uint32_t)C), block(kRouteChunk * 64);
   if (E <= 64)
-    topk_hist_kernel<1><<<grid, 256, 0, st>>>(logits, T, E, k, ids, w, cnt);
+    topk_hist_kernel<1><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt);
   else if (E <= 256)
-    topk_hist_kernel<4><<<grid, 256, 0, st>>>(logits, T, E, k, ids, w, cnt);
+    topk_hist_kernel<4><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt);
   else
-    topk_hist_kernel<16><<<grid, 256, 0, st>>>(logits, T, E, k, ids, w, cnt);
+    topk_hist_kernel<16><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   chunk_scan_kernel<<<dim3((uint32_t)E), 256, 0, st>>>(cnt, C, E, tot);

@@ -71,22 +71,23 @@ def moe_layer(x: torch.Tensor, logits: torch.Tensor, bank: ExpertBank, k: int,
     With ``keep`` the intermediate tensors are returned too (for parity checks)."""
     T = x.shape[0]
     R = T * k
+    # gate|up gathers its rows from token order through `sorted`, and with them each row's
+    # per-token scales (and code sums) straight from the quantiser's output
+    rt = _lib.moe_route_permute(logits, k, stream=stream)
     if bank.act == "mxfp4":  # MXFP4 activations into gate|up (bank packed for them)
         xq, xs = _lib.mxfp4_quant_act(x, stream=stream)
         xsum = None
-        rt = _lib.moe_route_permute(logits, k, xs=xs.view(torch.float32), stream=stream)
         hq, hs, hsum = _lib.mxfp4_grouped_expert_gemm(
-            xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"], R, _lib.EPI_SWIGLU_QUANT,
-            sorted_=rt["sorted"], k_route=k, stream=stream, with_sums=True)
+            xq, xs.view(torch.float32), bank.w_gu, bank.s_gu, rt["offsets"], R,
+            _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=k, stream=stream,
+            with_sums=True)
     else:
         # the quantiser also emits each (token, 128) group's code sum; the grouped GEMMs
         # take those in place of forming them from the tiles
         xq, xs, xsum = _lib.fp8_quant_act(x, _lib.GROUP, stream=stream, with_sums=True)
-        rt = _lib.moe_route_permute(logits, k, xs=xs, xsum=xsum, stream=stream)
         hq, hs, hsum = _lib.fp8_grouped_expert_gemm(
-            xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"], R, _lib.EPI_SWIGLU_QUANT,
-            sorted_=rt["sorted"], k_route=k, stream=stream, a_sums=rt["xsum_perm"],
-            with_sums=True)
+            xq, xs, bank.w_gu, bank.s_gu, rt["offsets"], R, _lib.EPI_SWIGLU_QUANT,
+            sorted_=rt["sorted"], k_route=k, stream=stream, a_sums=xsum, with_sums=True)
     y = _lib.fp8_grouped_expert_gemm(hq, hs, bank.w_dn, bank.s_dn, rt["offsets"], R,
                                      _lib.EPI_STORE, out_dtype=torch.bfloat16, stream=stream,
                                      a_sums=hsum)
@@ -113,8 +114,9 @@ class MoELayerRunner:
     """One MoE layer with every intermediate buffer allocated once (for serving loops and
     timing): call ``run(x, logits, bank)`` repeatedly; outputs are overwritten in place.
 
-    The optional ``events`` dict of (start, end) torch.cuda.Event pairs, keyed by stage
-    name, is recorded around the corresponding launches on the current stream."""
+    Every launch goes to one stream (``stream``, else the current one). The optional
+    ``events`` dict of (start, end) torch.cuda.Event pairs, keyed by stage name, is
+    recorded around the corresponding launches on that stream."""
 
     STAGES = ("quant", "route", "gate_up", "down", "combine")
 
@@ -135,10 +137,7 @@ class MoELayerRunner:
                           weights=torch.empty((T, k), dtype=f32, device=dev),
                           offsets=torch.empty(E + 1, dtype=i32, device=dev),
                           sorted=torch.empty(R, dtype=i32, device=dev),
-                          pos=torch.empty(R, dtype=i32, device=dev),
-                          xs_perm=torch.empty((H // _lib.GROUP, R), dtype=f32, device=dev))
-        if act != "mxfp4":
-            self.route["xsum_perm"] = torch.empty((H // _lib.GROUP, R), dtype=f32, device=dev)
+                          pos=torch.empty(R, dtype=i32, device=dev))
         nws = _lib.workspace_bytes(_lib.OP_ROUTE_PERMUTE, T, E, k)
         self.ws = torch.empty(max(nws, 256), dtype=u8, device=dev)
         self.hq = torch.empty((R, I), dtype=u8, device=dev)
@@ -158,37 +157,38 @@ class MoELayerRunner:
         mx = self.act == "mxfp4"
         if bank.act != self.act:
             raise ValueError(f"bank packed for {bank.act} activations, runner for {self.act}")
+        main = torch.cuda.current_stream() if stream is None else stream
         mark("quant", 0)
         if mx:
-            _lib.mxfp4_quant_act(x, q=self.xq, scales=self.xs, stream=stream)
+            _lib.mxfp4_quant_act(x, q=self.xq, scales=self.xs, stream=main)
         else:
             _lib.fp8_quant_act(x, _lib.GROUP, q=self.xq, scales=self.xs, sums=self.xsum,
-                               stream=stream)
+                               stream=main)
         mark("quant", 1)
         mark("route", 0)
-        _lib.moe_route_permute(logits, self.k, xs=self.xs.view(torch.float32), out=rt,
-                               ws=self.ws, stream=stream, xsum=None if mx else self.xsum)
+        _lib.moe_route_permute(logits, self.k, out=rt, ws=self.ws, stream=main)
         mark("route", 1)
         mark("gate_up", 0)
+        # rows gathered from token order through `sorted`, with their per-token scales
+        # (and code sums) straight from the quantiser's output
         if mx:
             _lib.mxfp4_grouped_expert_gemm(
-                self.xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"], self.R,
-                _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k, out=self.hq,
-                out_scales=self.hs, out_sums=self.hsum, stream=stream)
+                self.xq, self.xs.view(torch.float32), bank.w_gu, bank.s_gu, rt["offsets"],
+                self.R, _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k,
+                out=self.hq, out_scales=self.hs, out_sums=self.hsum, stream=main)
         else:
             _lib.fp8_grouped_expert_gemm(
-                self.xq, rt["xs_perm"], bank.w_gu, bank.s_gu, rt["offsets"], self.R,
+                self.xq, self.xs, bank.w_gu, bank.s_gu, rt["offsets"], self.R,
                 _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k, out=self.hq,
-                out_scales=self.hs, out_sums=self.hsum, stream=stream,
-                a_sums=rt["xsum_perm"])
+                out_scales=self.hs, out_sums=self.hsum, stream=main, a_sums=self.xsum)
         mark("gate_up", 1)
         mark("down", 0)
         _lib.fp8_grouped_expert_gemm(self.hq, self.hs, bank.w_dn, bank.s_dn, rt["offsets"],
-                                     self.R, _lib.EPI_STORE, out=self.y, stream=stream,
+                                     self.R, _lib.EPI_STORE, out=self.y, stream=main,
                                      a_sums=self.hsum)
         mark("down", 1)
         mark("combine", 0)
         _lib.moe_unpermute_combine(self.y, rt["pos"], rt["weights"], out=self.out,
-                                   stream=stream)
+                                   stream=main)
         mark("combine", 1)
         return self.out

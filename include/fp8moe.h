@@ -209,18 +209,19 @@ int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t
  * activation scale folded into the accumulator.
  *
  * For grouped row i in expert e's range [offsets[e], offsets[e+1]) and column n:
- *   y[i, n] = sum_g a_scales[g, i] * w_scales[e, n, g]
+ *   y[i, n] = sum_g s_a(i, g) * w_scales[e, n, g]
  *                   * sum_{k in group g} e4m3(a[r, k]) * int4(w[e, n, k])
- * with r = i, or r = sorted[i] / k_route when `sorted` is given (the A rows are then
- * gathered on the fly from token order and no permuted copy of them is needed; their
- * scales come already grouped, see moe_route_permute's xs_perm).
+ * with r = i, or r = sorted[i] / k_route when `sorted` is given. With `sorted` the A rows
+ * are gathered on the fly from token order, and so are their scales and code sums: the
+ * quantiser's outputs are read as they are, with no permuted copy of any of them.
  *
  *   a          e4m3 [Ra, K]  (Ra = R without `sorted`, Ra = R / k_route with it)
- *   a_scales   fp32 [K/128, R], group-major: the scale of group g of grouped row i is
- *              a_scales[g * R + i]
- *   a_sums     NULL, or fp32 [K/128, R] group-major: the sums of the e4m3 code values of
- *              each (grouped row, group) (fp8_quant_act's sums, gathered, or a previous
- *              SWIGLU_QUANT launch's out_sums). The kernel otherwise sums the rows itself
+ *   a_scales   without `sorted`: fp32 [K/128, R], group-major, s_a(i, g) = a_scales[g*R + i];
+ *              with it: fp32 [Ra, K/128] per token (fp8_quant_act's scales),
+ *              s_a(i, g) = a_scales[r * K/128 + g]
+ *   a_sums     NULL, or the sums of the e4m3 code values of each (row, group), laid out as
+ *              a_scales (fp8_quant_act's sums with `sorted`, or a previous SWIGLU_QUANT
+ *              launch's out_sums without it). The kernel otherwise sums the rows itself
  *              on the matrix core (one extra MFMA per 16 rows and group), a sum that may
  *              drop the lowest bits of tiny codes; both ways stay within the error bound.
  *   sorted     NULL, or int32 [R] pair ids from moe_route_permute
@@ -359,8 +360,10 @@ int32_t fp8moe_pack_expert_bank_mxfp4(const uint8_t* w, const float* w_scales, i
  *
  *   a          MXFP4 codes [rows, K/2] (mxfp4_quant_act), rows in token order when `sorted`
  *              is given (gathered on the fly), else already grouped
- *   a_scales   uint32 [K/128, R]: the four E8M0 bytes of (grouped row, 128-group) as one
- *              word, group-major (moe_route_permute's xs_perm of mxfp4_quant_act's scales)
+ *   a_scales   uint32 words, the four E8M0 bytes of (row, 128-group) as one word: with
+ *              `sorted`, mxfp4_quant_act's scales viewed as [rows, K/128] words; without
+ *              it, group-major [K/128, R] in grouped order (e.g. moe_route_permute's xs_perm
+ *              of those words)
  *   w, w_scales  from fp8moe_pack_expert_bank_mxfp4
  *   everything else as fp8_grouped_expert_gemm (epilogues, output layouts including
  *   out_sums, constraints); there is no a_sums (the kernel sums the scaled rows itself)

@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
     raw = ctypes.CDLL(LIB)
     for name in declared_functions():
         assert hasattr(raw, name), name
-    assert lib.fp8moe_abi_version() == 6
+    assert lib.fp8moe_abi_version() == 7
 
 
 def test_status_strings(lib):

@@ -57,13 +57,16 @@ def _gm(scales_rows):
     return dev(np.ascontiguousarray(scales_rows.T))
 
 
-def _gemm(aq, as_grouped, wp, ws, off, out_dtype=torch.float32, sorted_=None, k_route=1,
+def _gemm(aq, as_, wp, ws, off, out_dtype=torch.float32, sorted_=None, k_route=1,
           R=None):
-    """STORE-mode grouped GEMM. as_grouped: [R, K/128] scales of the grouped rows."""
+    """STORE-mode grouped GEMM. as_: [rows, K/128] scales of the rows of aq -- the grouped
+    rows without `sorted_` (passed group-major), the token rows with it (passed as they
+    are)."""
     f = _lib()
     R = aq.shape[0] if R is None else R
     w, s = _bank(wp, ws)
-    y = f.fp8_grouped_expert_gemm(dev(aq), _gm(as_grouped), w, s, dev(off), R,
+    y = f.fp8_grouped_expert_gemm(dev(aq), _gm(as_) if sorted_ is None else dev(as_), w, s,
+                                  dev(off), R,
                                   f.EPI_STORE, out_dtype,
                                   sorted_=None if sorted_ is None else dev(sorted_),
                                   k_route=k_route)
@@ -117,7 +120,7 @@ def test_on_the_fly_gather_equals_permuted_copy():
     R = c.T * c.k
     aq = permute_rows(xq, sorted_, c.k)
     as_ = permute_rows(xs, sorted_, c.k)
-    y_gather = host(_gemm(xq, as_, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k,
+    y_gather = host(_gemm(xq, xs, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k,
                           R=R))
     y_perm = host(_gemm(aq, as_, inp["w_gu"], inp["s_gu"], off))
     assert_bytes_equal(y_gather.view(np.uint32), y_perm.view(np.uint32), "gather vs permuted")
@@ -163,7 +166,7 @@ def test_swiglu_quant_epilogue(cfg):
     off, sorted_, _ = group_pairs(ids, c.E)
     R = c.T * c.k
     w, s = _bank(inp["w_gu"], inp["s_gu"])
-    args = (dev(xq), _gm(permute_rows(xs, sorted_, c.k)), w, s, dev(off), R)
+    args = (dev(xq), dev(xs), w, s, dev(off), R)
     hq, hs = f.fp8_grouped_expert_gemm(*args, f.EPI_SWIGLU_QUANT, sorted_=dev(sorted_),
                                        k_route=c.k)
     y32 = f.fp8_grouped_expert_gemm(*args, f.EPI_STORE, torch.float32, sorted_=dev(sorted_),
@@ -184,7 +187,7 @@ def test_gate_up_full_size_sampled():
     R = c.T * c.k
     aq = permute_rows(xq, sorted_, c.k)
     as_ = permute_rows(xs, sorted_, c.k)
-    y = host(_gemm(xq, as_, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k, R=R))
+    y = host(_gemm(xq, xs, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k, R=R))
     rng = np.random.default_rng(11)
     rows = rng.integers(0, R, 4000)
     cols = rng.integers(0, 2 * c.I, 4000)
@@ -326,9 +329,8 @@ def test_swiglu_epilogue_code_sums(cfg):
     off, sorted_, _ = group_pairs(ids, c.E)
     R = c.T * c.k
     w, s = _bank(inp["w_gu"], inp["s_gu"])
-    args = (dev(xq), _gm(permute_rows(xs, sorted_, c.k)), w, s, dev(off), R)
-    kw = dict(sorted_=dev(sorted_), k_route=c.k,
-              a_sums=_sums_gm(permute_rows(xq, sorted_, c.k)))
+    args = (dev(xq), dev(xs), w, s, dev(off), R)
+    kw = dict(sorted_=dev(sorted_), k_route=c.k, a_sums=dev(code_sums(xq).astype(np.float32)))
     hq, hs, hsum = f.fp8_grouped_expert_gemm(*args, f.EPI_SWIGLU_QUANT, **kw, with_sums=True)
     y32 = f.fp8_grouped_expert_gemm(*args, f.EPI_STORE, torch.float32, **kw)
     torch.cuda.synchronize()

@@ -95,13 +95,18 @@ def _words_gm(sc_rows):
     return dev(np.ascontiguousarray(w.T).view(np.int32))
 
 
-def _mx_gemm(codes, sc_grouped, wp, ws, off, epilogue=0, out_dtype=torch.float32, sorted_=None,
+def _mx_gemm(codes, sc, wp, ws, off, epilogue=0, out_dtype=torch.float32, sorted_=None,
              k_route=1, R=None):
+    """sc: the E8M0 bytes [rows, K/32] of the rows of `codes` -- grouped rows without
+    `sorted_` (passed group-major), token rows with it (passed per token, as the quantiser
+    writes them)."""
     from oracle.mx import pack_fp4
     f = _lib()
     R = codes.shape[0] if R is None else R
     w, s = f.pack_expert_bank(dev(wp), dev(ws), mxfp4=True)
-    r = f.mxfp4_grouped_expert_gemm(dev(pack_fp4(codes)), _words_gm(sc_grouped), w, s, dev(off),
+    words = (_words_gm(sc) if sorted_ is None
+             else dev(np.ascontiguousarray(sc).view(np.uint32).view(np.int32)))
+    r = f.mxfp4_grouped_expert_gemm(dev(pack_fp4(codes)), words, w, s, dev(off),
                                     R, epilogue, out_dtype,
                                     sorted_=None if sorted_ is None else dev(sorted_),
                                     k_route=k_route)
@@ -144,7 +149,7 @@ def test_gather_equals_permuted_copy_and_oracle():
     R = c.T * c.k
     ac = permute_rows(codes, sorted_, c.k)
     asc = permute_rows(sc, sorted_, c.k)
-    yg = host(_mx_gemm(codes, asc, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k, R=R))
+    yg = host(_mx_gemm(codes, sc, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k, R=R))
     yp = host(_mx_gemm(ac, asc, inp["w_gu"], inp["s_gu"], off))
     assert_bytes_equal(yg.view(np.uint32), yp.view(np.uint32), "gather vs permuted")
     ref, b = grouped_gemm_fp4act(ac, asc, inp["w_gu"], inp["s_gu"], off, with_bound=True)
@@ -171,10 +176,9 @@ def test_route_gathers_the_scale_words():
 def test_swiglu_quant_epilogue(cfg):
     c, inp, codes, sc, off, sorted_ = _routed(cfg)
     R = c.T * c.k
-    asc = permute_rows(sc, sorted_, c.k)
-    hq, hs = _mx_gemm(codes, asc, inp["w_gu"], inp["s_gu"], off, epilogue=1, sorted_=sorted_,
+    hq, hs = _mx_gemm(codes, sc, inp["w_gu"], inp["s_gu"], off, epilogue=1, sorted_=sorted_,
                       k_route=c.k, R=R)
-    y32 = _mx_gemm(codes, asc, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k, R=R)
+    y32 = _mx_gemm(codes, sc, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k, R=R)
     _swiglu_check(host(hq), np.ascontiguousarray(host(hs).T), host(y32))
 
 
@@ -183,7 +187,7 @@ def test_gate_up_full_size_sampled():
     R = c.T * c.k
     ac = permute_rows(codes, sorted_, c.k)
     asc = permute_rows(sc, sorted_, c.k)
-    y = host(_mx_gemm(codes, asc, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k, R=R))
+    y = host(_mx_gemm(codes, sc, inp["w_gu"], inp["s_gu"], off, sorted_=sorted_, k_route=c.k, R=R))
     rng = np.random.default_rng(13)
     rows = rng.integers(0, R, 4000)
     cols = rng.integers(0, 2 * c.I, 4000)
