@@ -273,7 +273,7 @@ def main():
                    "intermediate": c.I, "weight_banks_rotated": ROT},
         "grouped_gemm": {"tflops": gemm_tflops, "frac_fp8_peak": gemm_tflops / PEAK_FP8_TFLOPS,
                          "gate_up_us": per["gate_up"] * 1e3, "down_us": per["down"] * 1e3},
-        "stages_us": {s: per[s] * 1e3 for s in stages},
+        "stages_us": {s: v * 1e3 for s, v in per.items()},
         "roofline": {"kernel": "grouped_gemm gate|up (+SwiGLU+requant)", "bound": "mfma",
                      "achieved": gu_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": gu_tflops / PEAK_FP8_TFLOPS, "traffic": traffic,

@@ -350,3 +350,39 @@ def test_swiglu_epilogue_code_sums(cfg):
     cols = rng.integers(0, c.H, 3000)
     dref, db = grouped_gemm_rows(codes, hs_rows, inp["w_dn"], inp["s_dn"], off, rows, cols)
     check_close(y[rows, cols].astype(np.float64), dref, gemm_bound(db), "down with given sums")
+
+
+@pytest.mark.parametrize("k", [3, 6])
+def test_gather_with_k_not_a_power_of_two(k):
+    """Rows, scales and code sums gathered through `sorted` with k = 3 and 6 (pair id / k by
+    division, not a shift): bit for bit the GEMM on explicitly permuted copies, for STORE and
+    for the SwiGLU epilogue."""
+    f = _lib()
+    from oracle.quant import code_sums
+    rng = np.random.default_rng(30 + k)
+    T, H, E, I = 50, 256, 8, 256
+    x = (rng.standard_normal((T, H)) * rng.uniform(0.1, 10, (T, 1))).astype(np.float32)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    xq, xs = quant_group(x)
+    ids, _ = topk_route(logits, k)
+    off, sorted_, _ = group_pairs(ids, E)
+    R = T * k
+    wp = rng.integers(0, 256, size=(E, 2 * I, H // 2), dtype=np.uint8)
+    ws = rng.uniform(0.005, 0.02, size=(E, 2 * I, H // 128)).astype(np.float32)
+    w, s = _bank(wp, ws)
+    aq, as_ = permute_rows(xq, sorted_, k), permute_rows(xs, sorted_, k)
+    sums_tok = dev(code_sums(xq).astype(np.float32))
+    sums_grp = _sums_gm(aq)
+    for epi in (f.EPI_STORE, f.EPI_SWIGLU_QUANT):
+        g = f.fp8_grouped_expert_gemm(dev(xq), dev(xs), w, s, dev(off), R, epi, torch.float32,
+                                      sorted_=dev(sorted_), k_route=k, a_sums=sums_tok)
+        p = f.fp8_grouped_expert_gemm(dev(aq), _gm(as_), w, s, dev(off), R, epi, torch.float32,
+                                      a_sums=sums_grp)
+        torch.cuda.synchronize()
+        for a, b in (zip(g, p) if epi == f.EPI_SWIGLU_QUANT else [(g, p)]):
+            assert_bytes_equal(host(a).view(np.uint8), host(b).view(np.uint8), f"epi {epi}")
+    y = host(f.fp8_grouped_expert_gemm(dev(xq), dev(xs), w, s, dev(off), R, f.EPI_STORE,
+                                       torch.float32, sorted_=dev(sorted_), k_route=k))
+    torch.cuda.synchronize()
+    ref, b = grouped_gemm(aq, as_, wp, ws, off, with_bound=True)
+    check_close(y.astype(np.float64), ref, gemm_bound(b), f"gather k={k}")
