@@ -386,3 +386,17 @@ def test_gather_with_k_not_a_power_of_two(k):
     torch.cuda.synchronize()
     ref, b = grouped_gemm(aq, as_, wp, ws, off, with_bound=True)
     check_close(y.astype(np.float64), ref, gemm_bound(b), f"gather k={k}")
+
+
+@pytest.mark.parametrize("counts,K,N", [
+    ([17, 0, 23], 16384, 64),                     # the largest K the entry point takes
+    ([0] * 500 + [3] + [0] * 400 + [130] + [0] * 121 + [1], 256, 128),  # E = 1024
+])
+def test_limits_of_k_and_expert_count(counts, K, N):
+    """At the documented limits: K = 16384 (128 groups streamed per tile) and E = 1024
+    experts, nearly all empty, with a ragged tail in the few that have rows."""
+    assert len(counts) in (3, 1024)
+    aq, as_, wp, ws, off = _problem(counts, K, N, seed=K + len(counts))
+    y = host(_gemm(aq, as_, wp, ws, off)).astype(np.float64)
+    ref, b = grouped_gemm(aq, as_, wp, ws, off, with_bound=True)
+    check_close(y, ref, gemm_bound(b), f"grouped gemm K={K} E={len(counts)}")
