@@ -6,8 +6,8 @@
 // returned to their tokens with the router weights.
 //
 // HBM-bound gather: one thread per 8 consecutive columns (16-byte bf16 / 32-byte fp32
-// loads), the k rows summed in fp32 in increasing j -- a fixed order, so the result is
-// deterministic (no atomics).
+// loads), up to eight of a token's rows loaded together, the k rows summed in fp32 in
+// increasing j -- a fixed order, so the result is deterministic (no atomics).
 #include "common.h"
 #include "launch.h"
 
@@ -47,7 +47,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
   const int64_t h0 = ((int64_t)(blockIdx.x % HB) * 256 + threadIdx.x) * 8;
   if (h0 >= H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
+  int j = 0;
+  // eight rows at a time: their positions and weights, then all eight row loads in flight
+  // together, then the sums in increasing j (the same order as one row at a time)
+  for (; j + 8 <= k; j += 8) {
+    int64_t row[8];
+    float wj[8], f[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      row[u] = pos[t * k + j + u];
+      wj[u] = w[t * k + j + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) load8(y + row[u] * H + h0, f[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[u], f[u][i], acc[i]);
+  }
+  for (; j < k; ++j) {
     const int64_t row = pos[t * k + j];
     const float wj = w[t * k + j];
     float f[8];
