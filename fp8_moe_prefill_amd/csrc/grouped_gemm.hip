@@ -185,9 +185,11 @@ struct TileDesc {
 // in the matching K order (pack_bank with the FP4 layout). The MFMA applies the
 // activation scales itself, so the fold is one FMA by the weight scale.
 //
-// SUMS: the per-(row, K group) sums of the decoded A codes come in Asum (group-major like
-// As) and seed the accumulators directly; otherwise the kernel forms them on the matrix
-// core from the staged tile.
+// As and Asum: per token, row-major [a_rows, G], when the rows are gathered through
+// `sorted`; otherwise group-major [G, R] in grouped row order.
+// SUMS: the per-(row, K group) sums of the decoded A codes come in Asum (laid out like As)
+// and seed the accumulators directly; otherwise the kernel forms them on the matrix core
+// from the staged tile.
 template <int EPI, bool OUT_BF16, bool AF4, bool SUMS>
 __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const float* __restrict__ Asum,
