@@ -166,7 +166,7 @@ int32_t grouped_gemm(const uint8_t* a, const float* a_scales, const float* a_sum
   if (N < 16 || N >= (int64_t(1) << 24)) return FP8MOE_ERR_SHAPE;
   if (epilogue == FP8MOE_EPI_STORE && N % 64 != 0) return FP8MOE_ERR_SHAPE;
   if (epilogue == FP8MOE_EPI_SWIGLU_QUANT && N % 256 != 0) return FP8MOE_ERR_SHAPE;
-  if (sorted && k_route < 1) return FP8MOE_ERR_SHAPE;
+  if (sorted && (k_route < 1 || R % k_route != 0)) return FP8MOE_ERR_SHAPE;  // R = T * k
   if (R * K >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;  // 32-bit A row offsets
   if (N * (K / 2) >= (int64_t(1) << 32)) return FP8MOE_ERR_SHAPE;  // 32-bit offsets in one expert
   // 32-bit tile indexing: (128-row tiles, one more per expert) x (256-column tiles)

@@ -225,7 +225,8 @@ int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t
  *              on the matrix core (one extra MFMA per 16 rows and group), a sum that may
  *              drop the lowest bits of tiny codes; both ways stay within the error bound.
  *   sorted     NULL, or int32 [R] pair ids from moe_route_permute
- *   k_route    experts per token (used only with `sorted`)
+ *   k_route    experts per token (used only with `sorted`; R must then be a multiple of
+ *              it, R = T * k_route)
  *   w          the bank as laid out by fp8moe_pack_expert_bank
  *   w_scales   its scales, fp32 [E, K/128, N] (fp8moe_pack_expert_bank's w_scales_packed)
  *   offsets    int32 [E+1] on the device (from moe_route_permute), offsets[E] = R

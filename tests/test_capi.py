@@ -146,6 +146,7 @@ def test_grouped_gemm_validation(lib):
     assert _gg(lib, N=80) == SHAPE  # STORE needs N % 64 == 0
     assert _gg(lib, epi=1, N=384) == SHAPE  # SwiGLU needs N % 256 == 0
     assert _gg(lib, sorted_=P, kr=0) == SHAPE
+    assert _gg(lib, sorted_=P, kr=3) == SHAPE  # gathered rows: R = T * k_route
     assert _gg(lib, out=U) == ALIGN
     assert _gg(lib, R=0) == OK  # empty input is a no-op; nothing is launched
     assert _gg(lib, R=64, N=1 << 20, K=16384) == SHAPE  # N*K/2 >= 2^32
