@@ -207,7 +207,7 @@ def bench_stack(L: int, warmup: int, steps: int):
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: the benchmark runs on one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU expert-parallel path is not built", file=sys.stderr)
         sys.exit(2)
 
