@@ -159,8 +159,10 @@ int32_t grouped_gemm(const uint8_t* a, const float* a_scales, const float* a_sum
   if (epilogue == FP8MOE_EPI_STORE && out_dtype != FP8MOE_DTYPE_F32 &&
       out_dtype != FP8MOE_DTYPE_BF16)
     return FP8MOE_ERR_UNSUPPORTED;
-  if (!a || !a_scales || !w || !w_scales || !offsets || !out) return FP8MOE_ERR_NULL;
-  if (epilogue == FP8MOE_EPI_SWIGLU_QUANT && !out_scales) return FP8MOE_ERR_NULL;
+  if (!w || !w_scales || !offsets) return FP8MOE_ERR_NULL;
+  // the row-sized buffers may be NULL when there are no rows (empty arrays)
+  if (R != 0 && (!a || !a_scales || !out)) return FP8MOE_ERR_NULL;
+  if (R != 0 && epilogue == FP8MOE_EPI_SWIGLU_QUANT && !out_scales) return FP8MOE_ERR_NULL;
   if (R < 0 || R >= (int64_t(1) << 31) || E < 1 || E > kMaxE) return FP8MOE_ERR_SHAPE;
   if (K < FP8MOE_GROUP || K % FP8MOE_GROUP != 0 || K > kMaxGroupedK) return FP8MOE_ERR_SHAPE;
   if (N < 16 || N >= (int64_t(1) << 24)) return FP8MOE_ERR_SHAPE;

@@ -239,7 +239,8 @@ int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t
  *              when out_sums is not NULL, the code sums of h into out_sums = fp32
  *              [I/128, R] (ready to be the next GEMM's a_sums); out_sums must be NULL
  *              with STORE
- * Constraints: R >= 0 (R = 0 is a no-op), 1 <= E <= 1024, K % 128 == 0,
+ * Constraints: R >= 0 (R = 0 is a no-op; the row-sized buffers a, a_scales, a_sums, sorted,
+ * out, out_scales, out_sums may then be NULL), 1 <= E <= 1024, K % 128 == 0,
  * 128 <= K <= 16384, R*K < 2^32, N*K/2 < 2^32, (ceil(R/128) + E) * ceil(N/256) < 2^28;
  * STORE: N % 64 == 0; SWIGLU_QUANT: N % 256 == 0.
  */

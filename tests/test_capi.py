@@ -149,6 +149,13 @@ def test_grouped_gemm_validation(lib):
     assert _gg(lib, sorted_=P, kr=3) == SHAPE  # gathered rows: R = T * k_route
     assert _gg(lib, out=U) == ALIGN
     assert _gg(lib, R=0) == OK  # empty input is a no-op; nothing is launched
+    # with no rows the row-sized buffers may be NULL (torch's empty tensors), the bank not
+    f = lib.fp8_grouped_expert_gemm
+    assert f(None, None, None, None, 1, P, P, P, 0, 8, 512, 256, 1, 0, None, None, None,
+             None) == OK
+    assert f(None, None, None, None, 1, None, P, P, 0, 8, 512, 256, 0, 0, None, None, None,
+             None) == NULL
+    assert _gg(lib, a=None, R=1) == NULL
     assert _gg(lib, R=64, N=1 << 20, K=16384) == SHAPE  # N*K/2 >= 2^32
     # (ceil(R/128) + E) * ceil(N/256) >= 2^28: tile indices would not fit 32 bits
     assert _gg(lib, R=(1 << 25) - 128, N=(1 << 24) - 256, K=128) == SHAPE

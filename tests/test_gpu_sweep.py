@@ -1,0 +1,79 @@
+"""Seeded sweep of the grouped expert GEMM over many small shapes, against the oracle.
+
+Each case draws an expert count, a ragged row count per expert (empty experts, single
+rows, exact and partial 128-row tiles), K (1..12 groups), N, the epilogue, the row source
+(grouped rows, or rows gathered from token order through `sorted` with k = 1..6) and
+whether the code sums are given. STORE outputs are checked element by element within the
+GEMM bound; the SwiGLU epilogue's codes and scales against the oracle's SwiGLU of the same
+kernel's fp32 accumulators (run with the same inputs)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.moe import grouped_gemm
+from oracle.quant import code_sums, quant_group
+from oracle.route import group_pairs, permute_rows, topk_route
+from oracle.tol import check_close, gemm_bound
+from tests.gpu_util import dev, host
+from tests.test_gpu_grouped_gemm import _swiglu_check
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.choice([1, 2, 5, 8, 17, 64]))
+    K = 128 * int(rng.integers(1, 13))
+    swiglu = bool(rng.integers(0, 2))
+    N = 256 * int(rng.integers(1, 4)) if swiglu else 64 * int(rng.integers(1, 9))
+    gather = bool(rng.integers(0, 2)) and E >= 2
+    sums = bool(rng.integers(0, 2))
+    if gather:
+        k = int(rng.integers(1, min(6, E) + 1))
+        T = int(rng.integers(1, 90))
+        x = (rng.standard_normal((T, K)) * rng.uniform(0.01, 20, (T, 1))).astype(np.float32)
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        xq, xs = quant_group(x)
+        ids, _ = topk_route(logits, k)
+        off, sorted_, _ = group_pairs(ids, E)
+        aq, as_ = permute_rows(xq, sorted_, k), permute_rows(xs, sorted_, k)
+        src = (xq, xs, sorted_, k)
+    else:
+        counts = rng.choice([0, 1, 5, 127, 128, 129, 200], size=E)
+        R = int(counts.sum())
+        x = (rng.standard_normal((R, K)) * rng.uniform(0.01, 20, (R, 1))).astype(np.float32)
+        aq, as_ = quant_group(x)
+        off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        src = None
+    wp = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    ws = rng.uniform(0.002, 0.03, size=(E, N, K // 128)).astype(np.float32)
+    return dict(E=E, K=K, N=N, swiglu=swiglu, sums=sums, aq=aq, as_=as_, off=off, src=src,
+                wp=wp, ws=ws)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_grouped_gemm_sweep(seed):
+    import fp8_moe_prefill_amd as f
+    c = _case(seed)
+    aq, as_, off = c["aq"], c["as_"], c["off"]
+    R = aq.shape[0]
+    w, s = f.pack_expert_bank(dev(c["wp"]), dev(c["ws"]))
+    if c["src"] is None:
+        args = (dev(aq), dev(np.ascontiguousarray(as_.T)), w, s, dev(off), R)
+        kw = dict(a_sums=dev(np.ascontiguousarray(code_sums(aq).T.astype(np.float32)))
+                  if c["sums"] else None)
+    else:
+        xq, xs, sorted_, k = c["src"]
+        args = (dev(xq), dev(xs), w, s, dev(off), R)
+        kw = dict(sorted_=dev(sorted_), k_route=k,
+                  a_sums=dev(code_sums(xq).astype(np.float32)) if c["sums"] else None)
+    y = f.fp8_grouped_expert_gemm(*args, f.EPI_STORE, torch.float32, **kw)
+    torch.cuda.synchronize()
+    ref, b = grouped_gemm(aq, as_, c["wp"], c["ws"], off, with_bound=True)
+    check_close(host(y).astype(np.float64), ref, gemm_bound(b),
+                f"sweep {seed}: E={c['E']} K={c['K']} N={c['N']} R={R}")
+    if c["swiglu"] and R > 0:
+        hq, hs = f.fp8_grouped_expert_gemm(*args, f.EPI_SWIGLU_QUANT, **kw)
+        torch.cuda.synchronize()
+        _swiglu_check(host(hq), np.ascontiguousarray(host(hs).T), host(y))
