@@ -77,3 +77,42 @@ def test_grouped_gemm_sweep(seed):
         hq, hs = f.fp8_grouped_expert_gemm(*args, f.EPI_SWIGLU_QUANT, **kw)
         torch.cuda.synchronize()
         _swiglu_check(host(hq), np.ascontiguousarray(host(hs).T), host(y))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_moe_layer_sweep(seed):
+    """The whole layer (moe_layer: quantise with code sums, route, gate|up + SwiGLU, down,
+    combine) on seeded random shapes, checked stage by stage as the layer tests do:
+    quantiser bytes and routing indices bit-exact, the down GEMM and the combine on the
+    GPU's own intermediates within their bounds, the output against the oracle's layer."""
+    import fp8_moe_prefill_amd as f
+    from oracle.moe import combine, moe_layer
+    from oracle.numeric import cosine
+    from oracle.tol import half_ulp_bf16
+    from synth import moe_inputs
+    from synth.inputs import MoEConfig
+    from tests.gpu_util import assert_bytes_equal, bf16_values
+    rng = np.random.default_rng(2000 + seed)
+    E = int(rng.choice([1, 2, 3, 8, 16, 33]))
+    c = MoEConfig(name=f"sweep{seed}", T=int(rng.integers(1, 300)),
+                  H=128 * int(rng.choice([1, 2, 4, 8])), E=E,
+                  k=int(rng.integers(1, min(E, 8) + 1)), I=128 * int(rng.integers(1, 5)),
+                  zipf_s=float(rng.choice([0.0, 1.2])), seed=seed)
+    inp = moe_inputs(c)
+    bank = f.ExpertBank.from_host(inp, "cuda:0")
+    out, st = f.moe_layer(dev(inp["x"]), dev(inp["logits"]), bank, c.k, keep=True)
+    torch.cuda.synchronize()
+    ref = moe_layer(inp["x"], inp["logits"], inp["w_gu"], inp["s_gu"], inp["w_dn"],
+                    inp["s_dn"], c.k)
+    what = f"{c}"
+    for n in ("xq", "ids", "offsets", "sorted", "pos"):
+        assert_bytes_equal(host(st[n]), ref[n], f"{n} ({what})")
+    hq, hs = host(st["hq"]), np.ascontiguousarray(host(st["hs"]).T)
+    y_ref, b = grouped_gemm(hq, hs, inp["w_dn"], inp["s_dn"], ref["offsets"], with_bound=True)
+    y = bf16_values(st["y"])
+    check_close(y, y_ref, gemm_bound(b) + half_ulp_bf16(y_ref), f"down ({what})")
+    w = host(st["weights"]).astype(np.float64)
+    o_ref = combine(y, host(st["pos"]), w)
+    mag = combine(np.abs(y), host(st["pos"]), w)
+    check_close(bf16_values(out), o_ref, 1e-6 * mag + half_ulp_bf16(o_ref), f"combine ({what})")
+    assert cosine(bf16_values(out), ref["out"]) > 0.999, what
