@@ -116,3 +116,63 @@ def test_moe_layer_sweep(seed):
     mag = combine(np.abs(y), host(st["pos"]), w)
     check_close(bf16_values(out), o_ref, 1e-6 * mag + half_ulp_bf16(o_ref), f"combine ({what})")
     assert cosine(bf16_values(out), ref["out"]) > 0.999, what
+
+
+@pytest.mark.parametrize("seed", range(18))
+def test_dense_w8a8_sweep(seed):
+    """The W8A8 projection on seeded random shapes, for each scale granularity in turn
+    (per tensor, per row, block-128 weights with per-(row, 128) activations): M from 1 to
+    400 (the M <= 16 weight-streaming branch and the tiled one), ragged N (a multiple of
+    16), K from 128 to 2048. Quantiser bytes bit-exact; outputs within the GEMM bound; the
+    bf16 output equal to the rounded fp32 output."""
+    import fp8_moe_prefill_amd as f
+    from oracle.dense import block_gemm, dense_w8a8, dense_w8a8_rowwise, quantize_weight
+    from oracle.numeric import bf16_bits, round_bf16
+    from oracle.quant import (quant_block128_bf16, quant_group_bf16, quant_row_bf16,
+                              quant_tensor_bf16)
+    from synth import bf16_bits_from_f32
+    from tests.gpu_util import assert_bytes_equal
+    rng = np.random.default_rng(3000 + seed)
+    mode = ("tensor", "row", "block")[seed % 3]
+    M = int(rng.choice([1, 2, 7, 16])) if rng.integers(0, 2) else int(rng.integers(17, 400))
+    N = 16 * int(rng.integers(1, 50))
+    K = 128 * int(rng.integers(1, 17))
+    x = rng.standard_normal((M, K)) * rng.uniform(0.1, 10, (M, 1))
+    x[:, rng.integers(0, K, 3)] *= 20.0  # a few outlier channels
+    xb = bf16_bits_from_f32(x.astype(np.float32))
+    wb = bf16_bits_from_f32((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    what = f"{mode} M={M} N={N} K={K}"
+    ys = {}
+    for dt in (torch.float32, torch.bfloat16):
+        if mode == "tensor":
+            wq, sw = f.quantize_weight(dev(wb))
+            xq, sa = f.fp8_quant_act(dev(xb), 0)
+            y = f.fp8_dense_gemm(xq, sa, wq, sw, dt)
+        elif mode == "row":
+            wq, sw = f.quantize_weight(dev(wb))
+            xq, sa = f.fp8_quant_act(dev(xb), f.QUANT_ROW)
+            y = f.fp8_dense_gemm_rowwise(xq, sa, wq, sw, dt)
+        else:
+            wq, sw = f.fp8_quant_weight_block128(dev(wb))
+            xq, sa = f.fp8_quant_act(dev(xb), 128)
+            y = f.fp8_block_gemm(xq, sa, wq, sw, dt)
+        torch.cuda.synchronize()
+        ys[dt] = host(y)
+    if mode == "tensor":
+        rq, rblk = quant_tensor_bf16(xb)
+        rwq, rsw = quantize_weight(wb)
+        ref, b = dense_w8a8(rq, rblk[2], rwq, rsw, with_bound=True)
+    elif mode == "row":
+        rq, rs = quant_row_bf16(xb)
+        rwq, rsw = quantize_weight(wb)
+        ref, b = dense_w8a8_rowwise(rq, rs, rwq, rsw, with_bound=True)
+    else:
+        rq, rs = quant_group_bf16(xb)
+        rwq, rws = quant_block128_bf16(wb)
+        assert_bytes_equal(host(sw).view(np.uint32), rws.view(np.uint32), f"block scales ({what})")
+        ref, b = block_gemm(rq, rs, rwq, rws, with_bound=True)
+    assert_bytes_equal(host(xq), rq, f"activation codes ({what})")
+    assert_bytes_equal(host(wq), rwq, f"weight codes ({what})")
+    y32 = ys[torch.float32].astype(np.float64)
+    check_close(y32, ref, gemm_bound(b), what)
+    assert_bytes_equal(ys[torch.bfloat16], bf16_bits(round_bf16(y32)), f"bf16 = RNE(fp32) ({what})")
