@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("T,k,H,ydt", [(64, 2, 256, "bf16"), (100, 8, 2048, "bf16"),
-                                       (7, 1, 8, "f32"), (33, 32, 136, "f32")])
+                                       (7, 1, 8, "f32"), (33, 32, 136, "f32"),
+                                       (29, 11, 64, "bf16"), (5, 17, 24, "f32")])
 def test_combine(T, k, H, ydt):
     import fp8_moe_prefill_amd as f
     rng = np.random.default_rng(T * k + H)
