@@ -176,3 +176,39 @@ def test_dense_w8a8_sweep(seed):
     y32 = ys[torch.float32].astype(np.float64)
     check_close(y32, ref, gemm_bound(b), what)
     assert_bytes_equal(ys[torch.bfloat16], bf16_bits(round_bf16(y32)), f"bf16 = RNE(fp32) ({what})")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_moe_layer_mxfp4_sweep(seed):
+    """The layer with MXFP4 activations into gate|up on seeded random shapes: FP4 codes,
+    E8M0 bytes and routing bit-exact, the down GEMM on the GPU's own intermediates within
+    its bound, the output against the oracle's MXFP4 layer."""
+    import fp8_moe_prefill_amd as f
+    from oracle.mx import moe_layer_mxfp4, unpack_fp4
+    from oracle.numeric import cosine
+    from oracle.tol import half_ulp_bf16
+    from synth import moe_inputs
+    from synth.inputs import MoEConfig
+    from tests.gpu_util import assert_bytes_equal, bf16_values
+    rng = np.random.default_rng(4000 + seed)
+    E = int(rng.choice([1, 3, 8, 16, 33]))
+    c = MoEConfig(name=f"mxsweep{seed}", T=int(rng.integers(1, 300)),
+                  H=128 * int(rng.choice([1, 2, 4, 8])), E=E,
+                  k=int(rng.integers(1, min(E, 8) + 1)), I=128 * int(rng.integers(1, 5)),
+                  zipf_s=float(rng.choice([0.0, 1.2])), seed=seed)
+    inp = moe_inputs(c)
+    bank = f.ExpertBank.from_host(inp, "cuda:0", act="mxfp4")
+    out, st = f.moe_layer(dev(inp["x"]), dev(inp["logits"]), bank, c.k, keep=True)
+    torch.cuda.synchronize()
+    ref = moe_layer_mxfp4(inp["x"], inp["logits"], inp["w_gu"], inp["s_gu"], inp["w_dn"],
+                          inp["s_dn"], c.k)
+    what = f"{c}"
+    assert_bytes_equal(unpack_fp4(host(st["xq"])), ref["xq"], f"codes ({what})")
+    assert_bytes_equal(host(st["xs"]), ref["xs"], f"E8M0 scales ({what})")
+    for n in ("ids", "offsets", "sorted", "pos"):
+        assert_bytes_equal(host(st[n]), ref[n], f"{n} ({what})")
+    hq, hs = host(st["hq"]), np.ascontiguousarray(host(st["hs"]).T)
+    y_ref, b = grouped_gemm(hq, hs, inp["w_dn"], inp["s_dn"], ref["offsets"], with_bound=True)
+    y = bf16_values(st["y"])
+    check_close(y, y_ref, gemm_bound(b) + half_ulp_bf16(y_ref), f"down ({what})")
+    assert cosine(bf16_values(out), ref["out"]) > 0.999, what
