@@ -212,3 +212,18 @@ def test_moe_layer_mxfp4_sweep(seed):
     y = bf16_values(st["y"])
     check_close(y, y_ref, gemm_bound(b) + half_ulp_bf16(y_ref), f"down ({what})")
     assert cosine(bf16_values(out), ref["out"]) > 0.999, what
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_causal_attention_sweep(seed):
+    """Causal GQA attention of the depth stack on seeded random shapes: ragged T from 1 to
+    300 (partial 64-key blocks and 16-query blocks), head layouts with 1, 2 and 4 query
+    heads per kv head, two logit scales; within the derived bound of the existing attention
+    test, token 0 exactly its own value row."""
+    from tests.test_gpu_stack import test_attention_bound
+    rng = np.random.default_rng(5000 + seed)
+    n_kv = int(rng.choice([1, 2, 4]))
+    n_q = n_kv * int(rng.choice([1, 2, 4]))
+    T = int(rng.integers(1, 301))
+    std = float(rng.choice([0.5, 3.0]))
+    test_attention_bound(T, n_q, n_kv, std)
