@@ -54,7 +54,7 @@ __device__ __forceinline__ uint2 encode8(const F8& f, float inv) {
 // Chunks of 8 consecutive elements per thread: kChunks of them, a whole grid apart, all
 // loaded before any is processed (more loads in flight per thread hide the HBM latency);
 // the 16 consecutive lanes of a quarter wave hold one 128-group.
-constexpr int kChunks = 4;
+constexpr int kChunks = 2;
 __global__ __launch_bounds__(256) void quant_group_kernel(const uint4* __restrict__ x,
                                                           int64_t nchunks,
                                                           uint2* __restrict__ q,
