@@ -11,8 +11,8 @@ Sources (cited by page title and section in each function):
 * "FP8 grouped-expert prefill with on-chip int4-to-e4m3 dequant" (octopusresearch.org),
   section 1 Contribution -- the method: FP8 e4m3 dense q/k/v/o projections, one grouped
   expert GEMM per layer instead of per-token dispatch, int4 weights turned into e4m3
-  without unpacking the resident bank, a per-(token, group) activation scale folded into
-  the accumulator; sections 3-4 -- the logit-cosine parity gate.
+  without unpacking the resident bank, one dynamic activation scale per token and K group
+  applied inside the fp32 accumulation; sections 3-4 -- the logit-cosine parity gate.
 * FreeToken PR #389 "load-time per-tensor FP8 dense projections (W8A8 via _scaled_mm)",
   sections "What this adds", "Limits", "Testing" -- per-tensor e4m3 weights with one
   fp32 scale, a dynamic per-tensor activation scale, the zero-input scale floor.

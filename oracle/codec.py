@@ -3,8 +3,8 @@
 e4m3fn: 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent 15 with mantissa 7 is
 NaN, there is no infinity, the largest finite magnitude is 448. The format follows from
 the activation scale amax/448 in the memra-engine ``fp8_ffi`` module docs (module text:
-"f32 -> e4m3 with ONE per-batch scalar scale (amax/448)") and from the OCP e4m3 format
-the FP8 grouped-expert prefill note uses (section 1: "FP8 (e4m3)").
+one dynamic scale per tensor, amax/448) and from the OCP e4m3 format the FP8
+grouped-expert prefill note uses (section 1).
 
 Readings where the pages are silent (all plain IEEE-style choices):
 * rounding is to nearest, ties to the even code (mantissa LSB 0);

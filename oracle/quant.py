@@ -2,9 +2,9 @@
 
 Three granularities:
 
-* per (token, 128-wide K group): the FP8 grouped-expert prefill note, section 1 ("a
-  per-(token, group) activation scale folded into the accumulator path"); this feeds the
-  grouped expert GEMMs;
+* per (token, 128-wide K group): the FP8 grouped-expert prefill note, section 1 (one
+  dynamic scale for each token and K group, applied inside the fp32 accumulation); this
+  feeds the grouped expert GEMMs;
 * per tensor: FreeToken PR #389, "What this adds" (a dynamic per-tensor activation
   scale: an amax pass, then the cast), and the memra-engine ``fp8_ffi`` docs (module
   text: one scalar scale amax/448); this feeds the dense W8A8 projections and is also the

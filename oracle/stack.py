@@ -73,27 +73,38 @@ def _w8a8(x_bf16_vals, w_codes, w_scale):
     return dense_w8a8(qa, blk[2], w_codes, w_scale)
 
 
-def _moe_fp8(hn_bf16_vals, logits, lay, k):
+def _route(logits, k, forced=None):
+    """Top-k routing of one layer, or the given expert ids with their weights recomputed
+    from these logits (the softmax over the k forced experts' logits)."""
+    if forced is None:
+        return topk_route(logits, k)
+    ids = np.asarray(forced, np.int32)
+    sel = np.take_along_axis(np.asarray(logits, np.float64), ids.astype(np.int64), axis=1)
+    ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return ids, ex / ex.sum(axis=1, keepdims=True)
+
+
+def _moe_fp8(hn_bf16_vals, logits, lay, k, forced=None):
     """The FP8 MoE layer of ``moe.moe_layer`` on already-bf16 activations (values)."""
     from .moe import grouped_gemm, swiglu_quant
     from .quant import quant_group
 
     E = lay["w_gu"].shape[0]
     xq, xs = quant_group(np.asarray(hn_bf16_vals, np.float32))
-    ids, w = topk_route(logits, k)
+    ids, w = _route(logits, k, forced)
     offsets, sorted_, pos = group_pairs(ids, E)
     y_gu = grouped_gemm(permute_rows(xq, sorted_, k), permute_rows(xs, sorted_, k),
                         lay["w_gu"], lay["s_gu"], offsets)
     hq, hs, _ = swiglu_quant(y_gu)
     y_dn = round_bf16(grouped_gemm(hq, hs, lay["w_dn"], lay["s_dn"], offsets))
-    return combine(y_dn, pos, w)
+    return combine(y_dn, pos, w), ids
 
 
-def _moe_bf16(hn_bf16_vals, logits, lay, k):
+def _moe_bf16(hn_bf16_vals, logits, lay, k, forced=None):
     """Same routing; experts in float64 on the exactly dequantised int4 weights."""
     E = lay["w_gu"].shape[0]
     x = np.asarray(hn_bf16_vals, np.float64)
-    ids, w = topk_route(logits, k)
+    ids, w = _route(logits, k, forced)
     out = np.zeros_like(x)
     for e in range(E):
         t, j = np.nonzero(ids == e)
@@ -104,38 +115,53 @@ def _moe_bf16(hn_bf16_vals, logits, lay, k):
         h = round_bf16(swiglu(x[t] @ wgu.T))
         y = round_bf16(h @ wdn.T)
         np.add.at(out, t, w[t, j][:, None] * y)
-    return out
+    return out, ids
 
 
 def stack_forward(inp: dict, n_q: int, n_kv: int, d: int, k: int, fp8: bool = True,
-                  return_layers: bool = False):
+                  return_layers: bool = False, perturb=None, route_ids=None,
+                  return_routes: bool = False):
     """Run the stack on ``synth.stack_inputs`` data. Returns fp32 logits [T, V] (float64
-    array of fp32-rounded values) and, if asked, the per-layer residual streams."""
+    array of fp32-rounded values) and, if asked, the per-layer residual streams and the
+    per-layer expert ids.
+
+    Probes of the stack's sensitivity (none changes the arithmetic when left at None):
+    ``perturb`` is applied to every dense projection output (q/k/v and o) before its bf16
+    rounding; ``route_ids`` (one [T, k] array per layer) replaces the top-k choice of each
+    layer's experts, the weights coming from that layer's own router logits."""
     x = round_bf16(bf16_to_f32(inp["x0"]))
     nq = n_q * d
     nk = n_kv * d
-    trace = []
-    for lay in inp["layers"]:
+    trace, routes = [], []
+    pert = (lambda y: y) if perturb is None else perturb
+    for li, lay in enumerate(inp["layers"]):
         hn = round_bf16(rmsnorm(x))
         if fp8:
             wq, sw = quantize_weight(lay["w_qkv"])
-            qkv = round_bf16(_w8a8(hn, wq, sw))
+            qkv = round_bf16(pert(_w8a8(hn, wq, sw)))
         else:
-            qkv = round_bf16(hn @ bf16_to_f32(lay["w_qkv"]).astype(np.float64).T)
+            qkv = round_bf16(pert(hn @ bf16_to_f32(lay["w_qkv"]).astype(np.float64).T))
         att = round_bf16(causal_gqa_attention(qkv[:, :nq], qkv[:, nq:nq + nk],
                                               qkv[:, nq + nk:], n_q, n_kv, d))
         if fp8:
             wo, so = quantize_weight(lay["w_o"])
-            o = round_bf16(_w8a8(att, wo, so))
+            o = round_bf16(pert(_w8a8(att, wo, so)))
         else:
-            o = round_bf16(att @ bf16_to_f32(lay["w_o"]).astype(np.float64).T)
+            o = round_bf16(pert(att @ bf16_to_f32(lay["w_o"]).astype(np.float64).T))
         x = round_bf16(x + o)
         hn2 = round_bf16(rmsnorm(x))
         logits = (hn2 @ bf16_to_f32(lay["w_router"]).astype(np.float64).T).astype(np.float32)
-        moe = _moe_fp8(hn2, logits, lay, k) if fp8 else _moe_bf16(hn2, logits, lay, k)
+        forced = None if route_ids is None else route_ids[li]
+        moe, ids = (_moe_fp8 if fp8 else _moe_bf16)(hn2, logits, lay, k, forced)
+        routes.append(ids)
         x = round_bf16(x + round_bf16(moe))
         if return_layers:
             trace.append(x.copy())
     hf = round_bf16(rmsnorm(x))
-    out = (hf @ bf16_to_f32(inp["w_lm"]).astype(np.float64).T).astype(np.float32)
-    return (out.astype(np.float64), trace) if return_layers else out.astype(np.float64)
+    out = (hf @ bf16_to_f32(inp["w_lm"]).astype(np.float64).T).astype(np.float32).astype(np.float64)
+    res = (out,)
+    if return_layers:
+        res += (trace,)
+    if return_routes:
+        res += (routes,)
+    return res if len(res) > 1 else out
