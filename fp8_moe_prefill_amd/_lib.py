@@ -9,6 +9,8 @@ there is no CPU path. If the library is missing this module raises at import.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 
 import torch
@@ -91,6 +93,24 @@ def _check(fn: str, status: int) -> None:
         raise Fp8MoeError(fn, status)
 
 
+def _on_stream(fn):
+    """Run a wrapper with ``stream`` as torch's current stream, so that the outputs and
+    workspaces it allocates belong to that stream in the caching allocator: a temporary
+    freed when the wrapper returns is then reused only by work ordered after the kernels
+    that still read it (torch's rule for memory used on one stream)."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapped(*args, **kw):
+        stream = sig.bind_partial(*args, **kw).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kw)
+
+    return wrapped
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -138,6 +158,7 @@ def abi_version() -> int:
 # ------------------------------------------------------------------------------------
 
 
+@_on_stream
 def fp8_quant_act(x: torch.Tensor, group: int = GROUP, q=None, scales=None, ws=None,
                   stream=None, sums=None, with_sums: bool = False):
     """bf16 [M, K] -> (e4m3 codes uint8 [M, K], fp32 scales: [M, K/128] for group=128,
@@ -159,6 +180,7 @@ def fp8_quant_act(x: torch.Tensor, group: int = GROUP, q=None, scales=None, ws=N
     return (q, scales, sums) if sums is not None else (q, scales)
 
 
+@_on_stream
 def moe_route_permute(logits: torch.Tensor, k: int, xq=None, xs=None, out=None, ws=None,
                       stream=None, xsum=None) -> dict:
     """fp32 logits [T, E] -> dict(ids, weights, offsets, sorted, pos[, xq_perm][, xs_perm]
@@ -210,6 +232,7 @@ def moe_route_permute(logits: torch.Tensor, k: int, xq=None, xs=None, out=None, 
     return r
 
 
+@_on_stream
 def pack_expert_bank(w: torch.Tensor, w_scales: torch.Tensor, out=None, stream=None,
                      mxfp4: bool = False):
     """Canonical bank (packed int4 [E, N, K/2], low nibble = even k; fp32 scales
@@ -230,6 +253,7 @@ def pack_expert_bank(w: torch.Tensor, w_scales: torch.Tensor, out=None, stream=N
     return wp, sp
 
 
+@_on_stream
 def fp8_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=EPI_STORE,
                             out_dtype=torch.float32, sorted_=None, k_route: int = 1, out=None,
                             out_scales=None, stream=None, a_sums=None, out_sums=None,
@@ -247,6 +271,7 @@ def fp8_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=
                     out, out_scales, stream, False, a_sums, out_sums, with_sums)
 
 
+@_on_stream
 def mxfp4_grouped_expert_gemm(a, a_scales, w, w_scales, offsets, R: int, epilogue=EPI_STORE,
                               out_dtype=torch.float32, sorted_=None, k_route: int = 1,
                               out=None, out_scales=None, stream=None, out_sums=None,
@@ -317,6 +342,7 @@ def _grouped(a, a_scales, w, w_scales, offsets, R, epilogue, out_dtype, sorted_,
     return (out, out_scales, out_sums) if out_sums is not None else (out, out_scales)
 
 
+@_on_stream
 def mxfp4_quant_act(x: torch.Tensor, q=None, scales=None, stream=None):
     """bf16 [M, K] -> (MXFP4 codes uint8 [M, K/2], E8M0 scale bytes uint8 [M, K/32])."""
     _dev(x, "x", torch.bfloat16)
@@ -330,6 +356,7 @@ def mxfp4_quant_act(x: torch.Tensor, q=None, scales=None, stream=None):
     return q, scales
 
 
+@_on_stream
 def fp8_dense_gemm(a, a_scale_blk, w, w_scale, out_dtype=torch.bfloat16, out=None, stream=None):
     """e4m3 [M, K] x e4m3 [N, K]^T with scales s_a = a_scale_blk[2], s_w = w_scale[0]."""
     _dev(a, "a", torch.uint8)
@@ -346,6 +373,7 @@ def fp8_dense_gemm(a, a_scale_blk, w, w_scale, out_dtype=torch.bfloat16, out=Non
     return out
 
 
+@_on_stream
 def fp8_dense_gemm_rowwise(a, a_scales, w, w_scale, out_dtype=torch.bfloat16, out=None,
                            stream=None):
     """e4m3 [M, K] x e4m3 [N, K]^T with one activation scale per row (a_scales fp32 [M])
@@ -366,6 +394,7 @@ def fp8_dense_gemm_rowwise(a, a_scales, w, w_scale, out_dtype=torch.bfloat16, ou
     return out
 
 
+@_on_stream
 def fp8_quant_weight_block128(w, q=None, scales=None, stream=None):
     """bf16 weight [N, K] -> (e4m3 codes [N, K], fp32 block scales [ceil(N/128), K/128])."""
     _dev(w, "w", torch.bfloat16)
@@ -379,6 +408,7 @@ def fp8_quant_weight_block128(w, q=None, scales=None, stream=None):
     return q, scales
 
 
+@_on_stream
 def fp8_block_gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16, out=None, stream=None):
     """e4m3 [M, K] (scales fp32 [M, K/128]) x block-128 e4m3 [N, K] (scales fp32
     [ceil(N/128), K/128])."""
@@ -401,6 +431,7 @@ def fp8_block_gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16, out=None,
     return out
 
 
+@_on_stream
 def moe_unpermute_combine(y, pos, weights, out_dtype=torch.bfloat16, out=None, stream=None):
     """out[t] = sum_j weights[t, j] * y[pos[t*k + j]]."""
     _dev(y, "y")
@@ -423,6 +454,7 @@ def moe_unpermute_combine(y, pos, weights, out_dtype=torch.bfloat16, out=None, s
 RMSNORM_EPS = 1e-6
 
 
+@_on_stream
 def rmsnorm(x: torch.Tensor, delta=None, eps: float = RMSNORM_EPS, x_out=None, y=None,
             stream=None):
     """y = bf16(RMSNorm(x)) or, with ``delta``, x_out = bf16(x + delta) and
@@ -445,6 +477,7 @@ def rmsnorm(x: torch.Tensor, delta=None, eps: float = RMSNORM_EPS, x_out=None, y
     return (x_out, y) if delta is not None else y
 
 
+@_on_stream
 def bf16_gemm(a: torch.Tensor, w: torch.Tensor, out=None, stream=None):
     """fp32 [M, N] = a [M, K] . w [N, K]^T, bf16 operands."""
     _dev(a, "a", torch.bfloat16)
@@ -461,6 +494,7 @@ def bf16_gemm(a: torch.Tensor, w: torch.Tensor, out=None, stream=None):
     return out
 
 
+@_on_stream
 def causal_attention(qkv: torch.Tensor, n_q: int, n_kv: int, head_dim: int = 128, out=None,
                      ws=None, stream=None):
     """bf16 [T, (n_q + 2 n_kv) * d] fused q|k|v -> bf16 [T, n_q * d]."""

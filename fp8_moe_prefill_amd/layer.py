@@ -148,16 +148,16 @@ class MoELayerRunner:
 
     def run(self, x, logits, bank: ExpertBank, events=None, stream=None):
         ev = events or {}
+        main = torch.cuda.current_stream() if stream is None else stream
 
-        def mark(name, i):
+        def mark(name, i):  # on the stream the layer's kernels are launched on
             if name in ev:
-                ev[name][i].record()
+                ev[name][i].record(main)
 
         rt = self.route
         mx = self.act == "mxfp4"
         if bank.act != self.act:
             raise ValueError(f"bank packed for {bank.act} activations, runner for {self.act}")
-        main = torch.cuda.current_stream() if stream is None else stream
         mark("quant", 0)
         if mx:
             _lib.mxfp4_quant_act(x, q=self.xq, scales=self.xs, stream=main)
@@ -169,18 +169,7 @@ class MoELayerRunner:
         _lib.moe_route_permute(logits, self.k, out=rt, ws=self.ws, stream=main)
         mark("route", 1)
         mark("gate_up", 0)
-        # rows gathered from token order through `sorted`, with their per-token scales
-        # (and code sums) straight from the quantiser's output
-        if mx:
-            _lib.mxfp4_grouped_expert_gemm(
-                self.xq, self.xs.view(torch.float32), bank.w_gu, bank.s_gu, rt["offsets"],
-                self.R, _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k,
-                out=self.hq, out_scales=self.hs, out_sums=self.hsum, stream=main)
-        else:
-            _lib.fp8_grouped_expert_gemm(
-                self.xq, self.xs, bank.w_gu, bank.s_gu, rt["offsets"], self.R,
-                _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k, out=self.hq,
-                out_scales=self.hs, out_sums=self.hsum, stream=main, a_sums=self.xsum)
+        self.run_gate_up(bank, stream=main)
         mark("gate_up", 1)
         mark("down", 0)
         _lib.fp8_grouped_expert_gemm(self.hq, self.hs, bank.w_dn, bank.s_dn, rt["offsets"],
@@ -192,3 +181,21 @@ class MoELayerRunner:
                                    stream=main)
         mark("combine", 1)
         return self.out
+
+    def run_gate_up(self, bank: ExpertBank, stream=None):
+        """The gate|up stage alone (grouped GEMM + SwiGLU + requantisation) on the
+        quantised activations and routing the last ``run`` left in this runner."""
+        main = torch.cuda.current_stream() if stream is None else stream
+        rt = self.route
+        # rows gathered from token order through `sorted`, with their per-token scales
+        # (and code sums) straight from the quantiser's output
+        if self.act == "mxfp4":
+            _lib.mxfp4_grouped_expert_gemm(
+                self.xq, self.xs.view(torch.float32), bank.w_gu, bank.s_gu, rt["offsets"],
+                self.R, _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k,
+                out=self.hq, out_scales=self.hs, out_sums=self.hsum, stream=main)
+        else:
+            _lib.fp8_grouped_expert_gemm(
+                self.xq, self.xs, bank.w_gu, bank.s_gu, rt["offsets"], self.R,
+                _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k, out=self.hq,
+                out_scales=self.hs, out_sums=self.hsum, stream=main, a_sums=self.xsum)

@@ -137,8 +137,11 @@ def _swiglu_check(hq, hs, y_gu32):
     ds = np.abs(hs.astype(np.float64) - rs) / rs
     assert ds.max() <= 4e-6, ds.max()
     same = hq == rq
-    frac = same.mean()
-    assert frac >= 0.999, frac
+    # fewer than 1e-4 of the codes may differ (an fp32 discrepancy of about 1e-6 relative
+    # against a code spacing of 2^-4 flags about 2e-5 of them), each one only by the
+    # rounding-boundary rule below
+    miss = 1.0 - same.mean()
+    assert miss < 1e-4, miss
     if not same.all():
         i = np.nonzero(~same)
         # adjacent codes only (same sign; code indices one apart)

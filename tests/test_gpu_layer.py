@@ -133,3 +133,101 @@ def test_layer_mxfp4_activations(cfg, T):
         y = bf16_values(st["y"])[rows, cols]
         check_close(y, y_ref, gemm_bound(b) + half_ulp_bf16(y_ref), "down sampled")
     assert cosine(bf16_values(out), ref["out"]) > 0.999
+
+
+def test_layer_on_side_stream_while_current_stream_allocates():
+    """moe_layer(stream=s) with torch's current stream allocating and writing memory
+    while s still runs: the layer's temporaries (quantised rows, routing, intermediate
+    codes, down-GEMM rows) belong to s, so the current stream cannot be handed them before
+    s is done with them; the output equals the one computed on the current stream."""
+    import fp8_moe_prefill_amd as f
+    c = CONFIGS["moe_prefill"]
+    inp = moe_inputs(c, T=1024)
+    bank = f.ExpertBank.from_host(inp, "cuda:0")
+    x, lg = dev(inp["x"]), dev(inp["logits"])
+    ref = f.moe_layer(x, lg, bank, c.k)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        outs.append(f.moe_layer(x, lg, bank, c.k, stream=s))
+        # the current stream takes and overwrites memory at once (not ordered after s)
+        junk = [torch.full((1 << 20,), 7, dtype=torch.int32, device="cuda:0") for _ in range(48)]
+        del junk
+    s.synchronize()
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)
+
+
+def _skewed_rows(off, rng):
+    """Rows of the skewed layer to sample: the last row of every non-empty expert, the
+    first and last rows of each of expert 0's 128-row tiles and around its last partial
+    tile, and random rows."""
+    rows = [int(off[e + 1]) - 1 for e in range(len(off) - 1) if off[e + 1] > off[e]]
+    lo, hi = int(off[0]), int(off[1])
+    for m in range(lo, hi, 128):
+        rows += [m, min(m + 127, hi - 1)]
+    rows += list(range(max(lo, hi - 20), hi))
+    rows += rng.integers(0, int(off[-1]), 400).tolist()
+    return np.unique(np.array(rows, np.int64))
+
+
+def test_skewed_layer_gate_up_swiglu_and_tokens():
+    """The skewed large layer (16384 tokens, hidden 4096, 128 Zipf-routed experts with
+    empty ones, I = 1536): gate|up fp32 outputs on sampled rows (every expert's last row,
+    expert 0's ~16k rows at every tile boundary) within the element bound; the fused SwiGLU
+    codes and scales on those rows against the oracle's SwiGLU of the GPU's own
+    accumulators; and the layer output of sampled tokens against the oracle layer run on
+    those tokens (a token's output depends on its own row and routing only)."""
+    import fp8_moe_prefill_amd as f
+    from fp8_moe_prefill_amd import _lib
+    from oracle.moe import moe_layer as oracle_layer
+    from oracle.route import permute_rows
+    from tests.test_gpu_grouped_gemm import _swiglu_check
+    c = CONFIGS["moe_skewed"]
+    inp = moe_inputs(c)
+    bank = f.ExpertBank.from_host(inp, "cuda:0")
+    x, lg = dev(inp["x"]), dev(inp["logits"])
+    out, st = f.moe_layer(x, lg, bank, c.k, keep=True)
+    R = c.T * c.k
+    y32 = _lib.fp8_grouped_expert_gemm(st["xq"], st["xs"], bank.w_gu, bank.s_gu, st["offsets"],
+                                       R, _lib.EPI_STORE, torch.float32, sorted_=st["sorted"],
+                                       k_route=c.k, a_sums=st["xsum"])
+    torch.cuda.synchronize()
+    off = host(st["offsets"]).astype(np.int64)
+    ids, _ = topk_route(inp["logits"], c.k)
+    off_ref, sorted_, _ = group_pairs(ids, c.E)
+    assert_bytes_equal(off.astype(np.int32), off_ref, "offsets")
+    assert (np.diff(off) == 0).sum() >= 1 and np.diff(off).max() > 16000
+    rng = np.random.default_rng(5)
+    rows = _skewed_rows(off, rng)
+    xq, xs = quant_group_bf16(inp["x"])
+    aq, as_ = permute_rows(xq, sorted_, c.k), permute_rows(xs, sorted_, c.k)
+    # gate|up: 8 random columns and the first/last gate and up columns of each sampled row
+    N = 2 * c.I
+    cols = np.concatenate([rng.integers(0, N, (len(rows), 8)),
+                           np.tile([0, c.I - 1, c.I, N - 1], (len(rows), 1))], axis=1)
+    rr = np.repeat(rows, cols.shape[1])
+    cc = cols.reshape(-1)
+    yr, b = grouped_gemm_rows(aq, as_, inp["w_gu"], inp["s_gu"], off_ref, rr, cc)
+    y_rows = y32[torch.from_numpy(rows).cuda()].cpu().numpy()
+    yg = y_rows[np.repeat(np.arange(len(rows)), cols.shape[1]), cc].astype(np.float64)
+    check_close(yg, yr, gemm_bound(b), "skewed gate|up sampled")
+    # the fused SwiGLU + requantisation on those rows
+    hq = host(st["hq"])[rows]
+    hs = np.ascontiguousarray(host(st["hs"])[:, rows].T)
+    _swiglu_check(hq, hs, y_rows)
+    # end to end on sampled tokens: mostly tokens routed among the popular experts, plus
+    # tokens reaching the highest-index non-empty expert
+    last_e = int(np.nonzero(np.diff(off) > 0)[0].max())
+    popular = np.nonzero(ids.max(axis=1) < 20)[0]
+    rare = np.nonzero((ids == last_e).any(axis=1))[0]
+    toks = np.unique(np.concatenate([rng.choice(popular, 40, replace=False), rare[:4]]))
+    ref = oracle_layer(inp["x"][toks], inp["logits"][toks], inp["w_gu"], inp["s_gu"],
+                       inp["w_dn"], inp["s_dn"], c.k)
+    got = bf16_values(out)[toks]
+    assert cosine(got, ref["out"]) > 0.999
+    for i in range(len(toks)):
+        assert cosine(got[i], ref["out"][i]) > 0.99
