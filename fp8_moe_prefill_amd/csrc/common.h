@@ -1,7 +1,7 @@
 // Device helpers shared by the HIP kernels of the FP8 MoE prefill library (gfx950).
 //
 // e4m3 here is OCP e4m3fn: the format the activation scale amax/448 implies (memra-engine
-// fp8_ffi module docs: "f32 -> e4m3 with ONE per-batch scalar scale (amax/448)").
+// fp8_ffi module docs, module text: one dynamic scale per tensor, computed as amax/448).
 #pragma once
 
 #include <hip/hip_runtime.h>

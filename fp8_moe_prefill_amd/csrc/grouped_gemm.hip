@@ -344,8 +344,22 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   const float* ws_exp = Ws;
   const uint32_t lane16 = (uint32_t)lane * 16u;
 
-  auto dma_group = [&](int d, Stage& st) {
-    const int jd = d / G, gd = d - jd * G;
+  // The loads of one K group are prepared once per group (dma_prepare: the tile bookkeeping
+  // and the group's uniform source bases) and issued one instruction at a time (dma_issue,
+  // k = 0..10) between the MFMA steps of the group being computed. Issued together, the 88
+  // loads of a CU's eight waves queue in the memory pipeline for about a thousand cycles and
+  // stall the waves that issue them; spread out, the queue stays short.
+  int lj = 0, lg = -1;  // tile (of this workgroup's list) and K group being loaded
+  const uint8_t* ld_a = A;
+  const uint8_t* ld_b = W;
+  const float* ld_ws = Ws;
+  int64_t ld_as = 0;
+  auto dma_prepare = [&]() {
+    if (++lg == G) {
+      lg = 0;
+      ++lj;
+    }
+    const int gd = lg;
     if (gd == 0) {
       // a new tile enters the stream: set up its sources from the prefetched descriptor
       const TileDesc t = pend;
@@ -391,24 +405,35 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
     }
     // the next tile enters the stream at the next group: fetch its descriptor and rows now,
     // before this group's loads
-    if (gd == G - 1 && jd + 1 < my_tiles) {
-      pend = tile_of(jd + 1);
+    if (gd == G - 1 && lj + 1 < my_tiles) {
+      pend = tile_of(lj + 1);
       fetch_rows(pend);
     }
-    const uint8_t* ag = A + gd * (AF4 ? kGroup / 2 : kGroup);
-#pragma unroll
-    for (int j = 0; j < A_DMA; ++j) dma16(ag, a_off32[j], st.a + (wv * A_DMA + j) * 1024);
-    uint8_t* sb = st.b + wv * BW_BYTES;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) dma16(w_exp + b_blk[s] + gd * kBlockBytes, lane16, sb + s * 1024);
-    dma4(ws_exp + (int64_t)gd * N, ws_off32, st.ws + wv * WCOLS);
+    ld_a = A + gd * (AF4 ? kGroup / 2 : kGroup);
+    ld_b = w_exp + gd * kBlockBytes;
+    ld_ws = ws_exp + (int64_t)gd * N;
     // group gd of the rows' scales (and sums): column gd of the per-token arrays, or row gd
     // of the group-major ones
-    const int64_t as_base = sorted ? (int64_t)gd : (int64_t)gd * R;
-    if (lane < RPW) dma4(As + as_base, as_off32, st.as + wv * RPW);
-    // given code sums replace the in-kernel row sums: they land where the seeds go
-    if (SUMS && lane < RPW) dma4(Asum + as_base, as_off32, st.ra + wv * RPW);
+    ld_as = sorted ? (int64_t)gd : (int64_t)gd * R;
   };
+  // load k of the prepared group into stage st: the wave's four bank blocks first (they
+  // may come from HBM), then its rows of the A tile, the weight scales, and the rows'
+  // activation scales and code sums
+  auto dma_issue = [&](int k, Stage& st) {
+    if (k < 4) {
+      dma16(ld_b + b_blk[k], lane16, st.b + wv * BW_BYTES + k * 1024);
+    } else if (k < 4 + A_DMA) {
+      dma16(ld_a, a_off32[k - 4], st.a + (wv * A_DMA + k - 4) * 1024);
+    } else if (k == 4 + A_DMA) {
+      dma4(ld_ws, ws_off32, st.ws + wv * WCOLS);
+    } else if (k == 5 + A_DMA) {
+      if (lane < RPW) dma4(As + ld_as, as_off32, st.as + wv * RPW);
+    } else if (k == 6 + A_DMA) {
+      // given code sums replace the in-kernel row sums: they land where the seeds go
+      if (SUMS && lane < RPW) dma4(Asum + ld_as, as_off32, st.ra + wv * RPW);
+    }
+  };
+  constexpr int N_DMA = 7 + A_DMA;  // loads per wave and K group
 
   // sum of this wave's 16-row tile of the A tile of stage st -> st.ra as -sum/64, the
   // accumulator seed that removes the +8 offset of the B codes
@@ -452,9 +477,12 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   // MFMA of step i-2 (already complete), so the matrix core and the VALU work side by
   // side; a sched_barrier after every step pins that interleaving. The first group of a
   // tile initialises the accumulators (no separate zeroing).
-  auto group = [&](auto first_tag, auto tmax_tag, const Stage& cur) {
+  auto group = [&](auto first_tag, auto tmax_tag, const Stage& cur, auto&& issue) {
     constexpr bool FIRST = decltype(first_tag)::value;
     constexpr int tmax = decltype(tmax_tag)::value;
+    // MFMA step after which load k of the next group is issued: spread over the first two
+    // thirds of the group's steps (all up front when the group is a single row tile)
+    constexpr int kIssueStride = tmax == 8 ? 2 : tmax == 4 ? 1 : 0;
     const uint8_t* ta = cur.a;
     const uint8_t* tb = cur.b + wv * BW_BYTES;
     const float* ra = cur.ra;
@@ -537,6 +565,9 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
           pb[i % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               aop[t & 1], bop[s], seed[t & 1], 0, 0, 0, 0, 0, 0);
       }
+#pragma unroll
+      for (int k = 0; k < N_DMA; ++k)
+        if (k * kIssueStride == i) issue(k);
       if (i >= 2 && ((i - 2) >> 2) < tmax) fold(i - 2);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -651,7 +682,8 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   };
 
   // ---- prologue: group 0 loaded, its seeds formed
-  dma_group(0, ring[0]);
+  dma_prepare();
+  for (int k = 0; k < N_DMA; ++k) dma_issue(k, ring[0]);
   wait_all_loads();
   row_sums(ring[0]);
   lds_barrier();
@@ -665,8 +697,10 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   auto step = [&](auto first_tag, auto tmax_tag) {
     const int stage = s & 1;
     const bool more = s + 1 < total_steps;
-    if (more) dma_group(s + 1, ring[stage ^ 1]);
-    group(first_tag, tmax_tag, ring[stage]);
+    if (more) dma_prepare();
+    group(first_tag, tmax_tag, ring[stage], [&](int k) {
+      if (more) dma_issue(k, ring[stage ^ 1]);
+    });
     wait_all_loads();  // own loads of group s+1 landed
     if (more) row_sums(ring[stage ^ 1]);
     lds_barrier();

@@ -15,7 +15,7 @@
 // Scale rule amax/448: memra-engine fp8_ffi module docs.
 //
 // Both modes are HBM-bound streaming kernels: each thread reads 16-byte chunks (8 bf16),
-// four of them in flight at once, and writes 8 bytes per chunk; a 128-group is the 16
+// two of them in flight at once, and writes 8 bytes per chunk; a 128-group is the 16
 // consecutive lanes of a quarter wave, so its amax is a 4-step cross-lane reduction with
 // no LDS and no host synchronisation.
 #include "common.h"

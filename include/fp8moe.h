@@ -205,8 +205,8 @@ int32_t fp8moe_pack_expert_bank(const uint8_t* w, const float* w_scales, int64_t
  * fp8_grouped_expert_gemm -- one launch over every expert.
  *
  * [P1] section 1: a single grouped expert GEMM per layer; int4 weights turned into
- * e4m3 on-chip without unpacking the resident packed-int4 bank; the per-(token, group)
- * activation scale folded into the accumulator.
+ * e4m3 on-chip without unpacking the resident packed-int4 bank; one dynamic activation
+ * scale per (token, K group), applied inside the fp32 accumulation.
  *
  * For grouped row i in expert e's range [offsets[e], offsets[e+1]) and column n:
  *   y[i, n] = sum_g s_a(i, g) * w_scales[e, n, g]
@@ -436,8 +436,10 @@ int32_t fp8moe_bf16_gemm(const void* a, const void* w, int64_t M, int64_t N, int
  * [P1] sections 1 and 3: the attention core between the FP8 q/k/v and o projections
  * stays bf16. Reading used: no rotary embedding; query head h reads kv head
  * h / (n_q / n_kv); o[t, h] = sum_{s <= t} softmax_s(q[t, h] . k[s, kv] / sqrt(d)) v[s, kv]
- * with scores, softmax and the sum in fp32 and the weights rounded to bf16 for the
- * product with v (their row sum uses the same rounded weights).
+ * with scores, softmax and the sum in fp32. The softmax weights enter the product with v
+ * on the bf16 matrix cores as two bf16 terms, hi = bf16(p) and lo = bf16(p - hi) (about
+ * 16 significant bits), so that product keeps close to fp32 accuracy; the row sum of the
+ * weights is taken in fp32.
  *
  *   qkv   bf16 [T, (n_q + 2 n_kv) * d]: row t = [q heads | k heads | v heads], head-major
  *   out   out, bf16 [T, n_q * d], head-major
