@@ -10,9 +10,8 @@ from ._lib import (  # noqa: F401
     DTYPE_BF16, DTYPE_F32, EPI_STORE, EPI_SWIGLU_QUANT, GROUP, QUANT_ROW, Fp8MoeError,
     LIB_PATH, abi_version, bf16_gemm, causal_attention, fp8_dense_gemm, fp8_dense_gemm_rowwise,
     fp8_block_gemm, fp8_grouped_expert_gemm, fp8_quant_weight_block128, mxfp4_grouped_expert_gemm,
-    mxfp4_quant_act,
-    fp8_quant_act, moe_route_permute, moe_unpermute_combine, pack_expert_bank, rmsnorm,
-    workspace_bytes,
+    mxfp4_quant_act, fp8_quant_act, moe_route_permute, moe_route_permute_noalloc,
+    moe_unpermute_combine, pack_expert_bank, rmsnorm, workspace_bytes,
 )
 from .layer import ExpertBank, MoELayerRunner, moe_layer, quantize_weight, w8a8_linear  # noqa: F401
 from .stack import DepthStack, StackRunner  # noqa: F401

@@ -38,6 +38,10 @@ SIGNATURES = {
     "moe_route_permute": (_i32, [_c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "moe_route_permute_noalloc": (_i32, [_c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p,
+                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                         _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_void_p]),
     "fp8moe_pack_expert_bank": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p,
                                        _c_void_p, _c_void_p]),
     "fp8_grouped_expert_gemm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
@@ -180,6 +184,36 @@ def fp8_quant_act(x: torch.Tensor, group: int = GROUP, q=None, scales=None, ws=N
     return (q, scales, sums) if sums is not None else (q, scales)
 
 
+def _route_buffers(logits, k, xq, xs, xsum, out):
+    _dev(logits, "logits", torch.float32)
+    T, E = logits.shape
+    dev = logits.device
+    o = out if out is not None else {}
+
+    def buf(name, shape, dtype):
+        return o[name] if name in o else torch.empty(shape, dtype=dtype, device=dev)
+
+    r = dict(ids=buf("ids", (T, k), torch.int32), weights=buf("weights", (T, k), torch.float32),
+             offsets=buf("offsets", (E + 1,), torch.int32),
+             sorted=buf("sorted", (T * k,), torch.int32), pos=buf("pos", (T * k,), torch.int32))
+    H = 0
+    if xq is not None:
+        _dev(xq, "xq", torch.uint8)
+        H = xq.shape[1]
+        r["xq_perm"] = buf("xq_perm", (T * k, H), torch.uint8)
+    if xs is not None:
+        _dev(xs, "xs", torch.float32)
+        H = xs.shape[1] * GROUP
+        r["xs_perm"] = buf("xs_perm", (H // GROUP, T * k), torch.float32)
+    if xsum is not None:
+        _dev(xsum, "xsum", torch.float32)
+        r["xsum_perm"] = buf("xsum_perm", (H // GROUP, T * k), torch.float32)
+    head = (_ptr(logits), T, E, k, _ptr(r["ids"]), _ptr(r["weights"]), _ptr(r["offsets"]),
+            _ptr(r["sorted"]), _ptr(r["pos"]), _ptr(xq), _ptr(xs), H, _ptr(r.get("xq_perm")),
+            _ptr(r.get("xs_perm")), _ptr(xsum), _ptr(r.get("xsum_perm")))
+    return r, head
+
+
 @_on_stream
 def moe_route_permute(logits: torch.Tensor, k: int, xq=None, xs=None, out=None, ws=None,
                       stream=None, xsum=None) -> dict:
@@ -189,46 +223,23 @@ def moe_route_permute(logits: torch.Tensor, k: int, xq=None, xs=None, out=None, 
     ``xq`` (e4m3 [T, H]) is gathered into xq_perm [T*k, H]; ``xs`` (fp32 [T, H/128]) into
     xs_perm [H/128, T*k], group-major; ``xsum`` (the code sums, fp32 [T, H/128], only with
     ``xs``) into xsum_perm of the same layout as xs_perm. xq and xs may be given alone."""
-    _dev(logits, "logits", torch.float32)
+    r, head = _route_buffers(logits, k, xq, xs, xsum, out)
     T, E = logits.shape
-    dev = logits.device
-    o = out if out is not None else {}
-
-    def buf(name, shape, dtype):
-        return o[name] if name in o else torch.empty(shape, dtype=dtype, device=dev)
-
-    ids = buf("ids", (T, k), torch.int32)
-    w = buf("weights", (T, k), torch.float32)
-    offsets = buf("offsets", (E + 1,), torch.int32)
-    sorted_ = buf("sorted", (T * k,), torch.int32)
-    pos = buf("pos", (T * k,), torch.int32)
-    H = 0
-    xq_perm = xs_perm = None
-    if xq is not None:
-        _dev(xq, "xq", torch.uint8)
-        H = xq.shape[1]
-        xq_perm = buf("xq_perm", (T * k, H), torch.uint8)
-    if xs is not None:
-        _dev(xs, "xs", torch.float32)
-        H = xs.shape[1] * GROUP
-        xs_perm = buf("xs_perm", (H // GROUP, T * k), torch.float32)
-    xsum_perm = None
-    if xsum is not None:
-        _dev(xsum, "xsum", torch.float32)
-        xsum_perm = buf("xsum_perm", (H // GROUP, T * k), torch.float32)
     nbytes = workspace_bytes(OP_ROUTE_PERMUTE, T, E, k)
-    wsb = _workspace(nbytes, dev, ws)
-    _check("moe_route_permute", _lib.moe_route_permute(
-        _ptr(logits), T, E, k, _ptr(ids), _ptr(w), _ptr(offsets), _ptr(sorted_), _ptr(pos),
-        _ptr(xq), _ptr(xs), H, _ptr(xq_perm), _ptr(xs_perm), _ptr(xsum), _ptr(xsum_perm),
-        _ptr(wsb), nbytes, _stream(stream)))
-    r = dict(ids=ids, weights=w, offsets=offsets, sorted=sorted_, pos=pos)
-    if xq is not None:
-        r.update(xq_perm=xq_perm)
-    if xs is not None:
-        r.update(xs_perm=xs_perm)
-    if xsum is not None:
-        r.update(xsum_perm=xsum_perm)
+    wsb = _workspace(nbytes, logits.device, ws)
+    _check("moe_route_permute", _lib.moe_route_permute(*head, _ptr(wsb), nbytes,
+                                                       _stream(stream)))
+    return r
+
+
+@_on_stream
+def moe_route_permute_noalloc(logits: torch.Tensor, k: int, xq=None, xs=None, out=None,
+                              stream=None, xsum=None) -> dict:
+    """moe_route_permute with the library's static per-GPU workspace instead of a caller
+    one: the C call allocates nothing (outputs missing from ``out`` are still allocated
+    here, by torch). Calls that overlap in time on one GPU race on that workspace."""
+    r, head = _route_buffers(logits, k, xq, xs, xsum, out)
+    _check("moe_route_permute_noalloc", _lib.moe_route_permute_noalloc(*head, _stream(stream)))
     return r
 
 

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 7;
+constexpr int32_t kAbiVersion = 8;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 constexpr int64_t kMaxGroupedK = 16384;
@@ -26,6 +26,33 @@ size_t quant_ws(int64_t M, int64_t K, int32_t group) {
   if (group == 0 && M * K > fp8moe::kQuantFusedMax)
     return (size_t)fp8moe::kQuantPartials * sizeof(float);
   return 0;
+}
+
+// Argument checks shared by both routing entry points (everything but the workspace).
+int32_t check_route(const float* logits, int64_t T, int32_t E, int32_t k, const int32_t* ids,
+                    const float* weights, const int32_t* offsets, const int32_t* sorted,
+                    const int32_t* pos, const uint8_t* xq, const float* xs, int64_t H,
+                    const uint8_t* xq_perm, const float* xs_perm, const float* xsum,
+                    const float* xsum_perm) {
+  if (!logits || !ids || !weights || !offsets || !sorted || !pos) return FP8MOE_ERR_NULL;
+  // the row gather (xq -> xq_perm) and the scale gather (xs -> xs_perm) are independent
+  // options, each all-or-nothing; the code-sum gather (xsum -> xsum_perm) rides the scale
+  // gather
+  if ((xq != nullptr) != (xq_perm != nullptr)) return FP8MOE_ERR_NULL;
+  if ((xs != nullptr) != (xs_perm != nullptr)) return FP8MOE_ERR_NULL;
+  if ((xsum != nullptr) != (xsum_perm != nullptr)) return FP8MOE_ERR_NULL;
+  if (xsum && !xs) return FP8MOE_ERR_NULL;
+  if (xsum && (!aligned16(xsum) || !aligned16(xsum_perm))) return FP8MOE_ERR_ALIGN;
+  const bool rows = xq != nullptr, scales = xs != nullptr;
+  if (T < 1 || E < 1 || E > kMaxE || k < 1 || k > E || k > kMaxK) return FP8MOE_ERR_SHAPE;
+  if (T * (int64_t)k >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
+  if ((rows || scales) && (H < FP8MOE_GROUP || H % FP8MOE_GROUP != 0)) return FP8MOE_ERR_SHAPE;
+  const void* ptrs[] = {logits, ids, weights, offsets, sorted, pos};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
+  if (rows && (!aligned16(xq) || !aligned16(xq_perm))) return FP8MOE_ERR_ALIGN;
+  if (scales && (!aligned16(xs) || !aligned16(xs_perm))) return FP8MOE_ERR_ALIGN;
+  return FP8MOE_OK;
 }
 
 }  // namespace
@@ -96,25 +123,29 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, 
                           const uint8_t* xq, const float* xs, int64_t H, uint8_t* xq_perm,
                           float* xs_perm, const float* xsum, float* xsum_perm, void* ws,
                           size_t ws_bytes, void* stream) {
-  if (!logits || !ids || !weights || !offsets || !sorted || !pos || !ws) return FP8MOE_ERR_NULL;
-  // the row gather (xq -> xq_perm) and the scale gather (xs -> xs_perm) are independent
-  // options, each all-or-nothing; the code-sum gather (xsum -> xsum_perm) rides the scale
-  // gather
-  if ((xq != nullptr) != (xq_perm != nullptr)) return FP8MOE_ERR_NULL;
-  if ((xs != nullptr) != (xs_perm != nullptr)) return FP8MOE_ERR_NULL;
-  if ((xsum != nullptr) != (xsum_perm != nullptr)) return FP8MOE_ERR_NULL;
-  if (xsum && !xs) return FP8MOE_ERR_NULL;
-  if (xsum && (!aligned16(xsum) || !aligned16(xsum_perm))) return FP8MOE_ERR_ALIGN;
-  const bool rows = xq != nullptr, scales = xs != nullptr;
-  if (T < 1 || E < 1 || E > kMaxE || k < 1 || k > E || k > kMaxK) return FP8MOE_ERR_SHAPE;
-  if (T * (int64_t)k >= (int64_t(1) << 31)) return FP8MOE_ERR_SHAPE;
-  if ((rows || scales) && (H < FP8MOE_GROUP || H % FP8MOE_GROUP != 0)) return FP8MOE_ERR_SHAPE;
-  const void* ptrs[] = {logits, ids, weights, offsets, sorted, pos, ws};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return FP8MOE_ERR_ALIGN;
-  if (rows && (!aligned16(xq) || !aligned16(xq_perm))) return FP8MOE_ERR_ALIGN;
-  if (scales && (!aligned16(xs) || !aligned16(xs_perm))) return FP8MOE_ERR_ALIGN;
+  if (!ws) return FP8MOE_ERR_NULL;
+  const int32_t st = check_route(logits, T, E, k, ids, weights, offsets, sorted, pos, xq, xs,
+                                 H, xq_perm, xs_perm, xsum, xsum_perm);
+  if (st != FP8MOE_OK) return st;
+  if (!aligned16(ws)) return FP8MOE_ERR_ALIGN;
   if (ws_bytes < fp8moe::route_workspace_bytes(T, E)) return FP8MOE_ERR_WORKSPACE;
+  return launch_status(fp8moe::launch_route_permute(
+      logits, T, E, k, ids, weights, offsets, sorted, pos, xq, xs, H, xq_perm, xs_perm, xsum,
+      xsum_perm, ws, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_route_permute_noalloc(const float* logits, int64_t T, int32_t E, int32_t k,
+                                  int32_t* ids, float* weights, int32_t* offsets,
+                                  int32_t* sorted, int32_t* pos, const uint8_t* xq,
+                                  const float* xs, int64_t H, uint8_t* xq_perm, float* xs_perm,
+                                  const float* xsum, float* xsum_perm, void* stream) {
+  const int32_t st = check_route(logits, T, E, k, ids, weights, offsets, sorted, pos, xq, xs,
+                                 H, xq_perm, xs_perm, xsum, xsum_perm);
+  if (st != FP8MOE_OK) return st;
+  if (fp8moe::route_workspace_bytes(T, E) > fp8moe::kRouteScratchBytes)
+    return FP8MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (fp8moe::route_scratch(&ws) != hipSuccess) return FP8MOE_ERR_LAUNCH;
   return launch_status(fp8moe::launch_route_permute(
       logits, T, E, k, ids, weights, offsets, sorted, pos, xq, xs, H, xq_perm, xs_perm, xsum,
       xsum_perm, ws, static_cast<hipStream_t>(stream)));

@@ -32,6 +32,11 @@ hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32
                                 int32_t* pos, const uint8_t* xq, const float* xs, int64_t H,
                                 uint8_t* xq_perm, float* xs_perm, const float* xsum,
                                 float* xsum_perm, void* ws, hipStream_t st);
+// The routing workspace of the allocation-free call lives in a static device array of
+// kRouteScratchBytes per GPU. route_scratch() returns its device address on the current
+// device (resolved once per device, then cached); it never allocates.
+constexpr size_t kRouteScratchBytes = FP8MOE_ROUTE_SCRATCH_BYTES;
+hipError_t route_scratch(void** ptr);
 
 hipError_t launch_pack_bank(const uint8_t* w, const float* w_scales, int64_t E, int64_t N,
                             int64_t K, uint8_t* w_packed, float* ws_packed, hipStream_t st, bool fp4_layout = false);

@@ -19,11 +19,19 @@
 //                  writes sorted[] and pos[].
 //   4. gather:     optional copies of the e4m3 rows and (group-major) scales into grouped
 //                  order.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
 namespace fp8moe {
 namespace {
+
+// Workspace of the allocation-free routing call (per-chunk expert counts and the expert
+// totals). Every GPU the library runs on holds its own copy until the process ends. In
+// host code this name only stands in for the array: the device address comes from
+// hipGetSymbolAddress, per device, in route_scratch().
+static __device__ __align__(256) uint8_t scratch[kRouteScratchBytes];
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
@@ -244,6 +252,26 @@ __global__ __launch_bounds__(256) void gather_scales_kernel(const int32_t* __res
 }
 
 }  // namespace
+
+hipError_t route_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t route_workspace_bytes(int64_t T, int32_t E) {
   int64_t C = (T + kRouteChunk - 1) / kRouteChunk;

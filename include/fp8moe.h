@@ -56,7 +56,8 @@
  *     Quantisation rounds to nearest even, saturates to +-448 and keeps the sign of zero.
  *   - Alignment: every pointer must be 16-byte aligned.
  *   - Calls on different streams touching disjoint memory may run concurrently; the
- *     library keeps no global mutable state.
+ *     library keeps no global mutable state, except the device array behind
+ *     moe_route_permute_noalloc (the one entry point that takes no workspace).
  */
 #ifndef FP8MOE_H
 #define FP8MOE_H
@@ -172,6 +173,33 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
                           int32_t* pos, const uint8_t* xq, const float* xs, int64_t H,
                           uint8_t* xq_perm, float* xs_perm, const float* xsum,
                           float* xsum_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_permute_noalloc -- moe_route_permute without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, outputs, constraints and results are those of moe_route_permute, byte for
+ * byte (the same kernels run). The workspace is a static device array of
+ * FP8MOE_ROUTE_SCRATCH_BYTES that every GPU the library runs on holds from its first use
+ * until the process ends; its device address is looked up once per device, on the first
+ * call made with that device current. The call allocates and frees nothing.
+ *   - Limit: fp8moe_workspace_bytes(FP8MOE_OP_ROUTE_PERMUTE, T, E, k) must not exceed
+ *     FP8MOE_ROUTE_SCRATCH_BYTES (4 MiB: e.g. T = 65536 tokens at E = 256); larger calls
+ *     return FP8MOE_ERR_WORKSPACE and launch nothing.
+ *   - Every call on one GPU shares that GPU's array, and each call overwrites all of the
+ *     part it reads before reading it (nothing carries over between calls). Calls that
+ *     overlap in time on one GPU (different streams with no ordering between them) race
+ *     on the array and give undefined results; order them on one stream, or use
+ *     moe_route_permute with a workspace per stream.
+ *   - FP8MOE_ERR_LAUNCH also reports a failure to look up the array's address.
+ */
+#define FP8MOE_ROUTE_SCRATCH_BYTES ((size_t)4 << 20)
+int32_t moe_route_permute_noalloc(const float* logits, int64_t T, int32_t E, int32_t k,
+                                  int32_t* ids, float* weights, int32_t* offsets,
+                                  int32_t* sorted, int32_t* pos, const uint8_t* xq,
+                                  const float* xs, int64_t H, uint8_t* xq_perm, float* xs_perm,
+                                  const float* xsum, float* xsum_perm, void* stream);
 
 /*
  * fp8moe_pack_expert_bank -- one-time repacking of a packed-int4 expert bank (and its

@@ -41,7 +41,8 @@ def test_header_declares_the_five_entry_points():
     assert "fp8moe_workspace_bytes" in fns and "fp8moe_status_str" in fns
     for name in ["fp8moe_rmsnorm", "fp8moe_bf16_gemm", "fp8moe_causal_attention",
                  "fp8_dense_gemm_rowwise", "fp8_block_gemm", "fp8_quant_weight_block128",
-                 "mxfp4_quant_act", "fp8moe_pack_expert_bank_mxfp4", "mxfp4_grouped_expert_gemm"]:
+                 "mxfp4_quant_act", "fp8moe_pack_expert_bank_mxfp4", "mxfp4_grouped_expert_gemm",
+                 "moe_route_permute_noalloc"]:
         assert name in fns
 
 
@@ -49,7 +50,7 @@ def test_every_declared_symbol_is_exported(lib):
     raw = ctypes.CDLL(LIB)
     for name in declared_functions():
         assert hasattr(raw, name), name
-    assert lib.fp8moe_abi_version() == 7
+    assert lib.fp8moe_abi_version() == 8
 
 
 def test_status_strings(lib):
@@ -122,6 +123,26 @@ def test_route_validation(lib):
     assert _route(lib, xs=P, xsp=P, H=256, xsum=P) == NULL  # the sum pair comes together
     assert _route(lib, xsum=P, xsump=P) == NULL  # and only with the scale gather
     assert _route(lib, xs=P, xsp=P, H=256, xsum=P, xsump=U) == ALIGN
+
+
+def _route_na(lib, logits=P, T=64, E=8, k=2, ids=P, xq=None, xs=None, H=0, xqp=None, xsp=None,
+              xsum=None, xsump=None):
+    return lib.moe_route_permute_noalloc(logits, T, E, k, ids, P, P, P, P, xq, xs, H, xqp, xsp,
+                                         xsum, xsump, None)
+
+
+def test_route_noalloc_validation(lib):
+    # the same argument checks as moe_route_permute, all on the host before any launch
+    assert _route_na(lib, logits=None) == NULL
+    assert _route_na(lib, xq=P) == NULL
+    assert _route_na(lib, xs=P, xsp=P, H=256, xsum=P) == NULL
+    assert _route_na(lib, T=0) == SHAPE
+    assert _route_na(lib, E=4, k=5) == SHAPE
+    assert _route_na(lib, xs=P, xsp=P, H=100) == SHAPE
+    assert _route_na(lib, ids=U) == ALIGN
+    # past the 4 MiB static workspace: 2^20 tokens x 64 experts need 16 MiB of counts
+    assert lib.fp8moe_workspace_bytes(1, 1 << 20, 64, 8) > 4 << 20
+    assert _route_na(lib, T=1 << 20, E=64, k=8) == WS
 
 
 def _gg(lib, a=P, R=256, E=8, N=512, K=256, epi=0, dt=0, out_scales=P, sorted_=None, kr=1,
