@@ -69,6 +69,7 @@ constexpr int kBlockBytes = 16 * kGroup / 2;   // prepacked bank block: 16 colum
 constexpr float kWeightScaleMul = 512.f;       // 2^9: B codes are (q + 8) * 2^-9
 constexpr uint32_t kOnes = 0x38383838u;        // four e4m3 1.0
 constexpr int kMaxExperts = 1024;
+constexpr int kListedUnits = 64;  // tiles per workgroup looked up once, at the start
 
 // One pipeline stage in LDS: the A tile, the waves' packed B slices, the A scales of the
 // 128 rows, the weight scales of the 512 columns, and the row-sum seeds of its group.
@@ -203,6 +204,7 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   __shared__ int s_part[kMaxExperts];  // experts with a small (front) or tiny (back) last m-tile
   __shared__ int s_npart;              // tiny count << 11 | small count
   __shared__ int s_src[NW][RPW];  // pair ids of the rows each wave stages for the next tile
+  __shared__ int4 s_units[kListedUnits];  // this workgroup's first tiles: (e, row_begin, rows, nt)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in an SGPR
@@ -263,7 +265,10 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   const int sb_x = n_small * x / nx, ns_x = n_small * (x + 1) / nx - sb_x;
   const int tb_x = n_tiny * x / nx, nt_x = n_tiny * (x + 1) / nx - tb_x;
 
-  auto tile_of = [&](int j) {  // j-th unit of this workgroup: entry u + j * nwg_x
+  // j-th unit of this workgroup: entry u + j * nwg_x. Wave-uniform scalar walk (a binary
+  // search over the m-tile starts, scalar loads of the offsets); tile_of below serves the
+  // first kListedUnits units from the list formed once at the start.
+  auto tile_walk = [&](int j) {
     const int l = u + j * nwg_x;
     TileDesc d;
     if (l < nw_x) {
@@ -288,6 +293,46 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
                      __builtin_amdgcn_readfirstlane(s_mstart[d.e])) * BM;
     }
     d.rows = min(BM, sload(offsets + d.e + 1) - d.row_begin);
+    return d;
+  };
+  // The same lookup for unit j = tid, one per lane, all lanes at once (vector loads), into
+  // s_units: the per-tile walk above costs a chain of dependent LDS and scalar-memory
+  // round trips at every tile boundary.
+  {
+    const int j = tid;
+    const int l = u + j * nwg_x;
+    if (j < kListedUnits && l < nw_x + ns_x + nt_x) {
+      int e, row_begin, nt;
+      if (l < nw_x) {
+        const int L = wb_x + l, mt = L / NT;
+        nt = L - mt * NT;
+        int lo = 0, hi = E;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_mstart[mid] <= mt) lo = mid;
+          else hi = mid;
+        }
+        e = lo;
+        row_begin = offsets[lo] + (mt - s_mstart[lo]) * BM;
+      } else {
+        const bool small = l < nw_x + ns_x;
+        const int L = small ? sb_x + (l - nw_x) : tb_x + (l - nw_x - ns_x), i = L / NT;
+        nt = L - i * NT;
+        e = s_part[small ? i : kMaxExperts - 1 - i];
+        row_begin = offsets[e] + (s_mstart[e + 1] - s_mstart[e]) * BM;
+      }
+      s_units[j] = make_int4(e, row_begin, min(BM, offsets[e + 1] - row_begin), nt);
+    }
+    __syncthreads();
+  }
+  auto tile_of = [&](int j) {
+    if (j >= kListedUnits) return tile_walk(j);  // uniform
+    const int4 v = s_units[j];
+    TileDesc d;
+    d.e = __builtin_amdgcn_readfirstlane(v.x);
+    d.row_begin = __builtin_amdgcn_readfirstlane(v.y);
+    d.rows = __builtin_amdgcn_readfirstlane(v.z);
+    d.nt = __builtin_amdgcn_readfirstlane(v.w);
     return d;
   };
   // units [0, j_small) are whole, [j_small, j_tiny) small, [j_tiny, my_tiles) tiny
