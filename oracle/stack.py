@@ -120,7 +120,7 @@ def _moe_bf16(hn_bf16_vals, logits, lay, k, forced=None):
 
 def stack_forward(inp: dict, n_q: int, n_kv: int, d: int, k: int, fp8: bool = True,
                   return_layers: bool = False, perturb=None, route_ids=None,
-                  return_routes: bool = False):
+                  return_routes: bool = False, on_layer=None):
     """Run the stack on ``synth.stack_inputs`` data. Returns fp32 logits [T, V] (float64
     array of fp32-rounded values) and, if asked, the per-layer residual streams and the
     per-layer expert ids.
@@ -128,7 +128,8 @@ def stack_forward(inp: dict, n_q: int, n_kv: int, d: int, k: int, fp8: bool = Tr
     Probes of the stack's sensitivity (none changes the arithmetic when left at None):
     ``perturb`` is applied to every dense projection output (q/k/v and o) before its bf16
     rounding; ``route_ids`` (one [T, k] array per layer) replaces the top-k choice of each
-    layer's experts, the weights coming from that layer's own router logits."""
+    layer's experts, the weights coming from that layer's own router logits.
+    ``on_layer(li)`` is called after each layer (progress reports only)."""
     x = round_bf16(bf16_to_f32(inp["x0"]))
     nq = n_q * d
     nk = n_kv * d
@@ -157,6 +158,8 @@ def stack_forward(inp: dict, n_q: int, n_kv: int, d: int, k: int, fp8: bool = Tr
         x = round_bf16(x + round_bf16(moe))
         if return_layers:
             trace.append(x.copy())
+        if on_layer is not None:
+            on_layer(li)
     hf = round_bf16(rmsnorm(x))
     out = (hf @ bf16_to_f32(inp["w_lm"]).astype(np.float64).T).astype(np.float32).astype(np.float64)
     res = (out,)
