@@ -102,11 +102,11 @@ def _on_stream(fn):
     workspaces it allocates belong to that stream in the caching allocator: a temporary
     freed when the wrapper returns is then reused only by work ordered after the kernels
     that still read it (torch's rule for memory used on one stream)."""
-    sig = inspect.signature(fn)
+    pos = list(inspect.signature(fn).parameters).index("stream")
 
     @functools.wraps(fn)
     def wrapped(*args, **kw):
-        stream = sig.bind_partial(*args, **kw).arguments.get("stream")
+        stream = args[pos] if len(args) > pos else kw.get("stream")
         if stream is None:
             return fn(*args, **kw)
         with torch.cuda.stream(stream):

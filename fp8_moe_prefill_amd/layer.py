@@ -160,32 +160,31 @@ class MoELayerRunner:
             raise ValueError(f"bank packed for {bank.act} activations, runner for {self.act}")
         mark("quant", 0)
         if mx:
-            _lib.mxfp4_quant_act(x, q=self.xq, scales=self.xs, stream=main)
+            _lib.mxfp4_quant_act(x, q=self.xq, scales=self.xs, stream=stream)
         else:
             _lib.fp8_quant_act(x, _lib.GROUP, q=self.xq, scales=self.xs, sums=self.xsum,
-                               stream=main)
+                               stream=stream)
         mark("quant", 1)
         mark("route", 0)
-        _lib.moe_route_permute(logits, self.k, out=rt, ws=self.ws, stream=main)
+        _lib.moe_route_permute(logits, self.k, out=rt, ws=self.ws, stream=stream)
         mark("route", 1)
         mark("gate_up", 0)
-        self.run_gate_up(bank, stream=main)
+        self.run_gate_up(bank, stream=stream)
         mark("gate_up", 1)
         mark("down", 0)
         _lib.fp8_grouped_expert_gemm(self.hq, self.hs, bank.w_dn, bank.s_dn, rt["offsets"],
-                                     self.R, _lib.EPI_STORE, out=self.y, stream=main,
+                                     self.R, _lib.EPI_STORE, out=self.y, stream=stream,
                                      a_sums=self.hsum)
         mark("down", 1)
         mark("combine", 0)
         _lib.moe_unpermute_combine(self.y, rt["pos"], rt["weights"], out=self.out,
-                                   stream=main)
+                                   stream=stream)
         mark("combine", 1)
         return self.out
 
     def run_gate_up(self, bank: ExpertBank, stream=None):
         """The gate|up stage alone (grouped GEMM + SwiGLU + requantisation) on the
         quantised activations and routing the last ``run`` left in this runner."""
-        main = torch.cuda.current_stream() if stream is None else stream
         rt = self.route
         # rows gathered from token order through `sorted`, with their per-token scales
         # (and code sums) straight from the quantiser's output
@@ -193,9 +192,9 @@ class MoELayerRunner:
             _lib.mxfp4_grouped_expert_gemm(
                 self.xq, self.xs.view(torch.float32), bank.w_gu, bank.s_gu, rt["offsets"],
                 self.R, _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k,
-                out=self.hq, out_scales=self.hs, out_sums=self.hsum, stream=main)
+                out=self.hq, out_scales=self.hs, out_sums=self.hsum, stream=stream)
         else:
             _lib.fp8_grouped_expert_gemm(
                 self.xq, self.xs, bank.w_gu, bank.s_gu, rt["offsets"], self.R,
                 _lib.EPI_SWIGLU_QUANT, sorted_=rt["sorted"], k_route=self.k, out=self.hq,
-                out_scales=self.hs, out_sums=self.hsum, stream=main, a_sums=self.xsum)
+                out_scales=self.hs, out_sums=self.hsum, stream=stream, a_sums=self.xsum)
