@@ -12,13 +12,21 @@ between the launches), plus the roofline of the dominant kernel (the grouped gat
 FP8 MFMA bound) from HIP events around each stage on the launch stream over a second pass
 of the same K steps, and the CPU oracle timed on a bounded sample.
 
-The line also carries the depth stack (T=2048, L=8 by default, --stack 12 or 0): prefill
+Also on the line: the layer against the sum of its stages' rooflines; the layer replayed
+from HIP graphs (launch overhead removed; checked bit for bit against the eager layer);
+the W8A8 dense projections at 2048 x 4096 x {6144, 4096} (per-tensor, row-wise and
+block-128 scales); the layer with MXFP4 activations; the decode regime (16 tokens, M <= 16
+projections); the skewed large layer (16384 tokens, hidden 4096, 128 Zipf-routed experts,
+I = 1536) with its stage times and roofline fraction; the shader clock and the GEMM's HBM
+bytes from the committed rocprofv3 counter runs (null once the kernel source differs);
+the host CPU; and the depth stack (T=2048, L=8 by default, --stack 12 or 0): prefill
 tokens/s of the whole forward (L layers of W8A8 q/k/v/o, causal GQA attention, router and
 FP8 MoE, then the bf16 LM head), with its time against the sum of its parts' MFMA
 rooflines (FP8 parts at the FP8 peak, bf16 parts at the bf16 peak).
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] [--dense]
-                    [--stack {0,8,12}] [--stack-only]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] [--no-dense]
+                    [--no-skewed] [--no-mxfp4] [--no-decode] [--stack {0,8,12}]
+                    [--stack-only] [--layer-only]
 """
 
 from __future__ import annotations
@@ -38,7 +46,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "grouped FP8 expert GEMM TFLOP/s (% FP8 MFMA peak); MoE prefill tokens/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_gate_up_moe_prefill_traffic.json")
-GEMM_SOURCE = os.path.join(ROOT, "fp8_moe_prefill_amd", "csrc", "grouped_gemm.hip")
+CLOCK_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_moe_prefill_counters.json")
+GEMM_SOURCES = [os.path.join(ROOT, "fp8_moe_prefill_amd", "csrc", n)
+                for n in ("grouped_gemm.hip", "lds_dma.h", "common.h")]
 
 
 def _parse():
@@ -48,7 +58,10 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dense", action="store_true",
-                    help="also time the W8A8 dense projections (2048 x 4096 x {6144, 4096})")
+                    help="(default) time the W8A8 dense projections (2048 x 4096 x {6144, 4096})")
+    ap.add_argument("--no-dense", action="store_true", help="skip the W8A8 dense projections")
+    ap.add_argument("--no-skewed", action="store_true",
+                    help="skip the skewed large layer (16384 tokens, hidden 4096, 128 experts)")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--stack", type=int, default=8, choices=[0, 8, 12],
                     help="also time the depth stack of this many layers (0: skip)")
@@ -58,11 +71,24 @@ def _parse():
                     help="skip the decode-regime timings (16-token layer, M <= 16 projections)")
     ap.add_argument("--stack-only", action="store_true",
                     help="time only the depth stack (for profiling it alone)")
-    return ap.parse_args()
+    ap.add_argument("--layer-only", action="store_true",
+                    help="time only the 4096-token layer (no graph replay, clock sampling, "
+                         "dense, MXFP4, decode, stack, skewed or CPU legs): for counter runs")
+    args = ap.parse_args()
+    if args.layer_only:
+        args.no_dense = args.no_mxfp4 = args.no_decode = args.no_skewed = True
+        args.no_cpu_baseline = True
+        args.stack = 0
+    return args
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    """First 16 hex digits of the SHA-256 of the concatenated sources."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_per_launch():
@@ -72,9 +98,22 @@ def traffic_per_launch():
         d = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if d.get("kernel_source_sha256_16") != source_hash(GEMM_SOURCE):
+    if d.get("kernel_source_sha256_16") != source_hash(GEMM_SOURCES):
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def committed_clock():
+    """Shader clock under the grouped GEMMs from the committed rocprofv3 counter run
+    (SQ_BUSY_CYCLES per shader engine over the same dispatches' durations), or None when
+    the kernel source changed after it was taken."""
+    try:
+        d = json.load(open(CLOCK_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != source_hash(GEMM_SOURCES):
+        return None
+    return {"mhz": d.get("sclk_mhz"), "method": d.get("method"), "source": d.get("source")}
 
 
 def cpu_baseline(n_tokens: int, min_seconds: float = 10.0, max_reps: int = 5):
@@ -102,6 +141,32 @@ def cpu_baseline(n_tokens: int, min_seconds: float = 10.0, max_reps: int = 5):
             "kind": "oracle",
             "sample": f"the NumPy fp64 oracle MoE layer on the first {n_tokens} of the 4096 "
                       f"tokens (all 64 experts), {reps} runs, {total:.1f} s"}
+
+
+def layer_roofline_us(c) -> dict:
+    """Per-stage rooflines of one MoE layer, max(FLOP / FP8 peak, bytes / HBM), in us:
+    quant (bf16 in, e4m3 + scales + code sums out), routing (logits in, ids/weights and
+    grouping out), gate|up (bank + gathered rows + scales in, codes + scales + sums out),
+    down (bank + codes in, bf16 rows out), combine (rows + weights in, bf16 out)."""
+    T, H, E, k, I = c.T, c.H, c.E, c.k, c.I
+    R = T * k
+    G = 128
+
+    def us(flop, nbytes):
+        return max(flop / (PEAK_FP8_TFLOPS * 1e6), nbytes / (PEAK_HBM_GBS * 1e3))
+
+    bank_gu = E * 2 * I * H / 2 + E * 2 * I * (H / G) * 4
+    bank_dn = E * H * I / 2 + E * H * (I / G) * 4
+    st = {
+        "quant": us(0, T * H * 2 + T * H + 2 * T * (H / G) * 4),
+        "route": us(0, T * E * 4 + T * k * 8 + 2 * R * 4 + (E + 1) * 4),
+        "gate_up": us(4.0 * R * H * I, bank_gu + R * H + 2 * R * (H / G) * 4 + R * I
+                      + 2 * R * (I / G) * 4),
+        "down": us(2.0 * R * I * H, bank_dn + R * I + 2 * R * (I / G) * 4 + R * H * 2),
+        "combine": us(0, R * H * 2 + T * k * 8 + T * H * 2),
+    }
+    st["layer"] = sum(st.values())
+    return st
 
 
 def stack_flops(c):
@@ -279,8 +344,23 @@ def main():
                      "frac": gu_tflops / PEAK_FP8_TFLOPS, "traffic": traffic,
                      "algorithmic_flop_per_launch": flop_gu},
     }
+    out["host_launch_us_per_step"] = getattr(runner, "host_us_per_step", None)
+    roof = layer_roofline_us(c)
+    out["layer_roofline"] = {"us": roof["layer"], "frac": roof["layer"] / (ms_step * 1e3),
+                             "stages_us": {s: v for s, v in roof.items() if s != "layer"}}
+    if args.layer_only:
+        print(json.dumps(out))
+        return
+    try:
+        out["graph_replay"] = {"ms_per_step": time_graph_replay(runner, xs, lgs, banks,
+                                                                args.steps)}
+        out["graph_replay"]["tokens_per_s"] = c.T / (out["graph_replay"]["ms_per_step"] * 1e-3)
+    except RuntimeError as e:  # reported, never silently replaced by the eager number
+        out["graph_replay"] = {"error": str(e)}
+    out["sclk"] = committed_clock()
+    out["host"] = host_info()
 
-    if args.dense:
+    if not args.no_dense:
         d = dense_inputs(CONFIGS["dense_w8a8"])
         x = torch.from_numpy(d["x"].view(np.int16)).to(dev).view(torch.bfloat16)
         res = {}
@@ -299,7 +379,8 @@ def main():
             torch.cuda.synchronize()
             us = a.elapsed_time(b) / 20 * 1e3
             fl = 2.0 * x.shape[0] * w.shape[0] * x.shape[1]
-            res[wn] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12}
+            res[wn] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12,
+                       "frac_fp8_peak": fl / (us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS}
             # row-wise activation scales (one per token) on the same projection
             xr, sr = f.fp8_quant_act(x, f.QUANT_ROW)
             yr = f.fp8_dense_gemm_rowwise(xr, sr, wq, sw)
@@ -334,9 +415,102 @@ def main():
     if args.stack:
         out["stack"] = bench_stack(args.stack, args.warmup, min(args.steps, 20))
 
+    if not args.no_skewed:
+        del banks, runner
+        torch.cuda.empty_cache()
+        out["moe_skewed"] = bench_skewed(args.warmup, min(args.steps, 20), dev)
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
     print(json.dumps(out))
+
+
+def time_graph_replay(runner, xs, lgs, banks, steps):
+    """ms per layer step with each rotation's step captured once in a HIP graph and the
+    graphs replayed (launch overhead gone); the graphs are checked bit for bit against an
+    eager step on the same inputs."""
+    import torch
+
+    n = len(xs)
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(n):  # warm the allocator on the capture stream
+            runner.run(xs[i], lgs[i], banks[i])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            runner.run(xs[i], lgs[i], banks[i])
+        graphs.append(g)
+    torch.cuda.synchronize()
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    got = runner.out.clone()
+    runner.run(xs[0], lgs[0], banks[0])
+    torch.cuda.synchronize()
+    if not torch.equal(got, runner.out):
+        raise RuntimeError("graph replay differs from the eager layer")
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[i % n].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def host_info() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpu_threads": len(os.sched_getaffinity(0))}
+
+
+def bench_skewed(warmup: int, steps: int, dev) -> dict:
+    """The skewed large layer (16384 tokens, hidden 4096, 128 experts with Zipf(1.2)
+    routing and empty experts, top-8, I = 1536): layer time and per-stage times, the
+    grouped GEMMs' rate against the FP8 peak and the layer against its roofline. Its
+    1.2 GB bank does not fit the 256 MB Infinity Cache, so one bank is used."""
+    import numpy as np
+    import torch
+
+    import fp8_moe_prefill_amd as f
+    from synth import CONFIGS, moe_inputs
+
+    c = CONFIGS["moe_skewed"]
+    inp = moe_inputs(c)
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    lg = torch.from_numpy(inp["logits"]).to(dev)
+    bank = f.ExpertBank.from_host(inp, dev)
+    del inp
+    runner = f.MoELayerRunner(c.T, c.H, c.E, c.k, c.I, dev)
+    for _ in range(max(warmup, 1)):
+        runner.run(x, lg, bank)
+    torch.cuda.synchronize()
+    ms, per = time_layer(runner, [x], [lg], [bank], steps)
+    R = c.T * c.k
+    fl_gu, fl_dn = 4.0 * R * c.H * c.I, 2.0 * R * c.I * c.H
+    roof = layer_roofline_us(c)
+    gu_tf = fl_gu / (per["gate_up"] * 1e-3) / 1e12
+    dn_tf = fl_dn / (per["down"] * 1e-3) / 1e12
+    tf = (fl_gu + fl_dn) / ((per["gate_up"] + per["down"]) * 1e-3) / 1e12
+    return {"workload": "moe_skewed: T=16384 tokens, hidden 4096, 128 experts (Zipf 1.2 "
+                        "router bias, some experts empty), top-8, intermediate 1536",
+            "tokens_per_s": c.T / (ms * 1e-3), "ms_per_step": ms,
+            "stages_us": {s: v * 1e3 for s, v in per.items()},
+            "grouped_gemm": {"tflops": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS,
+                             "gate_up_tflops": gu_tf, "down_tflops": dn_tf},
+            "layer_roofline_us": roof["layer"],
+            "frac_layer_roofline": roof["layer"] / (ms * 1e3)}
 
 
 def time_layer(runner, xs, lgs, banks, steps):
@@ -352,11 +526,14 @@ def time_layer(runner, xs, lgs, banks, steps):
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
+    h0 = time.perf_counter()
     for i in range(steps):
         runner.run(xs[i % n], lgs[i % n], banks[i % n])
+    host_us = (time.perf_counter() - h0) / steps * 1e6  # launch cost on the host per step
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / steps
+    runner.host_us_per_step = host_us
     ev = [{s: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for s in stages} for _ in range(steps)]
     for i in range(steps):
