@@ -9,9 +9,11 @@
 // gfx950 design (one pass over the keys with a running max, so the T x T score matrix never
 // leaves registers):
 // * a workgroup owns one kv head, 16 queries and four query heads of that kv head's group,
-//   one per wave (small query blocks: more workgroups in flight for the causal imbalance); the K tile and the transposed V tile of 64 keys are staged once in LDS
-//   (double-buffered, next tile's global loads in flight during the MFMAs) and shared by
-//   the four waves;
+//   one per wave (small query blocks: more workgroups in flight for the causal
+//   imbalance); the K tile and the transposed V tile of 64 keys are staged once in LDS
+//   (double-buffered) and shared by the four waves; a tile's global loads are issued two
+//   tiles ahead into one of two register sets (one tile of compute is shorter than the
+//   load latency);
 // * each wave computes S^T = K Q^T (v_mfma_f32_16x16x32_bf16, keys as rows), so a lane's
 //   scores all belong to one query: the running max, the rescale of the output and the
 //   row sum need no lane exchange except the 4-lane max per tile;
@@ -23,6 +25,8 @@
 //   (zero-filled past T), so V^T tiles load as contiguous rows.
 // Workgroups are paired heavy with light (see the rank mapping) against the causal
 // imbalance.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -39,6 +43,7 @@ constexpr int VS = KT * 2;       // V^T tile row stride in LDS (bytes): 64 keys,
 // position s ^ (d % 16), so the 16 rows one operand read touches hit distinct banks.
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -115,29 +120,41 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   // 16 B each per thread
   const uint16_t* kbase = qkv + (n_q + j) * D;
   const uint16_t* vbase = vt + (int64_t)j * D * Tp;
-  uint4 rk[4], rv[4];
-  auto load_tile = [&](int kt) {
+  // two register sets for tiles in flight: the global loads of a tile are issued two
+  // iterations before it is used (one iteration of compute does not cover the load
+  // latency); set indices are compile-time constants, so they stay in registers
+  // (native vector types: arrays of the HIP uint4 struct were kept in scratch memory)
+  u32x4 rk0[4], rv0[4], rk1[4], rv1[4];
+  auto load_tile = [&](auto set_tag, int kt) {
+    constexpr int S = decltype(set_tag)::value;
+    u32x4* rk = S ? rk1 : rk0;
+    u32x4* rv = S ? rv1 : rv0;
     const int k0 = kt * KT;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i;
       const int key = min(k0 + (c >> 4), T - 1);
-      rk[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)key * ld + (c & 15) * 8);
-      rv[i] = *reinterpret_cast<const uint4*>(vbase + (int64_t)(c >> 3) * Tp + k0 + (c & 7) * 8);
+      rk[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * ld + (c & 15) * 8);
+      rv[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)(c >> 3) * Tp + k0 + (c & 7) * 8);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](auto set_tag, int buf) {
+    constexpr int S = decltype(set_tag)::value;
+    const u32x4* rk = S ? rk1 : rk0;
+    const u32x4* rv = S ? rv1 : rv0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i;
-      *reinterpret_cast<uint4*>(&sK[buf][(c >> 4) * KS + (c & 15) * 16]) = rk[i];
+      *reinterpret_cast<u32x4*>(&sK[buf][(c >> 4) * KS + (c & 15) * 16]) = rk[i];
       // 16-byte chunk j of row d holds slots 2j, 2j + 1: they land as chunk j ^ (sg / 2),
       // in swapped order when sg is odd
       const int d = c >> 3, sg = d & 15;
-      const uint4 v = (sg & 1) ? make_uint4(rv[i].z, rv[i].w, rv[i].x, rv[i].y) : rv[i];
-      *reinterpret_cast<uint4*>(&sV[buf][d * VS + ((c & 7) ^ (sg >> 1)) * 16]) = v;
+      const u32x4 v = (sg & 1) ? rv[i].zwxy : rv[i];
+      *reinterpret_cast<u32x4*>(&sV[buf][d * VS + ((c & 7) ^ (sg >> 1)) * 16]) = v;
     }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
   v4f o[NQT][8];
 #pragma unroll
@@ -148,14 +165,18 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) m_run[qt] = -INFINITY, l_part[qt] = 0.f;
 
-  load_tile(0);
-  store_tile(0);
+  // tile kt: loaded into register set kt % 2 at iteration kt - 2 (the prologue for tiles 0
+  // and 1), stored into LDS stage kt % 2 at the end of iteration kt - 1, computed at
+  // iteration kt
+  load_tile(I0{}, 0);
+  store_tile(I0{}, 0);
+  if (nkt > 1) load_tile(I1{}, 1);
   __syncthreads();
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) load_tile(kt + 1);
+  auto step = [&](auto par_tag, int kt) {
+    constexpr int P = decltype(par_tag)::value;  // kt % 2
+    const int cur = P;
+    if (kt + 2 < nkt) load_tile(par_tag, kt + 2);  // set P held tile kt, already in LDS
 
     // S^T[key 16 s + 4 g + r][query 16 qt + c16], s = 16-key subtile
     v4f st[NQT][4];
@@ -232,8 +253,12 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
       }
     }
 
-    if (more) store_tile(cur ^ 1);
+    if (kt + 1 < nkt) store_tile(std::integral_constant<int, P ^ 1>{}, cur ^ 1);
     __syncthreads();
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    step(I0{}, kt);
+    if (kt + 1 < nkt) step(I1{}, kt + 1);
   }
 
   if (!live) return;
