@@ -13,14 +13,19 @@
 //   imbalance); the K tile and the transposed V tile of 64 keys are staged once in LDS
 //   (double-buffered) and shared by the four waves; a tile's global loads are issued two
 //   tiles ahead into one of two register sets (one tile of compute is shorter than the
-//   load latency);
+//   load latency). The loads are buffer loads whose per-lane offsets are fixed for the
+//   whole kernel: only the scalar base moves from tile to tile, and keys past T read as
+//   zero (the range check of the buffer descriptor), so staging costs no vector ALU work;
 // * each wave computes S^T = K Q^T (v_mfma_f32_16x16x32_bf16, keys as rows), so a lane's
 //   scores all belong to one query: the running max, the rescale of the output and the
-//   row sum need no lane exchange except the 4-lane max per tile;
+//   row sum need no lane exchange except the 4-lane max per tile; the causal mask only
+//   exists in the code of the last (diagonal) tile of a query block;
 // * O^T = V^T P^T: P leaves the S^T accumulators as the B operand directly (same lane),
 //   split into two bf16 terms hi + lo so that the product keeps the fp32 softmax's
-//   accuracy (a single bf16 rounding of the weights would cost 2^-9 relative); V^T comes
-//   from LDS; the output accumulators are again per query;
+//   accuracy (a single bf16 rounding of the weights would cost 2^-9 relative). The
+//   accumulator layout puts keys 4g..4g+3 and 16+4g..16+4g+3 of each 32-key step in lane
+//   group g, so the V^T tile is stored in LDS in that key order: one 16-byte read per
+//   lane is one A operand;
 // * V is transposed once per layer into a [n_kv][d][T_pad] workspace by a small kernel
 //   (zero-filled past T), so V^T tiles load as contiguous rows.
 // Workgroups are paired heavy with light (see the rank mapping) against the causal
@@ -34,18 +39,25 @@ namespace fp8moe {
 namespace {
 
 constexpr int D = 128;        // head dim
-constexpr int NQT = 1;        // 16-query MFMA tiles per wave
-constexpr int QB = 16 * NQT;  // queries per workgroup
+constexpr int QB = 16;        // queries per workgroup
 constexpr int KT = 64;        // keys per tile
 constexpr int KS = D * 2 + 16;   // K tile row stride in LDS (bytes): 256 + 16 pad
 constexpr int VS = KT * 2;       // V^T tile row stride in LDS (bytes): 64 keys, no pad
-// V^T tile rows are XOR-swizzled in 8-byte slots (4 keys): slot s of row d sits at
-// position s ^ (d % 16), so the 16 rows one operand read touches hit distinct banks.
+// Dword 3 of a raw buffer descriptor on gfx9 data-parallel parts: 32-bit data format, no
+// swizzle, no index stride.
+constexpr int kBufferWord3 = 0x00020000;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// V^T tile in LDS: row d (128 B) holds 8 chunks of 16 B; chunk 4c + g holds keys
+// 32c + 4g .. +3, then 32c + 16 + 4g .. +3 (the key order of the P operand), at chunk
+// position (4c + g) ^ v_swz(d). The 16 rows one operand read touches then sit in 16
+// distinct 16-byte bank groups, whether the LDS serves 8 or 16 lanes per cycle.
+__device__ __forceinline__ int v_swz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 
 // max / sum of v over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes that hold the
 // same query): two lane-swap instructions of gfx950, no LDS round trip
@@ -62,19 +74,36 @@ __device__ __forceinline__ float sum4q(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// [T, ld] column block of V (kv head j) -> vt[j][d][t], zero for t in [T, Tp)
+// [T, ld] column block of V (kv head j, 64 columns) -> vt[j][d][t], zero for t in
+// [T, Tp). 16-byte loads of 8 columns, transposed through LDS, 16-byte stores of 8 keys.
 __global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ qkv,
                                                           int T, int ld, int v_col0, int Tp,
                                                           uint16_t* __restrict__ vt) {
-  __shared__ uint16_t tile[64][65];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][64 + 2];  // [column][key]
   const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64;  // c: column within the V block
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int r = q >> 3, cc = (q & 7) * 8;  // key r of the tile, columns cc .. cc + 7
     const int t = t0 + r;
-    tile[r][tx] = t < T ? qkv[(int64_t)t * ld + v_col0 + c0 + tx] : (uint16_t)0;
+    u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+    if (t < T) v = *reinterpret_cast<const u32x4*>(qkv + (int64_t)t * ld + v_col0 + c0 + cc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[cc + 2 * e][r] = (uint16_t)(v[e] & 0xFFFFu);
+      tile[cc + 2 * e + 1][r] = (uint16_t)(v[e] >> 16);
+    }
   }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) vt[(int64_t)(c0 + r) * Tp + t0 + tx] = tile[tx][r];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int c = q >> 3, kk = (q & 7) * 8;  // column c, keys kk .. kk + 7
+    u32x4 w;  // (132 c + 2 kk + 4 e) bytes: 4-byte aligned pairs of keys
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = *reinterpret_cast<const uint32_t*>(&tile[c][kk + 2 * e]);
+    *reinterpret_cast<u32x4*>(vt + (int64_t)(c0 + c) * Tp + t0 + kk) = w;
+  }
 }
 
 __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __restrict__ qkv,
@@ -105,37 +134,56 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   const int h = j * rep + min(hr, rep - 1);
   const int q0 = qb * QB;
   const int nkt = min(q0 + QB - 1, T - 1) / KT + 1;
+  const int qi = q0 + c16;  // this lane's query
 
-  // Q fragments: lane (g, c16) holds query q0 + 16 qt + c16, dims 32 kk + 8 g .. +7
-  bf16x8_t qf[NQT][4];
-#pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    const int t = min(q0 + 16 * qt + c16, T - 1);
+  // Q fragment: lane (g, c16) holds query q0 + c16, dims 32 kk + 8 g .. +7
+  bf16x8_t qf[4];
+  {
+    const int t = min(qi, T - 1);
     const uint16_t* src = qkv + (int64_t)t * ld + h * D + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[qt][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(src + 32 * kk));
+    for (int kk = 0; kk < 4; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + 32 * kk));
   }
 
-  // staging of one key tile: K rows (64 x 256 B) and V^T rows (128 x 128 B), 4 chunks of
-  // 16 B each per thread
-  const uint16_t* kbase = qkv + (n_q + j) * D;
-  const uint16_t* vbase = vt + (int64_t)j * D * Tp;
-  // two register sets for tiles in flight: the global loads of a tile are issued two
-  // iterations before it is used (one iteration of compute does not cover the load
-  // latency); set indices are compile-time constants, so they stay in registers
-  // (native vector types: arrays of the HIP uint4 struct were kept in scratch memory)
+  // Staging of one key tile: K rows (64 x 256 B) and V^T rows (128 x 128 B), 4 chunks of
+  // 16 B each per thread. Thread chunk c = tid + 256 i: K row c / 16, bytes 16 (c % 16);
+  // V^T row d = c / 8, keys 8 (c % 8) .. +7.
+  const int64_t k_bytes = (int64_t)T * ld * 2;  // < 2^32 (checked by the caller)
+  const char* kbase = reinterpret_cast<const char*>(qkv + (n_q + j) * D);
+  const char* vbase = reinterpret_cast<const char*>(vt + (int64_t)j * D * Tp);
+  const uint32_t k_voff = (uint32_t)((tid >> 4) * ld * 2 + (tid & 15) * 16);
+  const uint32_t k_step = (uint32_t)(16 * ld * 2);  // 16 rows: i -> i + 1
+  const uint32_t v_voff = (uint32_t)((tid >> 3) * Tp * 2 + (tid & 7) * 16);
+  const uint32_t v_step = (uint32_t)(32 * Tp * 2);  // 32 rows
+  const int v_bytes_max = (int)((int64_t)D * Tp * 2);
+  // LDS destinations: K chunk at row * KS + 16 (c % 16) (+ 16 KS per i); the two 8-byte
+  // halves of a V^T chunk (keys 8m .. 8m+3 and 8m+4 .. 8m+7, m = c % 8) go to chunks
+  // 4(m / 4) + 2(m % 2) and that + 1, half (m / 2) % 2 of each (+ 32 rows per i).
+  const int k_lds = (tid >> 4) * KS + (tid & 15) * 16;
+  int v_lds0, v_lds1;
+  {
+    const int d = tid >> 3, m = tid & 7;
+    const int ch0 = 4 * (m >> 2) + 2 * (m & 1), hf = ((m >> 1) & 1) * 8;
+    v_lds0 = d * VS + ((ch0 ^ v_swz(d)) << 4) + hf;
+    v_lds1 = d * VS + (((ch0 + 1) ^ v_swz(d)) << 4) + hf;
+  }
   u32x4 rk0[4], rv0[4], rk1[4], rv1[4];
   auto load_tile = [&](auto set_tag, int kt) {
     constexpr int S = decltype(set_tag)::value;
     u32x4* rk = S ? rk1 : rk0;
     u32x4* rv = S ? rv1 : rv0;
-    const int k0 = kt * KT;
+    const int64_t k_off = (int64_t)kt * KT * ld * 2;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(kbase + k_off), (short)0, (int)(k_bytes - k_off), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(vbase + kt * KT * 2), (short)0, v_bytes_max - kt * KT * 2,
+        kBufferWord3);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int key = min(k0 + (c >> 4), T - 1);
-      rk[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * ld + (c & 15) * 8);
-      rv[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)(c >> 3) * Tp + k0 + (c & 7) * 8);
+      rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            kr, (int)(k_voff + i * k_step), 0, 0));
+      rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            vr, (int)(v_voff + i * v_step), 0, 0));
     }
   };
   auto store_tile = [&](auto set_tag, int buf) {
@@ -144,26 +192,26 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
     const u32x4* rv = S ? rv1 : rv0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(&sK[buf][(c >> 4) * KS + (c & 15) * 16]) = rk[i];
-      // 16-byte chunk j of row d holds slots 2j, 2j + 1: they land as chunk j ^ (sg / 2),
-      // in swapped order when sg is odd
-      const int d = c >> 3, sg = d & 15;
-      const u32x4 v = (sg & 1) ? rv[i].zwxy : rv[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][d * VS + ((c & 7) ^ (sg >> 1)) * 16]) = v;
+      *reinterpret_cast<u32x4*>(&sK[buf][k_lds + 16 * KS * i]) = rk[i];
+      *reinterpret_cast<u32x2*>(&sV[buf][v_lds0 + 32 * VS * i]) = rv[i].xy;
+      *reinterpret_cast<u32x2*>(&sV[buf][v_lds1 + 32 * VS * i]) = rv[i].zw;
     }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
+  using F = std::false_type;
+  using Tr = std::true_type;
 
-  v4f o[NQT][8];
+  // A-operand offsets: K rows 16 s + c16, bytes 64 kk + 16 g; V^T rows 16 dt + c16, chunk
+  // 4c + g
+  const int k_rd = c16 * KS + g * 16;
+  const int v_rd0 = c16 * VS + (((0 + g) ^ v_swz(c16)) << 4);
+  const int v_rd1 = c16 * VS + (((4 + g) ^ v_swz(c16)) << 4);
+
+  v4f o[8];
 #pragma unroll
-  for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[qt][dt] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_run[NQT], l_part[NQT];
-#pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) m_run[qt] = -INFINITY, l_part[qt] = 0.f;
+  for (int dt = 0; dt < 8; ++dt) o[dt] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
 
   // tile kt: loaded into register set kt % 2 at iteration kt - 2 (the prologue for tiles 0
   // and 1), stored into LDS stage kt % 2 at the end of iteration kt - 1, computed at
@@ -173,107 +221,101 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   if (nkt > 1) load_tile(I1{}, 1);
   __syncthreads();
 
-  auto step = [&](auto par_tag, int kt) {
+  auto step = [&](auto par_tag, auto diag_tag, int kt) {
     constexpr int P = decltype(par_tag)::value;  // kt % 2
+    constexpr bool DIAG = decltype(diag_tag)::value;  // the last tile: keys past a query
     const int cur = P;
-    if (kt + 2 < nkt) load_tile(par_tag, kt + 2);  // set P held tile kt, already in LDS
+    if (!DIAG && kt + 2 < nkt) load_tile(par_tag, kt + 2);  // set P held tile kt
 
-    // S^T[key 16 s + 4 g + r][query 16 qt + c16], s = 16-key subtile
-    v4f st[NQT][4];
+    // S^T[key 16 s + 4 g + r][query c16]
+    v4f st[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) st[qt][s] = (v4f){0.f, 0.f, 0.f, 0.f};
+      st[s] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const bf16x8_t a = as_bf16x8(
-            *reinterpret_cast<const uint4*>(&sK[cur][(16 * s + c16) * KS + kk * 64 + g * 16]));
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt)
-          st[qt][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qt][kk], st[qt][s], 0, 0, 0);
+            *reinterpret_cast<const u32x4*>(&sK[cur][k_rd + 16 * s * KS + kk * 64]));
+        st[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], st[s], 0, 0, 0);
       }
     }
 
-    // online softmax in the log2 domain; only the last tile can hold keys past a query
-    const bool diag = kt == nkt - 1;
-    bf16x8_t pb[NQT][2], pl[NQT][2];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      const int qi = q0 + 16 * qt + c16;
-      float mx = -INFINITY;
+    // online softmax in the log2 domain (c_log2 > 0, so the max commutes with the scale)
+    if (DIAG) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = st[qt][s][r] * c_log2;
-          if (diag && kt * KT + 16 * s + 4 * g + r > qi) v = -INFINITY;
-          st[qt][s][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = max4q(mx);
-      const float m_new = fmaxf(m_run[qt], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
-      m_run[qt] = m_new;
-      float ls = 0.f;
+        for (int r = 0; r < 4; ++r)
+          if (kt * KT + 16 * s + 4 * g + r > qi) st[s][r] = -INFINITY;
+    }
+    float mx = st[0][0];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // p enters P.V as hi + lo, two bf16 terms (about 16 significant bits): the
-          // product keeps fp32-level accuracy on the bf16 matrix cores
-          const float p = __builtin_amdgcn_exp2f(st[qt][s][r] - m_new);
-          const __bf16 hi = (__bf16)p;
-          ls += p;
-          pb[qt][s >> 1][4 * (s & 1) + r] = hi;
-          pl[qt][s >> 1][4 * (s & 1) + r] = (__bf16)(p - (float)hi);
-        }
-      l_part[qt] = l_part[qt] * alpha + ls;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {  // uniform: some query's max moved
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[s][r]);
+    const float m_new = fmaxf(m_run, max4q(mx) * c_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    // p enters P.V as hi + lo, two bf16 terms (about 16 significant bits): the product
+    // keeps fp32-level accuracy on the bf16 matrix cores
+    u32x4 pb[2], pl[2];
+    float ls = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[qt][dt] *= alpha;
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int rp = 0; rp < 2; ++rp) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[s][2 * rp], c_log2, -m_new));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[s][2 * rp + 1], c_log2, -m_new));
+        ls += p0 + p1;
+        const uint32_t hw = bf16x2(p0, p1);
+        pb[s >> 1][2 * (s & 1) + rp] = hw;
+        pl[s >> 1][2 * (s & 1) + rp] = bf16x2(p0 - bf16_lo(hw), p1 - bf16_hi(hw));
       }
+    l_part = l_part * alpha + ls;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {  // uniform: some query's max moved
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
     }
 
-    // O^T[d 16 dt + 4 g + r][query 16 qt + c16] += V^T P^T over two 32-key steps; the key
-    // slots of lane group g are 32 c + 4 g + 0..3 and 32 c + 16 + 4 g + 0..3 for both
-    // operands
+    // O^T[d 16 dt + 4 g + r][query c16] += V^T P^T over two 32-key steps
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const uint8_t* vrow = &sV[cur][(16 * dt + c16) * VS];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + ((8 * c + g) ^ c16) * 8);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + ((8 * c + 4 + g) ^ c16) * 8);
-        const bf16x8_t a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-          o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qt][c], o[qt][dt], 0, 0, 0);
-          o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[qt][c], o[qt][dt], 0, 0, 0);
-        }
+        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            &sV[cur][(c ? v_rd1 : v_rd0) + 16 * dt * VS]));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb[c]), o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pl[c]), o[dt], 0, 0, 0);
       }
     }
 
-    if (kt + 1 < nkt) store_tile(std::integral_constant<int, P ^ 1>{}, cur ^ 1);
-    __syncthreads();
+    if (!DIAG) {
+      store_tile(std::integral_constant<int, P ^ 1>{}, cur ^ 1);  // tile kt + 1 exists
+      __syncthreads();
+    }
   };
-  for (int kt = 0; kt < nkt; kt += 2) {
-    step(I0{}, kt);
-    if (kt + 1 < nkt) step(I1{}, kt + 1);
+  // tiles 0 .. nkt - 2 are whole (no key past any query of the block), tile nkt - 1 is
+  // the diagonal one
+  const int nfull = nkt - 1;
+  int kt = 0;
+  for (; kt + 1 < nfull; kt += 2) {
+    step(I0{}, F{}, kt);
+    step(I1{}, F{}, kt + 1);
+  }
+  if (kt < nfull) {
+    step(I0{}, F{}, kt);
+    step(I1{}, Tr{}, kt + 1);
+  } else {
+    step(I0{}, Tr{}, kt);
   }
 
-  if (!live) return;
+  if (!live || qi >= T) return;
+  const float inv = 1.f / sum4q(l_part);
+  uint16_t* dst = out + (int64_t)qi * (n_q * D) + h * D + 4 * g;
 #pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    const float l = sum4q(l_part[qt]);
-    const int qi = q0 + 16 * qt + c16;
-    if (qi >= T) continue;
-    const float inv = 1.f / l;
-    uint16_t* dst = out + (int64_t)qi * (n_q * D) + h * D + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const v4f v = o[qt][dt] * inv;
-      *reinterpret_cast<uint2*>(dst + 16 * dt) = make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
-    }
+  for (int dt = 0; dt < 8; ++dt) {
+    const v4f v = o[dt] * inv;
+    *reinterpret_cast<uint2*>(dst + 16 * dt) = make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
   }
 }
 
