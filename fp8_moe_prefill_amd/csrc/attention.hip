@@ -41,8 +41,8 @@ namespace {
 constexpr int D = 128;        // head dim
 constexpr int QB = 16;        // queries per workgroup
 constexpr int KT = 64;        // keys per tile
-constexpr int KS = D * 2 + 16;   // K tile row stride in LDS (bytes): 256 + 16 pad
-constexpr int VS = KT * 2;       // V^T tile row stride in LDS (bytes): 64 keys, no pad
+constexpr int KS = D * 2;      // K tile row stride in LDS (bytes)
+constexpr int VS = KT * 2;     // V^T tile row stride in LDS (bytes): 64 keys
 // Dword 3 of a raw buffer descriptor on gfx9 data-parallel parts: 32-bit data format, no
 // swizzle, no index stride.
 constexpr int kBufferWord3 = 0x00020000;
@@ -53,11 +53,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// V^T tile in LDS: row d (128 B) holds 8 chunks of 16 B; chunk 4c + g holds keys
-// 32c + 4g .. +3, then 32c + 16 + 4g .. +3 (the key order of the P operand), at chunk
-// position (4c + g) ^ v_swz(d). The 16 rows one operand read touches then sit in 16
-// distinct 16-byte bank groups, whether the LDS serves 8 or 16 lanes per cycle.
-__device__ __forceinline__ int v_swz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
+// LDS layouts. K tile: row `key` (256 B) holds 16 chunks of 16 B, chunk c at position
+// c ^ (key % 16). V^T tile: row d (128 B) holds 8 chunks of 16 B; chunk 4c + g holds keys
+// 32c + 4g .. +3, then 32c + 16 + 4g .. +3 (the key order of the P operand), at position
+// (4c + g) ^ (d % 8). On gfx950 both measured free of bank conflicts for the 16-byte
+// operand reads (16 rows x 4 chunks per instruction) and for the staging writes, where
+// rows padded by 16 B, or an XOR that also folds in bit 3 of the row, measured 2-way.
+__device__ __forceinline__ int v_swz(int d) { return d & 7; }
 
 // max / sum of v over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes that hold the
 // same query): two lane-swap instructions of gfx950, no LDS round trip
@@ -156,10 +158,10 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   const uint32_t v_voff = (uint32_t)((tid >> 3) * Tp * 2 + (tid & 7) * 16);
   const uint32_t v_step = (uint32_t)(32 * Tp * 2);  // 32 rows
   const int v_bytes_max = (int)((int64_t)D * Tp * 2);
-  // LDS destinations: K chunk at row * KS + 16 (c % 16) (+ 16 KS per i); the two 8-byte
-  // halves of a V^T chunk (keys 8m .. 8m+3 and 8m+4 .. 8m+7, m = c % 8) go to chunks
-  // 4(m / 4) + 2(m % 2) and that + 1, half (m / 2) % 2 of each (+ 32 rows per i).
-  const int k_lds = (tid >> 4) * KS + (tid & 15) * 16;
+  // LDS destinations: K chunk c % 16 of row c / 16 (+ 16 rows per i, same position); the
+  // two 8-byte halves of a V^T chunk (keys 8m .. 8m+3 and 8m+4 .. 8m+7, m = c % 8) go to
+  // chunks 4(m / 4) + 2(m % 2) and that + 1, half (m / 2) % 2 of each (+ 32 rows per i).
+  const int k_lds = (tid >> 4) * KS + (((tid & 15) ^ (tid >> 4)) << 4);
   int v_lds0, v_lds1;
   {
     const int d = tid >> 3, m = tid & 7;
@@ -202,9 +204,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   using F = std::false_type;
   using Tr = std::true_type;
 
-  // A-operand offsets: K rows 16 s + c16, bytes 64 kk + 16 g; V^T rows 16 dt + c16, chunk
+  // A-operand offsets: K rows 16 s + c16, chunk 4 kk + g; V^T rows 16 dt + c16, chunk
   // 4c + g
-  const int k_rd = c16 * KS + g * 16;
+  int k_rd[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) k_rd[kk] = c16 * KS + (((4 * kk + g) ^ c16) << 4);
   const int v_rd0 = c16 * VS + (((0 + g) ^ v_swz(c16)) << 4);
   const int v_rd1 = c16 * VS + (((4 + g) ^ v_swz(c16)) << 4);
 
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const bf16x8_t a = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(&sK[cur][k_rd + 16 * s * KS + kk * 64]));
+            *reinterpret_cast<const u32x4*>(&sK[cur][k_rd[kk] + 16 * s * KS]));
         st[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], st[s], 0, 0, 0);
       }
     }
