@@ -92,6 +92,10 @@ hipError_t launch_bf16_gemm(const uint16_t* a, const uint16_t* w, int64_t M, int
     case 8: return launch_narrow<8>(a, w, M, N, K, out, st);
     default: break;
   }
+  if (tn::use_big_tiles(M, N))
+    return tn::launch<true, false, 2, false, false, true>(reinterpret_cast<const uint8_t*>(a),
+                                                          reinterpret_cast<const uint8_t*>(w), M,
+                                                          N, 2 * K, nullptr, nullptr, out, st);
   return tn::launch<true, false, 2>(reinterpret_cast<const uint8_t*>(a),
                                     reinterpret_cast<const uint8_t*>(w), M, N, 2 * K, nullptr,
                                     nullptr, out, st);

@@ -136,6 +136,15 @@ hipError_t launch_dense(const uint8_t* a, const float* a_s, const uint8_t* w,
                                                                          out);
     return hipGetLastError();
   }
+  if constexpr (!ROW_SCALE && !BLOCK) {
+    if (tn::use_big_tiles(M, N)) {
+      if (out_dtype == FP8MOE_DTYPE_BF16)
+        return tn::launch<false, true, 2, false, false, true>(a, w, M, N, K, a_s, w_scale, out,
+                                                              st);
+      return tn::launch<false, false, 2, false, false, true>(a, w, M, N, K, a_s, w_scale, out,
+                                                             st);
+    }
+  }
   if (out_dtype == FP8MOE_DTYPE_BF16)
     return tn::launch<false, true, kDenseStages, ROW_SCALE, BLOCK>(a, w, M, N, K, a_s, w_scale,
                                                                    out, st);

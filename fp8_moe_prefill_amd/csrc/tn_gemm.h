@@ -3,9 +3,15 @@
 // fp8moe_bf16_gemm).
 //
 // gfx950 design:
-// * Workgroup tile 128 x 128, 4 waves in a 2 x 2 grid of 64 x 64 (4 x 4 MFMA tiles each).
-//   One K step is 128 bytes of each row: one v_mfma_f32_16x16x128_f8f6f4 per 16 x 16 tile
-//   for e4m3, two v_mfma_f32_16x16x32_bf16 for bf16.
+// * Workgroup tile 128 x 128, 4 waves in a 2 x 2 grid of 64 x 64 (4 x 4 MFMA tiles each),
+//   or (BIG) 256 x 256, 8 waves in a 2 x 4 grid of 128 x 64 (8 x 4 MFMA tiles each, one
+//   workgroup per CU). One K step is 128 bytes of each row: one
+//   v_mfma_f32_16x16x128_f8f6f4 per 16 x 16 tile for e4m3, two v_mfma_f32_16x16x32_bf16
+//   for bf16. The LDS is what bounds the small tile: per MFMA a 64 x 64 wave tile reads
+//   1 KB of operands and the workgroup's DMA writes 0.5 KB, as much LDS time as the CU's
+//   matrix cores spend; the 128 x 64 wave tile of BIG reads 0.75 KB and its 256 x 256
+//   workgroup tile writes 0.25 KB per MFMA. BIG needs many tiles to fill the CUs, so the
+//   launch picks it by shape.
 // * Both operands go straight from global memory into LDS (LDS DMA, no VGPR staging, no
 //   LDS writes by the waves), each DMA instruction copying 8 whole 128-byte lines (8 rows
 //   of one K step) into 1 KB of LDS; the 16-byte chunks of a row are XOR-swizzled so that
@@ -29,25 +35,32 @@
 //   other wave on the SIMD keeps the matrix core busy meanwhile.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "lds_dma.h"
 
 namespace fp8moe {
 namespace tn {
 
-constexpr int TM = 128, TN = 128;  // tile rows and columns
+constexpr int TM = 128, TN = 128;  // tile rows and columns (BIG: 256 x 256)
 constexpr int KSTEP = 128;         // bytes of K per step
 constexpr int BLK = 1024;          // one operand block: 64 lanes x 16 bytes
 constexpr int kMaxBlockSteps = 128;  // BLOCK: K <= 16384
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-template <int STAGES>
+template <int STAGES, int ROWS>
 struct Smem {
-  uint8_t a[STAGES][16 * BLK];  // 8 row tiles x 2 halves
-  uint8_t b[STAGES][16 * BLK];  // 8 column tiles x 2 halves
-  float as[STAGES][TM];         // BLOCK: the step's scales of the tile's 128 rows
-  float ws[kMaxBlockSteps];     // BLOCK: the tile's weight-block scale of every K step
+  uint8_t a[STAGES][ROWS / 8 * BLK];  // ROWS / 16 row tiles x 2 halves
+  uint8_t b[STAGES][ROWS / 8 * BLK];  // ROWS / 16 column tiles x 2 halves
+  float as[STAGES][TM];               // BLOCK: the step's scales of the tile's 128 rows
+  float ws[kMaxBlockSteps];           // BLOCK: the tile's weight-block scale of every K step
+};
+template <int STAGES>
+struct SmemBig {
+  uint8_t a[STAGES][32 * BLK];
+  uint8_t b[STAGES][32 * BLK];
 };
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -71,37 +84,46 @@ __device__ __forceinline__ int col_of(int rho) {
 // scale_a[row] * scale_w[0] (one activation scale per row); with BLOCK, scale_a is fp32
 // [M, K/128] (per row and K group) and scale_w fp32 [ceil(N/128), K/128] (per weight
 // block), folded per K step; the bf16 path takes no scale.
-template <bool IN_BF16, bool OUT_BF16, int STAGES, bool ROW_SCALE = false, bool BLOCK = false>
-__global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restrict__ A,
+template <bool IN_BF16, bool OUT_BF16, int STAGES, bool ROW_SCALE = false, bool BLOCK = false,
+          bool BIG = false>
+__global__ __launch_bounds__(BIG ? 512 : 256, BIG ? 1 : 2) void tn_gemm_kernel(const uint8_t* __restrict__ A,
                                                          const uint8_t* __restrict__ W, int M,
                                                          int N, int row_bytes, int NTM,
                                                          int NTN,
                                                          const float* __restrict__ scale_a,
                                                          const float* __restrict__ scale_w,
                                                          void* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) Smem<STAGES> sm;
+  static_assert(!BIG || (!ROW_SCALE && !BLOCK && STAGES == 2), "BIG: per-tensor scales");
+  constexpr int NWAVE = BIG ? 8 : 4;
+  constexpr int HALF = NWAVE / 2;     // waves that load A (the rest load W)
+  constexpr int WNW = BIG ? 4 : 2;    // waves along N
+  constexpr int RT = BIG ? 8 : 4;     // 16-row tiles per wave
+  constexpr int TMB = 2 * RT * 16, TNB = WNW * 64;  // workgroup tile
+  using SmemT = typename std::conditional<BIG, SmemBig<STAGES>, Smem<STAGES, 128>>::type;
+  __shared__ __attribute__((aligned(16))) SmemT sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int g = lane >> 4, c16 = lane & 15;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / WNW, wn = wv % WNW;
   const uint32_t L = xcd_contiguous(blockIdx.x, gridDim.x);
   int tm, tn;
   grouped_tile(L, NTM, NTN, tm, tn);
-  const int m0 = tm * TM, n0 = tn * TN;
+  const int m0 = tm * TMB, n0 = tn * TNB;
   const int KS = row_bytes / KSTEP;
 
-  // DMA duty: 32 instructions per step (16 for the 128 rows of A, 16 for the 128 columns
-  // of W), 8 per wave; waves 0-1 load A, waves 2-3 load W. Instruction j of an operand
-  // copies its rows 8 (j % 16) .. + 7 as whole 128-byte lines: lane l takes row
-  // 8 (j % 16) + l / 8 and writes LDS position l % 8 of it, holding the line's 16-byte
-  // chunk (l % 8) ^ sw(row) (see lds_pos). voff[j] is that byte offset at K step 0.
-  const uint8_t* src = wv < 2 ? A : W;
+  // DMA duty: 8 instructions per wave and step (the 128 or 256 rows of A and of W, 8 rows
+  // per instruction); the first half of the waves loads A, the second W. Instruction j of
+  // a wave copies rows 8 (8 (wave % HALF) + j) .. + 7 as whole 128-byte lines: lane l
+  // takes row 8 (8 (wave % HALF) + j) + l / 8 and writes LDS position l % 8 of it, holding
+  // the line's 16-byte chunk (l % 8) ^ sw(row). voff[j] is that byte offset at K step 0.
+  const bool loads_a = wv < HALF;
+  const uint8_t* src = loads_a ? A : W;
   uint32_t voff[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int rho = 8 * (8 * (wv & 1) + j) + (lane >> 3);  // LDS row of this lane
+    const int rho = 8 * (8 * (wv % HALF) + j) + (lane >> 3);  // LDS row of this lane
     int row;
-    if (wv < 2) row = min(m0 + rho, M - 1);
+    if (loads_a) row = min(m0 + rho, M - 1);
     else row = min(n0 + col_of(rho), N - 1);
     const int chunk = (lane & 7) ^ sw(rho);
     voff[j] = (uint32_t)row * (uint32_t)row_bytes + 16u * (uint32_t)chunk;
@@ -115,23 +137,24 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
                             : 0u;
   // BLOCK: the tile's 128 columns are one weight block; its scales of all K steps go to
   // LDS once (published by the first step's barrier)
-  if (BLOCK)
+  if constexpr (BLOCK)
     for (int k = tid; k < KS; k += 256) sm.ws[k] = scale_w[(n0 / TN) * KS + k];
   auto issue = [&](int ks) {
     const int st = ks % STAGES;
-    uint8_t* dst = (wv < 2 ? sm.a[st] : sm.b[st]) + (wv & 1) * 8 * BLK;
+    uint8_t* dst = (loads_a ? sm.a[st] : sm.b[st]) + (wv % HALF) * 8 * BLK;
 #pragma unroll
     for (int j = 0; j < 8; ++j) dma16(src, voff[j] + (uint32_t)(ks * KSTEP), dst + j * BLK);
-    if (BLOCK && wv < 2) dma4(scale_a, soff + 4u * (uint32_t)ks, &sm.as[st][64 * wv]);
+    if constexpr (BLOCK)
+      if (wv < 2) dma4(scale_a, soff + 4u * (uint32_t)ks, &sm.as[st][64 * wv]);
   };
   // operand reads: tile T (16 rows), half h: row 16 T + c16, chunk 2 g + h
   const int x = sw(c16);
   const int rd0 = c16 * KSTEP + (((2 * g) ^ x) << 4);
   const int rd1 = c16 * KSTEP + (((2 * g + 1) ^ x) << 4);
 
-  v4f acc[4][4];
+  v4f acc[RT][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < RT; ++t)
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc[t][s] = (v4f){0.f, 0.f, 0.f, 0.f};
   // per-row activation scales of this lane's 16 output rows, loaded now so that their
@@ -157,23 +180,23 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
     if (ks + STAGES - 1 < KS) issue(ks + STAGES - 1);
     const uint8_t* sa = sm.a[ks % STAGES];
     const uint8_t* sb = sm.b[ks % STAGES];
-    if (IN_BF16) {
+    if constexpr (IN_BF16) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        bf16x8_t aop[4], bop[4];
+        bf16x8_t aop[RT], bop[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           bop[s] = __builtin_bit_cast(bf16x8_t, lds16(sb + (4 * wn + s) * 16 * KSTEP + (h ? rd1 : rd0)));
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          aop[t] = __builtin_bit_cast(bf16x8_t, lds16(sa + (4 * wm + t) * 16 * KSTEP + (h ? rd1 : rd0)));
+        for (int t = 0; t < RT; ++t)
+          aop[t] = __builtin_bit_cast(bf16x8_t, lds16(sa + (RT * wm + t) * 16 * KSTEP + (h ? rd1 : rd0)));
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < RT; ++t)
 #pragma unroll
           for (int s = 0; s < 4; ++s)
             acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[t], bop[s], acc[t][s], 0, 0, 0);
       }
-    } else if (BLOCK) {
+    } else if constexpr (BLOCK) {
       v8i aop[4], bop[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -209,8 +232,8 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
         for (int r = 0; r < 4; ++r)
           acc[i >> 2][i & 3][r] = fmaf(pb[i][r], sc[i >> 2][r], acc[i >> 2][i & 3][r]);
     } else {
-      // all operands of the step first (16 reads in flight), then the 16 MFMAs
-      v8i aop[4], bop[4];
+      // all operands of the step first (2 (RT + 4) reads in flight), then the 4 RT MFMAs
+      v8i aop[RT], bop[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const uint4 lo = lds16(sb + (4 * wn + s) * 16 * KSTEP + rd0);
@@ -219,14 +242,14 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint4 lo = lds16(sa + (4 * wm + t) * 16 * KSTEP + rd0);
-        const uint4 hi = lds16(sa + (4 * wm + t) * 16 * KSTEP + rd1);
+      for (int t = 0; t < RT; ++t) {
+        const uint4 lo = lds16(sa + (RT * wm + t) * 16 * KSTEP + rd0);
+        const uint4 hi = lds16(sa + (RT * wm + t) * 16 * KSTEP + rd1);
         aop[t] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           acc[t][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop[t], bop[s], acc[t][s],
@@ -239,12 +262,12 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
   const int c0 = n0 + 64 * wn + 4 * c16;
   const bool vec = (c0 + 3 < N) && ((N & 3) == 0);
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < RT; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = m0 + 64 * wm + 16 * t + 4 * g + r;
+      const int row = m0 + 16 * RT * wm + 16 * t + 4 * g + r;
       if (row >= M) continue;
-      const float scale = ROW_SCALE ? row_scale[t][r] * sw0 : tensor_scale;
+      const float scale = ROW_SCALE ? row_scale[t & 3][r] * sw0 : tensor_scale;
       const float v0 = acc[t][0][r] * scale, v1 = acc[t][1][r] * scale;
       const float v2 = acc[t][2][r] * scale, v3 = acc[t][3][r] * scale;
       const int64_t o = (int64_t)row * N + c0;
@@ -272,13 +295,38 @@ __global__ __launch_bounds__(256, 2) void tn_gemm_kernel(const uint8_t* __restri
     }
 }
 
-// Enqueue the kernel over ceil(M/128) x ceil(N/128) tiles; row_bytes = bytes per row of K.
-template <bool IN_BF16, bool OUT_BF16, int STAGES, bool ROW_SCALE = false, bool BLOCK = false>
+// Compute units of the current device (queried once per device).
+inline int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// BIG tiles (one workgroup per CU) when they give every CU at least two of them; fewer
+// would leave CUs idle for a whole round. By shape only: both tilings accumulate every
+// output over the same K steps in the same order, so the choice never changes a result.
+inline bool use_big_tiles(int64_t M, int64_t N) {
+  return ((M + 255) / 256) * ((N + 255) / 256) >= 2 * (int64_t)device_cus();
+}
+
+// Enqueue the kernel over ceil(M/128) x ceil(N/128) tiles (BIG: 256 x 256); row_bytes =
+// bytes per row of K.
+template <bool IN_BF16, bool OUT_BF16, int STAGES, bool ROW_SCALE = false, bool BLOCK = false,
+          bool BIG = false>
 hipError_t launch(const uint8_t* a, const uint8_t* w, int64_t M, int64_t N, int64_t row_bytes,
                   const float* scale_a, const float* scale_w, void* out, hipStream_t st) {
-  const int NTM = (int)((M + TM - 1) / TM), NTN = (int)((N + TN - 1) / TN);
-  tn_gemm_kernel<IN_BF16, OUT_BF16, STAGES, ROW_SCALE, BLOCK>
-      <<<dim3((uint32_t)(NTM * NTN)), 256, 0, st>>>(
+  constexpr int T = BIG ? 256 : 128;
+  const int NTM = (int)((M + T - 1) / T), NTN = (int)((N + T - 1) / T);
+  tn_gemm_kernel<IN_BF16, OUT_BF16, STAGES, ROW_SCALE, BLOCK, BIG>
+      <<<dim3((uint32_t)(NTM * NTN)), BIG ? 512 : 256, 0, st>>>(
       a, w, (int)M, (int)N, (int)row_bytes, NTM, NTN, scale_a, scale_w, out);
   return hipGetLastError();
 }

@@ -196,3 +196,27 @@ def test_block128_quant_ragged_and_outliers():
     rq, rs = quant_block128_bf16(w)
     assert_bytes_equal(host(q), rq, "codes")
     assert_bytes_equal(host(s).view(np.uint32), rs.view(np.uint32), "block scales")
+
+
+def test_big_tiles_sampled_and_equal_to_small_tiles():
+    """4000 x 8000 x 256 per-tensor: enough 256 x 256 tiles for the one-workgroup-per-CU
+    tiling (ragged in both M and N), sampled against the oracle with the last row and
+    column included; its first 300 rows must equal, bit for bit, the same product over
+    only those rows (128 x 128 tiles): both tilings run the same K steps per output."""
+    import fp8_moe_prefill_amd as f
+    rng = np.random.default_rng(21)
+    M, N, K = 4000, 8000, 256
+    x = bf16_bits_from_f32(rng.standard_normal((M, K)).astype(np.float32))
+    w = bf16_bits_from_f32((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    wq, sw = f.quantize_weight(dev(w))
+    xq, blk = f.fp8_quant_act(dev(x), 0)
+    y = f.fp8_dense_gemm(xq, blk, wq, sw, torch.float32)
+    y_small = f.fp8_dense_gemm(xq[:300].contiguous(), blk, wq, sw, torch.float32)
+    torch.cuda.synchronize()
+    y, y_small = host(y), host(y_small)
+    assert_bytes_equal(y[:300], y_small, "big tiles vs small tiles")
+    rows = rng.integers(0, M, 3000)
+    cols = rng.integers(0, N, 3000)
+    rows[:3], cols[:3] = [M - 1, M - 1, 0], [N - 1, 0, N - 1]
+    ref, b = dense_w8a8_entries(host(xq), host(blk)[2], host(wq), host(sw)[0], rows, cols)
+    check_close(y[rows, cols].astype(np.float64), ref, gemm_bound(b), "dense big tiles")

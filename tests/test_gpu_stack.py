@@ -136,6 +136,27 @@ def test_bf16_gemm_integer_exact(N):
     assert np.array_equal(host(out).astype(np.float64), ref)
 
 
+def test_bf16_gemm_big_tiles_ragged():
+    """2000 x 33000 x 320: the one-workgroup-per-CU 256 x 256 tiling with ragged edges in
+    M, N and the last K step; sampled within the bound, and its first 200 rows equal bit
+    for bit to the same product over only those rows (128 x 128 tiles)."""
+    import fp8_moe_prefill_amd as f
+    rng = np.random.default_rng(12)
+    M, N, K = 2000, 33000, 320
+    a, w = _bf16(rng, (M, K)), _bf16(rng, (N, K), 0.02)
+    out = host(f.bf16_gemm(dev(a), dev(w)))
+    small = host(f.bf16_gemm(dev(a[:200]), dev(w)))
+    torch.cuda.synchronize()
+    assert_bytes_equal(out[:200], small, "big tiles vs small tiles")
+    r = rng.integers(0, M, 4096)
+    c = rng.integers(0, N, 4096)
+    r[:3], c[:3] = [M - 1, M - 1, 0], [N - 1, 0, N - 1]
+    A, W = _vals(a[r]), _vals(w[c])
+    ref = np.einsum("ik,ik->i", A, W)
+    b = np.einsum("ik,ik->i", np.abs(A), np.abs(W))
+    check_close(out[r, c], ref, gemm_bound(b), "bf16 big tiles sampled")
+
+
 def test_bf16_gemm_lm_head_sampled():
     """The LM-head shape (2048 x 32000 x 2048), 4096 sampled outputs."""
     import fp8_moe_prefill_amd as f
