@@ -11,11 +11,12 @@
 // * a workgroup owns one kv head, 16 queries and four query heads of that kv head's group,
 //   one per wave (small query blocks: more workgroups in flight for the causal
 //   imbalance); the K tile and the transposed V tile of 64 keys are staged once in LDS
-//   (double-buffered) and shared by the four waves; a tile's global loads are issued two
-//   tiles ahead into one of two register sets (one tile of compute is shorter than the
-//   load latency). The loads are buffer loads whose per-lane offsets are fixed for the
-//   whole kernel: only the scalar base moves from tile to tile, and keys past T read as
-//   zero (the range check of the buffer descriptor), so staging costs no vector ALU work;
+//   (K in two stages, V^T in three) and shared by the four waves; a tile's global loads
+//   are issued two tiles ahead into one of two register sets (one tile of compute is
+//   shorter than the load latency). The loads are buffer loads whose per-lane offsets are
+//   fixed for the whole kernel: only the scalar base moves from tile to tile, and keys past
+//   T read as zero (the range check of the buffer descriptor), so staging costs no vector
+//   ALU work;
 // * each wave computes S^T = K Q^T (v_mfma_f32_16x16x32_bf16, keys as rows), so a lane's
 //   scores all belong to one query: the running max, the rescale of the output and the
 //   row sum need no lane exchange except the 4-lane max per tile; the causal mask only
@@ -26,6 +27,14 @@
 //   accumulator layout puts keys 4g..4g+3 and 16+4g..16+4g+3 of each 32-key step in lane
 //   group g, so the V^T tile is stored in LDS in that key order: one 16-byte read per
 //   lane is one A operand;
+// * software pipelining inside a wave: iteration kt issues the score MFMAs of tile kt,
+//   then the P.V MFMAs of tile kt - 1 while its VALU computes the softmax of tile kt (the
+//   two are independent), so the matrix core and the VALU of one wave work side by side.
+//   Tile kt - 1's rescale by its running max is applied at the start of iteration kt,
+//   before any MFMA, so that the score MFMAs, the softmax and the P.V MFMAs sit in one
+//   basic block the compiler can interleave. Per output element the rescales and adds run
+//   in the same order as without the pipelining. The third V^T stage lets tile kt + 1 be
+//   staged while tile kt - 1's V^T is still being read: one barrier per tile;
 // * V is transposed once per layer into a [n_kv][d][T_pad] workspace by a small kernel
 //   (zero-filled past T), so V^T tiles load as contiguous rows.
 // Workgroups are paired heavy with light (see the rank mapping) against the causal
@@ -114,7 +123,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
                                                            int ld, int n_q, int n_kv, int Tp,
                                                            int n_hg, float c_log2) {
   __shared__ __attribute__((aligned(16))) uint8_t sK[2][KT * KS];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[2][D * VS];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[3][D * VS];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int rep = n_q / n_kv;
@@ -188,15 +197,15 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
                                             vr, (int)(v_voff + i * v_step), 0, 0));
     }
   };
-  auto store_tile = [&](auto set_tag, int buf) {
+  auto store_tile = [&](auto set_tag, int kbuf, int vbuf) {
     constexpr int S = decltype(set_tag)::value;
     const u32x4* rk = S ? rk1 : rk0;
     const u32x4* rv = S ? rv1 : rv0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&sK[buf][k_lds + 16 * KS * i]) = rk[i];
-      *reinterpret_cast<u32x2*>(&sV[buf][v_lds0 + 32 * VS * i]) = rv[i].xy;
-      *reinterpret_cast<u32x2*>(&sV[buf][v_lds1 + 32 * VS * i]) = rv[i].zw;
+      *reinterpret_cast<u32x4*>(&sK[kbuf][k_lds + 16 * KS * i]) = rk[i];
+      *reinterpret_cast<u32x2*>(&sV[vbuf][v_lds0 + 32 * VS * i]) = rv[i].xy;
+      *reinterpret_cast<u32x2*>(&sV[vbuf][v_lds1 + 32 * VS * i]) = rv[i].zw;
     }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -218,18 +227,54 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
   float m_run = -INFINITY, l_part = 0.f;
 
   // tile kt: loaded into register set kt % 2 at iteration kt - 2 (the prologue for tiles 0
-  // and 1), stored into LDS stage kt % 2 at the end of iteration kt - 1, computed at
-  // iteration kt
+  // and 1), stored into K stage kt % 2 and V^T stage kt % 3 during iteration kt - 1 (the
+  // prologue for tile 0), published by that iteration's barrier; its scores and softmax
+  // are computed at iteration kt, its P.V at iteration kt + 1
   load_tile(I0{}, 0);
-  store_tile(I0{}, 0);
+  store_tile(I0{}, 0, 0);
   if (nkt > 1) load_tile(I1{}, 1);
   __syncthreads();
 
-  auto step = [&](auto par_tag, auto diag_tag, int kt) {
+  // P of the previous tile (register set by tile parity) and its rescale factor: tile kt's
+  // P.V runs at iteration kt + 1, beside the softmax of tile kt + 1
+  u32x4 pbs0[2], pls0[2], pbs1[2], pls1[2];
+  float alpha_prev = 1.f;
+  int vs = 0;  // V^T stage of tile kt: kt % 3
+  auto rescale = [&](float alpha) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {  // uniform: some query's max moved
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
+  };
+  auto pv = [&](auto set_tag, int vbuf) {
+    const u32x4* pb = decltype(set_tag)::value ? pbs1 : pbs0;
+    const u32x4* pl = decltype(set_tag)::value ? pls1 : pls0;
+    // O^T[d 16 dt + 4 g + r][query c16] += V^T P^T over two 32-key steps
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            &sV[vbuf][(c ? v_rd1 : v_rd0) + 16 * dt * VS]));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb[c]), o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pl[c]), o[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  auto step = [&](auto par_tag, auto diag_tag, auto first_tag, int kt) {
     constexpr int P = decltype(par_tag)::value;  // kt % 2
     constexpr bool DIAG = decltype(diag_tag)::value;  // the last tile: keys past a query
+    constexpr bool FIRST = decltype(first_tag)::value;  // kt == 0: no previous tile
     const int cur = P;
+    // the output as of tile kt - 2, rescaled to the running max of tile kt - 1, before
+    // tile kt - 1's P.V is added below
+    if (!FIRST) rescale(alpha_prev);
+    const int vs_prev = vs == 0 ? 2 : vs - 1, vs_next = vs == 2 ? 0 : vs + 1;
     if (!DIAG && kt + 2 < nkt) load_tile(par_tag, kt + 2);  // set P held tile kt
+    // tile kt + 1 into the K stage of tile kt - 1 and the V^T stage of tile kt - 2, both
+    // read for the last time in iteration kt - 1
+    if (!DIAG) store_tile(std::integral_constant<int, P ^ 1>{}, cur ^ 1, vs_next);
 
     // S^T[key 16 s + 4 g + r][query c16]
     v4f st[4];
@@ -262,7 +307,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
     m_run = m_new;
     // p enters P.V as hi + lo, two bf16 terms (about 16 significant bits): the product
     // keeps fp32-level accuracy on the bf16 matrix cores
-    u32x4 pb[2], pl[2];
+    u32x4* pb = P ? pbs1 : pbs0;
+    u32x4* pl = P ? pls1 : pls0;
     float ls = 0.f;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -276,41 +322,36 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const uint16_t* __res
         pl[s >> 1][2 * (s & 1) + rp] = bf16x2(p0 - bf16_lo(hw), p1 - bf16_hi(hw));
       }
     l_part = l_part * alpha + ls;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {  // uniform: some query's max moved
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    // the previous tile's P.V (its V^T stage vs_prev), then, at the diagonal tile, this
+    // tile's own
+    if (!FIRST) pv(std::integral_constant<int, P ^ 1>{}, vs_prev);
+    alpha_prev = alpha;
+    if (DIAG) {
+      rescale(alpha);
+      pv(par_tag, vs);
     }
-
-    // O^T[d 16 dt + 4 g + r][query c16] += V^T P^T over two 32-key steps
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            &sV[cur][(c ? v_rd1 : v_rd0) + 16 * dt * VS]));
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb[c]), o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pl[c]), o[dt], 0, 0, 0);
-      }
-    }
-
-    if (!DIAG) {
-      store_tile(std::integral_constant<int, P ^ 1>{}, cur ^ 1);  // tile kt + 1 exists
-      __syncthreads();
-    }
+    vs = vs_next;
+    if (!DIAG) __syncthreads();
   };
   // tiles 0 .. nkt - 2 are whole (no key past any query of the block), tile nkt - 1 is
   // the diagonal one
   const int nfull = nkt - 1;
-  int kt = 0;
-  for (; kt + 1 < nfull; kt += 2) {
-    step(I0{}, F{}, kt);
-    step(I1{}, F{}, kt + 1);
-  }
-  if (kt < nfull) {
-    step(I0{}, F{}, kt);
-    step(I1{}, Tr{}, kt + 1);
+  using T0 = std::true_type;
+  if (nfull == 0) {
+    step(I0{}, Tr{}, T0{}, 0);
   } else {
-    step(I0{}, Tr{}, kt);
+    step(I0{}, F{}, T0{}, 0);
+    int kt = 1;
+    for (; kt + 1 < nfull; kt += 2) {
+      step(I1{}, F{}, F{}, kt);
+      step(I0{}, F{}, F{}, kt + 1);
+    }
+    if (kt < nfull) {
+      step(I1{}, F{}, F{}, kt);
+      step(I0{}, Tr{}, F{}, kt + 1);
+    } else {
+      step(I1{}, Tr{}, F{}, kt);
+    }
   }
 
   if (!live || qi >= T) return;
