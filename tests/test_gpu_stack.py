@@ -195,7 +195,8 @@ def _attention_tol(q, k, n_q, n_kv, d, ref, bound, gpu):
 
 
 @pytest.mark.parametrize("T,n_q,n_kv,std", [(1, 4, 1, 1.0), (77, 8, 2, 1.0), (200, 4, 4, 1.0),
-                                            (130, 16, 4, 3.0), (2048, 16, 4, 1.0)])
+                                            (130, 16, 4, 3.0), (2048, 16, 4, 1.0),
+                                            (150, 8, 1, 1.0), (100, 6, 2, 3.0)])
 def test_attention_bound(T, n_q, n_kv, std):
     import fp8_moe_prefill_amd as f
     d = 128
