@@ -11,7 +11,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH, abi_version, bf16_gemm, causal_attention, fp8_dense_gemm, fp8_dense_gemm_rowwise,
     fp8_block_gemm, fp8_grouped_expert_gemm, fp8_quant_weight_block128, mxfp4_grouped_expert_gemm,
     mxfp4_quant_act, fp8_quant_act, moe_route_permute, moe_route_permute_noalloc,
-    moe_unpermute_combine, pack_expert_bank, rmsnorm, workspace_bytes,
+    moe_unpermute_combine, pack_expert_bank, quant_route, rmsnorm, workspace_bytes,
 )
 from .layer import ExpertBank, MoELayerRunner, moe_layer, quantize_weight, w8a8_linear  # noqa: F401
 from .stack import DepthStack, StackRunner  # noqa: F401

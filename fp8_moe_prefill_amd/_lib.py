@@ -42,6 +42,9 @@ SIGNATURES = {
                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                          _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                          _c_void_p]),
+    "fp8moe_quant_route": (_i32, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
     "fp8moe_pack_expert_bank": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p,
                                        _c_void_p, _c_void_p]),
     "fp8_grouped_expert_gemm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
@@ -241,6 +244,32 @@ def moe_route_permute_noalloc(logits: torch.Tensor, k: int, xq=None, xs=None, ou
     r, head = _route_buffers(logits, k, xq, xs, xsum, out)
     _check("moe_route_permute_noalloc", _lib.moe_route_permute_noalloc(*head, _stream(stream)))
     return r
+
+
+@_on_stream
+def quant_route(x: torch.Tensor, logits: torch.Tensor, k: int, q=None, scales=None, sums=None,
+                out=None, ws=None, stream=None, with_sums: bool = True):
+    """fp8_quant_act(x, GROUP) and moe_route_permute(logits, k) (no gathers) in one call:
+    returns (q, scales, sums or None, route dict), the same bytes as the two calls."""
+    _dev(x, "x", torch.bfloat16)
+    T, H = x.shape
+    if logits.shape[0] != T:
+        raise ValueError("x and logits must have the same number of rows")
+    if q is None:
+        q = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((T, H // GROUP), dtype=torch.float32, device=x.device)
+    if with_sums and sums is None:
+        sums = torch.empty((T, H // GROUP), dtype=torch.float32, device=x.device)
+    r, head = _route_buffers(logits, k, None, None, None, out)
+    E = logits.shape[1]
+    nbytes = workspace_bytes(OP_ROUTE_PERMUTE, T, E, k)
+    wsb = _workspace(nbytes, x.device, ws)
+    _check("fp8moe_quant_route", _lib.fp8moe_quant_route(
+        _ptr(x), T, H, _ptr(q), _ptr(scales), _ptr(sums), _ptr(logits), E, k,
+        _ptr(r["ids"]), _ptr(r["weights"]), _ptr(r["offsets"]), _ptr(r["sorted"]),
+        _ptr(r["pos"]), _ptr(wsb), nbytes, _stream(stream)))
+    return q, scales, sums, r
 
 
 @_on_stream

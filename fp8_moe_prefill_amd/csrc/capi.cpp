@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 8;
+constexpr int32_t kAbiVersion = 9;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 constexpr int64_t kMaxGroupedK = 16384;
@@ -132,6 +132,25 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k, 
   return launch_status(fp8moe::launch_route_permute(
       logits, T, E, k, ids, weights, offsets, sorted, pos, xq, xs, H, xq_perm, xs_perm, xsum,
       xsum_perm, ws, static_cast<hipStream_t>(stream)));
+}
+
+int32_t fp8moe_quant_route(const void* x, int64_t T, int64_t H, uint8_t* q, float* scales,
+                           float* sums, const float* logits, int32_t E, int32_t k,
+                           int32_t* ids, float* weights, int32_t* offsets, int32_t* sorted,
+                           int32_t* pos, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !q || !scales || !ws) return FP8MOE_ERR_NULL;
+  if (T < 1 || H < FP8MOE_GROUP || H % FP8MOE_GROUP != 0 || T > (int64_t(1) << 40) / H)
+    return FP8MOE_ERR_SHAPE;
+  const int32_t st = check_route(logits, T, E, k, ids, weights, offsets, sorted, pos, nullptr,
+                                 nullptr, H, nullptr, nullptr, nullptr, nullptr);
+  if (st != FP8MOE_OK) return st;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scales) || !aligned16(ws) ||
+      (sums && !aligned16(sums)))
+    return FP8MOE_ERR_ALIGN;
+  if (ws_bytes < fp8moe::route_workspace_bytes(T, E)) return FP8MOE_ERR_WORKSPACE;
+  return launch_status(fp8moe::launch_quant_route(
+      static_cast<const uint16_t*>(x), H, q, scales, sums, logits, T, E, k, ids, weights,
+      offsets, sorted, pos, ws, static_cast<hipStream_t>(stream)));
 }
 
 int32_t moe_route_permute_noalloc(const float* logits, int64_t T, int32_t E, int32_t k,

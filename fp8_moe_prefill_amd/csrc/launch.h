@@ -37,6 +37,12 @@ hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32
 // device (resolved once per device, then cached); it never allocates.
 constexpr size_t kRouteScratchBytes = FP8MOE_ROUTE_SCRATCH_BYTES;
 hipError_t route_scratch(void** ptr);
+// Group quantisation (with optional code sums) of x [T, H] and routing without gathers,
+// the quantiser and the top-k in one launch.
+hipError_t launch_quant_route(const uint16_t* x, int64_t H, uint8_t* q, float* scales,
+                              float* sums, const float* logits, int64_t T, int32_t E,
+                              int32_t k, int32_t* ids, float* w, int32_t* offsets,
+                              int32_t* sorted, int32_t* pos, void* ws, hipStream_t st);
 
 hipError_t launch_pack_bank(const uint8_t* w, const float* w_scales, int64_t E, int64_t N,
                             int64_t K, uint8_t* w_packed, float* ws_packed, hipStream_t st, bool fp4_layout = false);

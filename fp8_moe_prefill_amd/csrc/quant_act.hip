@@ -20,73 +20,23 @@
 // no LDS and no host synchronisation.
 #include "common.h"
 #include "launch.h"
+#include "quant_group.h"
 
 namespace fp8moe {
 namespace {
 
-struct F8 {
-  float v[8];
-};
+using qg::F8;
+using qg::amax8;
+using qg::encode8;
+using qg::kChunks;
+using qg::unpack8;
 
-__device__ __forceinline__ F8 unpack8(uint4 u) {
-  F8 f;
-  f.v[0] = bf16_lo(u.x); f.v[1] = bf16_hi(u.x);
-  f.v[2] = bf16_lo(u.y); f.v[3] = bf16_hi(u.y);
-  f.v[4] = bf16_lo(u.z); f.v[5] = bf16_hi(u.z);
-  f.v[6] = bf16_lo(u.w); f.v[7] = bf16_hi(u.w);
-  return f;
-}
-
-__device__ __forceinline__ float amax8(const F8& f) {
-  float m = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f.v[j]));  // fmaxf skips NaN
-  return m;
-}
-
-__device__ __forceinline__ uint2 encode8(const F8& f, float inv) {
-  uint2 r;
-  r.x = e4m3x4(f.v[0] * inv, f.v[1] * inv, f.v[2] * inv, f.v[3] * inv);
-  r.y = e4m3x4(f.v[4] * inv, f.v[5] * inv, f.v[6] * inv, f.v[7] * inv);
-  return r;
-}
-
-// Chunks of 8 consecutive elements per thread: kChunks of them, a whole grid apart, all
-// loaded before any is processed (more loads in flight per thread hide the HBM latency);
-// the 16 consecutive lanes of a quarter wave hold one 128-group.
-constexpr int kChunks = 2;
 __global__ __launch_bounds__(256) void quant_group_kernel(const uint4* __restrict__ x,
                                                           int64_t nchunks,
                                                           uint2* __restrict__ q,
                                                           float* __restrict__ scales,
                                                           float* __restrict__ sums) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  uint4 u[kChunks];
-#pragma unroll
-  for (int j = 0; j < kChunks; ++j) {
-    const int64_t i = i0 + j * stride;
-    // nchunks and stride are multiples of 16: groups are all-or-nothing
-    u[j] = i < nchunks ? x[i] : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < kChunks; ++j) {
-    const int64_t i = i0 + j * stride;
-    const F8 f = unpack8(u[j]);
-    const float m = max16(amax8(f));
-    float s, inv;
-    scale_pair(m, s, inv);
-    const uint2 c = encode8(f, inv);
-    // optional: the sum of the group's code values (the grouped GEMM's offset seed)
-    const float gs = sums ? sum16(e4m3_sum8(c.x, c.y)) : 0.f;
-    if (i < nchunks) {
-      q[i] = c;
-      if ((threadIdx.x & 15) == 0) {
-        scales[i >> 4] = s;
-        if (sums) sums[i >> 4] = gs;
-      }
-    }
-  }
+  qg::group_block(x, nchunks, q, scales, sums, blockIdx.x, gridDim.x, threadIdx.x);
 }
 
 __device__ __forceinline__ float block_max(float v, float* red) {

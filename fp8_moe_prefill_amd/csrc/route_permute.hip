@@ -23,6 +23,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "quant_group.h"
 
 namespace fp8moe {
 namespace {
@@ -97,14 +98,15 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
 // picks the k best one at a time: a per-lane best key over the lane's untaken experts,
 // the wave maximum, and the winner's key cleared.
 template <int NJ>  // experts per lane: E <= 64 * NJ
-__global__ __launch_bounds__(kRouteChunk * 64) void topk_hist_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ ids,
-    float* __restrict__ wts, int32_t* __restrict__ cnt) {
-  __shared__ int hist[kMaxE];
+__device__ __forceinline__ void topk_hist_block(const float* __restrict__ logits, int64_t T,
+                                                int E, int k, int32_t* __restrict__ ids,
+                                                float* __restrict__ wts,
+                                                int32_t* __restrict__ cnt, int64_t blk,
+                                                int* hist /* LDS [kMaxE] */) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   for (int e = threadIdx.x; e < E; e += kRouteChunk * 64) hist[e] = 0;
   __syncthreads();
-  const int64_t t = (int64_t)blockIdx.x * kRouteChunk + wv;
+  const int64_t t = blk * kRouteChunk + wv;
   if (t < T) {  // wave-uniform
     // keys of this lane's experts; a taken expert's key becomes 0
     uint64_t key[NJ];
@@ -146,7 +148,42 @@ __global__ __launch_bounds__(kRouteChunk * 64) void topk_hist_kernel(
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kRouteChunk * 64)
-    cnt[(int64_t)blockIdx.x * E + e] = hist[e];
+    cnt[blk * E + e] = hist[e];
+}
+
+
+template <int NJ>
+__global__ __launch_bounds__(kRouteChunk * 64) void topk_hist_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ wts, int32_t* __restrict__ cnt) {
+  __shared__ int hist[kMaxE];
+  topk_hist_block<NJ>(logits, T, E, k, ids, wts, cnt, blockIdx.x, hist);
+}
+
+// The group quantiser and the top-k selection in one launch: they are independent (the
+// activations and the router logits), the top-k is bound by its dependent pick chains and
+// the quantiser by HBM, so the first C workgroups (one chunk of tokens each) pick while
+// the rest quantise, each of those acting as four 256-thread quantiser blocks. While a
+// top-k workgroup holds half of a CU, one quantiser workgroup runs beside it, so its
+// threads keep kQuantRouteChunks chunks in flight (twice the standalone quantiser's).
+// Every output is the one the two separate launches produce.
+constexpr int kQuantRouteChunks = 4;
+template <int NJ>
+__global__ __launch_bounds__(kRouteChunk * 64) void quant_topk_kernel(
+    const uint4* __restrict__ x, int64_t nchunks, uint2* __restrict__ q,
+    float* __restrict__ scales, float* __restrict__ sums, int64_t nqblocks,
+    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ wts, int32_t* __restrict__ cnt, int64_t C) {
+  static_assert(kRouteChunk * 64 == 4 * 256, "one workgroup = four quantiser blocks");
+  __shared__ int hist[kMaxE];
+  const int64_t b = blockIdx.x;
+  if (b < C) {
+    topk_hist_block<NJ>(logits, T, E, k, ids, wts, cnt, b, hist);
+  } else {
+    const int tid = (int)threadIdx.x;
+    qg::group_block<kQuantRouteChunks>(x, nchunks, q, scales, sums, (b - C) * 4 + (tid >> 8),
+                                       nqblocks, tid & 255);
+  }
 }
 
 // One workgroup per expert: exclusive scan of its count over the chunks (in place) and
@@ -279,23 +316,17 @@ size_t route_workspace_bytes(int64_t T, int32_t E) {
   return (n + 255) & ~(size_t)255;
 }
 
-hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
-                                int32_t* ids, float* w, int32_t* offsets, int32_t* sorted,
-                                int32_t* pos, const uint8_t* xq, const float* xs, int64_t H,
-                                uint8_t* xq_perm, float* xs_perm, const float* xsum,
-                                float* xsum_perm, void* ws, hipStream_t st) {
-  int64_t C = (T + kRouteChunk - 1) / kRouteChunk;
+namespace {
+
+// chunk scan, scatter and the optional gathers, after the top-k and histogram launch
+hipError_t launch_route_tail(int64_t T, int32_t E, int32_t k, const int32_t* ids,
+                             int32_t* offsets, int32_t* sorted, int32_t* pos, const uint8_t* xq,
+                             const float* xs, int64_t H, uint8_t* xq_perm, float* xs_perm,
+                             const float* xsum, float* xsum_perm, void* ws, hipStream_t st) {
+  const int64_t C = (T + kRouteChunk - 1) / kRouteChunk;
   int32_t* cnt = static_cast<int32_t*>(ws);
   int32_t* tot = cnt + C * E;
-  const dim3 grid((uint32_t)C), block(kRouteChunk * 64);
-  if (E <= 64)
-    topk_hist_kernel<1><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt);
-  else if (E <= 256)
-    topk_hist_kernel<4><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt);
-  else
-    topk_hist_kernel<16><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   chunk_scan_kernel<<<dim3((uint32_t)E), 256, 0, st>>>(cnt, C, E, tot);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   scatter_kernel<<<dim3((uint32_t)C), 256, 0, st>>>(ids, T, E, k, cnt, tot, offsets, sorted,
@@ -315,6 +346,55 @@ hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32
     e = hipGetLastError();
   }
   return e;
+}
+
+}  // namespace
+
+hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
+                                int32_t* ids, float* w, int32_t* offsets, int32_t* sorted,
+                                int32_t* pos, const uint8_t* xq, const float* xs, int64_t H,
+                                uint8_t* xq_perm, float* xs_perm, const float* xsum,
+                                float* xsum_perm, void* ws, hipStream_t st) {
+  int64_t C = (T + kRouteChunk - 1) / kRouteChunk;
+  int32_t* cnt = static_cast<int32_t*>(ws);
+  const dim3 grid((uint32_t)C), block(kRouteChunk * 64);
+  if (E <= 64)
+    topk_hist_kernel<1><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt);
+  else if (E <= 256)
+    topk_hist_kernel<4><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt);
+  else
+    topk_hist_kernel<16><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_route_tail(T, E, k, ids, offsets, sorted, pos, xq, xs, H, xq_perm, xs_perm,
+                           xsum, xsum_perm, ws, st);
+}
+
+hipError_t launch_quant_route(const uint16_t* x, int64_t H, uint8_t* q, float* scales,
+                              float* sums, const float* logits, int64_t T, int32_t E,
+                              int32_t k, int32_t* ids, float* w, int32_t* offsets,
+                              int32_t* sorted, int32_t* pos, void* ws, hipStream_t st) {
+  const int64_t C = (T + kRouteChunk - 1) / kRouteChunk;
+  const int64_t nchunks = T * H / 8;
+  // quantiser workgroups of four 256-thread blocks, each thread kQuantRouteChunks chunks
+  const int64_t nq = (nchunks + 4 * 256 * kQuantRouteChunks - 1) / (4 * 256 * kQuantRouteChunks);
+  int32_t* cnt = static_cast<int32_t*>(ws);
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint2* qv = reinterpret_cast<uint2*>(q);
+  const dim3 grid((uint32_t)(C + nq)), block(kRouteChunk * 64);
+  if (E <= 64)
+    quant_topk_kernel<1><<<grid, block, 0, st>>>(xv, nchunks, qv, scales, sums, 4 * nq, logits,
+                                                  T, E, k, ids, w, cnt, C);
+  else if (E <= 256)
+    quant_topk_kernel<4><<<grid, block, 0, st>>>(xv, nchunks, qv, scales, sums, 4 * nq, logits,
+                                                  T, E, k, ids, w, cnt, C);
+  else
+    quant_topk_kernel<16><<<grid, block, 0, st>>>(xv, nchunks, qv, scales, sums, 4 * nq,
+                                                   logits, T, E, k, ids, w, cnt, C);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_route_tail(T, E, k, ids, offsets, sorted, pos, nullptr, nullptr, H, nullptr,
+                           nullptr, nullptr, nullptr, ws, st);
 }
 
 }  // namespace fp8moe

@@ -73,8 +73,8 @@ def moe_layer(x: torch.Tensor, logits: torch.Tensor, bank: ExpertBank, k: int,
     R = T * k
     # gate|up gathers its rows from token order through `sorted`, and with them each row's
     # per-token scales (and code sums) straight from the quantiser's output
-    rt = _lib.moe_route_permute(logits, k, stream=stream)
     if bank.act == "mxfp4":  # MXFP4 activations into gate|up (bank packed for them)
+        rt = _lib.moe_route_permute(logits, k, stream=stream)
         xq, xs = _lib.mxfp4_quant_act(x, stream=stream)
         xsum = None
         hq, hs, hsum = _lib.mxfp4_grouped_expert_gemm(
@@ -83,8 +83,9 @@ def moe_layer(x: torch.Tensor, logits: torch.Tensor, bank: ExpertBank, k: int,
             with_sums=True)
     else:
         # the quantiser also emits each (token, 128) group's code sum; the grouped GEMMs
-        # take those in place of forming them from the tiles
-        xq, xs, xsum = _lib.fp8_quant_act(x, _lib.GROUP, stream=stream, with_sums=True)
+        # take those in place of forming them from the tiles. Quantiser and routing in one
+        # call (the quantiser beside the top-k)
+        xq, xs, xsum, rt = _lib.quant_route(x, logits, k, stream=stream)
         hq, hs, hsum = _lib.fp8_grouped_expert_gemm(
             xq, xs, bank.w_gu, bank.s_gu, rt["offsets"], R, _lib.EPI_SWIGLU_QUANT,
             sorted_=rt["sorted"], k_route=k, stream=stream, a_sums=xsum, with_sums=True)
@@ -115,15 +116,21 @@ class MoELayerRunner:
     timing): call ``run(x, logits, bank)`` repeatedly; outputs are overwritten in place.
 
     Every launch goes to one stream (``stream``, else the current one). The optional
-    ``events`` dict of (start, end) torch.cuda.Event pairs, keyed by stage name, is
-    recorded around the corresponding launches on that stream."""
+    ``events`` dict of (start, end) torch.cuda.Event pairs, keyed by stage name (see
+    ``STAGES``), is recorded around the corresponding launches on that stream.
 
-    STAGES = ("quant", "route", "gate_up", "down", "combine")
+    With e4m3 activations the quantiser and the routing go through one call
+    (``fp8moe_quant_route``: the quantiser and the top-k share a launch; stage
+    "quant_route") unless ``fuse_quant_route`` is False; the outputs are the same bytes."""
 
-    def __init__(self, T: int, H: int, E: int, k: int, I: int, device, act: str = "e4m3"):
+    def __init__(self, T: int, H: int, E: int, k: int, I: int, device, act: str = "e4m3",
+                 fuse_quant_route: bool = True):
         R = T * k
         self.T, self.H, self.E, self.k, self.I, self.R = T, H, E, k, I, R
         self.act = act
+        self.fused = fuse_quant_route and act != "mxfp4"
+        self.STAGES = (("quant_route",) if self.fused else ("quant", "route")) + (
+            "gate_up", "down", "combine")
         dev = torch.device(device)
         u8, f32, i32 = torch.uint8, torch.float32, torch.int32
         if act == "mxfp4":  # codes [T, H/2]; E8M0 bytes [T, H/32] = [T, H/128] words
@@ -158,16 +165,22 @@ class MoELayerRunner:
         mx = self.act == "mxfp4"
         if bank.act != self.act:
             raise ValueError(f"bank packed for {bank.act} activations, runner for {self.act}")
-        mark("quant", 0)
-        if mx:
-            _lib.mxfp4_quant_act(x, q=self.xq, scales=self.xs, stream=stream)
+        if self.fused:
+            mark("quant_route", 0)
+            _lib.quant_route(x, logits, self.k, q=self.xq, scales=self.xs, sums=self.xsum,
+                             out=rt, ws=self.ws, stream=stream)
+            mark("quant_route", 1)
         else:
-            _lib.fp8_quant_act(x, _lib.GROUP, q=self.xq, scales=self.xs, sums=self.xsum,
-                               stream=stream)
-        mark("quant", 1)
-        mark("route", 0)
-        _lib.moe_route_permute(logits, self.k, out=rt, ws=self.ws, stream=stream)
-        mark("route", 1)
+            mark("quant", 0)
+            if mx:
+                _lib.mxfp4_quant_act(x, q=self.xq, scales=self.xs, stream=stream)
+            else:
+                _lib.fp8_quant_act(x, _lib.GROUP, q=self.xq, scales=self.xs, sums=self.xsum,
+                                   stream=stream)
+            mark("quant", 1)
+            mark("route", 0)
+            _lib.moe_route_permute(logits, self.k, out=rt, ws=self.ws, stream=stream)
+            mark("route", 1)
         mark("gate_up", 0)
         self.run_gate_up(bank, stream=stream)
         mark("gate_up", 1)

@@ -13,6 +13,8 @@
  *                            accumulator; optional fused SwiGLU + e4m3 requantisation
  *   fp8_dense_gemm           W8A8 GEMM with per-tensor activation and weight scales
  *   moe_unpermute_combine    weighted sum of each token's k expert rows
+ *   fp8moe_quant_route       fp8_quant_act (group mode) and moe_route_permute of one
+ *                            layer in one call (the quantiser beside the top-k)
  *
  * quantisation variants of those ([P2] "Limits"; [P4] the block-128 e4m3 class):
  *
@@ -173,6 +175,31 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
                           int32_t* pos, const uint8_t* xq, const float* xs, int64_t H,
                           uint8_t* xq_perm, float* xs_perm, const float* xsum,
                           float* xsum_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fp8moe_quant_route -- fp8_quant_act in group mode (FP8MOE_GROUP, optional code sums)
+ * of the layer's activations and moe_route_permute (no gathers) of its router logits in
+ * one call.
+ *
+ * [P1] section 1 runs the activation quantiser and the routing/grouping ahead of the one
+ * grouped GEMM per layer. The two read different inputs, so the library runs the
+ * quantiser and the top-k selection in one launch (the top-k waits on dependent picks,
+ * the quantiser on HBM) and then the rest of the routing.
+ *
+ *   x, q, scales, sums   as fp8_quant_act with M = T, K = H, group = FP8MOE_GROUP
+ *                        (sums may be NULL)
+ *   logits .. pos        as moe_route_permute (no gathers: its xq/xs pairs are absent)
+ *   ws                   workspace of fp8moe_workspace_bytes(FP8MOE_OP_ROUTE_PERMUTE, T,
+ *                        E, k) bytes (the group quantiser needs none)
+ * Every output is the one the two separate calls write, byte for byte.
+ * Constraints: those of both calls: T >= 1, H >= 128, H % 128 == 0, T*H < 2^40,
+ * 1 <= E <= 1024, 1 <= k <= min(E, 32), T*k < 2^31. x, q, scales, sums and ws 16-byte
+ * aligned.
+ */
+int32_t fp8moe_quant_route(const void* x, int64_t T, int64_t H, uint8_t* q, float* scales,
+                           float* sums, const float* logits, int32_t E, int32_t k,
+                           int32_t* ids, float* weights, int32_t* offsets, int32_t* sorted,
+                           int32_t* pos, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_route_permute_noalloc -- moe_route_permute without a workspace argument, for

@@ -42,7 +42,7 @@ def test_header_declares_the_five_entry_points():
     for name in ["fp8moe_rmsnorm", "fp8moe_bf16_gemm", "fp8moe_causal_attention",
                  "fp8_dense_gemm_rowwise", "fp8_block_gemm", "fp8_quant_weight_block128",
                  "mxfp4_quant_act", "fp8moe_pack_expert_bank_mxfp4", "mxfp4_grouped_expert_gemm",
-                 "moe_route_permute_noalloc"]:
+                 "moe_route_permute_noalloc", "fp8moe_quant_route"]:
         assert name in fns
 
 
@@ -50,7 +50,7 @@ def test_every_declared_symbol_is_exported(lib):
     raw = ctypes.CDLL(LIB)
     for name in declared_functions():
         assert hasattr(raw, name), name
-    assert lib.fp8moe_abi_version() == 8
+    assert lib.fp8moe_abi_version() == 9
 
 
 def test_status_strings(lib):
@@ -143,6 +143,30 @@ def test_route_noalloc_validation(lib):
     # past the 4 MiB static workspace: 2^20 tokens x 64 experts need 16 MiB of counts
     assert lib.fp8moe_workspace_bytes(1, 1 << 20, 64, 8) > 4 << 20
     assert _route_na(lib, T=1 << 20, E=64, k=8) == WS
+
+
+def _qr(lib, x=P, T=64, H=256, q=P, scales=P, sums=P, logits=P, E=8, k=2, ids=P, ws=P,
+        ws_bytes=1 << 20):
+    return lib.fp8moe_quant_route(x, T, H, q, scales, sums, logits, E, k, ids, P, P, P, P, ws,
+                                  ws_bytes, None)
+
+
+def test_quant_route_validation(lib):
+    # the checks of fp8_quant_act (group mode) and of moe_route_permute, on the host
+    for kw in ("x", "q", "scales", "logits", "ids", "ws"):
+        assert _qr(lib, **{kw: None}) == NULL, kw
+    assert _qr(lib, sums=None, ws_bytes=16) == WS  # sums are optional
+    assert _qr(lib, T=0) == SHAPE
+    assert _qr(lib, H=100) == SHAPE
+    assert _qr(lib, H=64) == SHAPE
+    assert _qr(lib, T=1 << 40, H=128) == SHAPE  # T*H >= 2^40
+    assert _qr(lib, E=0) == SHAPE
+    assert _qr(lib, E=4, k=5) == SHAPE
+    assert _qr(lib, E=1025, k=2) == SHAPE
+    assert _qr(lib, T=1 << 28, H=128, k=8) == SHAPE  # T*k >= 2^31
+    for kw in ("x", "q", "scales", "sums", "ids", "ws"):
+        assert _qr(lib, **{kw: U}) == ALIGN, kw
+    assert _qr(lib, ws_bytes=16) == WS
 
 
 def _gg(lib, a=P, R=256, E=8, N=512, K=256, epi=0, dt=0, out_scales=P, sorted_=None, kr=1,

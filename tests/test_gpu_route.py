@@ -117,3 +117,33 @@ def test_code_sum_gather():
                        "xs_perm")
     assert_bytes_equal(host(r["xsum_perm"]),
                        np.ascontiguousarray(permute_rows(xsum, sorted_, c.k).T), "xsum_perm")
+
+
+@pytest.mark.parametrize("T,H,E,k,with_sums", [(4096, 2048, 64, 8, True), (77, 256, 64, 8, True),
+                                               (1, 128, 8, 2, True), (300, 384, 128, 8, False),
+                                               (130, 512, 1024, 32, True), (2000, 1024, 256, 4,
+                                                                            True)])
+def test_quant_route_equals_the_two_calls(T, H, E, k, with_sums):
+    """fp8moe_quant_route (the group quantiser and the top-k in one launch) writes the
+    same bytes as fp8_quant_act(group 128) followed by moe_route_permute, for every
+    output; the routing is also checked against the oracle. Expert counts 64, 128-256 and
+    1024 take the three top-k kernels; ragged T leaves a partial chunk."""
+    import fp8_moe_prefill_amd as f
+    from synth import bf16_bits_from_f32
+    rng = np.random.default_rng(T + 7 * H + E)
+    x = bf16_bits_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    xd, ld = dev(x), dev(logits)
+    q, s, sums, r = f.quant_route(xd, ld, k, with_sums=with_sums)
+    ref = f.fp8_quant_act(xd, f.GROUP, with_sums=with_sums)
+    rr = f.moe_route_permute(ld, k)
+    torch.cuda.synchronize()
+    assert_bytes_equal(host(q), host(ref[0]), "codes")
+    assert_bytes_equal(host(s), host(ref[1]), "scales")
+    if with_sums:
+        assert_bytes_equal(host(sums), host(ref[2]), "code sums")
+    else:
+        assert sums is None
+    for name in ("ids", "weights", "offsets", "sorted", "pos"):
+        assert_bytes_equal(host(r[name]), host(rr[name]), name)
+    _check(logits, k, {n: host(t) for n, t in r.items()})
