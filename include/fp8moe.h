@@ -36,8 +36,9 @@
  *        (octopusresearch.org), section 1 Contribution.
  *   [P2] FreeToken PR #389 "load-time per-tensor FP8 dense projections (W8A8 via
  *        _scaled_mm)", sections "What this adds" and "Limits".
- *   [P3] DeepGEMM issue 338 "FP4 activations for fp8_fp4_mega_moe" (E2M1 activations to
- *        halve the dispatch buffer and run an MXF4 main loop).
+ *   [P3] DeepGEMM issue 338 (mirrored as #166), "[RFC] Support FP4 (E2M1) activation
+ *        dispatch in MegaMoE", body (E2M1 activations to halve the dispatch buffer and run
+ *        an MXF4 main loop).
  *   [P4] memra-engine fp8_ffi module docs (docs.rs), module text and struct Fp8Scratch.
  *   [P1] section 3 also names the depth stacks (L = 8 and 12) the note measures.
  *
