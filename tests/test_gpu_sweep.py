@@ -227,3 +227,48 @@ def test_causal_attention_sweep(seed):
     T = int(rng.integers(1, 301))
     std = float(rng.choice([0.5, 3.0]))
     test_attention_bound(T, n_q, n_kv, std)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_big_tile_gemm_sweep(seed):
+    """The 256 x 256 TN tiling (taken when it gives every CU two tiles) on seeded ragged
+    shapes, e4m3 per-tensor and bf16 in turn: sampled outputs within the GEMM bound, the
+    last row and column included, and the first rows equal bit for bit to the same product
+    over only those rows (which takes the 128 x 128 tiling)."""
+    import fp8_moe_prefill_amd as f
+    from oracle.dense import dense_w8a8_entries
+    from synth import bf16_bits_from_f32
+    from tests.gpu_util import assert_bytes_equal
+    rng = np.random.default_rng(6000 + seed)
+    bf16 = seed % 2 == 1
+    M = int(rng.integers(2049, 4100))
+    n_min = 256 * -(-512 // ((M + 255) // 256))  # enough 256-column tiles for 512 in all
+    N = n_min + (16 * int(rng.integers(0, 100)) if not bf16 else int(rng.integers(1, 1500)))
+    K = 128 * int(rng.integers(1, 5))
+    assert ((M + 255) // 256) * ((N + 255) // 256) >= 512
+    x = bf16_bits_from_f32(rng.standard_normal((M, K)).astype(np.float32))
+    w = bf16_bits_from_f32((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    m0 = int(rng.integers(1, 300))
+    if bf16:
+        y = host(f.bf16_gemm(dev(x), dev(w)))
+        y0 = host(f.bf16_gemm(dev(x[:m0]), dev(w)))
+    else:
+        wq, sw = f.quantize_weight(dev(w))
+        xq, blk = f.fp8_quant_act(dev(x), 0)
+        y = host(f.fp8_dense_gemm(xq, blk, wq, sw, torch.float32))
+        y0 = host(f.fp8_dense_gemm(xq[:m0].contiguous(), blk, wq, sw, torch.float32))
+    torch.cuda.synchronize()
+    what = f"{'bf16' if bf16 else 'e4m3'} M={M} N={N} K={K}"
+    assert_bytes_equal(y[:m0], y0, f"big vs small tiles ({what})")
+    r = rng.integers(0, M, 2000)
+    c = rng.integers(0, N, 2000)
+    r[:3], c[:3] = [M - 1, M - 1, 0], [N - 1, 0, N - 1]
+    if bf16:
+        from oracle.codec import bf16_to_f32
+        A = bf16_to_f32(x[r]).astype(np.float64)
+        W = bf16_to_f32(w[c]).astype(np.float64)
+        ref = np.einsum("ik,ik->i", A, W)
+        b = np.einsum("ik,ik->i", np.abs(A), np.abs(W))
+    else:
+        ref, b = dense_w8a8_entries(host(xq), host(blk)[2], host(wq), host(sw)[0], r, c)
+    check_close(y[r, c].astype(np.float64), ref, gemm_bound(b), what)
