@@ -79,7 +79,8 @@ def _ulp_tol(ref, gpu):
 # ------------------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("T,H", [(1, 8), (37, 264), (300, 2048), (6, 4104), (3, 8200)])
+@pytest.mark.parametrize("T,H", [(1, 8), (37, 264), (65, 520), (300, 2048), (33, 2056),
+                                 (5, 4096), (6, 4104), (3, 8200)])
 def test_rmsnorm_bit_exact(T, H):
     import fp8_moe_prefill_amd as f
     rng = np.random.default_rng(T * 1000 + H)
