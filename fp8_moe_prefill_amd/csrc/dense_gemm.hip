@@ -7,7 +7,8 @@
 // gfx950 design: with per-tensor scales the fp32 accumulator chains through the whole K
 // loop inside the MFMA (no per-group fold), and the scalar s_a * s_w is read from device
 // memory and applied once in the epilogue. For M > 16 the GEMM is the shared TN kernel
-// (tn_gemm.h: 128 x 128 tiles, operands DMA'd into LDS); decode shapes (M <= 16) take the
+// (tn_gemm.h: 128 x 128 tiles, or 128 x 192 / 256 x 256 where the shape fills the CUs with
+// them; operands DMA'd into LDS); decode shapes (M <= 16) take the
 // weight-streaming kernel below (memra-engine fp8_ffi module text draws the same line
 // between prefill, m >= 16, and decode).
 //
@@ -143,6 +144,13 @@ hipError_t launch_dense(const uint8_t* a, const float* a_s, const uint8_t* w,
                                                               st);
       return tn::launch<false, false, 2, false, false, true>(a, w, M, N, K, a_s, w_scale, out,
                                                              st);
+    }
+  }
+  if constexpr (!BLOCK) {
+    if (tn::use_wide_tiles(M, N)) {
+      if (out_dtype == FP8MOE_DTYPE_BF16)
+        return tn::launch_wide<true, ROW_SCALE>(a, w, M, N, K, a_s, w_scale, out, st);
+      return tn::launch_wide<false, ROW_SCALE>(a, w, M, N, K, a_s, w_scale, out, st);
     }
   }
   if (out_dtype == FP8MOE_DTYPE_BF16)

@@ -11,7 +11,7 @@
 //   1 KB of operands and the workgroup's DMA writes 0.5 KB, as much LDS time as the CU's
 //   matrix cores spend; the 128 x 64 wave tile of BIG reads 0.75 KB and its 256 x 256
 //   workgroup tile writes 0.25 KB per MFMA. BIG needs many tiles to fill the CUs, so the
-//   launch picks it by shape.
+//   launch picks it by shape; so it does the 128 x 192 tiling (WIDE, below).
 // * Both operands go straight from global memory into LDS (LDS DMA, no VGPR staging, no
 //   LDS writes by the waves), each DMA instruction copying 8 whole 128-byte lines (8 rows
 //   of one K step) into 1 KB of LDS; the 16-byte chunks of a row are XOR-swizzled so that
@@ -295,6 +295,173 @@ __global__ __launch_bounds__(BIG ? 512 : 256, BIG ? 1 : 2) void tn_gemm_kernel(c
     }
 }
 
+// WIDE: 128 x 192 workgroup tile for e4m3 operands, 4 waves in a 2 x 2 grid of 64 x 96
+// (4 x 6 MFMA tiles each, 96 accumulators per lane), two workgroups per CU (2 x 80 KB of
+// LDS). Per MFMA a 64 x 96 wave tile reads 0.83 KB of operands from LDS (1 KB for 64 x 64)
+// and the workgroup's DMA writes 0.42 KB (0.5 KB). Used where 128 x 192 tiles fill the
+// two workgroup slots of every CU in one round and 128 x 128 tiles would need a second,
+// partly empty one (the 2048 x 4096 x 6144 q/k/v projection: 512 against 768 tiles).
+// Every output is the same chain of K-step MFMAs as in the 128 x 128 kernel.
+// W's LDS row rho holds tile column col_of_wide(rho): wave wn's column tile s, lane c reads
+// row 96 wn + 16 s + c, which is column 96 wn + 4 c + s for s < 4 (each lane: four
+// consecutive columns) and 96 wn + 64 + 2 c + (s - 4) for s = 4, 5 (two more).
+__device__ __forceinline__ int col_of_wide(int rho) {
+  const int wn = rho / 96, r = rho - 96 * wn, s = r >> 4, c = r & 15;
+  return 96 * wn + (s < 4 ? 4 * c + s : 64 + 2 * c + (s - 4));
+}
+
+template <bool OUT_BF16, bool ROW_SCALE>
+__global__ __launch_bounds__(256, 2) void tn_gemm_wide_kernel(const uint8_t* __restrict__ A,
+                                                              const uint8_t* __restrict__ W,
+                                                              int M, int N, int row_bytes,
+                                                              int NTM, int NTN,
+                                                              const float* __restrict__ scale_a,
+                                                              const float* __restrict__ scale_w,
+                                                              void* __restrict__ out) {
+  constexpr int RT = 4, CT = 6;                  // 16-row and 16-column tiles per wave
+  constexpr int TMB = 128, TNB = 192;            // workgroup tile
+  constexpr int NA = TMB / 8, NB = TNB / 8;      // DMA blocks of A and of W per step
+  constexpr int PER = (NA + NB) / 4;             // DMA instructions per wave and step
+  static_assert((NA + NB) % 4 == 0, "DMA blocks split evenly over the 4 waves");
+  struct Ring {
+    uint8_t a[2][NA * BLK];
+    uint8_t b[2][NB * BLK];
+  };
+  __shared__ __attribute__((aligned(16))) Ring sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int g = lane >> 4, c16 = lane & 15;
+  const int wm = wv >> 1, wn = wv & 1;
+  const uint32_t L = xcd_contiguous(blockIdx.x, gridDim.x);
+  int tm, tn;
+  grouped_tile(L, NTM, NTN, tm, tn);
+  const int m0 = tm * TMB, n0 = tn * TNB;
+  const int KS = row_bytes / KSTEP;
+
+  // DMA duty: the step's NA + NB blocks (8 rows of 128 bytes each) are dealt to the waves
+  // in order, PER per wave: block i < NA is A rows 8 i .. 8 i + 7, the others W rows. Lane
+  // l takes row 8 i + l / 8 (of its operand) and writes LDS position l % 8 of it, holding
+  // the line's 16-byte chunk (l % 8) ^ sw(row). voff[j] is that byte offset at K step 0.
+  uint32_t voff[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = PER * wv + j;
+    const bool is_a = i < NA;
+    const int rho = 8 * (is_a ? i : i - NA) + (lane >> 3);
+    const int row = is_a ? min(m0 + rho, M - 1) : min(n0 + col_of_wide(rho), N - 1);
+    const int chunk = (lane & 7) ^ sw(rho);
+    voff[j] = (uint32_t)row * (uint32_t)row_bytes + 16u * (uint32_t)chunk;
+  }
+  auto issue = [&](int ks) {
+    const int st = ks & 1;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = PER * wv + j;  // wave-uniform
+      if (i < NA) dma16(A, voff[j] + (uint32_t)(ks * KSTEP), sm.a[st] + i * BLK);
+      else dma16(W, voff[j] + (uint32_t)(ks * KSTEP), sm.b[st] + (i - NA) * BLK);
+    }
+  };
+  const int x = sw(c16);
+  const int rd0 = c16 * KSTEP + (((2 * g) ^ x) << 4);
+  const int rd1 = c16 * KSTEP + (((2 * g + 1) ^ x) << 4);
+
+  v4f acc[RT][CT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int s = 0; s < CT; ++s) acc[t][s] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float row_scale[RT][4];
+  if (ROW_SCALE) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        row_scale[t][r] = scale_a[min(m0 + 64 * wm + 16 * t + 4 * g + r, M - 1)];
+  }
+
+  if (KS > 0) issue(0);
+  for (int ks = 0; ks < KS; ++ks) {
+    wait_loads<0>();
+    lds_barrier();  // every wave's loads of step ks landed; the other slot is free
+    if (ks + 1 < KS) issue(ks + 1);
+    const uint8_t* sa = sm.a[ks & 1];
+    const uint8_t* sb = sm.b[ks & 1];
+    v8i aop[RT], bop[CT];
+#pragma unroll
+    for (int s = 0; s < CT; ++s) {
+      const uint4 lo = lds16(sb + (CT * wn + s) * 16 * KSTEP + rd0);
+      const uint4 hi = lds16(sb + (CT * wn + s) * 16 * KSTEP + rd1);
+      bop[s] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const uint4 lo = lds16(sa + (RT * wm + t) * 16 * KSTEP + rd0);
+      const uint4 hi = lds16(sa + (RT * wm + t) * 16 * KSTEP + rd1);
+      aop[t] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int s = 0; s < CT; ++s)
+        acc[t][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop[t], bop[s], acc[t][s],
+                                                                     0, 0, 0, 0, 0, 0);
+  }
+
+  const float sw0 = scale_w[0];
+  const float tensor_scale = ROW_SCALE ? sw0 : scale_a[2] * sw0;
+  const int c0 = n0 + 96 * wn + 4 * c16;       // tiles 0..3: four consecutive columns
+  const int c1 = n0 + 96 * wn + 64 + 2 * c16;  // tiles 4, 5: two consecutive columns
+  const bool vec0 = (c0 + 3 < N) && ((N & 3) == 0);
+  const bool vec1 = (c1 + 1 < N) && ((N & 1) == 0);
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + 64 * wm + 16 * t + 4 * g + r;
+      if (row >= M) continue;
+      const float scale = ROW_SCALE ? row_scale[t][r] * sw0 : tensor_scale;
+      float v[CT];
+#pragma unroll
+      for (int s = 0; s < CT; ++s) v[s] = acc[t][s][r] * scale;
+      const int64_t o0 = (int64_t)row * N + c0, o1 = (int64_t)row * N + c1;
+      if (OUT_BF16) {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(out);
+        if (vec0) {
+          *reinterpret_cast<uint2*>(dst + o0) = make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            if (c0 + s < N) dst[o0 + s] = (uint16_t)f32_to_bf16(v[s]);
+        }
+        if (vec1) {
+          *reinterpret_cast<uint32_t*>(dst + o1) = bf16x2(v[4], v[5]);
+        } else {
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            if (c1 + s < N) dst[o1 + s] = (uint16_t)f32_to_bf16(v[4 + s]);
+        }
+      } else {
+        float* dst = reinterpret_cast<float*>(out);
+        if (vec0) {
+          *reinterpret_cast<float4*>(dst + o0) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            if (c0 + s < N) dst[o0 + s] = v[s];
+        }
+        if (vec1) {
+          *reinterpret_cast<float2*>(dst + o1) = make_float2(v[4], v[5]);
+        } else {
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            if (c1 + s < N) dst[o1 + s] = v[4 + s];
+        }
+      }
+    }
+}
+
 // Compute units of the current device (queried once per device).
 inline int device_cus() {
   static int cached[64];
@@ -315,6 +482,22 @@ inline int device_cus() {
 // output over the same K steps in the same order, so the choice never changes a result.
 inline bool use_big_tiles(int64_t M, int64_t N) {
   return ((M + 255) / 256) * ((N + 255) / 256) >= 2 * (int64_t)device_cus();
+}
+
+// WIDE tiles (128 x 192) when they fit the two workgroup slots of every CU in one round
+// and 128 x 128 tiles would not. By shape only, like BIG: the results are the same.
+inline bool use_wide_tiles(int64_t M, int64_t N) {
+  const int64_t slots = 2 * (int64_t)device_cus(), mt = (M + 127) / 128;
+  return mt * ((N + 191) / 192) <= slots && mt * ((N + 127) / 128) > slots;
+}
+
+template <bool OUT_BF16, bool ROW_SCALE>
+hipError_t launch_wide(const uint8_t* a, const uint8_t* w, int64_t M, int64_t N, int64_t row_bytes,
+                       const float* scale_a, const float* scale_w, void* out, hipStream_t st) {
+  const int NTM = (int)((M + 127) / 128), NTN = (int)((N + 191) / 192);
+  tn_gemm_wide_kernel<OUT_BF16, ROW_SCALE><<<dim3((uint32_t)(NTM * NTN)), 256, 0, st>>>(
+      a, w, (int)M, (int)N, (int)row_bytes, NTM, NTN, scale_a, scale_w, out);
+  return hipGetLastError();
 }
 
 // Enqueue the kernel over ceil(M/128) x ceil(N/128) tiles (BIG: 256 x 256); row_bytes =

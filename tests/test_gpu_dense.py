@@ -220,3 +220,42 @@ def test_big_tiles_sampled_and_equal_to_small_tiles():
     rows[:3], cols[:3] = [M - 1, M - 1, 0], [N - 1, 0, N - 1]
     ref, b = dense_w8a8_entries(host(xq), host(blk)[2], host(wq), host(sw)[0], rows, cols)
     check_close(y[rows, cols].astype(np.float64), ref, gemm_bound(b), "dense big tiles")
+
+
+@pytest.mark.parametrize("rowwise", [False, True])
+def test_wide_tiles_sampled_and_equal_to_small_tiles(rowwise):
+    """1000 x 12176 x 256: 128 x 192 tiles fill the two workgroup slots of every CU in one
+    round where 128 x 128 tiles would not, so the wide tiling runs (ragged in M and N: the
+    last column tile holds 80 columns). Its first 640 rows must equal, bit for bit, the
+    product over only those rows (128 x 128 tiles); bf16 output must be the rounded fp32
+    output; sampled entries with the last row and column against the oracle."""
+    import fp8_moe_prefill_amd as f
+    rng = np.random.default_rng(31 + rowwise)
+    M, N, K = 1000, 12176, 256
+    x = bf16_bits_from_f32(rng.standard_normal((M, K)).astype(np.float32))
+    w = bf16_bits_from_f32((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    wq, sw = f.quantize_weight(dev(w))
+    if rowwise:
+        xq, sa = f.fp8_quant_act(dev(x), f.QUANT_ROW)
+        gemm = lambda a, s, dt: f.fp8_dense_gemm_rowwise(a, s, wq, sw, dt)
+        y = gemm(xq, sa, torch.float32)
+        y_small = gemm(xq[:640].contiguous(), sa[:640].contiguous(), torch.float32)
+        y16 = gemm(xq, sa, torch.bfloat16)
+    else:
+        xq, sa = f.fp8_quant_act(dev(x), 0)
+        gemm = lambda a, dt: f.fp8_dense_gemm(a, sa, wq, sw, dt)
+        y = gemm(xq, torch.float32)
+        y_small = gemm(xq[:640].contiguous(), torch.float32)
+        y16 = gemm(xq, torch.bfloat16)
+    torch.cuda.synchronize()
+    y, y_small, y16 = host(y), host(y_small), host(y16)
+    assert_bytes_equal(y[:640], y_small, "wide tiles vs small tiles")
+    assert_bytes_equal(y16, bf16_bits(round_bf16(y.astype(np.float64))), "bf16 = RNE(fp32)")
+    rows = rng.integers(0, M, 3000)
+    cols = rng.integers(0, N, 3000)
+    rows[:4], cols[:4] = [M - 1, M - 1, 0, 639], [N - 1, 0, N - 1, N - 80]
+    if rowwise:
+        ref, b = dense_w8a8_rowwise_entries(host(xq), host(sa), host(wq), host(sw)[0], rows, cols)
+    else:
+        ref, b = dense_w8a8_entries(host(xq), host(sa)[2], host(wq), host(sw)[0], rows, cols)
+    check_close(y[rows, cols].astype(np.float64), ref, gemm_bound(b), "dense wide tiles")
