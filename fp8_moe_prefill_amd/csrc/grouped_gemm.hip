@@ -762,6 +762,297 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
   for (int j = j_tiny; j < my_tiles; ++j) unit(j, std::integral_constant<int, 1>{});
 }
 
+// ---- Few rows per expert (decode-sized batches) ----
+// When the routed rows average only a few per expert, nearly every tile of the kernel above
+// is a single 16-row MFMA tile whose K groups are waited for one at a time: the kernel then
+// runs at the latency of one group's loads per group, not at HBM speed. This variant cuts
+// each expert's rows into units of 16 (one MFMA row tile) x 256 accumulator columns and
+// keeps three K groups of a unit in flight through a four-deep ring of compact stages (the
+// 16 A rows, the waves' packed B slices, the scales). Every output is formed by the same
+// MFMAs, seeds and fold, in the same order, as in the kernel above.
+constexpr int R16 = 16;        // rows per unit
+constexpr int kRows16PerExpert = 4;  // used when R <= 4 E
+constexpr int kRing16 = 4;     // stages in flight
+struct __attribute__((aligned(16))) Stage16 {
+  uint8_t a[R16 * kGroup];     // 16 rows, chunks swizzled as in the big tile (a_off)
+  uint8_t b[NW * BW_BYTES];    // each wave's packed B slice
+  float ws[WCOLS_WG];          // weight scales of the 256 columns (as staged by ws_col)
+  float as[R16];               // activation scales of the 16 rows
+  float ra[R16];               // row-sum seeds (given code sums, scaled in place)
+};
+
+template <int EPI, bool OUT_BF16, bool SUMS>
+__global__ __launch_bounds__(NT_THREADS, 2) void grouped_rows16_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ As, const float* __restrict__ Asum,
+    const int32_t* __restrict__ sorted, int k_route, int a_rows, const uint8_t* __restrict__ W,
+    const float* __restrict__ Ws, const int32_t* __restrict__ offsets, int R, int E, int N,
+    int K, int NT, void* __restrict__ out, float* __restrict__ out_scales,
+    float* __restrict__ out_sums) {
+  __shared__ Stage16 ring[kRing16];
+  __shared__ int s_tmp[NW];
+  __shared__ float s_amax[NW * R16];
+  __shared__ float s_inv[R16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[R16 * 128];
+  extern __shared__ int s_ustart[];  // [E + 1]: units of 16 rows before expert e
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, c16 = lane & 15;
+  const int G = K / kGroup;
+  const int I = N / 2;
+  const int NB = N / 16;
+  const int NG = N / 64;
+  const int kshift = (k_route & (k_route - 1)) == 0 ? __builtin_ctz(k_route) : -1;
+
+  {  // units per expert, ceil(count / 16), and their exclusive scan (4 experts per thread)
+    constexpr int EPT = kMaxExperts / NT_THREADS;
+    int nu[EPT], sum = 0;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid * EPT + j;
+      nu[j] = e < E ? (offsets[e + 1] - offsets[e] + R16 - 1) / R16 : 0;
+      sum += nu[j];
+    }
+    int run = block_inclusive_scan(sum, s_tmp) - sum;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid * EPT + j;
+      if (e < E) s_ustart[e] = run;
+      run += nu[j];
+      if (e == E - 1) s_ustart[E] = run;
+    }
+    __syncthreads();
+  }
+  // units (16-row chunk, n-tile), n-tile fastest, dealt to the XCDs in contiguous ranges;
+  // the workgroups of XCD x take every nwg_x-th unit of its range
+  const int n_units = __builtin_amdgcn_readfirstlane(s_ustart[E]) * NT;
+  const int nx = min(8, (int)gridDim.x);
+  const int x = (int)blockIdx.x % nx, u = (int)blockIdx.x / nx;
+  const int nwg_x = ((int)gridDim.x - x + nx - 1) / nx;
+  const int ub_x = n_units * x / nx, nu_x = n_units * (x + 1) / nx - ub_x;
+
+  auto tile_block = [&](int nt, int s) {  // bank block of MFMA tile s of this wave
+    int b;
+    if (EPI == FP8MOE_EPI_SWIGLU_QUANT)
+      b = 4 * (2 * nt + (wv >> 1) + (s >= 2 ? I / 64 : 0)) + 2 * (wv & 1) + (s & 1);
+    else
+      b = 4 * (4 * nt + wv) + s;
+    return min(b, 4 * NG - 1);
+  };
+  auto ws_col = [&](int nt, int l) {  // weight-scale column staged by lane l of this wave
+    int c;
+    if (EPI == FP8MOE_EPI_SWIGLU_QUANT)
+      c = (l >= 32 ? I : 0) + 64 * (2 * nt + (wv >> 1)) + 4 * ((l & 31) >> 1) + 2 * (wv & 1) +
+          (l & 1);
+    else
+      c = 64 * (4 * nt + wv) + l;
+    return min(c, N - 1);
+  };
+  const v8i ones = {(int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes,
+                    (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes};
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t lane16 = (uint32_t)lane * 16u;
+  constexpr int NPER = SUMS ? 8 : 7;  // loads per wave and K group
+
+  for (int l = u; l < nu_x; l += nwg_x) {
+    const int L = ub_x + l, mt = L / NT, nt = L - mt * NT;
+    int lo = 0, hi = E;  // s_ustart[lo] <= mt < s_ustart[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(s_ustart[mid]) <= mt) lo = mid;
+      else hi = mid;
+    }
+    const int e = lo;
+    const int row_begin =
+        sload(offsets + e) + (mt - __builtin_amdgcn_readfirstlane(s_ustart[e])) * R16;
+    const int rows = min(R16, sload(offsets + e + 1) - row_begin);
+
+    // this wave's bank blocks and weight-scale columns, and their first groups' loads: they
+    // do not depend on the unit's rows, so they go out before the row lookups below
+    const uint32_t ws_off32 = (uint32_t)ws_col(nt, lane) * 4u;
+    uint32_t b_blk[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b_blk[s] = (uint32_t)tile_block(nt, s) * (uint32_t)G * kBlockBytes;
+    const uint8_t* w_exp = W + (int64_t)e * NB * G * kBlockBytes;
+    const float* ws_exp = Ws + (int64_t)e * G * N;
+    auto issue_b = [&](int g) {  // 5 loads
+      Stage16& st = ring[g % kRing16];
+      const uint8_t* bsrc = w_exp + g * kBlockBytes;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        dma16(bsrc + b_blk[s], lane16, st.b + wv * BW_BYTES + s * 1024);
+      dma4(ws_exp + (int64_t)g * N, ws_off32, st.ws + wv * WCOLS);
+    };
+    // every wave is done with the ring (the previous unit's last group) before it refills,
+    // and nothing of the previous unit is still counted against this unit's waits
+    wait_all_loads();
+    lds_barrier();
+#pragma unroll
+    for (int p = 0; p < kRing16 - 1; ++p)
+      if (p < G) issue_b(p);
+
+    // rows 4 wv .. 4 wv + 3 of the unit: A (lanes 0..31, one 16-byte chunk each), the
+    // activation scales and code sums (lanes 0..3)
+    int tok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gr = row_begin + min(4 * wv + i, rows - 1);  // grouped row (uniform)
+      int t;
+      if (sorted) {
+        const int p = sload(sorted + gr);
+        t = kshift >= 0 ? (p >> kshift) : (p / k_route);
+      } else {
+        t = gr;
+      }
+      tok[i] = max(min(t, a_rows - 1), 0);
+    }
+    auto pick = [&](int i) { return i == 0 ? tok[0] : i == 1 ? tok[1] : i == 2 ? tok[2] : tok[3]; };
+    const int ra_i = (lane >> 3) & 3;  // A: lanes 0..31 stage row 4 wv + lane / 8
+    const int rl = 4 * wv + ra_i;
+    const uint32_t a_off32 =
+        (uint32_t)pick(ra_i) * (uint32_t)K + (uint32_t)(((lane & 7) ^ a_swz(rl)) * 16);
+    const int rs_i = lane & 3;         // scales and sums: lanes 0..3 stage row 4 wv + lane
+    const uint32_t as_off32 =
+        sorted ? (uint32_t)pick(rs_i) * (uint32_t)G * 4u
+               : (uint32_t)max(min(row_begin + min(4 * wv + rs_i, rows - 1), R - 1), 0) * 4u;
+    auto issue_a = [&](int g) {  // 2 loads, 3 with the code sums
+      Stage16& st = ring[g % kRing16];
+      if (lane < 32) dma16(A + g * kGroup, a_off32, st.a + wv * 4 * kGroup);
+      const int64_t sg = sorted ? (int64_t)g : (int64_t)g * R;
+      if (lane < 4) dma4(As + sg, as_off32, st.as + 4 * wv);
+      if (SUMS && lane < 4) dma4(Asum + sg, as_off32, st.ra + 4 * wv);
+    };
+#pragma unroll
+    for (int p = 0; p < kRing16 - 1; ++p)
+      if (p < G) issue_a(p);
+    auto issue = [&](int g) {
+      issue_b(g);
+      issue_a(g);
+    };
+
+    float acc[4][4];
+    for (int g = 0; g < G; ++g) {
+      // this group's loads landed; those of at most two later groups stay in flight (the
+      // first group waits for all of the prologue, whose loads went out B first)
+      const int later = g == 0 ? 0 : min(kRing16 - 2, G - 1 - g);
+      if (later >= 2) wait_loads<2 * NPER>();
+      else if (later == 1) wait_loads<NPER>();
+      else wait_loads<0>();
+      Stage16& cur = ring[g % kRing16];
+      if (SUMS && lane < 4) cur.ra[4 * wv + lane] *= -0.015625f;
+      lds_barrier();  // the group is in for every wave; stage (g - 1) % 4 is free
+      if (g + kRing16 - 1 < G) issue(g + kRing16 - 1);
+
+      const uint8_t* tb = cur.b + wv * BW_BYTES;
+      v8i bop[4];
+      float sw[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bop[s] = convert_b(*reinterpret_cast<const uint4*>(&tb[s * 1024 + lane * 16]));
+        const int wi = EPI == FP8MOE_EPI_SWIGLU_QUANT ? (s >= 2 ? 32 : 0) + 2 * c16 + (s & 1)
+                                                      : 4 * c16 + s;
+        sw[s] = cur.ws[wv * WCOLS + wi] * kWeightScaleMul;
+      }
+      const v8i aop = lds_a_operand(cur.a, c16, q);
+      v4f seed;
+      if constexpr (SUMS) {
+        const float4 c4 = *reinterpret_cast<const float4*>(&cur.ra[4 * q]);
+        seed = (v4f){c4.x, c4.y, c4.z, c4.w};
+      } else {
+        const v4f pr =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, ones, zero, 0, 0, 0, 0, 0, 0);
+        seed = (v4f){pr[0] * -0.015625f, pr[1] * -0.015625f, pr[2] * -0.015625f,
+                     pr[3] * -0.015625f};
+      }
+      const float4 a4 = *reinterpret_cast<const float4*>(&cur.as[4 * q]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[s], seed, 0, 0,
+                                                                       0, 0, 0, 0);
+        if (g == 0) {
+          acc[s][0] = p[0] * (a4.x * sw[s]);
+          acc[s][1] = p[1] * (a4.y * sw[s]);
+          acc[s][2] = p[2] * (a4.z * sw[s]);
+          acc[s][3] = p[3] * (a4.w * sw[s]);
+        } else {
+          acc[s][0] = fmaf(p[0], a4.x * sw[s], acc[s][0]);
+          acc[s][1] = fmaf(p[1], a4.y * sw[s], acc[s][1]);
+          acc[s][2] = fmaf(p[2], a4.z * sw[s], acc[s][2]);
+          acc[s][3] = fmaf(p[3], a4.w * sw[s], acc[s][3]);
+        }
+      }
+    }
+
+    // epilogue: output element (s, r) of this lane is row 4 q + r of the unit
+    if (EPI == FP8MOE_EPI_STORE) {
+      const int col0 = nt * WCOLS_WG + wv * WCOLS + 4 * c16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * q + r;
+        if (row < rows && col0 < N) {
+          const int64_t o = (int64_t)(row_begin + row) * N + col0;
+          if (OUT_BF16)
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + o) =
+                make_uint2(bf16x2(acc[0][r], acc[1][r]), bf16x2(acc[2][r], acc[3][r]));
+          else
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o) =
+                make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+        }
+      }
+    } else {
+      // SwiGLU + e4m3 per (row, the unit's 128 h columns), as in the kernel above
+      float m[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        m[r] = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+          const float gt = acc[sp][r], up = acc[sp + 2][r];
+          const float hv = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
+          acc[sp][r] = hv;
+          m[r] = fmaxf(m[r], fabsf(hv));
+        }
+      }
+      const float mr = row4_max16(m, c16);
+      if (c16 < 4) s_amax[wv * R16 + 4 * q + 2 * (c16 & 1) + ((c16 >> 1) & 1)] = mr;
+      lds_barrier();
+      const int hcol = nt * 128;
+      if (tid < R16) {
+        float mx = s_amax[tid];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) mx = fmaxf(mx, s_amax[w * R16 + tid]);
+        float sc, inv;
+        scale_pair(mx, sc, inv);
+        s_inv[tid] = inv;
+        if (tid < rows && hcol < I) out_scales[(int64_t)(hcol / kGroup) * R + row_begin + tid] = sc;
+      }
+      lds_barrier();
+      const int hc = 64 * (wv >> 1) + 4 * c16 + 2 * (wv & 1);  // this lane's h column pair
+      const float4 inv4 = *reinterpret_cast<const float4*>(&s_inv[4 * q]);
+      const float inv[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t c2 = e4m3x2_finite(acc[0][r] * inv[r], acc[1][r] * inv[r]);
+        *reinterpret_cast<uint16_t*>(&s_codes[(4 * q + r) * 128 + hc]) = (uint16_t)c2;
+      }
+      lds_barrier();
+      if (tid < R16 * 8) {  // waves 0 and 1, all lanes: the 8 lanes tid .. tid + 7 share a row
+        const int row = tid >> 3, ch = tid & 7;
+        const uint4 c = *reinterpret_cast<const uint4*>(&s_codes[row * 128 + ch * 16]);
+        uint8_t* o8 = reinterpret_cast<uint8_t*>(out);
+        if (row < rows && hcol < I)
+          *reinterpret_cast<uint4*>(&o8[(int64_t)(row_begin + row) * I + hcol + ch * 16]) = c;
+        if (out_sums) {
+          const float v = sum8(e4m3_sum8(c.x, c.y) + e4m3_sum8(c.z, c.w));
+          if (ch == 0 && row < rows && hcol < I)
+            out_sums[(int64_t)(hcol / kGroup) * R + row_begin + row] = v;
+        }
+      }
+      // the next unit's first barrier orders these LDS reads before s_amax is rewritten
+    }
+  }
+}
+
 int cu_count() {
   static int cached[64];
   int dev = 0;
@@ -791,9 +1082,31 @@ hipError_t launch_grouped(const uint8_t* a, const float* a_scales, const float* 
   const int NT = epilogue == FP8MOE_EPI_SWIGLU_QUANT ? (int)((N / 2 + 127) / 128)
                                                      : (int)((N + WCOLS_WG - 1) / WCOLS_WG);
   if (mtiles * NT >= (int64_t(1) << 28)) return hipErrorInvalidValue;  // 32-bit tile indexing
-  const int64_t grid = std::min<int64_t>(2 * (int64_t)cu_count(), mtiles * NT);
   const int a_rows = (int)(sorted ? R / k_route : R);
-  dim3 g((uint32_t)grid), block(NT_THREADS);
+  dim3 block(NT_THREADS);
+  if constexpr (!AF4) {
+    // a few rows per expert on average (decode-sized batches): 16-row units, deeper ring
+    if (R <= kRows16PerExpert * (int64_t)E) {
+      const int64_t units = ((R + R16 - 1) / R16 + E) * NT;  // bound over all experts
+      dim3 g((uint32_t)std::min<int64_t>(2 * (int64_t)cu_count(), units));
+      const size_t dyn = (size_t)(E + 1) * sizeof(int);
+      if (epilogue == FP8MOE_EPI_SWIGLU_QUANT)
+        grouped_rows16_kernel<FP8MOE_EPI_SWIGLU_QUANT, false, SUMS><<<g, block, dyn, st>>>(
+            a, a_scales, a_sums, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E,
+            (int)N, (int)K, NT, out, out_scales, out_sums);
+      else if (out_dtype == FP8MOE_DTYPE_BF16)
+        grouped_rows16_kernel<FP8MOE_EPI_STORE, true, SUMS><<<g, block, dyn, st>>>(
+            a, a_scales, a_sums, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E,
+            (int)N, (int)K, NT, out, nullptr, nullptr);
+      else
+        grouped_rows16_kernel<FP8MOE_EPI_STORE, false, SUMS><<<g, block, dyn, st>>>(
+            a, a_scales, a_sums, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E,
+            (int)N, (int)K, NT, out, nullptr, nullptr);
+      return hipGetLastError();
+    }
+  }
+  const int64_t grid = std::min<int64_t>(2 * (int64_t)cu_count(), mtiles * NT);
+  dim3 g((uint32_t)grid);
   if (epilogue == FP8MOE_EPI_SWIGLU_QUANT)
     grouped_gemm_kernel<FP8MOE_EPI_SWIGLU_QUANT, false, AF4, SUMS><<<g, block, 0, st>>>(
         a, a_scales, a_sums, sorted, k_route, a_rows, w, w_scales, offsets, (int)R, E, (int)N,

@@ -403,3 +403,70 @@ def test_limits_of_k_and_expert_count(counts, K, N):
     y = host(_gemm(aq, as_, wp, ws, off)).astype(np.float64)
     ref, b = grouped_gemm(aq, as_, wp, ws, off, with_bound=True)
     check_close(y, ref, gemm_bound(b), f"grouped gemm K={K} E={len(counts)}")
+
+
+def _pad_experts(wp, ws, off, pad):
+    """The same problem with `pad` empty experts appended (never read: no rows)."""
+    wp_p = np.concatenate([wp, np.zeros((pad,) + wp.shape[1:], wp.dtype)])
+    ws_p = np.concatenate([ws, np.ones((pad,) + ws.shape[1:], ws.dtype)])
+    off_p = np.concatenate([off, np.full(pad, off[-1], np.int32)])
+    return wp_p, ws_p, off_p
+
+
+def _all_outputs(f, args, a_sums, **kw):
+    y32 = f.fp8_grouped_expert_gemm(*args, f.EPI_STORE, torch.float32, a_sums=a_sums, **kw)
+    y16 = f.fp8_grouped_expert_gemm(*args, f.EPI_STORE, torch.bfloat16, a_sums=a_sums, **kw)
+    hq, hs, hsum = f.fp8_grouped_expert_gemm(*args, f.EPI_SWIGLU_QUANT, a_sums=a_sums,
+                                             with_sums=True, **kw)
+    torch.cuda.synchronize()
+    return [host(t) for t in (y32, y16, hq, hs, hsum)]
+
+
+@pytest.mark.parametrize("sums", [False, True])
+def test_rows16_kernel_equals_tile_kernel(sums):
+    """A few routed rows per expert (R <= 4 E) take the kernel of 16-row units with the
+    deeper load ring; the same problem with its trailing empty experts dropped (R > 4 E)
+    takes the 128-row-tile kernel. Both form every output with the same MFMAs, seeds and
+    fold, so the fp32, bf16 and SwiGLU outputs (codes, scales, code sums) must agree bit for
+    bit; the fp32 output is also checked against the oracle. An expert of 37 rows spans
+    three units, the last ragged."""
+    f = _lib()
+    counts = [5, 37, 1, 0, 16, 2, 17]  # R = 78 > 4 * 7; with 13 empty experts, 78 <= 80
+    K, N = 512, 512
+    aq, as_, wp, ws, off = _problem(counts, K, N, seed=77)
+    R = int(sum(counts))
+    wp_p, ws_p, off_p = _pad_experts(wp, ws, off, 13)
+    a_sums = _sums_gm(aq) if sums else None
+    outs = []
+    for wpx, wsx, offx in ((wp, ws, off), (wp_p, ws_p, off_p)):
+        w, s = _bank(wpx, wsx)
+        outs.append(_all_outputs(f, (dev(aq), _gm(as_), w, s, dev(offx), R), a_sums))
+    for name, a, b in zip(("fp32", "bf16", "codes", "scales", "code sums"), *outs):
+        assert_bytes_equal(a.view(np.uint8), b.view(np.uint8), f"16-row units vs tiles: {name}")
+    ref, bnd = grouped_gemm(aq, as_, wp, ws, off, with_bound=True)
+    check_close(outs[1][0].astype(np.float64), ref, gemm_bound(bnd), "16-row units fp32")
+
+
+def test_rows16_kernel_gather_equals_tile_kernel():
+    """The same comparison with the rows gathered from token order through `sorted` and
+    per-token scales and code sums (the layer's gate|up call): 7 tokens, top-4 of 6 experts
+    (R = 28 > 24), then of the same 6 plus 14 empty ones."""
+    f = _lib()
+    rng = np.random.default_rng(78)
+    T, k, E0, K, N = 7, 4, 6, 384, 256
+    x = (rng.standard_normal((T, K)) * rng.uniform(0.1, 10, (T, 1))).astype(np.float32)
+    xq, xs = quant_group(x)
+    ids = np.stack([rng.permutation(E0)[:k] for _ in range(T)]).astype(np.int32)
+    from oracle.quant import code_sums
+    xsum = code_sums(xq).astype(np.float32)
+    wp = rng.integers(0, 256, size=(E0, N, K // 2), dtype=np.uint8)
+    ws = rng.uniform(0.005, 0.02, size=(E0, N, K // 128)).astype(np.float32)
+    outs = []
+    for E in (E0, E0 + 14):
+        off, sorted_, _ = group_pairs(ids, E)
+        wpx, wsx, _ = _pad_experts(wp, ws, off[:E0 + 1], E - E0)
+        w, s = _bank(wpx, wsx)
+        outs.append(_all_outputs(f, (dev(xq), dev(xs), w, s, dev(off), T * k), dev(xsum),
+                                 sorted_=dev(sorted_), k_route=k))
+    for name, a, b in zip(("fp32", "bf16", "codes", "scales", "code sums"), *outs):
+        assert_bytes_equal(a.view(np.uint8), b.view(np.uint8), f"gather, 16-row units vs tiles: {name}")
