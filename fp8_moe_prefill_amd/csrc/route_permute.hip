@@ -254,6 +254,75 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   }
 }
 
+// Small count tables (C * E <= kScanInScatter, E <= 256): the scan is done by the scatter
+// workgroups themselves, one launch fewer. Workgroup c sums the raw table: every expert's
+// total (for the expert offsets) and its count over the chunks before c (the chunk's base),
+// 256 / E threads per expert over interleaved chunks, then adds the slices in a fixed order.
+// The rows come out identical to the separate scan and scatter (integer sums).
+constexpr int64_t kScanInScatter = 65536;
+__global__ __launch_bounds__(256) void scatter_scan_kernel(const int32_t* __restrict__ ids,
+                                                           int64_t T, int E, int k,
+                                                           const int32_t* __restrict__ cnt,
+                                                           int64_t C,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted,
+                                                           int32_t* __restrict__ pos) {
+  __shared__ int s_off[kMaxE + 1];
+  __shared__ int s_base[256];
+  __shared__ int s_tot[256], s_bef[256];
+  __shared__ int s_e[kRouteChunk * kMaxK];
+  __shared__ int tmp[4];
+  const int64_t c = blockIdx.x;
+  const int t = threadIdx.x;
+  const int S = 256 / E;  // threads per expert
+  {
+    const int e = t % E, sl = t / E;
+    int tot = 0, bef = 0;
+    if (sl < S) {
+#pragma unroll 8
+      for (int64_t cc = sl; cc < C; cc += S) {
+        const int v = cnt[cc * E + e];
+        tot += v;
+        bef += cc < c ? v : 0;
+      }
+    }
+    s_tot[t] = tot;
+    s_bef[t] = bef;
+  }
+  __syncthreads();
+  if (t < E) {
+    int tot = 0, bef = 0;
+    for (int sl = 0; sl < S; ++sl) {
+      tot += s_tot[sl * E + t];
+      bef += s_bef[sl * E + t];
+    }
+    s_base[t] = bef;
+    s_tot[t] = tot;  // slice 0 of expert t is only read by thread t, above
+  }
+  __syncthreads();
+  // expert offsets: exclusive scan of the totals, one expert per thread
+  const int tv = t < E ? s_tot[t] : 0;
+  const int inc = block_inclusive_scan256(tv, tmp);
+  if (t < E) s_off[t] = inc - tv;
+  if (t == 255) s_off[E] = inc;  // = T*k
+  const int64_t p0 = c * kRouteChunk * k;
+  int64_t pend = (c + 1) * kRouteChunk;
+  if (pend > T) pend = T;
+  const int np = (int)(pend * k - p0);
+  for (int i = t; i < np; i += 256) s_e[i] = ids[p0 + i];
+  __syncthreads();
+  if (c == 0)
+    for (int e = t; e <= E; e += 256) offsets[e] = s_off[e];
+  for (int i = t; i < np; i += 256) {
+    const int e = s_e[i];
+    int rank = 0;
+    for (int j = 0; j < i; ++j) rank += (s_e[j] == e);
+    const int row = s_off[e] + s_base[e] + rank;
+    sorted[row] = (int32_t)(p0 + i);
+    pos[p0 + i] = row;
+  }
+}
+
 // Grouped row i <- token sorted[i] / k: its e4m3 row (H bytes), 16 bytes per thread.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const int32_t* __restrict__ sorted,
                                                           int k, int64_t R, int64_t H,
@@ -327,10 +396,15 @@ hipError_t launch_route_tail(int64_t T, int32_t E, int32_t k, const int32_t* ids
   int32_t* cnt = static_cast<int32_t*>(ws);
   int32_t* tot = cnt + C * E;
   hipError_t e;
-  chunk_scan_kernel<<<dim3((uint32_t)E), 256, 0, st>>>(cnt, C, E, tot);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  scatter_kernel<<<dim3((uint32_t)C), 256, 0, st>>>(ids, T, E, k, cnt, tot, offsets, sorted,
-                                                    pos);
+  if (E <= 256 && C * E <= kScanInScatter) {
+    scatter_scan_kernel<<<dim3((uint32_t)C), 256, 0, st>>>(ids, T, E, k, cnt, C, offsets,
+                                                           sorted, pos);
+  } else {
+    chunk_scan_kernel<<<dim3((uint32_t)E), 256, 0, st>>>(cnt, C, E, tot);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    scatter_kernel<<<dim3((uint32_t)C), 256, 0, st>>>(ids, T, E, k, cnt, tot, offsets, sorted,
+                                                      pos);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t R = T * k;
   if (xq != nullptr) {
