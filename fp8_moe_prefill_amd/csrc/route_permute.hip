@@ -9,11 +9,12 @@
 // Design: a stable counting sort with no order-dependent atomics, so every output is a
 // pure function of the logits.
 //   1. topk_hist:  one wave per token selects the top k by (logit desc, expert asc): each
-//                  pick is the wave maximum of a 64-bit key (order-preserving logit bits,
-//                  then the inverted expert index) reduced with DPP only; a workgroup of
-//                  16 waves owns a chunk of 16 tokens and counts its pairs per expert in
-//                  LDS (integer adds commute).
-//   2. chunk_scan: one workgroup per expert scans that expert's per-chunk counts.
+//                  pick is the wave maximum of the order-preserving logit bits (32-bit, DPP
+//                  max steps), then the lowest expert index holding it (a ballot); a
+//                  workgroup of 16 waves owns a chunk of 16 tokens and counts its pairs per
+//                  expert in LDS (integer adds commute).
+//   2. chunk_scan: one workgroup per expert scans that expert's per-chunk counts (for
+//                  small count tables the scatter workgroups do this themselves).
 //   3. scatter:    one workgroup per chunk recomputes the expert offsets (a scan over E),
 //                  ranks each pair among the chunk's earlier pairs of the same expert and
 //                  writes sorted[] and pos[].
@@ -53,50 +54,40 @@ __device__ __forceinline__ int block_inclusive_scan256(int v, int* tmp /*[4]*/) 
   return v + add;
 }
 
-// Orderable 64-bit key of (logit, expert): a larger key is a larger logit, then a lower
-// expert index. The float's bits map to an unsigned order (negatives flipped, -0 taken as
-// +0); -inf keys stay above 0, the key of a taken expert.
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+// Orderable bits of a logit: a larger value is a larger unsigned number (negatives flipped,
+// -0 taken as +0, since they compare equal); -inf stays above 0, the mark of a taken expert.
+__device__ __forceinline__ uint32_t order_bits(float v) {
   uint32_t b = __float_as_uint(v);
-  if ((b << 1) == 0u) b = 0u;  // -0 ranks as +0 (they compare equal)
-  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)o << 32) | (uint32_t)(~e);
+  if ((b << 1) == 0u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-__device__ __forceinline__ float key_value(uint64_t k) {
-  const uint32_t o = (uint32_t)(k >> 32);
+__device__ __forceinline__ float order_value(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
-__device__ __forceinline__ int key_index(uint64_t k) { return (int)~(uint32_t)k; }
 
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max64(uint64_t v) {
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, 0xF, 0xF, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, 0xF, 0xF, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > v ? o : v;
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false));
 }
 
-// Largest key of the wave, as a wave-uniform value: row_shr steps carry each 16-lane
-// row's maximum into its last lane, row_bcast:15 and row_bcast:31 carry them into lane
-// 63; all VALU, no branches.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
-  k = dpp_max64<0x111>(k);  // row_shr:1
-  k = dpp_max64<0x112>(k);  // row_shr:2
-  k = dpp_max64<0x114>(k);  // row_shr:4
-  k = dpp_max64<0x118>(k);  // row_shr:8
-  k = dpp_max64<0x142>(k);  // row_bcast:15
-  k = dpp_max64<0x143>(k);  // row_bcast:31
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+// Largest value of the wave, wave-uniform: row_shr steps carry each 16-lane row's maximum
+// into its last lane, row_bcast:15 and row_bcast:31 carry them into lane 63; VALU only.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max<0x111>(v);  // row_shr:1
+  v = dpp_max<0x112>(v);  // row_shr:2
+  v = dpp_max<0x114>(v);  // row_shr:4
+  v = dpp_max<0x118>(v);  // row_shr:8
+  v = dpp_max<0x142>(v);  // row_bcast:15
+  v = dpp_max<0x143>(v);  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Top-k of each token and the per-chunk expert histogram. A workgroup owns a chunk of
 // kRouteChunk tokens, one wave per token (the k picks of a token are a dependent chain,
 // so the tokens of a chunk run side by side); lane e holds experts e, e+64, ... The wave
-// picks the k best one at a time: a per-lane best key over the lane's untaken experts,
-// the wave maximum, and the winner's key cleared.
+// picks the k best one at a time: the wave maximum of the orderable values of the untaken
+// experts, then, among the experts holding it, the lowest index (a ballot per lane slot,
+// the lowest slot and lane first), whose value is cleared.
 template <int NJ>  // experts per lane: E <= 64 * NJ
 __device__ __forceinline__ void topk_hist_block(const float* __restrict__ logits, int64_t T,
                                                 int E, int k, int32_t* __restrict__ ids,
@@ -108,27 +99,34 @@ __device__ __forceinline__ void topk_hist_block(const float* __restrict__ logits
   __syncthreads();
   const int64_t t = blk * kRouteChunk + wv;
   if (t < T) {  // wave-uniform
-    // keys of this lane's experts; a taken expert's key becomes 0
-    uint64_t key[NJ];
+    // orderable values of this lane's experts; a taken expert's becomes 0
+    uint32_t val[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j;
       float lv = e < E ? logits[t * E + e] : -INFINITY;
       if (lv != lv) lv = -INFINITY;  // NaN ranks as -inf: every pick stays a valid expert
-      key[j] = e < E ? topk_key(lv, e) : 0;
+      val[j] = e < E ? order_bits(lv) : 0u;
     }
     float my_v = -INFINITY, top_v = 0.f;
     int my_i = 0;
     for (int s = 0; s < k; ++s) {
-      uint64_t best = key[0];
+      uint32_t best = val[0];
 #pragma unroll
-      for (int j = 1; j < NJ; ++j) best = key[j] > best ? key[j] : best;
-      const uint64_t w = wave_max_key(best);
-      const int bi = key_index(w);
-      const float bv = key_value(w);
+      for (int j = 1; j < NJ; ++j) best = max(best, val[j]);
+      const uint32_t m = wave_max_u32(best);
+      // the lowest expert index holding m: slot j first (experts 64 j + lane), then lane
+      int bi = 0;
+#pragma unroll
+      for (int j = NJ - 1; j >= 0; --j) {
+        const uint64_t hit = __ballot(val[j] == m);
+        if (hit) bi = 64 * j + (int)__builtin_ctzll(hit);
+      }
+      bi = __builtin_amdgcn_readfirstlane(bi);
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        if (bi == lane + 64 * j) key[j] = 0;
+        if (bi == lane + 64 * j) val[j] = 0u;
+      const float bv = order_value(m);
       if (lane == s) {
         my_v = bv;
         my_i = bi;
