@@ -161,11 +161,11 @@ __global__ __launch_bounds__(kRouteChunk * 64) void topk_hist_kernel(
 // The group quantiser and the top-k selection in one launch: they are independent (the
 // activations and the router logits), the top-k is bound by its dependent pick chains and
 // the quantiser by HBM, so the first C workgroups (one chunk of tokens each) pick while
-// the rest quantise, each of those acting as four 256-thread quantiser blocks. While a
-// top-k workgroup holds half of a CU, one quantiser workgroup runs beside it, so its
-// threads keep kQuantRouteChunks chunks in flight (twice the standalone quantiser's).
-// Every output is the one the two separate launches produce.
-constexpr int kQuantRouteChunks = 4;
+// the rest quantise, each of those acting as four 256-thread quantiser blocks, each
+// thread with kQuantRouteChunks chunks in flight (as many as the standalone quantiser's:
+// with the 32-bit pick, four or eight measured slower). Every output is the one the two
+// separate launches produce.
+constexpr int kQuantRouteChunks = 2;
 template <int NJ>
 __global__ __launch_bounds__(kRouteChunk * 64) void quant_topk_kernel(
     const uint4* __restrict__ x, int64_t nchunks, uint2* __restrict__ q,
