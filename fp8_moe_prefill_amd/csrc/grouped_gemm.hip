@@ -771,7 +771,7 @@ __global__ __launch_bounds__(NT_THREADS, 2) void grouped_gemm_kernel(
 // 16 A rows, the waves' packed B slices, the scales). Every output is formed by the same
 // MFMAs, seeds and fold, in the same order, as in the kernel above.
 constexpr int R16 = 16;        // rows per unit
-constexpr int kRows16PerExpert = 4;  // used when R <= 4 E
+constexpr int kRows16PerExpert = 16;  // used when R <= 16 E (measured crossover: 32 E)
 constexpr int kRing16 = 4;     // stages in flight
 struct __attribute__((aligned(16))) Stage16 {
   uint8_t a[R16 * kGroup];     // 16 rows, chunks swizzled as in the big tile (a_off)

@@ -422,20 +422,24 @@ def _all_outputs(f, args, a_sums, **kw):
     return [host(t) for t in (y32, y16, hq, hs, hsum)]
 
 
+ROWS16_PER_EXPERT = 16  # the launcher takes the 16-row-unit kernel when R <= 16 E
+
+
 @pytest.mark.parametrize("sums", [False, True])
 def test_rows16_kernel_equals_tile_kernel(sums):
-    """A few routed rows per expert (R <= 4 E) take the kernel of 16-row units with the
-    deeper load ring; the same problem with its trailing empty experts dropped (R > 4 E)
-    takes the 128-row-tile kernel. Both form every output with the same MFMAs, seeds and
-    fold, so the fp32, bf16 and SwiGLU outputs (codes, scales, code sums) must agree bit for
-    bit; the fp32 output is also checked against the oracle. An expert of 37 rows spans
-    three units, the last ragged."""
+    """A few routed rows per expert (R <= 16 E) take the kernel of 16-row units; the same
+    problem with its trailing empty experts dropped (R > 16 E) takes the 128-row-tile
+    kernel. Both form every output with the same MFMAs, seeds and fold, so the fp32, bf16
+    and SwiGLU outputs (codes, scales, code sums) must agree bit for bit; the fp32 output is
+    also checked against the oracle. Experts of 37 and 35 rows span three units each, the
+    last ragged."""
     f = _lib()
-    counts = [5, 37, 1, 0, 16, 2, 17]  # R = 78 > 4 * 7; with 13 empty experts, 78 <= 80
+    counts = [5, 37, 1, 35]  # R = 78 > 16 * 4; with one empty expert more, 78 <= 80
     K, N = 512, 512
     aq, as_, wp, ws, off = _problem(counts, K, N, seed=77)
     R = int(sum(counts))
-    wp_p, ws_p, off_p = _pad_experts(wp, ws, off, 13)
+    assert R > ROWS16_PER_EXPERT * len(counts) and R <= ROWS16_PER_EXPERT * (len(counts) + 1)
+    wp_p, ws_p, off_p = _pad_experts(wp, ws, off, 1)
     a_sums = _sums_gm(aq) if sums else None
     outs = []
     for wpx, wsx, offx in ((wp, ws, off), (wp_p, ws_p, off_p)):
@@ -449,11 +453,12 @@ def test_rows16_kernel_equals_tile_kernel(sums):
 
 def test_rows16_kernel_gather_equals_tile_kernel():
     """The same comparison with the rows gathered from token order through `sorted` and
-    per-token scales and code sums (the layer's gate|up call): 7 tokens, top-4 of 6 experts
-    (R = 28 > 24), then of the same 6 plus 14 empty ones."""
+    per-token scales and code sums (the layer's gate|up call): 25 tokens, top-4 of 6
+    experts (R = 100 > 96), then of the same 6 plus one empty expert (100 <= 112)."""
     f = _lib()
     rng = np.random.default_rng(78)
-    T, k, E0, K, N = 7, 4, 6, 384, 256
+    T, k, E0, K, N = 25, 4, 6, 384, 256
+    assert T * k > ROWS16_PER_EXPERT * E0 and T * k <= ROWS16_PER_EXPERT * (E0 + 1)
     x = (rng.standard_normal((T, K)) * rng.uniform(0.1, 10, (T, 1))).astype(np.float32)
     xq, xs = quant_group(x)
     ids = np.stack([rng.permutation(E0)[:k] for _ in range(T)]).astype(np.int32)
@@ -462,7 +467,7 @@ def test_rows16_kernel_gather_equals_tile_kernel():
     wp = rng.integers(0, 256, size=(E0, N, K // 2), dtype=np.uint8)
     ws = rng.uniform(0.005, 0.02, size=(E0, N, K // 128)).astype(np.float32)
     outs = []
-    for E in (E0, E0 + 14):
+    for E in (E0, E0 + 1):
         off, sorted_, _ = group_pairs(ids, E)
         wpx, wsx, _ = _pad_experts(wp, ws, off[:E0 + 1], E - E0)
         w, s = _bank(wpx, wsx)
