@@ -16,7 +16,7 @@ Also on the line: the layer against the sum of its stages' rooflines; the layer 
 from HIP graphs (launch overhead removed; checked bit for bit against the eager layer);
 the W8A8 dense projections at 2048 x 4096 x {6144, 4096} (per-tensor, row-wise and
 block-128 scales); the layer with MXFP4 activations; the decode regime (16 tokens, M <= 16
-projections); the skewed large layer (16384 tokens, hidden 4096, 128 Zipf-routed experts,
+projections; replayed from HIP graphs, with the eager host-issued times beside them); the skewed large layer (16384 tokens, hidden 4096, 128 Zipf-routed experts,
 I = 1536) with its stage times and roofline fraction; the shader clock and the GEMM's HBM
 bytes from the committed rocprofv3 counter runs (null once the kernel source differs);
 the host CPU; and the depth stack (T=2048, L=8 by default, --stack 12 or 0): prefill
@@ -214,10 +214,30 @@ def bench_decode(steps: int = 20):
                 f.fp8_dense_gemm(xq, blk, ws[i % ROT_DECODE][0], ws[i % ROT_DECODE][1], out=y)
             b.record()
             torch.cuda.synchronize()
-            us = a.elapsed_time(b) / steps * 1e3
+            us_eager = a.elapsed_time(b) / steps * 1e3
+            # the same calls captured once in a HIP graph and replayed: the kernels' own time
+            # (issued one by one from Python, a call this small is bound by the host)
+            ref = y.clone()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for i in range(steps):
+                    f.fp8_dense_gemm(xq, blk, ws[i % ROT_DECODE][0], ws[i % ROT_DECODE][1],
+                                     out=y)
+            gr.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(y, ref):
+                raise RuntimeError("decode W8A8 graph replay differs from the eager call")
+            reps = 5
+            a.record()
+            for _ in range(reps):
+                gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / (reps * steps) * 1e3
             nbytes = N * K + M * K + 2 * M * N
             res[f"M{M}_N{N}_K{K}"] = {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9,
-                                      "frac_hbm": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+                                      "frac_hbm": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                      "us_eager": us_eager}
     return res
 
 
@@ -586,9 +606,14 @@ def bench_decode_regime(c, xs, lgs, banks, dev) -> dict:
         rd.run(xs[i % len(banks)][:Td], lgs[i % len(banks)][:Td], banks[i % len(banks)])
     b.record()
     torch.cuda.synchronize()
-    us = a.elapsed_time(b) / 30 * 1e3
+    us_eager = a.elapsed_time(b) / 30 * 1e3
+    # replayed from HIP graphs (checked bit for bit against the eager layer): the GPU's own
+    # time; issued call by call from Python the 16-token layer is close to host-bound
+    xd = [x[:Td] for x in xs[:len(banks)]]
+    ld = [lg[:Td] for lg in lgs[:len(banks)]]
+    us = time_graph_replay(rd, xd, ld, list(banks), 30) * 1e3
     bank_bytes = 3 * c.E * c.H * c.I // 2 + 3 * c.E * c.H * c.I * 4 // 128
-    out["decode_moe"] = {"tokens": Td, "us_per_layer": us,
+    out["decode_moe"] = {"tokens": Td, "us_per_layer": us, "us_per_layer_eager": us_eager,
                          "bank_GBps": bank_bytes / (us * 1e-6) / 1e9,
                          "frac_hbm": bank_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
     out["decode_w8a8"] = bench_decode()
