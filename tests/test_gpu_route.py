@@ -147,3 +147,19 @@ def test_quant_route_equals_the_two_calls(T, H, E, k, with_sums):
     for name in ("ids", "weights", "offsets", "sorted", "pos"):
         assert_bytes_equal(host(r[name]), host(rr[name]), name)
     _check(logits, k, {n: host(t) for n, t in r.items()})
+
+
+@pytest.mark.parametrize("T,E,k", [
+    (16384, 64, 8),   # C * E = 1024 * 64 = 65536: the largest table scanned inside the scatter
+    (16400, 64, 8),   # 1025 chunks: one past it, the separate chunk scan
+    (4000, 256, 4),   # E = 256, one thread per expert in the scatter's table sums
+    (1000, 257, 4),   # E = 257: past the scatter's scan, the separate chunk scan
+    (333, 3, 2),      # E = 3: 85 threads per expert over interleaved chunks, one idle
+])
+def test_scan_inside_scatter_and_separate_scan(T, E, k):
+    """Both ways of forming the per-expert chunk bases (the scan inside the scatter for small
+    count tables, the separate scan kernel otherwise) against the oracle, bit for bit, at
+    shapes on both sides of the limit and with ties in the logits."""
+    rng = np.random.default_rng(T + E)
+    lg = np.round(rng.standard_normal((T, E)) * 4).astype(np.float32) / 4  # many exact ties
+    _check(lg, k, _gpu_route(lg, k))
