@@ -26,7 +26,7 @@ rooflines (FP8 parts at the FP8 peak, bf16 parts at the bf16 peak).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] [--no-dense]
                     [--no-skewed] [--no-mxfp4] [--no-decode] [--stack {0,8,12}]
-                    [--stack-only] [--layer-only]
+                    [--stack-only] [--layer-only] [--decode-only]
 """
 
 from __future__ import annotations
@@ -71,6 +71,9 @@ def _parse():
                     help="skip the decode-regime timings (16-token layer, M <= 16 projections)")
     ap.add_argument("--stack-only", action="store_true",
                     help="time only the depth stack (for profiling it alone)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode regime (16-token layer, M <= 16 projections): "
+                         "for profiling it alone")
     ap.add_argument("--layer-only", action="store_true",
                     help="time only the 4096-token layer (no graph replay, clock sampling, "
                          "dense, MXFP4, decode, stack, skewed or CPU legs): for counter runs")
@@ -324,6 +327,19 @@ def main():
         banks.append(f.ExpertBank.from_host(inp, dev))
     runner = f.MoELayerRunner(c.T, c.H, c.E, c.k, c.I, dev)
     R = c.T * c.k
+
+    if args.decode_only:
+        d = bench_decode_regime(c, xs, lgs, banks, dev)
+        print(json.dumps({"metric": "decode MoE layer us (16 tokens)",
+                          "value": d["decode_moe"]["us_per_layer"], "unit": "us",
+                          "n_gpus": 1, "steps": 30, "warmup": 3,
+                          "ms_per_step": d["decode_moe"]["us_per_layer"] * 1e-3,
+                          "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+                          "dtype": "e4m3", "data": "synthetic",
+                          "config": {"workload": "decode_moe: the 64-expert layer (hidden "
+                                                 "2048, top-8, intermediate 768) at 16 tokens"},
+                          **d}))
+        return
 
     for i in range(args.warmup):
         runner.run(xs[i % ROT], lgs[i % ROT], banks[i % ROT])

@@ -20,6 +20,8 @@
 //                  writes sorted[] and pos[].
 //   4. gather:     optional copies of the e4m3 rows and (group-major) scales into grouped
 //                  order.
+// A batch of one chunk (at most 16 tokens, decode sizes) skips steps 2 and 3 as launches:
+// its top-k workgroup scans its own histogram and places the pairs itself.
 #include <mutex>
 
 #include "common.h"
@@ -88,14 +90,32 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // picks the k best one at a time: the wave maximum of the orderable values of the untaken
 // experts, then, among the experts holding it, the lowest index (a ballot per lane slot,
 // the lowest slot and lane first), whose value is cleared.
+//
+// One chunk only (T <= kRouteChunk, offsets given): the grouping follows in the same
+// workgroup. The exclusive scan of the histogram is the expert offsets, and routed pair i
+// (token-major) goes to grouped row offsets[e] + the number of pairs j < i routed to the
+// same expert e: the rows the separate scan and scatter launches give a first chunk. A
+// token's k picks are distinct experts, so those earlier pairs are one per earlier token
+// that picked e: a bit per token in a per-expert mask (OR commutes), counted by popcount.
 template <int NJ>  // experts per lane: E <= 64 * NJ
 __device__ __forceinline__ void topk_hist_block(const float* __restrict__ logits, int64_t T,
                                                 int E, int k, int32_t* __restrict__ ids,
                                                 float* __restrict__ wts,
                                                 int32_t* __restrict__ cnt, int64_t blk,
-                                                int* hist /* LDS [kMaxE] */) {
+                                                int* hist /* LDS [kMaxE] */,
+                                                int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ sorted,
+                                                int32_t* __restrict__ pos) {
+  static_assert(kMaxE == kRouteChunk * 64, "one expert per thread in the one-chunk scan");
+  static_assert(kRouteChunk <= 32, "one mask bit per token of the chunk");
+  __shared__ uint32_t s_mask[kMaxE];  // one chunk: bit t set if token t picked the expert
+  __shared__ int s_wtot[kRouteChunk];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += kRouteChunk * 64) hist[e] = 0;
+  for (int e = threadIdx.x; e < E; e += kRouteChunk * 64) {
+    hist[e] = 0;
+    if (offsets != nullptr) s_mask[e] = 0u;
+  }
+  int pick = -1;  // this lane's expert, lanes < k of a wave with a token
   __syncthreads();
   const int64_t t = blk * kRouteChunk + wv;
   if (t < T) {  // wave-uniform
@@ -142,20 +162,48 @@ __device__ __forceinline__ void topk_hist_block(const float* __restrict__ logits
       ids[t * k + lane] = my_i;
       wts[t * k + lane] = ex / sum;
       atomicAdd(&hist[my_i], 1);
+      if (offsets != nullptr) atomicOr(&s_mask[my_i], 1u << wv);  // blk = 0: token wv
+      pick = my_i;
     }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kRouteChunk * 64)
     cnt[blk * E + e] = hist[e];
+  if (offsets == nullptr) return;  // uniform (a kernel argument)
+  // exclusive scan of the histogram, one expert per thread: within each wave, then the
+  // totals of the earlier waves
+  const int e = threadIdx.x;
+  const int v = e < E ? hist[e] : 0;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) s_wtot[wv] = inc;
+  __syncthreads();
+  for (int j = 0; j < wv; ++j) inc += s_wtot[j];
+  if (e < E) {
+    hist[e] = inc - v;  // thread e alone read hist[e], before the barrier
+    offsets[e] = inc - v;
+  }
+  if (e == E - 1) offsets[E] = inc;  // = T * k
+  __syncthreads();
+  if (pick >= 0) {  // pair wv * k + lane
+    const int row = hist[pick] + __popc(s_mask[pick] & ((1u << wv) - 1u));
+    sorted[row] = wv * k + lane;
+    pos[wv * k + lane] = row;
+  }
 }
 
 
 template <int NJ>
 __global__ __launch_bounds__(kRouteChunk * 64) void topk_hist_kernel(
     const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ ids,
-    float* __restrict__ wts, int32_t* __restrict__ cnt) {
+    float* __restrict__ wts, int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
   __shared__ int hist[kMaxE];
-  topk_hist_block<NJ>(logits, T, E, k, ids, wts, cnt, blockIdx.x, hist);
+  topk_hist_block<NJ>(logits, T, E, k, ids, wts, cnt, blockIdx.x, hist, offsets, sorted, pos);
 }
 
 // The group quantiser and the top-k selection in one launch: they are independent (the
@@ -171,12 +219,13 @@ __global__ __launch_bounds__(kRouteChunk * 64) void quant_topk_kernel(
     const uint4* __restrict__ x, int64_t nchunks, uint2* __restrict__ q,
     float* __restrict__ scales, float* __restrict__ sums, int64_t nqblocks,
     const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ ids,
-    float* __restrict__ wts, int32_t* __restrict__ cnt, int64_t C) {
+    float* __restrict__ wts, int32_t* __restrict__ cnt, int64_t C, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
   static_assert(kRouteChunk * 64 == 4 * 256, "one workgroup = four quantiser blocks");
   __shared__ int hist[kMaxE];
   const int64_t b = blockIdx.x;
   if (b < C) {
-    topk_hist_block<NJ>(logits, T, E, k, ids, wts, cnt, b, hist);
+    topk_hist_block<NJ>(logits, T, E, k, ids, wts, cnt, b, hist, offsets, sorted, pos);
   } else {
     const int tid = (int)threadIdx.x;
     qg::group_block<kQuantRouteChunks>(x, nchunks, q, scales, sums, (b - C) * 4 + (tid >> 8),
@@ -393,8 +442,10 @@ hipError_t launch_route_tail(int64_t T, int32_t E, int32_t k, const int32_t* ids
   const int64_t C = (T + kRouteChunk - 1) / kRouteChunk;
   int32_t* cnt = static_cast<int32_t*>(ws);
   int32_t* tot = cnt + C * E;
-  hipError_t e;
-  if (E <= 256 && C * E <= kScanInScatter) {
+  hipError_t e = hipSuccess;
+  if (C == 1) {
+    // one chunk: the top-k workgroup has already written offsets, sorted and pos
+  } else if (E <= 256 && C * E <= kScanInScatter) {
     scatter_scan_kernel<<<dim3((uint32_t)C), 256, 0, st>>>(ids, T, E, k, cnt, C, offsets,
                                                            sorted, pos);
   } else {
@@ -430,12 +481,16 @@ hipError_t launch_route_permute(const float* logits, int64_t T, int32_t E, int32
   int64_t C = (T + kRouteChunk - 1) / kRouteChunk;
   int32_t* cnt = static_cast<int32_t*>(ws);
   const dim3 grid((uint32_t)C), block(kRouteChunk * 64);
+  // one chunk: the top-k workgroup also writes the grouping
+  int32_t* o1 = C == 1 ? offsets : nullptr;
+  int32_t* s1 = C == 1 ? sorted : nullptr;
+  int32_t* p1 = C == 1 ? pos : nullptr;
   if (E <= 64)
-    topk_hist_kernel<1><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt);
+    topk_hist_kernel<1><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt, o1, s1, p1);
   else if (E <= 256)
-    topk_hist_kernel<4><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt);
+    topk_hist_kernel<4><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt, o1, s1, p1);
   else
-    topk_hist_kernel<16><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt);
+    topk_hist_kernel<16><<<grid, block, 0, st>>>(logits, T, E, k, ids, w, cnt, o1, s1, p1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_route_tail(T, E, k, ids, offsets, sorted, pos, xq, xs, H, xq_perm, xs_perm,
@@ -454,15 +509,18 @@ hipError_t launch_quant_route(const uint16_t* x, int64_t H, uint8_t* q, float* s
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint2* qv = reinterpret_cast<uint2*>(q);
   const dim3 grid((uint32_t)(C + nq)), block(kRouteChunk * 64);
+  int32_t* o1 = C == 1 ? offsets : nullptr;  // one chunk: the grouping in the same launch
+  int32_t* s1 = C == 1 ? sorted : nullptr;
+  int32_t* p1 = C == 1 ? pos : nullptr;
   if (E <= 64)
     quant_topk_kernel<1><<<grid, block, 0, st>>>(xv, nchunks, qv, scales, sums, 4 * nq, logits,
-                                                  T, E, k, ids, w, cnt, C);
+                                                  T, E, k, ids, w, cnt, C, o1, s1, p1);
   else if (E <= 256)
     quant_topk_kernel<4><<<grid, block, 0, st>>>(xv, nchunks, qv, scales, sums, 4 * nq, logits,
-                                                  T, E, k, ids, w, cnt, C);
+                                                  T, E, k, ids, w, cnt, C, o1, s1, p1);
   else
     quant_topk_kernel<16><<<grid, block, 0, st>>>(xv, nchunks, qv, scales, sums, 4 * nq,
-                                                   logits, T, E, k, ids, w, cnt, C);
+                                                   logits, T, E, k, ids, w, cnt, C, o1, s1, p1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_route_tail(T, E, k, ids, offsets, sorted, pos, nullptr, nullptr, H, nullptr,

@@ -163,3 +163,30 @@ def test_scan_inside_scatter_and_separate_scan(T, E, k):
     rng = np.random.default_rng(T + E)
     lg = np.round(rng.standard_normal((T, E)) * 4).astype(np.float32) / 4  # many exact ties
     _check(lg, k, _gpu_route(lg, k))
+
+
+@pytest.mark.parametrize("T", [1, 7, 16, 17])
+@pytest.mark.parametrize("E,k", [(1, 1), (3, 2), (64, 8), (257, 32), (1024, 32), (1024, 1)])
+def test_one_chunk_grouping_in_the_topk_launch(T, E, k):
+    """A batch of at most 16 tokens (one chunk) is grouped by the top-k workgroup itself (its
+    histogram scanned for the offsets, the pairs ranked in LDS); 17 tokens take the separate
+    launches. Both against the oracle, bit for bit, with ties in the logits, through
+    moe_route_permute (with the row and scale gather) and through the fused quantiser +
+    routing call."""
+    import fp8_moe_prefill_amd as f
+    from synth import bf16_bits_from_f32
+    rng = np.random.default_rng(1000 * T + E + k)
+    lg = np.round(rng.standard_normal((T, E)) * 2).astype(np.float32) / 2  # many exact ties
+    H = 256
+    xq = rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+    xs = rng.uniform(0.001, 1, size=(T, H // 128)).astype(np.float32)
+    gpu = _gpu_route(lg, k, xq, xs)
+    _, _, sorted_, _ = _check(lg, k, gpu)
+    assert_bytes_equal(gpu["xq_perm"], permute_rows(xq, sorted_, k), "gathered rows")
+    assert_bytes_equal(gpu["xs_perm"].view(np.uint32),
+                       np.ascontiguousarray(permute_rows(xs, sorted_, k).T).view(np.uint32),
+                       "gathered scales")
+    x = bf16_bits_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+    q, s, _, r = f.quant_route(dev(x), dev(lg), k)
+    torch.cuda.synchronize()
+    _check(lg, k, {n: host(t) for n, t in r.items()})
