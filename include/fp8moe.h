@@ -185,7 +185,8 @@ int32_t moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t k,
  * [P1] section 1 runs the activation quantiser and the routing/grouping ahead of the one
  * grouped GEMM per layer. The two read different inputs, so the library runs the
  * quantiser and the top-k selection in one launch (the top-k waits on dependent picks,
- * the quantiser on HBM) and then the rest of the routing.
+ * the quantiser on HBM) and then the rest of the routing (for T <= 16 that launch also
+ * groups the pairs, and no other follows).
  *
  *   x, q, scales, sums   as fp8_quant_act with M = T, K = H, group = FP8MOE_GROUP
  *                        (sums may be NULL)
