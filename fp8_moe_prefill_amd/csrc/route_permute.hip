@@ -84,6 +84,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Rank of a routed pair among the earlier pairs of its chunk routed to the same expert, the
+// order a stable grouping keeps. A token's k picks are distinct experts, so those earlier
+// pairs are one per earlier token of the chunk that picked the expert: with bit t of
+// `mask` set when token t of the chunk picked it (set by LDS ORs, which commute), the rank
+// is the number of bits below the pair's own token.
+__device__ __forceinline__ int chunk_rank(uint32_t mask, int token_in_chunk) {
+  static_assert(kRouteChunk <= 32, "one mask bit per token of the chunk");
+  return __popc(mask & ((1u << token_in_chunk) - 1u));
+}
+
 // Top-k of each token and the per-chunk expert histogram. A workgroup owns a chunk of
 // kRouteChunk tokens, one wave per token (the k picks of a token are a dependent chain,
 // so the tokens of a chunk run side by side); lane e holds experts e, e+64, ... The wave
@@ -94,9 +104,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // One chunk only (T <= kRouteChunk, offsets given): the grouping follows in the same
 // workgroup. The exclusive scan of the histogram is the expert offsets, and routed pair i
 // (token-major) goes to grouped row offsets[e] + the number of pairs j < i routed to the
-// same expert e: the rows the separate scan and scatter launches give a first chunk. A
-// token's k picks are distinct experts, so those earlier pairs are one per earlier token
-// that picked e: a bit per token in a per-expert mask (OR commutes), counted by popcount.
+// same expert e (chunk_rank): the rows the separate scan and scatter launches give a first
+// chunk.
 template <int NJ>  // experts per lane: E <= 64 * NJ
 __device__ __forceinline__ void topk_hist_block(const float* __restrict__ logits, int64_t T,
                                                 int E, int k, int32_t* __restrict__ ids,
@@ -107,7 +116,6 @@ __device__ __forceinline__ void topk_hist_block(const float* __restrict__ logits
                                                 int32_t* __restrict__ sorted,
                                                 int32_t* __restrict__ pos) {
   static_assert(kMaxE == kRouteChunk * 64, "one expert per thread in the one-chunk scan");
-  static_assert(kRouteChunk <= 32, "one mask bit per token of the chunk");
   __shared__ uint32_t s_mask[kMaxE];  // one chunk: bit t set if token t picked the expert
   __shared__ int s_wtot[kRouteChunk];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -190,7 +198,7 @@ __device__ __forceinline__ void topk_hist_block(const float* __restrict__ logits
   if (e == E - 1) offsets[E] = inc;  // = T * k
   __syncthreads();
   if (pick >= 0) {  // pair wv * k + lane
-    const int row = hist[pick] + __popc(s_mask[pick] & ((1u << wv) - 1u));
+    const int row = hist[pick] + chunk_rank(s_mask[pick], wv);
     sorted[row] = wv * k + lane;
     pos[wv * k + lane] = row;
   }
@@ -263,7 +271,9 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
                                                       int32_t* __restrict__ pos) {
   __shared__ int s_off[kMaxE + 1];
   __shared__ int s_e[kRouteChunk * kMaxK];
+  __shared__ uint32_t s_mask[kMaxE];  // bit t: token t of the chunk picked the expert
   __shared__ int tmp[4];
+  for (int e = threadIdx.x; e < E; e += 256) s_mask[e] = 0u;  // ordered by the scan's barriers
   // expert offsets: exclusive scan of the totals, 4 experts per thread
   int loc[4];
   int sum = 0;
@@ -287,14 +297,17 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   int64_t pend = (c + 1) * kRouteChunk;
   if (pend > T) pend = T;
   const int np = (int)(pend * k - p0);
-  for (int i = threadIdx.x; i < np; i += 256) s_e[i] = ids[p0 + i];
+  for (int i = threadIdx.x; i < np; i += 256) {
+    const int e = ids[p0 + i];
+    s_e[i] = e;
+    atomicOr(&s_mask[e], 1u << (i / k));
+  }
   __syncthreads();
   if (c == 0)
     for (int e = threadIdx.x; e <= E; e += 256) offsets[e] = s_off[e];
   for (int i = threadIdx.x; i < np; i += 256) {
-    int e = s_e[i];
-    int rank = 0;
-    for (int j = 0; j < i; ++j) rank += (s_e[j] == e);
+    const int e = s_e[i];
+    const int rank = chunk_rank(s_mask[e], i / k);
     int row = s_off[e] + cbase[c * E + e] + rank;
     sorted[row] = (int32_t)(p0 + i);
     pos[p0 + i] = row;
@@ -318,10 +331,12 @@ __global__ __launch_bounds__(256) void scatter_scan_kernel(const int32_t* __rest
   __shared__ int s_base[256];
   __shared__ int s_tot[256], s_bef[256];
   __shared__ int s_e[kRouteChunk * kMaxK];
+  __shared__ uint32_t s_mask[256];  // bit t: token t of the chunk picked the expert
   __shared__ int tmp[4];
   const int64_t c = blockIdx.x;
   const int t = threadIdx.x;
   const int S = 256 / E;  // threads per expert
+  if (t < E) s_mask[t] = 0u;  // ordered by the barriers below
   {
     const int e = t % E, sl = t / E;
     int tot = 0, bef = 0;
@@ -356,14 +371,17 @@ __global__ __launch_bounds__(256) void scatter_scan_kernel(const int32_t* __rest
   int64_t pend = (c + 1) * kRouteChunk;
   if (pend > T) pend = T;
   const int np = (int)(pend * k - p0);
-  for (int i = t; i < np; i += 256) s_e[i] = ids[p0 + i];
+  for (int i = t; i < np; i += 256) {
+    const int e = ids[p0 + i];
+    s_e[i] = e;
+    atomicOr(&s_mask[e], 1u << (i / k));
+  }
   __syncthreads();
   if (c == 0)
     for (int e = t; e <= E; e += 256) offsets[e] = s_off[e];
   for (int i = t; i < np; i += 256) {
     const int e = s_e[i];
-    int rank = 0;
-    for (int j = 0; j < i; ++j) rank += (s_e[j] == e);
+    const int rank = chunk_rank(s_mask[e], i / k);
     const int row = s_off[e] + s_base[e] + rank;
     sorted[row] = (int32_t)(p0 + i);
     pos[p0 + i] = row;
